@@ -1,0 +1,182 @@
+/*
+ * CPU oracle for the BitNet b1.58 BitLinear forward pass.
+ * TEST INFRASTRUCTURE ONLY -- see oracle.h for the sources and the readings.
+ *
+ * Plain single-threaded C11, built with -O2 -ffp-contract=off and without
+ * -ffast-math, so every fp32 operation below is one IEEE-754 round-to-nearest
+ * operation in the order written. nearbyintf runs under the default
+ * FE_TONEAREST mode, i.e. ties go to the even integer.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <string.h>
+
+static float bf16_bits_to_float(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Round an fp32 value to bf16 bits, nearest with ties to even (finite input). */
+static uint16_t float_to_bf16_bits(float f) {
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    uint32_t lsb = (u >> 16) & 1u;
+    u += 0x7FFFu + lsb;
+    return (uint16_t)(u >> 16);
+}
+
+/* Mean absolute value of the whole matrix [P3a]: fp64 row sums in order. */
+void oracle_absmean_rowsums(const float* W, int64_t N, int64_t K, double* R) {
+    for (int64_t n = 0; n < N; ++n) {
+        const float* row = W + n * K;
+        double s = 0.0;
+        for (int64_t k = 0; k < K; ++k) s += (double)fabsf(row[k]);
+        R[n] = s;
+    }
+}
+
+float oracle_absmean_gamma(const float* W, int64_t N, int64_t K) {
+    double total = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+        const float* row = W + n * K;
+        double s = 0.0;
+        for (int64_t k = 0; k < K; ++k) s += (double)fabsf(row[k]);
+        total += s;
+    }
+    return (float)(total / (double)(N * K));
+}
+
+/* Scale by the (eps-guarded) mean, take the nearest integer, clip to
+ * {-1, 0, +1} [P3a]. */
+void oracle_ternarize(const float* W, int64_t N, int64_t K, float gamma,
+                      float eps, int8_t* q) {
+    const float s = gamma + eps;
+    for (int64_t i = 0; i < N * K; ++i) {
+        float r = W[i] / s;
+        float t = nearbyintf(r);
+        if (t > 1.0f) t = 1.0f;
+        if (t < -1.0f) t = -1.0f;
+        q[i] = (int8_t)t;
+    }
+}
+
+/* Two bits per ternary weight [P3b]: code c = q + 1. */
+void oracle_pack(const int8_t* q, int64_t N, int64_t K, uint32_t* packed) {
+    const int64_t words = K / 16;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t j = 0; j < words; ++j) {
+            uint32_t w = 0;
+            for (int i = 0; i < 16; ++i) {
+                uint32_t c = (uint32_t)(q[n * K + 16 * j + i] + 1);
+                int shift = 8 * (i % 4) + 2 * (i / 4);
+                w |= c << shift;
+            }
+            packed[n * words + j] = w;
+        }
+    }
+}
+
+void oracle_unpack(const uint32_t* packed, int64_t N, int64_t K, int8_t* q) {
+    const int64_t words = K / 16;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t j = 0; j < words; ++j) {
+            uint32_t w = packed[n * words + j];
+            for (int i = 0; i < 16; ++i) {
+                int shift = 8 * (i % 4) + 2 * (i / 4);
+                q[n * K + 16 * j + i] = (int8_t)((int)((w >> shift) & 3u) - 1);
+            }
+        }
+    }
+}
+
+/* 8-bit activations [P1], per token by absmax into [-127, 127]. */
+void oracle_act_quant(const uint16_t* x, int64_t M, int64_t K,
+                      const uint16_t* gain, float rms_eps,
+                      int8_t* x_q, float* scale, double* rms_out) {
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t* row = x + m * K;
+        /* z = x * g is exact in fp32: two 8-bit significands. */
+        float a = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float z = bf16_bits_to_float(row[k]);
+            if (gain) z = z * bf16_bits_to_float(gain[k]);
+            float mag = fabsf(z);
+            if (mag > a) a = mag;
+        }
+        if (!(a > 1e-5f)) a = 1e-5f;
+        const float inv = 127.0f / a;
+        for (int64_t k = 0; k < K; ++k) {
+            float z = bf16_bits_to_float(row[k]);
+            if (gain) z = z * bf16_bits_to_float(gain[k]);
+            float t = nearbyintf(z * inv);
+            if (t > 127.0f) t = 127.0f;
+            if (t < -127.0f) t = -127.0f;
+            x_q[m * K + k] = (int8_t)t;
+        }
+        if (gain) {
+            /* RMSNorm [P1]: rms = sqrt(mean(x^2) + eps); the normalised
+             * token's absmax is a / rms. */
+            double ss = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double v = (double)bf16_bits_to_float(row[k]);
+                ss += v * v;
+            }
+            double rms = sqrt(ss / (double)K + (double)rms_eps);
+            scale[m] = (float)((double)a / (127.0 * rms));
+            if (rms_out) rms_out[m] = rms;
+        } else {
+            scale[m] = a / 127.0f;
+        }
+    }
+}
+
+/* Integer product of int8 activations and ternary weights [P3c], [P5]. */
+void oracle_int_matmul(const int8_t* x_q, int64_t M, int64_t K,
+                       const int8_t* q, int64_t N, int32_t* acc) {
+    for (int64_t m = 0; m < M; ++m) {
+        const int8_t* xr = x_q + m * K;
+        for (int64_t n = 0; n < N; ++n) {
+            const int8_t* wr = q + n * K;
+            int32_t s = 0;
+            for (int64_t k = 0; k < K; ++k) s += (int32_t)xr[k] * (int32_t)wr[k];
+            acc[m * N + n] = s;
+        }
+    }
+}
+
+void oracle_addsub_matmul(const int8_t* x_q, int64_t M, int64_t K,
+                          const int8_t* q, int64_t N, int32_t* acc) {
+    for (int64_t m = 0; m < M; ++m) {
+        const int8_t* xr = x_q + m * K;
+        for (int64_t n = 0; n < N; ++n) {
+            const int8_t* wr = q + n * K;
+            int32_t plus = 0, minus = 0;
+            for (int64_t k = 0; k < K; ++k) {
+                if (wr[k] == 1) plus += xr[k];
+                else if (wr[k] == -1) minus += xr[k];
+            }
+            acc[m * N + n] = plus - minus;
+        }
+    }
+}
+
+/* Rescale of the integer result [P1]. */
+void oracle_epilogue(const int32_t* acc, int64_t M, int64_t N,
+                     const float* scale, float gamma, float* y) {
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            y[m * N + n] = (float)((double)acc[m * N + n] * (double)scale[m] *
+                                   (double)gamma);
+}
+
+void oracle_relu2_glu(const float* g, const float* u, int64_t count,
+                      uint16_t* h) {
+    for (int64_t i = 0; i < count; ++i) {
+        float r = g[i] > 0.0f ? g[i] : 0.0f;
+        float sq = r * r;
+        h[i] = float_to_bf16_bits(sq * u[i]);
+    }
+}
