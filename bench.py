@@ -1,0 +1,377 @@
+#!/usr/bin/env python3
+"""BitLinear forward benchmark on one MI355X.
+
+Headline (`value`): decode packed-weight GB/s of a 2B4T-shaped FFN stack
+(gate/up 2560 -> 6912, squared-ReLU gating, down 6912 -> 2560) at M = 1, 4
+and 16 tokens. One step runs, for each M and each of L layers: per-token act
+quant -> gate and up BitLinears -> relu(gate)^2 * up -> act quant -> down
+BitLinear. The L layers hold distinct copies of the packed weights (identical
+content, distinct addresses) whose total exceeds twice the 256 MB Infinity
+Cache, so every BitLinear streams its weights from HBM. Weights are quantised
+once before the timed region (offline in the method); that pass is timed and
+reported separately. The step is captured in a HIP graph and replayed.
+
+Also reported: the decode GEMV's roofline (per-launch HIP-event timing of the
+same launches), the prefill GEMM at M = 4096 (int8 TOPS against the MFMA
+peak), and the CPU oracle timed on a bounded sample of the decode step.
+
+    python bench.py [--steps K] [--warmup W] [--layers L]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "BitLinear decode packed-weight GB/s (% HBM peak); prefill int8 TOPS (% MFMA)"
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
+I8_PEAK_TOPS = 5000.0       # MI355X dense int8 MFMA, published
+DECODE_WORKLOAD = 2         # 2B4T-shaped FFN at decode
+PREFILL_WORKLOAD = 3        # one 4096-token sequence
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__,
+                                formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--layers", type=int, default=40,
+                   help="distinct weight copies per projection (default 40: 531 MB)")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="CPU-oracle sample budget (0 disables the leg)")
+    p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-graph", action="store_true", help="time eager launches instead")
+    return p.parse_args()
+
+
+def host_info():
+    cpu = platform.processor()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return cpu, os.cpu_count()
+
+
+class Timer:
+    """Per-launch HIP event pairs on the launching (current) stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def run(self, key, fn):
+        t = self.torch
+        a = t.cuda.Event(enable_timing=True)
+        b = t.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        self.pairs.setdefault(key, []).append((a, b))
+
+    def total_ms(self, key):
+        return sum(a.elapsed_time(b) for a, b in self.pairs.get(key, []))
+
+    def count(self, key):
+        return len(self.pairs.get(key, []))
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the BitLinear path here runs on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import ternary_weight_linear_quant_amd as bl
+    from ternary_weight_linear_quant_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    bl.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+
+    def bf16_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev) \
+            .view(torch.bfloat16)
+
+    # ------------------------------------------------ decode workload ----
+    _, projs, Ms = wl.WORKLOADS[DECODE_WORKLOAD]
+    shapes = {name: (K, N) for name, K, N in projs}
+    Wdev = {name: torch.from_numpy(wl.weights(DECODE_WORKLOAD, i, N, K)).to(dev)
+            for i, (name, K, N) in enumerate(projs)}
+
+    # Weight preparation (offline): timed once per matrix after a warm call.
+    base = {}
+    wp_ms = 0.0
+    wp_bytes = 0
+    for name, W in Wdev.items():
+        bl.quantize_weights(W)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        base[name] = bl.quantize_weights(W)
+        b.record()
+        torch.cuda.synchronize()
+        wp_ms += a.elapsed_time(b)
+        wp_bytes += W.numel() * 4
+    del Wdev
+
+    L = args.layers
+    layers = [{name: (pk.clone(), g.clone()) for name, (pk, g) in base.items()}
+              for _ in range(L)]
+    packed_per_layer = sum(pk.numel() * 4 for pk, _ in base.values())
+
+    Kin, Nff = shapes["gate"]
+    bufs = {}
+    for M in Ms:
+        x = bf16_dev(wl.activations(DECODE_WORKLOAD, 9, M, Kin))
+        bufs[M] = dict(
+            x=x,
+            xq=torch.empty((M, Kin), dtype=torch.int8, device=dev),
+            xs=torch.empty(M, dtype=torch.float32, device=dev),
+            yg=torch.empty((M, Nff), dtype=torch.float32, device=dev),
+            yu=torch.empty((M, Nff), dtype=torch.float32, device=dev),
+            h=torch.empty((M, Nff), dtype=torch.bfloat16, device=dev),
+            hq=torch.empty((M, Nff), dtype=torch.int8, device=dev),
+            hs=torch.empty(M, dtype=torch.float32, device=dev),
+            yd=torch.empty((M, Kin), dtype=torch.float32, device=dev),
+        )
+
+    def decode_step(timer=None):
+        def run(key, fn):
+            if timer is None:
+                fn()
+            else:
+                timer.run(key, fn)
+        for M in Ms:
+            B = bufs[M]
+            for lay in layers:
+                run("act_quant", lambda: bl.quantize_acts(B["x"], out=(B["xq"], B["xs"])))
+                run(("gemv", M, "gate"), lambda: bl.bitlinear(B["xq"], B["xs"], *lay["gate"],
+                                                              out=B["yg"]))
+                run(("gemv", M, "up"), lambda: bl.bitlinear(B["xq"], B["xs"], *lay["up"],
+                                                            out=B["yu"]))
+                run("glue", lambda: bl.relu2_glu(B["yg"], B["yu"], out=B["h"]))
+                run("act_quant", lambda: bl.quantize_acts(B["h"], out=(B["hq"], B["hs"])))
+                run(("gemv", M, "down"), lambda: bl.bitlinear(B["hq"], B["hs"], *lay["down"],
+                                                              out=B["yd"]))
+
+    decode_step()
+    torch.cuda.synchronize()
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            decode_step()
+        torch.cuda.synchronize()
+
+    def replay():
+        if graph is not None:
+            graph.replay()
+        else:
+            decode_step()
+
+    for _ in range(args.warmup):
+        replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    packed_per_step = packed_per_layer * L * len(Ms)
+    value = packed_per_step / (ms_per_step * 1e-3) / 1e9
+
+    # Per-launch event timing of the same decode launches (eager, same buffers).
+    timer = Timer(torch)
+    decode_step(timer)
+    torch.cuda.synchronize()
+    gemv_ms = 0.0
+    gemv_launches = 0
+    gemv_bytes = 0
+    per_shape = {}
+    for M in Ms:
+        for name, (K, N) in shapes.items():
+            key = ("gemv", M, name)
+            ms = timer.total_ms(key)
+            n = timer.count(key)
+            alg = N * K // 4 + M * K + 4 * M + 4 + 4 * M * N
+            gemv_ms += ms
+            gemv_launches += n
+            gemv_bytes += alg * n
+            per_shape[f"M{M}_{name}"] = {
+                "avg_us": round(1e3 * ms / n, 3),
+                "GBps": round(alg * n / (ms * 1e-3) / 1e9, 1)}
+    achieved = gemv_bytes / (gemv_ms * 1e-3) / 1e9
+    roofline = {
+        "bound": "hbm", "kernel": "k_gemv (decode GEMV, all launches of one step)",
+        "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+        "launches": gemv_launches, "avg_us": round(1e3 * gemv_ms / gemv_launches, 3),
+        "alg_bytes_per_launch": round(gemv_bytes / gemv_launches),
+        "per_shape": per_shape,
+        "act_quant_avg_us": round(1e3 * timer.total_ms("act_quant") / timer.count("act_quant"), 3),
+        "glue_avg_us": round(1e3 * timer.total_ms("glue") / timer.count("glue"), 3),
+    }
+    used_graph = graph is not None
+    del layers, graph, timer
+    torch.cuda.empty_cache()
+    print(f"decode: {value:.1f} GB/s per step, GEMV {achieved:.1f} GB/s", file=sys.stderr,
+          flush=True)
+
+    # ------------------------------------------------ prefill GEMM leg ----
+    prefill = None
+    if not args.no_prefill:
+        _, pprojs, pMs = wl.WORKLOADS[PREFILL_WORKLOAD]
+        Mp = pMs[0]
+        legs = []
+        for i, (name, K, N) in enumerate(pprojs):
+            W = torch.from_numpy(wl.weights(PREFILL_WORKLOAD, i, N, K)).to(dev)
+            pk, g = bl.quantize_weights(W)
+            del W
+            x = bf16_dev(wl.activations(PREFILL_WORKLOAD, i, Mp, K))
+            xq, xs = bl.quantize_acts(x)
+            y = torch.empty((Mp, N), dtype=torch.float32, device=dev)
+            legs.append((name, K, N, x, xq, xs, pk, g, y))
+
+        def prefill_step(timer=None):
+            for name, K, N, x, xq, xs, pk, g, y in legs:
+                if timer is None:
+                    bl.quantize_acts(x, out=(xq, xs))
+                    bl.bitlinear(xq, xs, pk, g, out=y)
+                else:
+                    timer.run("act_quant", lambda: bl.quantize_acts(x, out=(xq, xs)))
+                    timer.run(("gemm", name), lambda: bl.bitlinear(xq, xs, pk, g, out=y))
+
+        prefill_step()
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            prefill_step()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        reps = max(5, args.steps)
+        a.record()
+        for _ in range(reps):
+            prefill_step()
+        b.record()
+        torch.cuda.synchronize()
+        p_ms = a.elapsed_time(b) / reps
+        ops = sum(2 * Mp * N * K for _, K, N, *_ in legs)
+        tp = Timer(torch)
+        for _ in range(reps):
+            prefill_step(tp)
+        torch.cuda.synchronize()
+        per = {}
+        gemm_ms = 0.0
+        gemm_n = 0
+        for name, K, N, *_ in legs:
+            ms = tp.total_ms(("gemm", name))
+            n = tp.count(("gemm", name))
+            gemm_ms += ms
+            gemm_n += n
+            per[name] = {"M": Mp, "K": K, "N": N, "avg_us": round(1e3 * ms / n, 2),
+                         "TOPS": round(2 * Mp * N * K * n / (ms * 1e-3) / 1e12, 1)}
+        gemm_tops = ops * reps / (gemm_ms * 1e-3) / 1e12
+        prefill = {
+            "workload": "prefill_4096 (M=4096; up 2560->6912, down 6912->2560)",
+            "ms_per_step": round(p_ms, 4),
+            "step_TOPS": round(ops / (p_ms * 1e-3) / 1e12, 1),
+            "roofline": {"bound": "mfma", "kernel": "k_gemm", "achieved": round(gemm_tops, 1),
+                         "peak": I8_PEAK_TOPS, "unit": "TOPS",
+                         "frac": round(gemm_tops / I8_PEAK_TOPS, 4), "traffic": None,
+                         "per_projection": per},
+            "act_quant_avg_us": round(1e3 * tp.total_ms("act_quant") / tp.count("act_quant"), 2),
+        }
+        del legs
+        torch.cuda.empty_cache()
+        print(f"prefill: GEMM {gemm_tops:.1f} TOPS", file=sys.stderr, flush=True)
+
+    # ------------------------------------------------ CPU oracle leg ----
+    cpu_baseline = None
+    if args.cpu_seconds > 0:
+        import oracle
+        codes = {}
+        for i, (name, K, N) in enumerate(projs):
+            _, g_ref, q_ref = oracle.quantize_weights(wl.weights(DECODE_WORKLOAD, i, N, K))
+            codes[name] = (q_ref, g_ref)
+        xs_host = {M: wl.activations(DECODE_WORKLOAD, 9, M, Kin) for M in Ms}
+        layers_done = 0
+        t_start = time.perf_counter()
+        while True:
+            for M in Ms:
+                xq, sc = oracle.act_quant(xs_host[M])
+                yg = oracle.epilogue(oracle.int_matmul(xq, codes["gate"][0]), sc, codes["gate"][1])
+                yu = oracle.epilogue(oracle.int_matmul(xq, codes["up"][0]), sc, codes["up"][1])
+                h = oracle.relu2_glu(yg, yu)
+                hq, hs = oracle.act_quant(h)
+                oracle.epilogue(oracle.int_matmul(hq, codes["down"][0]), hs, codes["down"][1])
+            layers_done += 1
+            el = time.perf_counter() - t_start
+            if el >= args.cpu_seconds:
+                break
+        cpu_value = packed_per_layer * len(Ms) * layers_done / el / 1e9
+        cpu_baseline = {
+            "value": round(cpu_value, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{layers_done} layer(s) of the decode step (M=1,4,16; gate, up, glue, "
+                      f"down; act quant, int matmul, epilogue) in {el:.1f} s, single-threaded "
+                      f"C oracle, weights pre-quantised like the GPU step",
+        }
+
+    cpu_model, ncpu = host_info()
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {
+            "workload": "ffn_2b4t_decode: gate/up 2560->6912, relu^2 gating, down 6912->2560",
+            "tokens_per_pass": list(Ms), "layers": L,
+            "packed_weight_bytes_per_step": packed_per_step,
+            "hip_graph": used_graph,
+            "parallelism": "single GPU",
+        },
+        "frac_hbm_step": round(value / HBM_PEAK_GBS, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu_baseline,
+        "prefill": prefill,
+        "weight_prep": {"matrices": list(base), "ms_total": round(wp_ms, 3),
+                        "fp32_read_GBps": round(wp_bytes / (wp_ms * 1e-3) / 1e9, 1)},
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "host_cpu": cpu_model, "host_nproc": ncpu},
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,160 @@
+/*
+ * bitlinear.h -- C ABI of the MI355X (gfx950) BitNet b1.58 BitLinear library.
+ *
+ * The library computes the BitLinear forward pass: latent weights are
+ * quantised once to ternary codes {-1, 0, +1} with one scale per matrix and
+ * stored at 2 bits per weight; activations are quantised per token to int8;
+ * their product is accumulated exactly in int32 and rescaled to fp32.
+ *
+ * Sources (prose only; the pages print no formula or listing):
+ *   comrad404.com, "BitNet b1.58: что показала работа Microsoft об «эре
+ *     1-битных LLM»", section «Метод: как устроен BitNet b1.58» -- ternary
+ *     weights via absmean quantisation, 8-bit activations, RMSNorm, no biases,
+ *     and the forward order: normalise, quantise activations, ternary
+ *     weights, low-bit matmul, rescale.
+ *   inferownia.pl, "BitNet b1.58: era 1-bitowych LLM-ów" -- section
+ *     "„Trenowany od zera” — i czemu to nie jest zwykła kwantyzacja" (the whole
+ *     matrix is scaled by its mean absolute value, entries go to the nearest
+ *     of {-1, 0, +1}); section "Skąd te 1,58 bita" (two bits per stored
+ *     ternary value); section "Mnożenie? Jakie mnożenie" (+1 adds, -1
+ *     subtracts, 0 is skipped).
+ *   juhe.plus (Habr repost), section «Когда - три лучше двух» -- y = W x as
+ *     a sum over +1 weights minus a sum over -1 weights.
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers (hipMalloc'd or equivalent) on
+ *     the current HIP device; the caller owns all memory. The library never
+ *     allocates, on the hot path or elsewhere, and keeps no state beyond a
+ *     cached device count.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call only enqueues work on `stream` and never synchronises, so it
+ *     may be captured into a HIP graph. Calls on different streams may run
+ *     concurrently when their output buffers do not overlap.
+ *   - Arguments are validated on the host before anything is enqueued. On any
+ *     violation the call returns BL_ERR_INVALID_ARG and enqueues nothing.
+ *     If no HIP device is visible the call returns BL_ERR_NO_DEVICE. A failed
+ *     launch returns BL_ERR_HIP (bl_last_hip_error() gives the hipError_t).
+ *     Faults inside kernels surface at the caller's next synchronisation.
+ *   - Shapes: M tokens, K input features, N output features; 1 <= M, N,
+ *     64 <= K, K % 64 == 0, and M*K, N*K below 2^31. Base pointers of x,
+ *     x_q, W and W_packed must be 16-byte aligned.
+ *   - Inputs must be finite; non-finite values are outside the contract.
+ *   - Every result is deterministic: the same inputs give the same bits.
+ */
+#ifndef BITLINEAR_H
+#define BITLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    BL_OK = 0,
+    BL_ERR_INVALID_ARG = 1,
+    BL_ERR_HIP = 2,
+    BL_ERR_NO_DEVICE = 3
+};
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* bl_status_string(int status);
+
+/* hipError_t of the most recent BL_ERR_HIP returned on this thread (0 if none). */
+int bl_last_hip_error(void);
+
+/* Library version string (static). */
+const char* bl_version(void);
+
+/* Bytes of the packed weight buffer: N*K/4 (2 bits per weight); 0 if the shape
+ * is invalid. Host-only, no device needed. */
+size_t bl_packed_bytes(int64_t N, int64_t K);
+
+/* Bytes of the workspace bl_quantize_weights needs: 8*N (fp64 row sums);
+ * 0 if the shape is invalid. Host-only. */
+size_t bl_quantize_weights_workspace_bytes(int64_t N, int64_t K);
+
+/* Absmean ternary weight quantisation and 2-bit packing (offline, once per
+ * matrix). Source: inferownia.pl "BitNet b1.58: era 1-bitowych LLM-ów",
+ * section "„Trenowany od zera”" (absmean, nearest of {-1,0,+1}) and section
+ * "Skąd te 1,58 bita" (two bits per weight).
+ *
+ *   W          in   fp32 [N][K] row-major (out_features x in_features), latent
+ *                   weights.
+ *   W_packed   out  uint32 [N][K/16] (bl_packed_bytes(N,K) bytes). Code
+ *                   c = q + 1 in {0,1,2}; weight k of row n lives in word k/16
+ *                   at bits 8*(i%4) + 2*(i/4), i = k % 16, so
+ *                   (word >> 2p) & 0x03030303 holds the codes of weights
+ *                   16j+4p .. 16j+4p+3 in bytes 0..3.
+ *   gamma      out  one fp32 (device): gamma = (float)(S / (N*K)) where S sums,
+ *                   in fp64, the per-row sums R_n = sum_k |W[n][k]| (each in
+ *                   fp64, k increasing) in increasing n.
+ *   workspace  tmp  >= bl_quantize_weights_workspace_bytes(N,K) bytes, 8-byte
+ *                   aligned; contents undefined afterwards.
+ * Codes: q = clamp(rne(W / (gamma + 1e-5f)), -1, 1), fp32 correctly rounded
+ * division, ties to even. */
+int bl_quantize_weights(const float* W, int64_t N, int64_t K,
+                        uint32_t* W_packed, float* gamma,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Per-token absmax int8 activation quantisation, optionally fused with the
+ * RMSNorm that precedes BitLinear. Source: comrad404.com page above, section
+ * «Метод: как устроен BitNet b1.58» (8-bit activations; normalise, then
+ * quantise).
+ *
+ *   x          in   bf16 [M][K] row-major, raw uint16 bits.
+ *   rms_gain   in   NULL for plain quantisation, else bf16 [K] RMSNorm gain.
+ *   rms_eps    in   RMSNorm epsilon (> 0 when rms_gain != NULL; else ignored).
+ *   x_q        out  int8 [M][K].
+ *   x_scale    out  fp32 [M], dequantisation multiplier (x ~ x_q * x_scale).
+ * Per token m, with z_k = x_k (plain) or z_k = x_k * g_k (fused; exact in
+ * fp32): a = max(max_k |z_k|, 1e-5f); x_q = clamp(rne(z_k * (127.0f / a)),
+ * -127, 127) with fp32 correctly rounded quotient and product, ties to even.
+ * Plain: x_scale = a / 127.0f. Fused: x_scale = (float)(a / (127 * rms)) with
+ * rms = sqrt(sum_k x_k^2 / K + rms_eps) in fp64 (within 1e-6 relative of the
+ * sequential-sum value; codes are exact). */
+int bl_quantize_acts(const uint16_t* x, int64_t M, int64_t K,
+                     const uint16_t* rms_gain, float rms_eps,
+                     int8_t* x_q, float* x_scale, void* stream);
+
+/* BitLinear product: y = (x_q . q^T) * x_scale * gamma, no bias.
+ * Source: inferownia.pl page above, section "Mnożenie? Jakie mnożenie", and
+ * juhe.plus section «Когда - три лучше двух» (ternary weights turn the product
+ * into additions and subtractions); comrad404.com «Метод…» (rescale after the
+ * low-bit matmul).
+ *
+ *   x_q, x_scale  in  int8 [M][K] and fp32 [M] from bl_quantize_acts.
+ *   W_packed, gamma in packed weights [N][K/16] and fp32 gamma (device) from
+ *                 bl_quantize_weights.
+ *   y          out  fp32 [M][N] row-major: y[m][n] = (float)acc[m][n] *
+ *                   (x_scale[m] * gamma) in fp32 (within 2.5e-7 relative of
+ *                   the fp64-evaluated product).
+ *   acc        out  optional int32 [M][N]: acc[m][n] = sum_k q[n][k]*x_q[m][k],
+ *                   exact (|acc| <= 127*K). NULL to skip.
+ * Small M runs a weight-streaming GEMV, large M an int8 MFMA GEMM; both give
+ * identical bits. */
+int bl_bitlinear(const int8_t* x_q, const float* x_scale, int64_t M, int64_t K,
+                 const uint32_t* W_packed, const float* gamma, int64_t N,
+                 float* y, int32_t* acc, void* stream);
+
+/* As bl_bitlinear with an explicit kernel choice, for testing and tuning:
+ * path 0 = automatic, 1 = GEMV (requires M <= 16 and M*K <= 128 KiB),
+ * 2 = GEMM. Any other value, or an unsupported choice, is BL_ERR_INVALID_ARG. */
+int bl_bitlinear_path(const int8_t* x_q, const float* x_scale, int64_t M,
+                      int64_t K, const uint32_t* W_packed, const float* gamma,
+                      int64_t N, float* y, int32_t* acc, int path, void* stream);
+
+/* Squared-ReLU gating between the gate/up and down projections of a 2B4T-style
+ * FFN: h[i] = bf16_rne((r*r) * up[i]) with r = gate[i] > 0 ? gate[i] : 0, all
+ * fp32. Source: inferownia.pl page above, section "Zrób to sam — Microsoft
+ * wypuścił konkretny model", and kripta.biz (2B4T article): the 2B4T FFN uses
+ * squared ReLU. gate, up: fp32 [count]; h: bf16 bits [count]. count >= 1;
+ * pointers 16-byte aligned. */
+int bl_relu2_glu(const float* gate, const float* up, int64_t count,
+                 uint16_t* h, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BITLINEAR_H */

@@ -1,0 +1,177 @@
+"""Thin Python binding of the gfx950 BitLinear library (libbitlinear.so).
+
+Argument marshalling only: every step of the BitLinear forward runs in the
+HIP kernels behind the C ABI declared in include/bitlinear.h. PyTorch supplies
+device memory and the current stream. There is no fallback: if the library is
+not built, or no GPU is present, every call raises.
+
+    W_packed, gamma = quantize_weights(W)          # fp32 [N][K] on the GPU
+    x_q, x_scale = quantize_acts(x, rms_gain=g)    # bf16 [M][K]
+    y = bitlinear(x_q, x_scale, W_packed, gamma)   # fp32 [M][N]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["lib", "library_path", "quantize_weights", "quantize_acts", "bitlinear",
+           "relu2_glu", "BitLinearError", "packed_bytes"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
+_lib = None
+
+BL_OK, BL_ERR_INVALID_ARG, BL_ERR_HIP, BL_ERR_NO_DEVICE = 0, 1, 2, 3
+
+# name -> (argtypes, restype); the same names and order as include/bitlinear.h
+_P, _I, _F, _S = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+_SIGNATURES = {
+    "bl_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "bl_last_hip_error": ([], ctypes.c_int),
+    "bl_version": ([], ctypes.c_char_p),
+    "bl_packed_bytes": ([_I, _I], _S),
+    "bl_quantize_weights_workspace_bytes": ([_I, _I], _S),
+    "bl_quantize_weights": ([_P, _I, _I, _P, _P, _P, _S, _P], ctypes.c_int),
+    "bl_quantize_acts": ([_P, _I, _I, _P, _F, _P, _P, _P], ctypes.c_int),
+    "bl_bitlinear": ([_P, _P, _I, _I, _P, _P, _I, _P, _P, _P], ctypes.c_int),
+    "bl_bitlinear_path": ([_P, _P, _I, _I, _P, _P, _I, _P, _P, ctypes.c_int, _P],
+                          ctypes.c_int),
+    "bl_relu2_glu": ([_P, _P, _I, _P, _P], ctypes.c_int),
+}
+
+
+class BitLinearError(RuntimeError):
+    pass
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Load libbitlinear.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise BitLinearError(
+                f"{_LIB_PATH} is missing: build it with "
+                "`python -c 'import __graft_entry__ as g; g.build()'` "
+                "(or python ternary_weight_linear_quant_amd/build.py)")
+        handle = ctypes.CDLL(_LIB_PATH)
+        for name, (args, res) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = handle
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != BL_OK:
+        L = lib()
+        msg = L.bl_status_string(status).decode()
+        if status == BL_ERR_HIP:
+            msg += f" (hipError_t {L.bl_last_hip_error()})"
+        raise BitLinearError(f"{what}: {msg}")
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev(t, dtype, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise BitLinearError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise BitLinearError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise BitLinearError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def packed_bytes(N: int, K: int) -> int:
+    return lib().bl_packed_bytes(N, K)
+
+
+def quantize_weights(W, workspace=None):
+    """W: fp32 [N][K] -> (W_packed int32 [N][K/16] holding the uint32 words,
+    gamma fp32 [1]). Calls bl_quantize_weights."""
+    torch = _torch()
+    N, K = W.shape
+    L = lib()
+    packed = torch.empty((N, K // 16), dtype=torch.int32, device=W.device)
+    gamma = torch.empty(1, dtype=torch.float32, device=W.device)
+    ws_bytes = L.bl_quantize_weights_workspace_bytes(N, K)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 8) // 8, dtype=torch.float64, device=W.device)
+    _check(L.bl_quantize_weights(_dev(W, torch.float32, "W"), N, K,
+                                 _dev(packed, torch.int32, "W_packed"),
+                                 _dev(gamma, torch.float32, "gamma"),
+                                 _dev(workspace, workspace.dtype, "workspace"),
+                                 workspace.numel() * workspace.element_size(),
+                                 _stream_ptr(W)), "bl_quantize_weights")
+    return packed, gamma
+
+
+def quantize_acts(x, rms_gain=None, rms_eps: float = 1e-5, out=None):
+    """x: bf16 (or int16 bf16 bits) [M][K] -> (x_q int8 [M][K], x_scale fp32 [M]).
+    rms_gain: optional bf16 [K] -> fused RMSNorm. Calls bl_quantize_acts."""
+    torch = _torch()
+    M, K = x.shape
+    if x.dtype == torch.int16:
+        x = x.view(torch.bfloat16)
+    if out is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+        xs = torch.empty(M, dtype=torch.float32, device=x.device)
+    else:
+        xq, xs = out
+    gp = None
+    if rms_gain is not None:
+        if rms_gain.dtype == torch.int16:
+            rms_gain = rms_gain.view(torch.bfloat16)
+        gp = _dev(rms_gain, torch.bfloat16, "rms_gain")
+    _check(lib().bl_quantize_acts(_dev(x, torch.bfloat16, "x"), M, K, gp, float(rms_eps),
+                                  _dev(xq, torch.int8, "x_q"),
+                                  _dev(xs, torch.float32, "x_scale"), _stream_ptr(x)),
+           "bl_quantize_acts")
+    return xq, xs
+
+
+def bitlinear(x_q, x_scale, W_packed, gamma, return_acc: bool = False, path: int = 0,
+              out=None):
+    """y[m][n] = (x_q . q^T)[m][n] * x_scale[m] * gamma -> fp32 [M][N].
+    path: 0 auto, 1 GEMV, 2 GEMM. Calls bl_bitlinear_path."""
+    torch = _torch()
+    M, K = x_q.shape
+    N = W_packed.shape[0]
+    if W_packed.shape[1] * 16 != K:
+        raise BitLinearError("W_packed shape does not match K")
+    y = torch.empty((M, N), dtype=torch.float32, device=x_q.device) if out is None else out
+    acc = torch.empty((M, N), dtype=torch.int32, device=x_q.device) if return_acc else None
+    _check(lib().bl_bitlinear_path(_dev(x_q, torch.int8, "x_q"),
+                                   _dev(x_scale, torch.float32, "x_scale"), M, K,
+                                   _dev(W_packed, torch.int32, "W_packed"),
+                                   _dev(gamma, torch.float32, "gamma"), N,
+                                   _dev(y, torch.float32, "y"),
+                                   None if acc is None else _dev(acc, torch.int32, "acc"),
+                                   int(path), _stream_ptr(x_q)), "bl_bitlinear")
+    return (y, acc) if return_acc else y
+
+
+def relu2_glu(gate, up, out=None):
+    """h = bf16(relu(gate)^2 * up), same shape. Calls bl_relu2_glu."""
+    torch = _torch()
+    h = torch.empty(gate.shape, dtype=torch.bfloat16, device=gate.device) if out is None else out
+    if gate.shape != up.shape:
+        raise BitLinearError("gate and up shapes differ")
+    _check(lib().bl_relu2_glu(_dev(gate, torch.float32, "gate"), _dev(up, torch.float32, "up"),
+                              gate.numel(), _dev(h, torch.bfloat16, "h"), _stream_ptr(gate)),
+           "bl_relu2_glu")
+    return h

@@ -1,0 +1,53 @@
+// Shared device helpers for the gfx950 BitLinear kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bl {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// One packed word holds 16 two-bit codes c = q + 1; (w >> 2p) & 0x03030303
+// gives the codes of weights 4p..4p+3 of the word in bytes 0..3. A byte
+// permute with the table {0xFF, 0x00, 0x01} turns each code into the signed
+// int8 weight, so the result is the 16 weights in k order as MFMA operand
+// bytes.
+__device__ __forceinline__ v4i expand_word(uint32_t w) {
+    const uint32_t m = 0x03030303u;
+    const uint32_t lut = 0x000100FFu;  // byte 0 -> -1, 1 -> 0, 2 -> +1
+    v4i r;
+    r[0] = (int)__builtin_amdgcn_perm(0u, lut, w & m);
+    r[1] = (int)__builtin_amdgcn_perm(0u, lut, (w >> 2) & m);
+    r[2] = (int)__builtin_amdgcn_perm(0u, lut, (w >> 4) & m);
+    r[3] = (int)__builtin_amdgcn_perm(0u, lut, (w >> 6) & m);
+    return r;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+}  // namespace bl

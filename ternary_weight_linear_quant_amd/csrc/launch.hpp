@@ -1,0 +1,28 @@
+// Host-side launch entry points of the kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bl {
+
+hipError_t launch_quantize_weights(const float* W, int64_t N, int64_t K, uint32_t* packed,
+                                   float* gamma, double* rowsums, hipStream_t stream);
+
+hipError_t launch_quantize_acts(const uint16_t* x, int64_t M, int64_t K, const uint16_t* gain,
+                                float rms_eps, int8_t* xq, float* scale, hipStream_t stream);
+
+// Decode GEMV (M <= 16, x held in LDS). Returns hipErrorInvalidValue if the
+// shape does not fit the kernel.
+bool gemv_supported(int64_t M, int64_t K);
+hipError_t launch_gemv(const int8_t* xq, const float* xs, int M, int K, const uint32_t* Wp,
+                       const float* gamma, int N, float* y, int32_t* acc, hipStream_t stream);
+
+// Prefill GEMM (any M).
+hipError_t launch_gemm(const int8_t* xq, const float* xs, int M, int K, const uint32_t* Wp,
+                       const float* gamma, int N, float* y, int32_t* acc, hipStream_t stream);
+
+hipError_t launch_relu2_glu(const float* g, const float* u, int64_t count, uint16_t* h,
+                            hipStream_t stream);
+
+}  // namespace bl

@@ -1,0 +1,112 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/bitlinear.h declares, and rejects invalid arguments on the host before
+anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import ternary_weight_linear_quant_amd as bl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitlinear.h")
+
+
+@pytest.fixture(scope="session")
+def L():
+    if not os.path.exists(bl.library_path()):
+        from ternary_weight_linear_quant_amd import build
+        build.build()
+    return bl.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bl_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_three_calls():
+    names = _declared_functions()
+    for n in ("bl_quantize_weights", "bl_quantize_acts", "bl_bitlinear"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    names = _declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), f"{n} not exported"
+
+
+def test_binding_signatures_cover_header():
+    assert set(_declared_functions()) == set(bl._SIGNATURES)
+
+
+def test_host_helpers(L):
+    assert L.bl_packed_bytes(28672, 8192) == 28672 * 8192 // 4
+    assert L.bl_packed_bytes(10, 100) == 0
+    assert L.bl_packed_bytes(0, 64) == 0
+    assert L.bl_quantize_weights_workspace_bytes(2560, 6912) == 8 * 2560
+    assert L.bl_status_string(0) == b"BL_OK"
+    assert L.bl_status_string(1) == b"BL_ERR_INVALID_ARG"
+    assert L.bl_status_string(99) == b"BL_ERR_UNKNOWN"
+    assert L.bl_version().startswith(b"bitlinear")
+
+
+P = ctypes.c_void_p
+A = P(0x100000)        # aligned fake address, never dereferenced
+MIS = P(0x100001)      # misaligned
+
+
+def test_invalid_arguments_rejected_before_launch(L):
+    E = bl.BL_ERR_INVALID_ARG
+    # null pointers
+    assert L.bl_bitlinear(None, A, 1, 64, A, A, 16, A, None, None) == E
+    assert L.bl_bitlinear(A, A, 1, 64, A, A, 16, None, None, None) == E
+    # shapes
+    assert L.bl_bitlinear(A, A, 0, 64, A, A, 16, A, None, None) == E
+    assert L.bl_bitlinear(A, A, 1, 100, A, A, 16, A, None, None) == E
+    assert L.bl_bitlinear(A, A, 1, 32, A, A, 16, A, None, None) == E
+    assert L.bl_bitlinear(A, A, 1, 64, A, A, 0, A, None, None) == E
+    assert L.bl_bitlinear(A, A, 1 << 20, 1 << 12, A, A, 16, A, None, None) == E
+    # alignment
+    assert L.bl_bitlinear(MIS, A, 1, 64, A, A, 16, A, None, None) == E
+    assert L.bl_bitlinear(A, A, 1, 64, MIS, A, 16, A, None, None) == E
+    # path selection
+    assert L.bl_bitlinear_path(A, A, 1, 64, A, A, 16, A, None, 3, None) == E
+    assert L.bl_bitlinear_path(A, A, 17, 64, A, A, 16, A, None, 1, None) == E
+    assert L.bl_bitlinear_path(A, A, 16, 16384, A, A, 16, A, None, 1, None) == E
+    # weight quantisation
+    assert L.bl_quantize_weights(A, 16, 64, A, A, A, 8 * 15, None) == E
+    assert L.bl_quantize_weights(A, 16, 64, A, A, P(0x100004), 8 * 16, None) == E
+    assert L.bl_quantize_weights(A, 16, 48, A, A, A, 8 * 16, None) == E
+    assert L.bl_quantize_weights(None, 16, 64, A, A, A, 8 * 16, None) == E
+    # activation quantisation
+    assert L.bl_quantize_acts(A, 1, 64, A, 0.0, A, A, None) == E
+    assert L.bl_quantize_acts(A, 1, 64, MIS, 1e-5, A, A, None) == E
+    assert L.bl_quantize_acts(MIS, 1, 64, None, 0.0, A, A, None) == E
+    assert L.bl_quantize_acts(A, 1, 96, None, 0.0, A, A, None) == E
+    # glue
+    assert L.bl_relu2_glu(A, A, 0, A, None) == E
+    assert L.bl_relu2_glu(A, MIS, 4, A, None) == E
+
+
+def test_no_device_status(L):
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible; this checks the no-device path")
+    D = bl.BL_ERR_NO_DEVICE
+    assert L.bl_bitlinear(A, A, 1, 64, A, A, 16, A, None, None) == D
+    assert L.bl_quantize_acts(A, 1, 64, None, 0.0, A, A, None) == D
+    assert L.bl_quantize_weights(A, 16, 64, A, A, A, 8 * 16, None) == D
+    assert L.bl_relu2_glu(A, A, 4, A, None) == D
+
+
+def test_binding_fails_loudly_without_gpu():
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible")
+    with pytest.raises(bl.BitLinearError):
+        bl.quantize_weights(torch.zeros(16, 64))
