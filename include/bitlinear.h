@@ -154,6 +154,29 @@ int bl_bitlinear_path(const int8_t* x_q, const float* x_scale, int64_t M,
 int bl_relu2_glu(const float* gate, const float* up, int64_t count,
                  uint16_t* h, void* stream);
 
+/* Two BitLinear products that share one quantised input -- the gate and up
+ * projections of an FFN -- in a single launch: y1 = BitLinear(x_q, W1) and
+ * y2 = BitLinear(x_q, W2), each exactly as bl_bitlinear computes it (same
+ * bits). Same contract as bl_bitlinear per product (no acc output); N1 and N2
+ * may differ. Source: comrad404.com page above, section «Метод: как устроен
+ * BitNet b1.58» (the LLaMA-style block whose FFN projections are BitLinear),
+ * and inferownia.pl page above, section "Mnożenie? Jakie mnożenie". */
+int bl_bitlinear_pair(const int8_t* x_q, const float* x_scale, int64_t M, int64_t K,
+                      const uint32_t* W1, const float* gamma1, int64_t N1, float* y1,
+                      const uint32_t* W2, const float* gamma2, int64_t N2, float* y2,
+                      void* stream);
+
+/* Squared-ReLU gating fused with the per-token int8 quantisation of its
+ * result: h = bf16_rne((relu(gate)^2) * up) as in bl_relu2_glu, then h_q /
+ * h_scale exactly as bl_quantize_acts(h, rms_gain = NULL) computes them (same
+ * bits), without writing h. gate, up: fp32 [M][K]; h_q: int8 [M][K]; h_scale:
+ * fp32 [M]. Shape rules of bl_quantize_acts; pointers 16-byte aligned. Source:
+ * inferownia.pl page above, section "Zrób to sam — Microsoft wypuścił
+ * konkretny model" (squared ReLU) and comrad404.com «Метод…» (8-bit
+ * activations). */
+int bl_relu2_glu_quant(const float* gate, const float* up, int64_t M, int64_t K, int8_t* h_q,
+                       float* h_scale, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -15,7 +15,7 @@ import ctypes
 import os
 
 __all__ = ["lib", "library_path", "quantize_weights", "quantize_acts", "bitlinear",
-           "relu2_glu", "BitLinearError", "packed_bytes"]
+           "bitlinear_pair", "relu2_glu", "relu2_glu_quant", "BitLinearError", "packed_bytes"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
@@ -37,6 +37,8 @@ _SIGNATURES = {
     "bl_bitlinear_path": ([_P, _P, _I, _I, _P, _P, _I, _P, _P, ctypes.c_int, _P],
                           ctypes.c_int),
     "bl_relu2_glu": ([_P, _P, _I, _P, _P], ctypes.c_int),
+    "bl_bitlinear_pair": ([_P, _P, _I, _I, _P, _P, _I, _P, _P, _P, _I, _P, _P], ctypes.c_int),
+    "bl_relu2_glu_quant": ([_P, _P, _I, _I, _P, _P, _P], ctypes.c_int),
 }
 
 
@@ -175,3 +177,43 @@ def relu2_glu(gate, up, out=None):
                               gate.numel(), _dev(h, torch.bfloat16, "h"), _stream_ptr(gate)),
            "bl_relu2_glu")
     return h
+
+
+def bitlinear_pair(x_q, x_scale, W1, gamma1, W2, gamma2, out=None):
+    """(y1, y2): two BitLinears sharing x_q in one launch. Calls bl_bitlinear_pair."""
+    torch = _torch()
+    M, K = x_q.shape
+    N1, N2 = W1.shape[0], W2.shape[0]
+    if W1.shape[1] * 16 != K or W2.shape[1] * 16 != K:
+        raise BitLinearError("packed weight shapes do not match K")
+    if out is None:
+        y1 = torch.empty((M, N1), dtype=torch.float32, device=x_q.device)
+        y2 = torch.empty((M, N2), dtype=torch.float32, device=x_q.device)
+    else:
+        y1, y2 = out
+    _check(lib().bl_bitlinear_pair(_dev(x_q, torch.int8, "x_q"),
+                                   _dev(x_scale, torch.float32, "x_scale"), M, K,
+                                   _dev(W1, torch.int32, "W1"), _dev(gamma1, torch.float32, "gamma1"),
+                                   N1, _dev(y1, torch.float32, "y1"),
+                                   _dev(W2, torch.int32, "W2"), _dev(gamma2, torch.float32, "gamma2"),
+                                   N2, _dev(y2, torch.float32, "y2"), _stream_ptr(x_q)),
+           "bl_bitlinear_pair")
+    return y1, y2
+
+
+def relu2_glu_quant(gate, up, out=None):
+    """(h_q int8, h_scale fp32) of h = bf16(relu(gate)^2 * up). Calls bl_relu2_glu_quant."""
+    torch = _torch()
+    M, K = gate.shape
+    if gate.shape != up.shape:
+        raise BitLinearError("gate and up shapes differ")
+    if out is None:
+        hq = torch.empty((M, K), dtype=torch.int8, device=gate.device)
+        hs = torch.empty(M, dtype=torch.float32, device=gate.device)
+    else:
+        hq, hs = out
+    _check(lib().bl_relu2_glu_quant(_dev(gate, torch.float32, "gate"), _dev(up, torch.float32, "up"),
+                                    M, K, _dev(hq, torch.int8, "h_q"),
+                                    _dev(hs, torch.float32, "h_scale"), _stream_ptr(gate)),
+           "bl_relu2_glu_quant")
+    return hq, hs

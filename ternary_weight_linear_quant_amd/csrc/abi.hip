@@ -115,6 +115,36 @@ int bl_bitlinear(const int8_t* x_q, const float* x_scale, int64_t M, int64_t K,
     return bl_bitlinear_path(x_q, x_scale, M, K, W_packed, gamma, N, y, acc, 0, stream);
 }
 
+int bl_bitlinear_pair(const int8_t* x_q, const float* x_scale, int64_t M, int64_t K,
+                      const uint32_t* W1, const float* gamma1, int64_t N1, float* y1,
+                      const uint32_t* W2, const float* gamma2, int64_t N2, float* y2,
+                      void* stream) {
+    if (!x_q || !x_scale || !W1 || !gamma1 || !y1 || !W2 || !gamma2 || !y2)
+        return BL_ERR_INVALID_ARG;
+    if (!shape_ok(M, K) || !shape_ok(N1, K) || !shape_ok(N2, K)) return BL_ERR_INVALID_ARG;
+    if (M > (int64_t{1} << 31) / N1 || M > (int64_t{1} << 31) / N2) return BL_ERR_INVALID_ARG;
+    if (!aligned16(x_q) || !aligned16(W1) || !aligned16(W2)) return BL_ERR_INVALID_ARG;
+    if (int s = device_status()) return s;
+    hipStream_t st = as_stream(stream);
+    if (bl::gemv_supported(M, K))
+        return hip_status(bl::launch_gemv_pair(x_q, x_scale, (int)M, (int)K, W1, gamma1, (int)N1,
+                                               y1, W2, gamma2, (int)N2, y2, st));
+    int e = hip_status(bl::launch_gemm(x_q, x_scale, (int)M, (int)K, W1, gamma1, (int)N1, y1,
+                                       nullptr, st));
+    if (e) return e;
+    return hip_status(bl::launch_gemm(x_q, x_scale, (int)M, (int)K, W2, gamma2, (int)N2, y2,
+                                      nullptr, st));
+}
+
+int bl_relu2_glu_quant(const float* gate, const float* up, int64_t M, int64_t K, int8_t* h_q,
+                       float* h_scale, void* stream) {
+    if (!gate || !up || !h_q || !h_scale) return BL_ERR_INVALID_ARG;
+    if (!shape_ok(M, K)) return BL_ERR_INVALID_ARG;
+    if (!aligned16(gate) || !aligned16(up) || !aligned16(h_q)) return BL_ERR_INVALID_ARG;
+    if (int s = device_status()) return s;
+    return hip_status(bl::launch_relu2_glu_quant(gate, up, M, K, h_q, h_scale, as_stream(stream)));
+}
+
 int bl_relu2_glu(const float* gate, const float* up, int64_t count, uint16_t* h, void* stream) {
     if (!gate || !up || !h || count < 1) return BL_ERR_INVALID_ARG;
     if (count > (int64_t{1} << 40)) return BL_ERR_INVALID_ARG;

@@ -38,6 +38,24 @@ __device__ __forceinline__ v4i expand_word(uint32_t w) {
     return r;
 }
 
+// Same 16 weights NEGATED (-q), in 9 instructions instead of 11. The
+// fields of bit-pairs 1 and 3 are masked in place, giving selectors
+// {0, 4, 8}: 0 and 4 pick byte 0 of the second and first permute source,
+// and 8 replicates bit 15 of the second source (set) into 0xFF. A product
+// accumulated with these bytes is the exact negative of the true sum.
+__device__ __forceinline__ v4i expand_word_neg(uint32_t w) {
+    const uint32_t m0 = 0x03030303u, m1 = 0x0C0C0C0Cu;
+    const uint32_t lut0 = 0x00FF0001u;  // sel 0 -> +1, 1 -> 0, 2 -> -1
+    const uint32_t lut1 = 0x00008001u;  // sel 0 -> +1, 4 -> 0 (src0), 8 -> -1
+    const uint32_t t = w >> 4;
+    v4i r;
+    r[0] = (int)__builtin_amdgcn_perm(0u, lut0, w & m0);
+    r[1] = (int)__builtin_amdgcn_perm(0u, lut1, w & m1);
+    r[2] = (int)__builtin_amdgcn_perm(0u, lut0, t & m0);
+    r[3] = (int)__builtin_amdgcn_perm(0u, lut1, t & m1);
+    return r;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));

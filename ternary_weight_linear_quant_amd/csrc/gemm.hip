@@ -1,57 +1,106 @@
-// Prefill BitLinear (many tokens): int8 MFMA GEMM over ternary tiles expanded
-// to int8 in LDS.
+// Prefill BitLinear (many tokens): int8 MFMA GEMM over 2-bit ternary weights.
 //
 // Source: inferownia.pl, "BitNet b1.58: era 1-bitowych LLM-ów", section
 // "Mnożenie? Jakie mnożenie", and juhe.plus (Habr repost), section «Когда - три
 // лучше двух»: a ternary weight turns each multiply into an add, a subtract or
 // nothing. At prefill the work is compute-bound (2*M*N*K int8 operations over
-// 2 bits of weight and M*K bytes of activations), so the add/subtract is
-// carried out by the int8 matrix cores on weights expanded to {-1, 0, +1}
-// bytes: every product is exact and the int32 sums are exact.
+// 2 bits of weight and M*K bytes of activations), so the add/subtract is run
+// on the int8 matrix cores with the weights expanded to {-1, 0, +1} bytes:
+// every product and every int32 sum is exact.
 //
-// y = x_q . q^T: the MFMA A operand is the activation tile (rows = tokens), the
-// B operand the weight tile (rows = output features); both are k-contiguous.
-// Workgroup: 256 threads = 4 waves in a 2 x 2 grid, block tile BM x BN, K step
-// 64, v_mfma_i32_32x32x32_i8. Per K step each thread loads its share of the
-// activation tile (16 B chunks) and of the packed weight tile (one 16 B load =
-// 64 weights of one row), expands the weights with byte permutes, and stores
-// both into the idle half of a double-buffered LDS tile (16 B chunks XOR-
-// swizzled by row against bank conflicts). The epilogue scales the exact int32
-// sums by x_scale[m] * gamma and stores fp32 rows of 128 contiguous bytes.
+// y = x_q . q^T with v_mfma_i32_32x32x32_i8: A = activation tile (rows =
+// tokens), B = weight tile (rows = output features), both k-contiguous.
+// Workgroup: 256 threads = 4 waves in a 2 x 2 grid over a BM x BN tile; K step
+// 128. A STAGES-deep LDS ring is filled with global_load_lds_dwordx4 (each
+// lane's 16 bytes land directly in LDS, no register staging): per stage the
+// activation tile (BM x 128 B) and the PACKED weight tile (BN x 32 B, 2 bits
+// per weight). Loads for stage kt+STAGES-1 are issued before computing stage
+// kt, and an explicit vmcnt wait keeps STAGES-1 stages in flight.
+//
+// Fragment reads: lane (r, g) of a B fragment reads 16 B = 4 packed words of
+// its weight row; word s feeds k-substep s after expansion to 16 signed bytes
+// with byte permutes (v_perm), so the weights cross LDS at 2 bits. The A lane
+// (r, g) reads, for substep s, the 16 activation bytes of the same k positions
+// (chunk 4g + s of its row). 16-byte chunks are XOR-swizzled by row so that
+// these reads are free of bank conflicts.
 //
 // Roofline: MFMA (int8). Algorithmic work per call = 2*M*N*K operations.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace bl {
 
-constexpr int kGemmThreads = 256;
-constexpr int kBK = 64;
+constexpr int kBK = 128;            // k per stage
+constexpr int kARow = kBK;          // activation bytes per row per stage
+constexpr int kBRow = kBK / 4;      // packed weight bytes per row per stage
 
-// 16-byte chunk c (0..3) of LDS row r lives at chunk position c ^ swz(r).
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 3; }
+// Physical 16-byte chunk of logical chunk c in LDS row r: c ^ swz(r). Both
+// depend only on r % 32, so fragment addresses of different 32-row tiles
+// differ by constants. Any 8 (A: 128-byte rows) or 16 aligned consecutive
+// rows map their reads of one logical chunk to distinct banks, for 32 or 64
+// LDS banks alike.
+__device__ __forceinline__ int swz_a(int r) { return (r ^ ((r >> 3) & 3)) & 7; }
+__device__ __forceinline__ int swz_b(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
 
-template <int BM, int BN>
-__global__ __launch_bounds__(kGemmThreads) void k_gemm(
+// s_waitcnt with vmcnt = n (other counters unconstrained), n < 64.
+#define BL_WAIT_VMCNT(n) \
+    __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | ((((n) >> 4) & 3) << 14))
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+
+// 16 bytes per lane from global memory straight into LDS at
+// lds_base + 16 * lane (global_load_lds_dwordx4). lds_base must be wave-
+// uniform. Issued through asm so that the compiler does not add its own
+// conservative waits before later LDS reads; completion is tracked with
+// explicit vmcnt waits. M0 is saved and restored around the load.
+__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(gptr), "s"(lds_base)
+        : "memory");
+}
+
+// WPE: waves per SIMD the register allocation must allow (2 lets two
+// workgroups share a CU so that one's barrier gaps are filled by the other).
+template <int BM, int BN, int WGM, int WGN, int STAGES, int WPE>
+__global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_gemm(
     const int8_t* __restrict__ xq, const float* __restrict__ xs, int M, int K,
     const uint32_t* __restrict__ Wp, const float* __restrict__ gamma_p, int N,
     float* __restrict__ y, int32_t* __restrict__ acc_out) {
-    constexpr int WM = BM / 2, WN = BN / 2;
+    constexpr int NW = WGM * WGN;               // waves per workgroup
+    constexpr int WM = BM / WGM, WN = BN / WGN;  // wave tile
     constexpr int TM = WM / 32, TN = WN / 32;
-    constexpr int A_PER = BM * 4 / kGemmThreads;  // 16 B activation chunks per thread
-    static_assert(A_PER >= 1 && BN <= kGemmThreads, "tile shape");
+    constexpr int A_STAGE = BM * kARow;
+    constexpr int B_STAGE = BN * kBRow;
+    constexpr int STAGE = A_STAGE + B_STAGE;
+    constexpr int A_ROWS = BM / NW;              // activation rows loaded per wave
+    constexpr int A_INSTR = A_ROWS / 8;          // 8 rows of 128 B per instruction
+    // Weight rows: 32 rows of 32 B per instruction, spread over the first
+    // B_WAVES waves.
+    constexpr int B_WAVES = BN / 32 < NW ? BN / 32 : NW;
+    constexpr int B_INSTR = BN / 32 / B_WAVES;
+    constexpr int B_ROWS = 32 * B_INSTR;         // weight rows loaded per loading wave
+    static_assert(TM >= 1 && TN >= 1 && A_INSTR >= 1 && B_INSTR >= 1, "tile shape");
+    static_assert(A_ROWS % 8 == 0 && B_WAVES * B_ROWS == BN, "tile shape");
+    static_assert((A_INSTR + B_INSTR) * (STAGES - 1) < 64, "vmcnt range");
 
-    __shared__ __align__(16) int8_t As[2][BM * kBK];
-    __shared__ __align__(16) int8_t Bs[2][BN * kBK];
+    extern __shared__ __align__(16) uint8_t smem[];
 
     const int tid = threadIdx.x;
-    const int wave = tid / kWave, lane = tid % kWave;
-    const int wm0 = (wave % 2) * WM, wn0 = (wave / 2) * WN;
+    const int lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wm0 = (wave % WGM) * WM, wn0 = (wave / WGM) * WN;
 
-    // Tile order: hand each XCD (workgroups are dealt round-robin to the 8
-    // XCDs) a contiguous range of tile ids, then walk tiles in groups of 8
-    // row tiles so neighbouring workgroups share activation and weight tiles
-    // in the XCD's L2.
+    // Tile order: each XCD (workgroups are dealt round-robin to the 8 XCDs)
+    // gets a contiguous range of tile ids, walked in groups of 8 row tiles so
+    // neighbouring workgroups share activation and weight tiles in its L2.
     const int nM = (M + BM - 1) / BM, nN = (N + BN - 1) / BN;
     const int total = nM * nN;
     const int b = blockIdx.x;
@@ -65,44 +114,53 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(
     const int bn = (t % (G * nN)) / gsize;
     const int m0 = bm * BM, n0 = bn * BN;
 
-    // Global -> register staging assignments.
-    const int8_t* a_src[A_PER];
-    int a_lds[A_PER];
+    const int KT = (K + kBK - 1) / kBK;
+    const bool k_tail = (K % kBK) != 0;  // last stage holds 64 valid k
+
+    // Per-lane global sources for the stage loads (k offset added per stage).
+    // A instruction i of this wave: rows 8i + lane/8 of the wave's A_ROWS;
+    // the lane's LDS slot is physical chunk lane%8 of that row.
+    const int8_t* a_src[A_INSTR];
+    int a_chunk[A_INSTR];
 #pragma unroll
-    for (int i = 0; i < A_PER; ++i) {
-        const int id = tid + kGemmThreads * i;
-        const int r = id / 4, c = id % 4;
-        const int gm = min(m0 + r, M - 1);
-        a_src[i] = xq + (size_t)gm * K + 16 * c;
-        a_lds[i] = r * kBK + 16 * (c ^ swz(r));
+    for (int i = 0; i < A_INSTR; ++i) {
+        const int r = wave * A_ROWS + 8 * i + lane / 8;
+        a_chunk[i] = (lane % 8) ^ swz_a(r);
+        a_src[i] = xq + (size_t)min(m0 + r, M - 1) * K;
     }
-    const bool b_ld = tid < BN;
-    const int b_row = tid;
-    const uint32_t* b_src = Wp + (size_t)min(n0 + b_row, N - 1) * (K / 16);
+    const bool b_loader = wave < B_WAVES;  // wave-uniform
+    const uint8_t* b_src[B_INSTR];
+    int b_chunk[B_INSTR];
+#pragma unroll
+    for (int i = 0; i < B_INSTR; ++i) {
+        const int r = min(wave, B_WAVES - 1) * B_ROWS + 32 * i + lane / 2;
+        b_chunk[i] = (lane % 2) ^ swz_b(r);
+        b_src[i] = reinterpret_cast<const uint8_t*>(Wp) + (size_t)min(n0 + r, N - 1) * (K / 4);
+    }
 
-    uint4 a_reg[A_PER];
-    uint4 b_reg = make_uint4(0, 0, 0, 0);
+    const uint32_t smem_base = (uint32_t)(size_t)(lds_u8_t*)smem;
 
-    auto gload = [&](int kt) {
+    auto issue = [&](int kt) {
+        const uint32_t st = smem_base + (uint32_t)((kt % STAGES) * STAGE);
+        const int k0 = kt * kBK;
+        const bool tail = k_tail && kt == KT - 1;
 #pragma unroll
-        for (int i = 0; i < A_PER; ++i)
-            a_reg[i] = *reinterpret_cast<const uint4*>(a_src[i] + (size_t)kt * kBK);
-        if (b_ld) b_reg = *reinterpret_cast<const uint4*>(b_src + 4 * kt);
-    };
-    auto lstore = [&](int buf) {
+        for (int i = 0; i < A_INSTR; ++i) {
+            int c = a_chunk[i];
+            if (tail && c >= 4) c -= 4;  // beyond K: any valid address (B is zero there)
+            lds_dma16(a_src[i] + k0 + 16 * c, st + (wave * A_ROWS + 8 * i) * kARow);
+        }
+        if (b_loader) {
 #pragma unroll
-        for (int i = 0; i < A_PER; ++i)
-            *reinterpret_cast<uint4*>(&As[buf][a_lds[i]]) = a_reg[i];
-        if (b_ld) {
-            const uint32_t w4[4] = {b_reg.x, b_reg.y, b_reg.z, b_reg.w};
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const v4i e = expand_word(w4[c]);
-                *reinterpret_cast<v4i*>(&Bs[buf][b_row * kBK + 16 * (c ^ swz(b_row))]) = e;
+            for (int i = 0; i < B_INSTR; ++i) {
+                const int c = tail ? 0 : b_chunk[i];
+                lds_dma16(b_src[i] + k0 / 4 + 16 * c,
+                          st + A_STAGE + (wave * B_ROWS + 32 * i) * kBRow);
             }
         }
     };
 
+    // Accumulators hold the NEGATED sums (the weights are expanded as -q).
     v16i acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -111,28 +169,84 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
 
-    const int KT = K / kBK;
-    gload(0);
-    lstore(0);
-    __syncthreads();
-
     const int fr = lane % 32, fg = lane / 32;
+
+    // Fragment reads from LDS stage `kt % STAGES`.
+    auto read_b = [&](uint4* bp, int kt) {
+        const uint8_t* Bs = smem + (kt % STAGES) * STAGE + A_STAGE;
+        // Last stage of a K that is not a multiple of 128: the upper 64 k
+        // (lane group 1) lie past K, so that group's codes become zeros.
+        const uint32_t keep = (k_tail && kt == KT - 1 && fg) ? 0u : 0xFFFFFFFFu;
+        const uint32_t fill = 0x55555555u & ~keep;  // code 1 = weight 0
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int r = wn0 + 32 * j + fr;
+            uint4 v = *reinterpret_cast<const uint4*>(Bs + r * kBRow + 16 * (fg ^ swz_b(r)));
+            v.x = (v.x & keep) | fill;
+            v.y = (v.y & keep) | fill;
+            v.z = (v.z & keep) | fill;
+            v.w = (v.w & keep) | fill;
+            bp[j] = v;
+        }
+    };
+    auto read_a = [&](v4i* af, int kt, int s) {
+        const uint8_t* As = smem + (kt % STAGES) * STAGE;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int r = wm0 + 32 * i + fr;
+            af[i] = *reinterpret_cast<const v4i*>(As + r * kARow + 16 * ((4 * fg + s) ^ swz_a(r)));
+        }
+    };
+    auto expand = [&](v4i* bf, const uint4* bp, int s) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const uint32_t w = s == 0 ? bp[j].x : s == 1 ? bp[j].y : s == 2 ? bp[j].z : bp[j].w;
+            bf[j] = expand_word_neg(w);
+        }
+    };
+
+    // Pipeline. Stage kt+STAGES-1 is issued in the middle of step kt, right
+    // after a barrier that (a) follows this wave's wait for stage kt+1, so
+    // stage kt+1 is visible to every wave, and (b) proves every wave is done
+    // with step kt-1, whose buffer is the one being refilled. Step kt+1's
+    // first fragments are then read during the second half of step kt, so
+    // the matrix cores never wait on LDS at a step boundary.
+    constexpr int LOADS_B = A_INSTR + B_INSTR;   // per stage, weight-loading waves
+    constexpr int LOADS_A = A_INSTR;             // per stage, other waves
+    static_assert(STAGES >= 3, "pipeline depth");
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st)
+        if (st < KT) issue(st);
+    // Stage 0 landed: STAGES-2 later stages may still be in flight.
+    {
+        const int after = min(STAGES - 2, KT - 1);
+        if (after >= 2) {
+            if (b_loader) BL_WAIT_VMCNT(LOADS_B * 2); else BL_WAIT_VMCNT(LOADS_A * 2);
+        } else if (after == 1) {
+            if (b_loader) BL_WAIT_VMCNT(LOADS_B); else BL_WAIT_VMCNT(LOADS_A);
+        } else {
+            BL_WAIT_VMCNT(0);
+        }
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    }
+    uint4 bp[TN], bpn[TN];
+    v4i af[TM], an[TM], bf[TN], bfn[TN];
+    read_b(bp, 0);
+    read_a(af, 0, 0);
+    expand(bf, bp, 0);
+
     for (int kt = 0; kt < KT; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < KT) gload(kt + 1);
+        const bool more = kt + 1 < KT;
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int c = 2 * s + fg;
-            v4i af[TM], bf[TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int r = wm0 + 32 * i + fr;
-                af[i] = *reinterpret_cast<const v4i*>(&As[buf][r * kBK + 16 * (c ^ swz(r))]);
-            }
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int r = wn0 + 32 * j + fr;
-                bf[j] = *reinterpret_cast<const v4i*>(&Bs[buf][r * kBK + 16 * (c ^ swz(r))]);
+        for (int s = 0; s < 4; ++s) {
+            // Next fragments: same step for s < 3, else the first of kt+1.
+            if (s < 3) {
+                read_a(an, kt, s + 1);
+                expand(bfn, bp, s + 1);
+            } else if (more) {
+                read_a(an, kt + 1, 0);
+                expand(bfn, bpn, 0);
             }
 #pragma unroll
             for (int i = 0; i < TM; ++i)
@@ -140,9 +254,28 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(
                 for (int j = 0; j < TN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j],
                                                                       0, 0, 0);
+            if (s == 1 && more) {
+                // Stage kt+1 landed once the stages issued after it are the
+                // only loads outstanding.
+                const int after = min(STAGES - 3, KT - 2 - kt);
+                if (after >= 1) {
+                    if (b_loader) BL_WAIT_VMCNT(LOADS_B); else BL_WAIT_VMCNT(LOADS_A);
+                } else {
+                    BL_WAIT_VMCNT(0);
+                }
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+                if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
+                read_b(bpn, kt + 1);
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i) af[i] = an[i];
+#pragma unroll
+            for (int j = 0; j < TN; ++j) bf[j] = bfn[j];
+            __builtin_amdgcn_sched_barrier(0);
         }
-        if (kt + 1 < KT) lstore(buf ^ 1);
-        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bp[j] = bpn[j];
     }
 
     // Epilogue. C layout of the 32x32 MFMA: lane l, register v holds row
@@ -153,27 +286,41 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int m = m0 + wm0 + 32 * i + 8 * (v / 4) + 4 * (lane / 32) + (v % 4);
-            if (m >= M) continue;
-            const float sc = xs[m] * gm;
+            if (m < M) {
+                const float sc = xs[m] * gm;
+                float* yrow = y + (size_t)m * N;
+                int32_t* arow = acc_out ? acc_out + (size_t)m * N : nullptr;
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int n = n0 + wn0 + 32 * j + (lane % 32);
-                if (n < N) {
-                    y[(size_t)m * N + n] = (float)acc[i][j][v] * sc;
-                    if (acc_out) acc_out[(size_t)m * N + n] = acc[i][j][v];
+                for (int j = 0; j < TN; ++j) {
+                    const int n = n0 + wn0 + 32 * j + (lane % 32);
+                    if (n < N) {
+                        const int32_t a = -acc[i][j][v];
+                        yrow[n] = (float)a * sc;
+                        if (arow) arow[n] = a;
+                    }
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int WGM, int WGN, int STAGES, int WPE>
 static hipError_t launch_gemm_tile(const int8_t* xq, const float* xs, int M, int K,
                                    const uint32_t* Wp, const float* gamma, int N, float* y,
                                    int32_t* acc, hipStream_t stream) {
+    constexpr size_t lds = (size_t)STAGES * (BM * kARow + BN * kBRow);
+    static bool attr_set = false;
+    if (lds > 64 * 1024 && !attr_set) {
+        hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&k_gemm<BM, BN, WGM, WGN, STAGES, WPE>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
     const int blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    hipLaunchKernelGGL((k_gemm<BM, BN>), dim3(blocks), dim3(kGemmThreads), 0, stream, xq, xs, M,
-                       K, Wp, gamma, N, y, acc);
+    hipLaunchKernelGGL((k_gemm<BM, BN, WGM, WGN, STAGES, WPE>), dim3(blocks), dim3(64 * WGM * WGN),
+                       lds, stream, xq, xs, M, K, Wp, gamma, N, y, acc);
     return hipGetLastError();
 }
 
@@ -183,10 +330,13 @@ hipError_t launch_gemm(const int8_t* xq, const float* xs, int M, int K, const ui
         return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
     };
     constexpr int kCUs = 256;
-    if (tiles(256, 256) >= kCUs) return launch_gemm_tile<256, 256>(xq, xs, M, K, Wp, gamma, N, y, acc, stream);
-    if (tiles(256, 128) >= kCUs) return launch_gemm_tile<256, 128>(xq, xs, M, K, Wp, gamma, N, y, acc, stream);
-    if (tiles(128, 128) >= kCUs) return launch_gemm_tile<128, 128>(xq, xs, M, K, Wp, gamma, N, y, acc, stream);
-    return launch_gemm_tile<64, 128>(xq, xs, M, K, Wp, gamma, N, y, acc, stream);
+    if (tiles(256, 256) >= kCUs)
+        return launch_gemm_tile<256, 256, 4, 2, 3, 2>(xq, xs, M, K, Wp, gamma, N, y, acc, stream);
+    if (tiles(256, 128) >= kCUs)
+        return launch_gemm_tile<256, 128, 4, 2, 3, 2>(xq, xs, M, K, Wp, gamma, N, y, acc, stream);
+    if (tiles(128, 128) >= kCUs)
+        return launch_gemm_tile<128, 128, 2, 2, 3, 2>(xq, xs, M, K, Wp, gamma, N, y, acc, stream);
+    return launch_gemm_tile<64, 128, 2, 2, 3, 2>(xq, xs, M, K, Wp, gamma, N, y, acc, stream);
 }
 
 }  // namespace bl

@@ -25,4 +25,13 @@ hipError_t launch_gemm(const int8_t* xq, const float* xs, int M, int K, const ui
 hipError_t launch_relu2_glu(const float* g, const float* u, int64_t count, uint16_t* h,
                             hipStream_t stream);
 
+// Squared-ReLU gating fused with the per-token quantisation of its output.
+hipError_t launch_relu2_glu_quant(const float* gate, const float* up, int64_t M, int64_t K,
+                                  int8_t* hq, float* scale, hipStream_t stream);
+
+// Two decode GEMVs sharing one quantised input, in one launch.
+hipError_t launch_gemv_pair(const int8_t* xq, const float* xs, int M, int K, const uint32_t* W1,
+                            const float* g1, int N1, float* y1, const uint32_t* W2,
+                            const float* g2, int N2, float* y2, hipStream_t stream);
+
 }  // namespace bl

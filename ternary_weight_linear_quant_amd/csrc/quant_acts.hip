@@ -1,44 +1,97 @@
 // Per-token absmax int8 activation quantisation, optionally fused with the
-// RMSNorm that precedes BitLinear.
+// RMSNorm that precedes BitLinear, and the same quantisation fused with the
+// squared-ReLU gating of a 2B4T-style FFN.
 //
 // Source: comrad404.com, "BitNet b1.58: что показала работа Microsoft об
 // «эре 1-битных LLM»", section «Метод: как устроен BitNet b1.58»: activations
 // are carried as 8-bit integers, and the input is normalised (RMSNorm) before
-// it is quantised.
+// it is quantised. inferownia.pl, "BitNet b1.58: era 1-bitowych LLM-ów",
+// section "Zrób to sam — Microsoft wypuścił konkretny model", and kripta.biz
+// (2B4T article): the 2B4T FFN uses squared ReLU.
 //
-// One workgroup per token. Pass 1 reduces max|z| (exact, order-free) and, when
-// fused, sum x^2 in fp64; pass 2 re-reads the token (L2-resident) and writes
-// the codes. Codes: rne(z * (127/a)) clamped to [-127, 127] in fp32; since a
-// positive per-token factor cancels in absmax quantisation, the codes of
-// RMSNorm(x) are those of z = x*g (exact in fp32) and 1/rms goes into the
-// scale. Roofline: HBM, 2 B read + 1 B written per element.
+// One workgroup per token, one pass over memory: each thread loads its
+// 16-byte vectors of the token once and keeps them in registers while the
+// workgroup reduces max|z| (exact, order-free) and, when fused, sum x^2 in
+// fp64; then it writes the codes. Codes: rne(z * (127/a)) clamped to
+// [-127, 127] in fp32; since a positive per-token factor cancels in absmax
+// quantisation, the codes of RMSNorm(x) are those of z = x*g (exact in fp32)
+// and 1/rms goes into the scale. Tokens longer than the register cache take a
+// second pass that re-reads them (L2-resident). Roofline: HBM, 2 B read +
+// 1 B written per element (8 B read for the gated variant).
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace bl {
 
 constexpr int kActThreads = 256;
+constexpr int kActCache = 14;  // 16-byte vectors cached per thread (K <= 28672)
+
+template <typename T>
+__device__ __forceinline__ T block_reduce(T v, T* scratch, bool is_max) {
+    const int wave = threadIdx.x / kWave;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const T other = __shfl_xor(v, o, kWave);
+        v = is_max ? (v > other ? v : other) : v + other;
+    }
+    if ((threadIdx.x % kWave) == 0) scratch[wave] = v;
+    __syncthreads();
+    T r = scratch[0];
+#pragma unroll
+    for (int w = 1; w < kActThreads / kWave; ++w) r = is_max ? (r > scratch[w] ? r : scratch[w]) : r + scratch[w];
+    return r;
+}
+
+// 8 bf16 (one 16-byte vector) -> 8 int8 codes packed in a uint2.
+__device__ __forceinline__ uint2 quant8(const uint32_t dw[4], const uint32_t gw[4], bool fused,
+                                        float inv) {
+    uint32_t packed[2] = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float z = bf16_to_f32((dw[i] >> (16 * h)) & 0xFFFFu);
+            if (fused) z = z * bf16_to_f32((gw[i] >> (16 * h)) & 0xFFFFu);
+            float t = __builtin_rintf(z * inv);
+            t = fminf(fmaxf(t, -127.0f), 127.0f);
+            const uint32_t b = (uint32_t)((int)t) & 0xFFu;
+            const int e = 2 * i + h;
+            packed[e / 4] |= b << (8 * (e % 4));
+        }
+    }
+    return make_uint2(packed[0], packed[1]);
+}
 
 template <bool FUSED>
 __global__ __launch_bounds__(kActThreads) void k_act_quant(
     const uint16_t* __restrict__ x, int64_t K, const uint16_t* __restrict__ gain,
     float rms_eps, int8_t* __restrict__ xq, float* __restrict__ scale) {
+    __shared__ float s_max[kActThreads / kWave];
+    __shared__ double s_ss[kActThreads / kWave];
     const int64_t m = blockIdx.x;
     const uint4* row = reinterpret_cast<const uint4*>(x + m * K);
     const uint4* grow = reinterpret_cast<const uint4*>(gain);
     const int tid = threadIdx.x;
-    const int64_t nvec = K / 8;  // 8 bf16 per 16 bytes
+    const int nvec = (int)(K / 8);  // 8 bf16 per 16 bytes
+    const bool cached = nvec <= kActCache * kActThreads;
 
+    uint4 cx[kActCache];
+    uint4 cg[kActCache];
+    if (cached) {
+#pragma unroll
+        for (int j = 0; j < kActCache; ++j) {
+            const int v = tid + kActThreads * j;
+            if (v < nvec) {
+                cx[j] = row[v];
+                if (FUSED) cg[j] = grow[v];
+            }
+        }
+    }
     float amax = 0.0f;
     double ss = 0.0;
-    for (int64_t v = tid; v < nvec; v += kActThreads) {
-        const uint4 d = row[v];
+    auto scan = [&](const uint4 d, const uint4 gv) {
         const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
-        uint32_t gw[4] = {0, 0, 0, 0};
-        if (FUSED) {
-            const uint4 g = grow[v];
-            gw[0] = g.x; gw[1] = g.y; gw[2] = g.z; gw[3] = g.w;
-        }
+        const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -52,52 +105,34 @@ __global__ __launch_bounds__(kActThreads) void k_act_quant(
                 amax = fmaxf(amax, fabsf(z));
             }
         }
-    }
-
-    __shared__ float s_max[kActThreads / kWave];
-    __shared__ double s_ss[kActThreads / kWave];
-    amax = wave_max(amax);
-    if (FUSED) ss = wave_sum(ss);
-    const int wave = tid / kWave;
-    if ((tid % kWave) == 0) {
-        s_max[wave] = amax;
-        if (FUSED) s_ss[wave] = ss;
-    }
-    __syncthreads();
-    amax = s_max[0];
-    double ss_tot = FUSED ? s_ss[0] : 0.0;
+    };
+    if (cached) {
 #pragma unroll
-    for (int w = 1; w < kActThreads / kWave; ++w) {
-        amax = fmaxf(amax, s_max[w]);
-        if (FUSED) ss_tot += s_ss[w];
+        for (int j = 0; j < kActCache; ++j)
+            if (tid + kActThreads * j < nvec) scan(cx[j], FUSED ? cg[j] : cx[j]);
+    } else {
+        for (int v = tid; v < nvec; v += kActThreads) scan(row[v], FUSED ? grow[v] : row[v]);
     }
+    amax = block_reduce(amax, s_max, true);
+    double ss_tot = 0.0;
+    if (FUSED) ss_tot = block_reduce(ss, s_ss, false);
     const float a = amax > 1e-5f ? amax : 1e-5f;
     const float inv = 127.0f / a;  // correctly rounded
 
     uint2* out = reinterpret_cast<uint2*>(xq + m * K);
-    for (int64_t v = tid; v < nvec; v += kActThreads) {
-        const uint4 d = row[v];
+    auto emit = [&](int v, const uint4 d, const uint4 gv) {
         const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
-        uint32_t gw[4] = {0, 0, 0, 0};
-        if (FUSED) {
-            const uint4 g = grow[v];
-            gw[0] = g.x; gw[1] = g.y; gw[2] = g.z; gw[3] = g.w;
-        }
-        uint32_t packed[2] = {0, 0};
+        const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+        out[v] = quant8(dw, gw, FUSED, inv);
+    };
+    if (cached) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                float z = bf16_to_f32((dw[i] >> (16 * h)) & 0xFFFFu);
-                if (FUSED) z = z * bf16_to_f32((gw[i] >> (16 * h)) & 0xFFFFu);
-                float t = __builtin_rintf(z * inv);
-                t = fminf(fmaxf(t, -127.0f), 127.0f);
-                const uint32_t b = (uint32_t)((int)t) & 0xFFu;
-                const int e = 2 * i + h;  // element 0..7 of the vector
-                packed[e / 4] |= b << (8 * (e % 4));
-            }
+        for (int j = 0; j < kActCache; ++j) {
+            const int v = tid + kActThreads * j;
+            if (v < nvec) emit(v, cx[j], FUSED ? cg[j] : cx[j]);
         }
-        out[v] = make_uint2(packed[0], packed[1]);
+    } else {
+        for (int v = tid; v < nvec; v += kActThreads) emit(v, row[v], FUSED ? grow[v] : row[v]);
     }
     if (tid == 0) {
         if (FUSED) {
@@ -109,6 +144,89 @@ __global__ __launch_bounds__(kActThreads) void k_act_quant(
     }
 }
 
+// h = bf16_rne((relu(g)^2) * u) for one 4-wide fp32 vector, as two dwords of
+// bf16 bits.
+__device__ __forceinline__ uint2 relu2_gate4(const float4 g, const float4 u) {
+    auto one = [](float gv, float uv) -> uint32_t {
+        const float r = gv > 0.0f ? gv : 0.0f;
+        const float sq = r * r;
+        return f32_to_bf16_rne(sq * uv);
+    };
+    return make_uint2(one(g.x, u.x) | (one(g.y, u.y) << 16), one(g.z, u.z) | (one(g.w, u.w) << 16));
+}
+
+// Squared-ReLU gating fused with per-token absmax quantisation of its bf16
+// result: identical to bl_relu2_glu followed by bl_quantize_acts (plain).
+constexpr int kGluCache = 12;  // 4-element vectors cached per thread (K <= 12288)
+
+__global__ __launch_bounds__(kActThreads) void k_relu2_glu_quant(
+    const float* __restrict__ gate, const float* __restrict__ up, int64_t K,
+    int8_t* __restrict__ hq, float* __restrict__ scale) {
+    __shared__ float s_max[kActThreads / kWave];
+    const int64_t m = blockIdx.x;
+    const float4* grow = reinterpret_cast<const float4*>(gate + m * K);
+    const float4* urow = reinterpret_cast<const float4*>(up + m * K);
+    const int tid = threadIdx.x;
+    const int nvec = (int)(K / 4);
+    const bool cached = nvec <= kGluCache * kActThreads;
+
+    uint2 ch[kGluCache];
+    float amax = 0.0f;
+    auto absmax2 = [&](const uint2 h) {
+        amax = fmaxf(amax, fabsf(bf16_to_f32(h.x & 0xFFFFu)));
+        amax = fmaxf(amax, fabsf(bf16_to_f32(h.x >> 16)));
+        amax = fmaxf(amax, fabsf(bf16_to_f32(h.y & 0xFFFFu)));
+        amax = fmaxf(amax, fabsf(bf16_to_f32(h.y >> 16)));
+    };
+    if (cached) {
+        float4 cg[kGluCache], cu[kGluCache];
+#pragma unroll
+        for (int j = 0; j < kGluCache; ++j) {
+            const int v = tid + kActThreads * j;
+            if (v < nvec) {
+                cg[j] = grow[v];
+                cu[j] = urow[v];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kGluCache; ++j) {
+            if (tid + kActThreads * j < nvec) {
+                ch[j] = relu2_gate4(cg[j], cu[j]);
+                absmax2(ch[j]);
+            }
+        }
+    } else {
+        for (int v = tid; v < nvec; v += kActThreads) absmax2(relu2_gate4(grow[v], urow[v]));
+    }
+    amax = block_reduce(amax, s_max, true);
+    const float a = amax > 1e-5f ? amax : 1e-5f;
+    const float inv = 127.0f / a;
+
+    uint32_t* out = reinterpret_cast<uint32_t*>(hq + m * K);
+    auto emit = [&](int v, const uint2 h) {
+        const uint32_t hw[2] = {h.x, h.y};
+        uint32_t packed = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float z = bf16_to_f32((hw[e / 2] >> (16 * (e % 2))) & 0xFFFFu);
+            float t = __builtin_rintf(z * inv);
+            t = fminf(fmaxf(t, -127.0f), 127.0f);
+            packed |= ((uint32_t)((int)t) & 0xFFu) << (8 * e);
+        }
+        out[v] = packed;
+    };
+    if (cached) {
+#pragma unroll
+        for (int j = 0; j < kGluCache; ++j) {
+            const int v = tid + kActThreads * j;
+            if (v < nvec) emit(v, ch[j]);
+        }
+    } else {
+        for (int v = tid; v < nvec; v += kActThreads) emit(v, relu2_gate4(grow[v], urow[v]));
+    }
+    if (tid == 0) scale[m] = a / 127.0f;
+}
+
 hipError_t launch_quantize_acts(const uint16_t* x, int64_t M, int64_t K, const uint16_t* gain,
                                 float rms_eps, int8_t* xq, float* scale, hipStream_t stream) {
     if (gain)
@@ -117,6 +235,13 @@ hipError_t launch_quantize_acts(const uint16_t* x, int64_t M, int64_t K, const u
     else
         hipLaunchKernelGGL(k_act_quant<false>, dim3((unsigned)M), dim3(kActThreads), 0, stream, x,
                            K, gain, rms_eps, xq, scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_relu2_glu_quant(const float* gate, const float* up, int64_t M, int64_t K,
+                                  int8_t* hq, float* scale, hipStream_t stream) {
+    hipLaunchKernelGGL(k_relu2_glu_quant, dim3((unsigned)M), dim3(kActThreads), 0, stream, gate,
+                       up, K, hq, scale);
     return hipGetLastError();
 }
 

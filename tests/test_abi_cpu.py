@@ -91,6 +91,15 @@ def test_invalid_arguments_rejected_before_launch(L):
     # glue
     assert L.bl_relu2_glu(A, A, 0, A, None) == E
     assert L.bl_relu2_glu(A, MIS, 4, A, None) == E
+    assert L.bl_relu2_glu_quant(A, A, 1, 100, A, A, None) == E
+    assert L.bl_relu2_glu_quant(A, A, 0, 64, A, A, None) == E
+    assert L.bl_relu2_glu_quant(A, MIS, 1, 64, A, A, None) == E
+    assert L.bl_relu2_glu_quant(A, A, 1, 64, A, None, None) == E
+    # pair
+    assert L.bl_bitlinear_pair(A, A, 1, 64, A, A, 16, A, None, A, 16, A, None) == E
+    assert L.bl_bitlinear_pair(A, A, 1, 64, A, A, 16, A, A, A, 0, A, None) == E
+    assert L.bl_bitlinear_pair(A, A, 1, 96, A, A, 16, A, A, A, 16, A, None) == E
+    assert L.bl_bitlinear_pair(A, A, 1, 64, MIS, A, 16, A, A, A, 16, A, None) == E
 
 
 def test_no_device_status(L):
@@ -102,6 +111,8 @@ def test_no_device_status(L):
     assert L.bl_quantize_acts(A, 1, 64, None, 0.0, A, A, None) == D
     assert L.bl_quantize_weights(A, 16, 64, A, A, A, 8 * 16, None) == D
     assert L.bl_relu2_glu(A, A, 4, A, None) == D
+    assert L.bl_relu2_glu_quant(A, A, 1, 64, A, A, None) == D
+    assert L.bl_bitlinear_pair(A, A, 1, 64, A, A, 16, A, A, A, 16, A, None) == D
 
 
 def test_binding_fails_loudly_without_gpu():

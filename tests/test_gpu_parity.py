@@ -366,3 +366,59 @@ def test_relu2_glu_parity():
         h = bl.relu2_glu(dev_f32(g.ravel()[:count]), dev_f32(u.ravel()[:count]))
         assert np.array_equal(h.view(torch.int16).cpu().numpy().view(np.uint16),
                               oracle.relu2_glu(g.ravel()[:count], u.ravel()[:count]))
+
+
+# --------------------------------------------------------- fused entries ----
+
+@pytest.mark.parametrize("M,K,N1,N2", [(1, 2560, 6912, 6912), (4, 3200, 8640, 8640),
+                                       (16, 2560, 200, 57), (40, 320, 300, 129)])
+def test_bitlinear_pair_matches_two_calls_and_oracle(M, K, N1, N2):
+    q1, xq, xs, g1 = _product_case(M, K, N1, 60)
+    rng = np.random.default_rng(61)
+    q2 = rand_codes(rng, N2, K)
+    g2 = np.float32(0.0203)
+    args = (torch.from_numpy(xq).to(DEV), dev_f32(xs))
+    W1, W2 = dev_packed(oracle.pack(q1)), dev_packed(oracle.pack(q2))
+    G1, G2 = dev_f32([g1]), dev_f32([g2])
+    y1, y2 = bl.bitlinear_pair(*args, W1, G1, W2, G2)
+    r1 = bl.bitlinear(*args, W1, G1)
+    r2 = bl.bitlinear(*args, W2, G2)
+    assert torch.equal(y1.view(torch.int32), r1.view(torch.int32))
+    assert torch.equal(y2.view(torch.int32), r2.view(torch.int32))
+    assert_y_close(y1.cpu().numpy(), oracle.bitlinear(xq, xs, q1, g1)[0], "pair 1")
+    assert_y_close(y2.cpu().numpy(), oracle.bitlinear(xq, xs, q2, g2)[0], "pair 2")
+
+
+@pytest.mark.parametrize("M,K", [(1, 6912), (4, 6912), (16, 8640), (3, 64), (2, 28672),
+                                 (300, 2560)])
+def test_relu2_glu_quant_matches_oracle(M, K):
+    g, u = wl.ffn_hidden(62, K, M, K)
+    hq, hs = bl.relu2_glu_quant(dev_f32(g), dev_f32(u))
+    h_ref = oracle.relu2_glu(g, u)
+    hq_ref, hs_ref = oracle.act_quant(h_ref)
+    assert np.array_equal(hq.cpu().numpy(), hq_ref)
+    assert np.array_equal(hs.cpu().numpy(), hs_ref)
+    # Same bits as the two unfused calls.
+    h = bl.relu2_glu(dev_f32(g), dev_f32(u))
+    hq2, hs2 = bl.quantize_acts(h)
+    assert torch.equal(hq, hq2) and torch.equal(hs, hs2)
+
+
+def test_ffn_block_fused_path_equals_unfused():
+    """Decode FFN step through the fused entry points gives the same bits as
+    the unfused sequence (which the stage-wise test checks against the oracle)."""
+    wid = 2
+    _, projs, _ = wl.WORKLOADS[wid]
+    dev = {name: gpu_weights(wl.weights(wid, i, N, K)) for i, (name, K, N) in enumerate(projs)}
+    for M in (1, 4, 16):
+        x = dev_bf16(wl.activations(wid, 9, M, 2560))
+        xq, xs = bl.quantize_acts(x)
+        yg, yu = bl.bitlinear_pair(xq, xs, *dev["gate"], *dev["up"])
+        hq, hs = bl.relu2_glu_quant(yg, yu)
+        y = bl.bitlinear(hq, hs, *dev["down"])
+        rg = bl.bitlinear(xq, xs, *dev["gate"])
+        ru = bl.bitlinear(xq, xs, *dev["up"])
+        rq, rs = bl.quantize_acts(bl.relu2_glu(rg, ru))
+        ry = bl.bitlinear(rq, rs, *dev["down"])
+        assert torch.equal(hq, rq) and torch.equal(hs, rs)
+        assert torch.equal(y.view(torch.int32), ry.view(torch.int32))
