@@ -14,12 +14,13 @@
 // l -> row l % 16, k-group l / 16) and every KS-th 256-weight chunk of K. Each
 // lane loads 16 bytes of its row per chunk (4 packed words = 64 weights); the
 // 4 lanes of a row cover 64 contiguous bytes. A wave issues the loads of up to
-// 8 chunks at once, before anything else, so the whole weight stream of a
+// 4 chunks at once, before anything else, so the whole weight stream of a
 // small matrix is in flight within the first microsecond; longer rows are
-// double-buffered in batches of 8. Word s of a lane's 16 bytes feeds MFMA s;
-// the B operand (lane l -> token l % 16) reads the 16 activation bytes of the
-// same k positions from LDS, where the whole [M][K] int8 activation block is
-// staged once per workgroup. Tokens >= M read zero. Waves that split K for
+// double-buffered in batches of 4. Registers are capped for 8 waves per SIMD,
+// which keeps the 70B-class grids resident in one round. Word s of a lane's
+// 16 bytes feeds MFMA s; the B operand (lane l -> token l % 16) reads the 16
+// activation bytes of the same k positions from LDS, where the whole [M][K]
+// int8 activation block is staged once per workgroup. Tokens >= M read zero. Waves that split K for
 // the same rows reduce in LDS; the epilogue rescales by x_scale[m] * gamma.
 //
 // One launch may cover two weight matrices that share the input (the gate
@@ -37,7 +38,7 @@ constexpr int kGemvThreads = 256;
 constexpr int kGemvMaxM = 16;
 constexpr int64_t kGemvMaxXBytes = 128 * 1024;
 constexpr int kXPad = 16;  // LDS row padding (bytes) against bank conflicts
-constexpr int kNB = 8;     // chunks per lane in flight per batch
+constexpr int kNB = 4;     // chunks per lane in flight per batch
 
 struct GemvMat {
     const uint32_t* W;
@@ -52,7 +53,7 @@ struct GemvArgs {
 };
 
 template <int RG>
-__global__ __launch_bounds__(kGemvThreads) void k_gemv(const int8_t* __restrict__ xq,
+__global__ __launch_bounds__(kGemvThreads, 8) void k_gemv(const int8_t* __restrict__ xq,
                                                        const float* __restrict__ xs, int M,
                                                        int K, GemvArgs args) {
     constexpr int KS = 4 / RG;  // waves splitting K within a row group
