@@ -56,6 +56,51 @@ __device__ __forceinline__ v4i expand_word_neg(uint32_t w) {
     return r;
 }
 
+typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+
+// LDS byte offset of a pointer into shared memory.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+    return (uint32_t)(size_t)(const lds_u8_t*)p;
+}
+
+// 16 bytes per lane from global memory straight into LDS at
+// lds_base + 16 * lane (global_load_lds_dwordx4). lds_base must be wave-
+// uniform. Issued through asm so that the compiler adds no conservative
+// waits before later LDS reads; completion is tracked with explicit vmcnt
+// waits (vector memory operations complete in issue order). M0 is saved and
+// restored around the load.
+__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(gptr), "s"(lds_base)
+        : "memory");
+}
+
+// s_waitcnt with vmcnt = n (other counters unconstrained), n < 64.
+#define BL_WAIT_VMCNT(n) \
+    __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | ((((n) >> 4) & 3) << 14))
+
+// Wait until at most n (0..8, wave-uniform) vector memory operations are
+// outstanding.
+__device__ __forceinline__ void wait_vmcnt_le8(int n) {
+    switch (n) {
+        case 0: BL_WAIT_VMCNT(0); break;
+        case 1: BL_WAIT_VMCNT(1); break;
+        case 2: BL_WAIT_VMCNT(2); break;
+        case 3: BL_WAIT_VMCNT(3); break;
+        case 4: BL_WAIT_VMCNT(4); break;
+        case 5: BL_WAIT_VMCNT(5); break;
+        case 6: BL_WAIT_VMCNT(6); break;
+        case 7: BL_WAIT_VMCNT(7); break;
+        default: BL_WAIT_VMCNT(8); break;
+    }
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));

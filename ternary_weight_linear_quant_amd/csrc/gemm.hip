@@ -44,29 +44,6 @@ constexpr int kBRow = kBK / 4;      // packed weight bytes per row per stage
 __device__ __forceinline__ int swz_a(int r) { return (r ^ ((r >> 3) & 3)) & 7; }
 __device__ __forceinline__ int swz_b(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
 
-// s_waitcnt with vmcnt = n (other counters unconstrained), n < 64.
-#define BL_WAIT_VMCNT(n) \
-    __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | ((((n) >> 4) & 3) << 14))
-
-typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
-
-// 16 bytes per lane from global memory straight into LDS at
-// lds_base + 16 * lane (global_load_lds_dwordx4). lds_base must be wave-
-// uniform. Issued through asm so that the compiler does not add its own
-// conservative waits before later LDS reads; completion is tracked with
-// explicit vmcnt waits. M0 is saved and restored around the load.
-__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %2\n\t"
-        "global_load_lds_dwordx4 %1, off\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(gptr), "s"(lds_base)
-        : "memory");
-}
-
 // WPE: waves per SIMD the register allocation must allow (2 lets two
 // workgroups share a CU so that one's barrier gaps are filled by the other).
 template <int BM, int BN, int WGM, int WGN, int STAGES, int WPE>

@@ -20,7 +20,11 @@
 // which keeps the 70B-class grids resident in one round. Word s of a lane's
 // 16 bytes feeds MFMA s; the B operand (lane l -> token l % 16) reads the 16
 // activation bytes of the same k positions from LDS, where the whole [M][K]
-// int8 activation block is staged once per workgroup. Tokens >= M read zero. Waves that split K for
+// int8 activation block is staged once per workgroup by direct global-to-LDS
+// loads issued before the weight loads, token-minor so that a fragment read
+// is 16 consecutive 16-byte slots. Only that staging is waited for before the
+// workgroup barrier, so the weight stream stays in flight. Tokens >= M read
+// zero. Waves that split K for
 // the same rows reduce in LDS; the epilogue rescales by x_scale[m] * gamma.
 //
 // One launch may cover two weight matrices that share the input (the gate
@@ -37,8 +41,6 @@ namespace bl {
 constexpr int kGemvThreads = 256;
 constexpr int kGemvMaxM = 16;
 constexpr int64_t kGemvMaxXBytes = 128 * 1024;
-constexpr int kXPad = 16;  // LDS row padding (bytes) against bank conflicts
-constexpr int kNB = 4;     // chunks per lane in flight per batch
 
 struct GemvMat {
     const uint32_t* W;
@@ -52,8 +54,10 @@ struct GemvArgs {
     GemvMat mat[2];
 };
 
-template <int RG>
-__global__ __launch_bounds__(kGemvThreads, 8) void k_gemv(const int8_t* __restrict__ xq,
+// R: ring of chunk loads in flight per lane; WPE: waves per SIMD the register
+// allocation must allow (short rows want many waves, long rows a deep ring).
+template <int RG, int R, int WPE>
+__global__ __launch_bounds__(kGemvThreads, WPE) void k_gemv(const int8_t* __restrict__ xq,
                                                        const float* __restrict__ xs, int M,
                                                        int K, GemvArgs args) {
     constexpr int KS = 4 / RG;  // waves splitting K within a row group
@@ -66,7 +70,8 @@ __global__ __launch_bounds__(kGemvThreads, 8) void k_gemv(const int8_t* __restri
     const int N = P.N;
 
     const int tid = threadIdx.x;
-    const int wave = tid / kWave, lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int lane = tid % kWave;
     const int rg = wave % RG, ks = wave / RG;
     const int r = lane % 16, g = lane / 16;
     const int row0 = lb * (16 * RG) + rg * 16;
@@ -77,54 +82,64 @@ __global__ __launch_bounds__(kGemvThreads, 8) void k_gemv(const int8_t* __restri
     // This wave's chunks: c_i = ks + KS * i, i < nw.
     const int nw = ks < nfull ? (nfull - ks + KS - 1) / KS : 0;
 
-    // 1. First batch of weight loads, before anything waits.
-    uint4 wb[kNB];
-#pragma unroll
-    for (int i = 0; i < kNB; ++i)
-        if (i < nw) wb[i] = *reinterpret_cast<const uint4*>(wrow + 16 * (ks + KS * i));
-
-    // 2. Stage the activations: M rows of K bytes, 16 B per thread per step.
-    const int xstride = K + kXPad;
-    {
-        const int cpr = K / 16;  // 16-byte chunks per row
-        const int nchunks = M * cpr;
-        const uint4* src = reinterpret_cast<const uint4*>(xq);
-        for (int c = tid; c < nchunks; c += kGemvThreads) {
-            const int mm = c / cpr, cc = c - mm * cpr;
-            *reinterpret_cast<uint4*>(smem + mm * xstride + 16 * cc) = src[c];
+    // 1. Activations straight into LDS, issued first. LDS layout: 16-byte
+    //    chunk j of token t at slot j*M + t, so the 16 tokens of a B fragment
+    //    read 16 consecutive slots. Each DMA instruction fills 64 slots.
+    const int cpr = K / 16;
+    const int total = M * cpr;
+    const uint32_t xbase = lds_offset(smem);
+    for (int p0 = wave * kWave; p0 < total; p0 += kGemvThreads) {
+        const int p = p0 + lane;
+        if (p < total) {
+            const int j = p / M, t = p - j * M;
+            lds_dma16(xq + (size_t)t * K + 16 * j, xbase + 16 * p0);
         }
     }
+    asm volatile("" ::: "memory");
+
+    // 2. Up to R chunks of weight loads, before anything waits.
+    uint4 wb[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+        if (i < nw) wb[i] = *reinterpret_cast<const uint4*>(wrow + 16 * (ks + KS * i));
+    asm volatile("" ::: "memory");
+
+    // 3. Wait for this wave's activation DMA only (the weight loads, issued
+    //    after it, may stay in flight), then make every wave's part visible.
+    wait_vmcnt_le8(min(nw, R));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+
     const int tok = lane % 16;
     const bool tok_ok = tok < M;
-    const int8_t* xrow =
-        reinterpret_cast<const int8_t*>(smem) + (tok_ok ? tok : 0) * xstride + 64 * g;
-    __syncthreads();
+    const int8_t* xl = reinterpret_cast<const int8_t*>(smem) + 16 * (tok_ok ? tok : 0);
 
     v4i acc = {0, 0, 0, 0};
     const v4i zero = {0, 0, 0, 0};
+    // B fragment of chunk c, sub-step s: activation chunk j = 16c + 4g + s.
     auto process = [&](const uint4 wv, int c) {
         const uint32_t w4[4] = {wv.x, wv.y, wv.z, wv.w};
-        const int8_t* xb = xrow + 256 * c;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const v4i a = expand_word_neg(w4[s]);
-            const v4i b = tok_ok ? *reinterpret_cast<const v4i*>(xb + 16 * s) : zero;
+            const int j = 16 * c + 4 * g + s;
+            const v4i b = tok_ok ? *reinterpret_cast<const v4i*>(xl + 16 * j * M) : zero;
             acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc, 0, 0, 0);
         }
     };
 
-    // 3. Batches: issue the next batch's loads, then consume the current one.
-    for (int b0 = 0; b0 < nw; b0 += kNB) {
-        uint4 wn[kNB];
-        const int nb = b0 + kNB;
+    // 4. Ring of R chunk slots: consume a chunk, then refill its slot with
+    //    the chunk R ahead, so up to R loads stay in flight.
+    for (int b0 = 0; b0 < nw; b0 += R) {
 #pragma unroll
-        for (int i = 0; i < kNB; ++i)
-            if (nb + i < nw) wn[i] = *reinterpret_cast<const uint4*>(wrow + 16 * (ks + KS * (nb + i)));
-#pragma unroll
-        for (int i = 0; i < kNB; ++i)
-            if (b0 + i < nw) process(wb[i], ks + KS * (b0 + i));
-#pragma unroll
-        for (int i = 0; i < kNB; ++i) wb[i] = wn[i];
+        for (int i = 0; i < R; ++i) {
+            const int ci = b0 + i;
+            if (ci < nw) {
+                process(wb[i], ks + KS * ci);
+                if (ci + R < nw)
+                    wb[i] = *reinterpret_cast<const uint4*>(wrow + 16 * (ks + KS * (ci + R)));
+            }
+        }
     }
 
     // Tail: KW % 16 words (a multiple of 4, since K % 64 == 0). Lane group g
@@ -135,11 +150,11 @@ __global__ __launch_bounds__(kGemvThreads, 8) void k_gemv(const int8_t* __restri
         const uint4 wv = gv ? *reinterpret_cast<const uint4*>(wrow + 16 * nfull)
                             : make_uint4(0, 0, 0, 0);
         const uint32_t w4[4] = {wv.x, wv.y, wv.z, wv.w};
-        const int8_t* xb = xrow + 256 * nfull;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const v4i a = gv ? expand_word_neg(w4[s]) : zero;
-            const v4i b = (gv && tok_ok) ? *reinterpret_cast<const v4i*>(xb + 16 * s) : zero;
+            const int j = 16 * nfull + 4 * g + s;
+            const v4i b = (gv && tok_ok) ? *reinterpret_cast<const v4i*>(xl + 16 * j * M) : zero;
             acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc, 0, 0, 0);
         }
     }
@@ -174,22 +189,30 @@ bool gemv_supported(int64_t M, int64_t K) {
     return M >= 1 && M <= kGemvMaxM && M * K <= kGemvMaxXBytes;
 }
 
-template <int RG>
-static hipError_t launch_gemv_rg(const int8_t* xq, const float* xs, int M, int K,
+template <int RG, int R, int WPE>
+static hipError_t launch_gemv_cfg(const int8_t* xq, const float* xs, int M, int K,
                                  const GemvArgs& args, hipStream_t stream) {
-    const size_t lds = (size_t)M * (K + kXPad);
+    const size_t lds = (size_t)M * K;
     static bool attr_set = false;
     if (lds > 64 * 1024 && !attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv<RG>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv<RG, R, WPE>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)(kGemvMaxXBytes + kGemvMaxM * kXPad));
+                                           (int)kGemvMaxXBytes);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     const int blocks = args.mat[0].blocks + args.mat[1].blocks;
-    hipLaunchKernelGGL(k_gemv<RG>, dim3(blocks), dim3(kGemvThreads), lds, stream, xq, xs, M, K,
+    hipLaunchKernelGGL((k_gemv<RG, R, WPE>), dim3(blocks), dim3(kGemvThreads), lds, stream, xq, xs, M, K,
                        args);
     return hipGetLastError();
+}
+
+// Rows of more than 8 chunks per wave (K > 8192) take the deep ring.
+static hipError_t launch_gemv_auto(const int8_t* xq, const float* xs, int M, int K,
+                                   const GemvArgs& args, hipStream_t stream) {
+    const int chunks_per_wave = (K / 256 + 3) / 4;
+    if (chunks_per_wave > 8) return launch_gemv_cfg<1, 8, 1>(xq, xs, M, K, args, stream);
+    return launch_gemv_cfg<1, 4, 8>(xq, xs, M, K, args, stream);
 }
 
 static GemvMat make_mat(const uint32_t* Wp, const float* gamma, int N, float* y, int32_t* acc,
@@ -210,7 +233,7 @@ hipError_t launch_gemv(const int8_t* xq, const float* xs, int M, int K, const ui
     GemvArgs a;
     a.mat[0] = make_mat(Wp, gamma, N, y, acc, 16);
     a.mat[1] = make_mat(nullptr, nullptr, 1, nullptr, nullptr, 16);
-    return launch_gemv_rg<1>(xq, xs, M, K, a, stream);
+    return launch_gemv_auto(xq, xs, M, K, a, stream);
 }
 
 hipError_t launch_gemv_pair(const int8_t* xq, const float* xs, int M, int K, const uint32_t* W1,
@@ -220,7 +243,7 @@ hipError_t launch_gemv_pair(const int8_t* xq, const float* xs, int M, int K, con
     GemvArgs a;
     a.mat[0] = make_mat(W1, g1, N1, y1, nullptr, 16);
     a.mat[1] = make_mat(W2, g2, N2, y2, nullptr, 16);
-    return launch_gemv_rg<1>(xq, xs, M, K, a, stream);
+    return launch_gemv_auto(xq, xs, M, K, a, stream);
 }
 
 }  // namespace bl
