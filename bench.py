@@ -3,16 +3,17 @@
 
 Headline (`value`): decode packed-weight GB/s of a 2B4T-shaped FFN stack
 (gate/up 2560 -> 6912, squared-ReLU gating, down 6912 -> 2560) at M = 1, 4
-and 16 tokens. One step runs, for each M and each of L layers: per-token act
-quant -> gate and up BitLinears (one launch) -> relu(gate)^2 * up fused with
-the act quant of its output -> down BitLinear. The L layers hold distinct copies of the packed weights (identical
+and 16 tokens. One step runs, for each M and each of L layers, one
+bl_ffn_relu2 call: per-token act quant -> gate and up BitLinears ->
+relu(gate)^2 * up -> act quant -> down BitLinear (two launches for M <= 4,
+four for M = 16). The L layers hold distinct copies of the packed weights (identical
 content, distinct addresses) whose total exceeds twice the 256 MB Infinity
 Cache, so every BitLinear streams its weights from HBM. Weights are quantised
 once before the timed region (offline in the method); that pass is timed and
 reported separately. The step is captured in a HIP graph and replayed.
 
-Also reported: the decode GEMV's roofline (per-launch HIP-event timing of the
-same launches), the prefill GEMM at M = 4096 (int8 TOPS against the MFMA
+Also reported: the roofline of the decode weight-stream kernel (HIP-event
+timing of a graph of its launches), per-M rates, the prefill GEMM at M = 4096 (int8 TOPS against the MFMA
 peak), and the CPU oracle timed on a bounded sample of the decode step.
 
     python bench.py [--steps K] [--warmup W] [--layers L]
@@ -143,42 +144,47 @@ def main():
     Kin, Nff = shapes["gate"]
     bufs = {}
     for M in Ms:
-        x = bf16_dev(wl.activations(DECODE_WORKLOAD, 9, M, Kin))
         bufs[M] = dict(
-            x=x,
-            xq=torch.empty((M, Kin), dtype=torch.int8, device=dev),
-            xs=torch.empty(M, dtype=torch.float32, device=dev),
-            yg=torch.empty((M, Nff), dtype=torch.float32, device=dev),
-            yu=torch.empty((M, Nff), dtype=torch.float32, device=dev),
-            hq=torch.empty((M, Nff), dtype=torch.int8, device=dev),
-            hs=torch.empty(M, dtype=torch.float32, device=dev),
-            yd=torch.empty((M, Kin), dtype=torch.float32, device=dev),
+            x=bf16_dev(wl.activations(DECODE_WORKLOAD, 9, M, Kin)),
+            y=torch.empty((M, Kin), dtype=torch.float32, device=dev),
+            ws=bl.ffn_relu2_workspace(M, Kin, Nff, dev),
         )
 
-    def decode_step(gemv_only=False):
-        """One decode pass: for each M and layer, act quant -> gate/up BitLinear
-        pair (one launch) -> squared-ReLU gating fused with the act quant of its
-        output -> down BitLinear. gemv_only replays just the two BitLinear
-        launches (on the buffers a full step left behind) for the roofline."""
+    def decode_pass(M):
+        """All L layers at one token count: act quant -> gate and up
+        BitLinears -> relu(gate)^2 * up -> act quant -> down BitLinear, as one
+        bl_ffn_relu2 call per layer (two launches for M <= 4, four above)."""
+        B = bufs[M]
+        for lay in layers:
+            bl.ffn_relu2(B["x"], *lay["gate"], *lay["up"], *lay["down"], workspace=B["ws"],
+                         out=B["y"])
+
+    def decode_step():
         for M in Ms:
-            B = bufs[M]
-            for lay in layers:
-                if not gemv_only:
-                    bl.quantize_acts(B["x"], out=(B["xq"], B["xs"]))
-                bl.bitlinear_pair(B["xq"], B["xs"], *lay["gate"], *lay["up"],
-                                  out=(B["yg"], B["yu"]))
-                if not gemv_only:
-                    bl.relu2_glu_quant(B["yg"], B["yu"], out=(B["hq"], B["hs"]))
-                bl.bitlinear(B["hq"], B["hs"], *lay["down"], out=B["yd"])
+            decode_pass(M)
+
+    def capture(fn):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            fn()
+        torch.cuda.synchronize()
+        return gr
+
+    def time_graph(gr, reps):
+        gr.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            gr.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
 
     decode_step()
     torch.cuda.synchronize()
-    graph = None
-    if not args.no_graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            decode_step()
-        torch.cuda.synchronize()
+    graph = None if args.no_graph else capture(decode_step)
 
     def replay():
         if graph is not None:
@@ -200,46 +206,41 @@ def main():
     packed_per_step = packed_per_layer * L * len(Ms)
     value = packed_per_step / (ms_per_step * 1e-3) / 1e9
 
-    # Roofline of the decode GEMV: the same BitLinear launches of one step
-    # (gate/up pair + down, every M and layer, same buffers) captured alone in
-    # a HIP graph and timed with HIP events on the replaying stream.
-    ggraph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(ggraph):
-        decode_step(gemv_only=True)
-    torch.cuda.synchronize()
-    ggraph.replay()
-    torch.cuda.synchronize()
-    reps = 5
-    ga = torch.cuda.Event(enable_timing=True)
-    gb = torch.cuda.Event(enable_timing=True)
-    ga.record()
-    for _ in range(reps):
-        ggraph.replay()
-    gb.record()
-    torch.cuda.synchronize()
-    gemv_ms = ga.elapsed_time(gb) / reps
-    gemv_launches = 2 * L * len(Ms)
-    Kd, Nd = shapes["down"]
-    gemv_bytes = 0
+    # Per token count, and the roofline of the weight-streaming kernel: the
+    # M = 1 pass is nothing but k_ffn_gemv launches (gate/up + down per
+    # layer), replayed from its own HIP graph and timed with HIP events on
+    # the replaying stream.
+    per_M = {}
     for M in Ms:
-        pair = 2 * (Nff * Kin // 4 + 4 + 4 * M * Nff) + M * Kin + 4 * M
-        down = Nd * Kd // 4 + M * Kd + 4 * M + 4 + 4 * M * Nd
-        gemv_bytes += L * (pair + down)
-    achieved = gemv_bytes / (gemv_ms * 1e-3) / 1e9
+        gm = capture(lambda M=M: decode_pass(M))
+        ms = time_graph(gm, 5)
+        per_M[f"M{M}"] = {"ms": round(ms, 4), "launches_per_layer": 2 if M <= 4 else 4,
+                          "packed_GBps": round(packed_per_layer * L / (ms * 1e-3) / 1e9, 1)}
+        if M == 1:
+            ms1 = ms
+        del gm
+    Kd, Nd = shapes["down"]
+    M = 1
+    bytes_a = 2 * (Nff * Kin // 4 + 4) + 2 * M * Kin + 2 * M * Nff
+    bytes_b = Nd * Kd // 4 + 4 + 2 * M * Kd + 4 * M * Nd
+    launches = 2 * L
+    achieved = (bytes_a + bytes_b) * L / (ms1 * 1e-3) / 1e9
     roofline = {
-        "bound": "hbm", "kernel": "k_gemv (decode GEMV: gate/up pair and down launches)",
+        "bound": "hbm",
+        "kernel": "k_ffn_gemv (decode weight stream: gate/up+gating and act-quant+down "
+                  "launches of the M=1 pass)",
         "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-        "launches": gemv_launches, "avg_us": round(1e3 * gemv_ms / gemv_launches, 3),
-        "alg_bytes_per_launch": round(gemv_bytes / gemv_launches),
-        "timing": "HIP graph of the step's GEMV launches only, events on the replay stream",
+        "launches": launches, "avg_us": round(1e3 * ms1 / launches, 3),
+        "alg_bytes_per_launch": round((bytes_a + bytes_b) / 2),
+        "timing": "HIP graph of the M=1 pass (k_ffn_gemv launches only), HIP events on "
+                  "the replay stream",
     }
-    del ggraph
     used_graph = graph is not None
     del layers, graph
     torch.cuda.empty_cache()
-    print(f"decode: {value:.1f} GB/s per step, GEMV {achieved:.1f} GB/s "
-          f"({roofline['avg_us']} us/launch)", file=sys.stderr, flush=True)
+    print(f"decode: {value:.1f} GB/s per step, weight-stream kernel {achieved:.1f} GB/s "
+          f"({roofline['avg_us']} us/launch), per M {per_M}", file=sys.stderr, flush=True)
 
     # ------------------------------------------------ prefill GEMM leg ----
     prefill = None
@@ -362,6 +363,7 @@ def main():
             "parallelism": "single GPU",
         },
         "frac_hbm_step": round(value / HBM_PEAK_GBS, 4),
+        "per_M": per_M,
         "roofline": roofline,
         "cpu_baseline": cpu_baseline,
         "prefill": prefill,

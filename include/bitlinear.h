@@ -177,6 +177,35 @@ int bl_bitlinear_pair(const int8_t* x_q, const float* x_scale, int64_t M, int64_
 int bl_relu2_glu_quant(const float* gate, const float* up, int64_t M, int64_t K, int8_t* h_q,
                        float* h_scale, void* stream);
 
+/* Bytes of the workspace bl_ffn_relu2 needs for these shapes (0 if the
+ * shapes are invalid). Host-only. */
+size_t bl_ffn_relu2_workspace_bytes(int64_t M, int64_t K, int64_t N_ff);
+
+/* One FFN step of a 2B4T-style block (no residual, no norm):
+ *   x_q, x_scale = quantize_acts(x)                 (plain, per token)
+ *   h = bf16_rne(relu(BitLinear(x, W_gate))^2 * BitLinear(x, W_up))
+ *   y = BitLinear(quantize_acts(h), W_down)
+ * with every step exactly as the single calls compute it, so y has the bits
+ * of bl_quantize_acts -> bl_bitlinear (gate, up) -> bl_relu2_glu ->
+ * bl_quantize_acts -> bl_bitlinear (down). Source: inferownia.pl page above,
+ * section "Zrób to sam — Microsoft wypuścił konkretny model" (2B4T, squared
+ * ReLU) and section "Mnożenie? Jakie mnożenie"; comrad404.com «Метод…»
+ * (8-bit activations before each low-bit product).
+ *
+ *   x          in   bf16 [M][K] (raw bits).
+ *   W_gate, W_up    packed [N_ff][K/16] with their gammas (device).
+ *   W_down     in   packed [K][N_ff/16] with its gamma (device).
+ *   y          out  fp32 [M][K].
+ *   workspace  tmp  >= bl_ffn_relu2_workspace_bytes(M, K, N_ff) bytes,
+ *                   256-byte aligned; contents undefined afterwards.
+ * Shapes follow the rules above for (M, K), (M, N_ff) and both weight
+ * matrices. For M <= 4 (M dividing 256) the step runs in two launches, with
+ * each workgroup quantising its activations itself; otherwise in four. */
+int bl_ffn_relu2(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate,
+                 const float* gamma_gate, const uint32_t* W_up, const float* gamma_up,
+                 int64_t N_ff, const uint32_t* W_down, const float* gamma_down, float* y,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

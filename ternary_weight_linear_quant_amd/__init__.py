@@ -15,7 +15,8 @@ import ctypes
 import os
 
 __all__ = ["lib", "library_path", "quantize_weights", "quantize_acts", "bitlinear",
-           "bitlinear_pair", "relu2_glu", "relu2_glu_quant", "BitLinearError", "packed_bytes"]
+           "bitlinear_pair", "relu2_glu", "relu2_glu_quant", "ffn_relu2", "ffn_relu2_workspace",
+           "BitLinearError", "packed_bytes"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
@@ -39,6 +40,8 @@ _SIGNATURES = {
     "bl_relu2_glu": ([_P, _P, _I, _P, _P], ctypes.c_int),
     "bl_bitlinear_pair": ([_P, _P, _I, _I, _P, _P, _I, _P, _P, _P, _I, _P, _P], ctypes.c_int),
     "bl_relu2_glu_quant": ([_P, _P, _I, _I, _P, _P, _P], ctypes.c_int),
+    "bl_ffn_relu2_workspace_bytes": ([_I, _I, _I], _S),
+    "bl_ffn_relu2": ([_P, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _S, _P], ctypes.c_int),
 }
 
 
@@ -217,3 +220,39 @@ def relu2_glu_quant(gate, up, out=None):
                                     _dev(hs, torch.float32, "h_scale"), _stream_ptr(gate)),
            "bl_relu2_glu_quant")
     return hq, hs
+
+
+def ffn_relu2_workspace(M: int, K: int, N_ff: int, device=None):
+    """A workspace tensor sized by bl_ffn_relu2_workspace_bytes."""
+    torch = _torch()
+    n = lib().bl_ffn_relu2_workspace_bytes(M, K, N_ff)
+    if n == 0:
+        raise BitLinearError("invalid FFN shapes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def ffn_relu2(x, W_gate, gamma_gate, W_up, gamma_up, W_down, gamma_down, workspace=None,
+              out=None):
+    """y fp32 [M][K] of one 2B4T-style FFN step on bf16 x. Calls bl_ffn_relu2."""
+    torch = _torch()
+    if x.dtype == torch.int16:
+        x = x.view(torch.bfloat16)
+    M, K = x.shape
+    N_ff = W_gate.shape[0]
+    if W_gate.shape[1] * 16 != K or W_up.shape != W_gate.shape or \
+            W_down.shape[0] != K or W_down.shape[1] * 16 != N_ff:
+        raise BitLinearError("FFN weight shapes do not match")
+    if workspace is None:
+        workspace = ffn_relu2_workspace(M, K, N_ff, x.device)
+    y = torch.empty((M, K), dtype=torch.float32, device=x.device) if out is None else out
+    _check(lib().bl_ffn_relu2(_dev(x, torch.bfloat16, "x"), M, K,
+                              _dev(W_gate, torch.int32, "W_gate"),
+                              _dev(gamma_gate, torch.float32, "gamma_gate"),
+                              _dev(W_up, torch.int32, "W_up"),
+                              _dev(gamma_up, torch.float32, "gamma_up"), N_ff,
+                              _dev(W_down, torch.int32, "W_down"),
+                              _dev(gamma_down, torch.float32, "gamma_down"),
+                              _dev(y, torch.float32, "y"),
+                              _dev(workspace, torch.uint8, "workspace"),
+                              workspace.numel(), _stream_ptr(x)), "bl_ffn_relu2")
+    return y

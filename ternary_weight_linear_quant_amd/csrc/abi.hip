@@ -37,6 +37,30 @@ int hip_status(hipError_t e) {
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// Workspace of bl_ffn_relu2: 256-byte aligned segments.
+struct FfnWorkspace {
+    size_t h, xq, xs, yg, yu, hq, hs, total;
+};
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+FfnWorkspace ffn_layout(int64_t M, int64_t K, int64_t N) {
+    FfnWorkspace w;
+    size_t o = 0;
+    w.h = o;  o += align256((size_t)(2 * M * N));
+    w.xq = o; o += align256((size_t)(M * K));
+    w.xs = o; o += align256((size_t)(4 * M));
+    w.yg = o; o += align256((size_t)(4 * M * N));
+    w.yu = o; o += align256((size_t)(4 * M * N));
+    w.hq = o; o += align256((size_t)(M * N));
+    w.hs = o; o += align256((size_t)(4 * M));
+    w.total = o;
+    return w;
+}
+
+bool ffn_shapes_ok(int64_t M, int64_t K, int64_t N) {
+    return shape_ok(M, K) && shape_ok(M, N) && shape_ok(N, K) && shape_ok(K, N) &&
+           M <= (int64_t{1} << 31) / N;
+}
+
 }  // namespace
 
 extern "C" {
@@ -134,6 +158,61 @@ int bl_bitlinear_pair(const int8_t* x_q, const float* x_scale, int64_t M, int64_
     if (e) return e;
     return hip_status(bl::launch_gemm(x_q, x_scale, (int)M, (int)K, W2, gamma2, (int)N2, y2,
                                       nullptr, st));
+}
+
+size_t bl_ffn_relu2_workspace_bytes(int64_t M, int64_t K, int64_t N_ff) {
+    if (!ffn_shapes_ok(M, K, N_ff)) return 0;
+    return ffn_layout(M, K, N_ff).total;
+}
+
+int bl_ffn_relu2(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate,
+                 const float* gamma_gate, const uint32_t* W_up, const float* gamma_up,
+                 int64_t N_ff, const uint32_t* W_down, const float* gamma_down, float* y,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+    if (!x || !W_gate || !gamma_gate || !W_up || !gamma_up || !W_down || !gamma_down || !y ||
+        !workspace)
+        return BL_ERR_INVALID_ARG;
+    if (!ffn_shapes_ok(M, K, N_ff)) return BL_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(W_down) ||
+        !aligned16(y) || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return BL_ERR_INVALID_ARG;
+    const FfnWorkspace L = ffn_layout(M, K, N_ff);
+    if (workspace_bytes < L.total) return BL_ERR_INVALID_ARG;
+    if (int s = device_status()) return s;
+    hipStream_t st = as_stream(stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    auto* h = reinterpret_cast<uint16_t*>(ws + L.h);
+    if (bl::ffn_fused_supported(M, K, N_ff))
+        return hip_status(bl::launch_ffn_fused(x, (int)M, (int)K, W_gate, gamma_gate, W_up,
+                                               gamma_up, (int)N_ff, W_down, gamma_down, h, y,
+                                               st));
+    // Unfused sequence: act quant -> gate/up -> gating + act quant -> down.
+    auto* xq = reinterpret_cast<int8_t*>(ws + L.xq);
+    auto* xs = reinterpret_cast<float*>(ws + L.xs);
+    auto* yg = reinterpret_cast<float*>(ws + L.yg);
+    auto* yu = reinterpret_cast<float*>(ws + L.yu);
+    auto* hq = reinterpret_cast<int8_t*>(ws + L.hq);
+    auto* hs = reinterpret_cast<float*>(ws + L.hs);
+    const int m = (int)M, k = (int)K, n = (int)N_ff;
+    hipError_t e = bl::launch_quantize_acts(x, M, K, nullptr, 0.0f, xq, xs, st);
+    if (e == hipSuccess) {
+        if (bl::gemv_supported(M, K)) {
+            e = bl::launch_gemv_pair(xq, xs, m, k, W_gate, gamma_gate, n, yg, W_up, gamma_up, n,
+                                     yu, st);
+        } else {
+            e = bl::launch_gemm(xq, xs, m, k, W_gate, gamma_gate, n, yg, nullptr, st);
+            if (e == hipSuccess)
+                e = bl::launch_gemm(xq, xs, m, k, W_up, gamma_up, n, yu, nullptr, st);
+        }
+    }
+    if (e == hipSuccess) e = bl::launch_relu2_glu_quant(yg, yu, M, N_ff, hq, hs, st);
+    if (e == hipSuccess) {
+        if (bl::gemv_supported(M, N_ff))
+            e = bl::launch_gemv(hq, hs, m, n, W_down, gamma_down, k, y, nullptr, st);
+        else
+            e = bl::launch_gemm(hq, hs, m, n, W_down, gamma_down, k, y, nullptr, st);
+    }
+    return hip_status(e);
 }
 
 int bl_relu2_glu_quant(const float* gate, const float* up, int64_t M, int64_t K, int8_t* h_q,

@@ -1,0 +1,243 @@
+// Decode step of a 2B4T-style FFN in two launches.
+//
+// Source: inferownia.pl, "BitNet b1.58: era 1-bitowych LLM-ów", sections
+// "Mnożenie? Jakie mnożenie" (ternary product as adds and subtracts) and
+// "Zrób to sam — Microsoft wypuścił konkretny model" (2B4T: squared ReLU);
+// comrad404.com, "BitNet b1.58: что показала работа Microsoft об «эре
+// 1-битных LLM»", section «Метод: как устроен BitNet b1.58» (8-bit
+// activations, quantised before each low-bit product).
+//
+// Launch A: every workgroup quantises the layer input x (bf16 [M][K]) per
+//   token into LDS itself, then computes 16 rows of BOTH the gate and the up
+//   projection (waves 0-1 gate, 2-3 up, K split two ways) and writes
+//   h = bf16(relu(y_gate)^2 * y_up) for those rows.
+// Launch B: every workgroup quantises h per token into LDS itself and
+//   computes 16 rows of the down projection (K split four ways) into y.
+// Each step uses exactly the arithmetic of bl_quantize_acts, bl_bitlinear
+// and bl_relu2_glu, so the output bits equal the unfused sequence. The
+// per-workgroup quantisation re-reads the M tokens from L2 in every
+// workgroup, which is cheap for M <= 4 and removes two launches per layer.
+//
+// Ordering inside a workgroup: the activation loads are issued first, the
+// R weight-chunk loads right after (always R, clamped to the wave's range),
+// so waiting for the activations leaves the weight stream in flight; LDS
+// barriers wait on LDS traffic only.
+//
+// Roofline: HBM / launch latency. Algorithmic bytes per layer = packed
+// weights of the three matrices + 2*M*K (x) + 2*M*N_ff (h, written and read)
+// + 4*M*K (y).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace bl {
+
+constexpr int kFfnThreads = 256;
+constexpr int kFfnCache = 8;  // 16-value activation units cached per thread
+constexpr int kFfnR = 4;      // weight chunks in flight per lane
+
+// lgkmcnt(0) only: LDS traffic done, vector loads may stay in flight.
+#define BL_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14))
+
+__device__ __forceinline__ void lds_barrier() {
+    BL_WAIT_LGKM0();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t relu2_gate_bits(float g, float u) {
+    const float r = g > 0.0f ? g : 0.0f;
+    const float sq = r * r;
+    return f32_to_bf16_rne(sq * u);
+}
+
+template <bool GLU>
+__global__ __launch_bounds__(kFfnThreads) void k_ffn_gemv(
+    const uint16_t* __restrict__ xin, int M, int K, const uint32_t* __restrict__ W0,
+    const float* __restrict__ g0, const uint32_t* __restrict__ W1,
+    const float* __restrict__ g1, int N, float* __restrict__ y, uint16_t* __restrict__ h) {
+    constexpr int KS = GLU ? 2 : 4;
+    extern __shared__ __align__(16) uint8_t smem[];  // int8 activations, token-minor
+    __shared__ v4i red[4][kWave];
+    __shared__ float s_amax[4][16];
+    __shared__ float s_scale[16];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int lane = tid % kWave;
+    const int mat = GLU ? wave / 2 : 0;
+    const int ks = GLU ? wave % 2 : wave;
+    const uint32_t* W = (GLU && mat) ? W1 : W0;
+    const int r = lane % 16, g = lane / 16;
+    const int row0 = blockIdx.x * 16;
+    const int row = min(row0 + r, N - 1);
+    const int KW = K / 16;
+    const int nfull = KW / 16;  // >= KS (checked on the host)
+    const uint32_t* wrow = W + (size_t)row * KW + 4 * g;
+    const int nw = (nfull - ks + KS - 1) / KS;
+
+    // 1. Activation loads: unit u = 16 consecutive values of one token; the
+    //    units of thread t all belong to token t % M (M divides 256).
+    const int U = M * (K / 16);
+    const int mt = tid % M;
+    uint4 xa[kFfnCache], xb[kFfnCache];
+#pragma unroll
+    for (int i = 0; i < kFfnCache; ++i) {
+        const int u = tid + kFfnThreads * i;
+        if (u < U) {
+            const uint4* src = reinterpret_cast<const uint4*>(xin + (size_t)mt * K + 16 * (u / M));
+            xa[i] = src[0];
+            xb[i] = src[1];
+        }
+    }
+    asm volatile("" ::: "memory");  // keep the activation loads first
+    // 2. The first R weight chunks (clamped to this wave's range, so the
+    //    count is fixed and the waits below are exact).
+    uint4 wb[kFfnR];
+#pragma unroll
+    for (int i = 0; i < kFfnR; ++i)
+        wb[i] = *reinterpret_cast<const uint4*>(wrow + 16 * (ks + KS * min(i, nw - 1)));
+
+    // 3. Per-token absmax (exact, order-free) of the cached units.
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kFfnCache; ++i) {
+        if (tid + kFfnThreads * i < U) {
+            const uint32_t w8[8] = {xa[i].x, xa[i].y, xa[i].z, xa[i].w,
+                                    xb[i].x, xb[i].y, xb[i].z, xb[i].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                amax = fmaxf(amax, fabsf(bf16_to_f32(w8[e] & 0xFFFFu)));
+                amax = fmaxf(amax, fabsf(bf16_to_f32(w8[e] >> 16)));
+            }
+        }
+    }
+    // Lanes with equal lane % M hold the same token.
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        if (o >= M) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+    if (lane < M) s_amax[wave][lane] = amax;
+    lds_barrier();
+    float a = fmaxf(fmaxf(s_amax[0][mt], s_amax[1][mt]), fmaxf(s_amax[2][mt], s_amax[3][mt]));
+    a = a > 1e-5f ? a : 1e-5f;
+    const float inv = 127.0f / a;
+    if (tid < M) s_scale[tid] = a / 127.0f;
+
+    // 4. Codes into LDS slot u (chunk u / M of token u % M).
+#pragma unroll
+    for (int i = 0; i < kFfnCache; ++i) {
+        const int u = tid + kFfnThreads * i;
+        if (u < U) {
+            const uint32_t w8[8] = {xa[i].x, xa[i].y, xa[i].z, xa[i].w,
+                                    xb[i].x, xb[i].y, xb[i].z, xb[i].w};
+            uint32_t q[4] = {0, 0, 0, 0};
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float z = bf16_to_f32((w8[e / 2] >> (16 * (e % 2))) & 0xFFFFu);
+                float t = __builtin_rintf(z * inv);
+                t = fminf(fmaxf(t, -127.0f), 127.0f);
+                q[e / 4] |= ((uint32_t)((int)t) & 0xFFu) << (8 * (e % 4));
+            }
+            *reinterpret_cast<uint4*>(smem + 16 * u) = make_uint4(q[0], q[1], q[2], q[3]);
+        }
+    }
+    lds_barrier();
+
+    // 5. Ternary x int8 product on the matrix cores (negated weights).
+    const int tok = lane % 16;
+    const bool tok_ok = tok < M;
+    const int8_t* xl = reinterpret_cast<const int8_t*>(smem) + 16 * (tok_ok ? tok : 0);
+    v4i acc = {0, 0, 0, 0};
+    const v4i zero = {0, 0, 0, 0};
+    auto process = [&](const uint4 wv, int c) {
+        const uint32_t w4[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const v4i av = expand_word_neg(w4[s]);
+            const int j = 16 * c + 4 * g + s;
+            const v4i bv = tok_ok ? *reinterpret_cast<const v4i*>(xl + 16 * j * M) : zero;
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, acc, 0, 0, 0);
+        }
+    };
+    for (int b0 = 0; b0 < nw; b0 += kFfnR) {
+#pragma unroll
+        for (int i = 0; i < kFfnR; ++i) {
+            const int ci = b0 + i;
+            if (ci < nw) {
+                process(wb[i], ks + KS * ci);
+                if (ci + kFfnR < nw)
+                    wb[i] = *reinterpret_cast<const uint4*>(wrow + 16 * (ks + KS * (ci + kFfnR)));
+            }
+        }
+    }
+    // Tail chunk (KW % 16 words, a multiple of 4): the last K-split wave.
+    const int rem = KW - 16 * nfull;
+    if (rem != 0 && ks == KS - 1) {
+        const bool gv = 4 * g < rem;
+        const uint4 wv = gv ? *reinterpret_cast<const uint4*>(wrow + 16 * nfull)
+                            : make_uint4(0, 0, 0, 0);
+        const uint32_t w4[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const v4i av = gv ? expand_word_neg(w4[s]) : zero;
+            const int j = 16 * nfull + 4 * g + s;
+            const v4i bv = (gv && tok_ok) ? *reinterpret_cast<const v4i*>(xl + 16 * j * M) : zero;
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, acc, 0, 0, 0);
+        }
+    }
+
+    // 6. Reduce the K split and write the epilogue (wave 0).
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave != 0 || !tok_ok) return;
+    const float xs = s_scale[tok];
+    const int nbase = row0 + 4 * (lane / 16);
+    if (GLU) {
+        const v4i ga = -(red[0][lane] + red[1][lane]);
+        const v4i ua = -(red[2][lane] + red[3][lane]);
+        const float sg = xs * (*g0), su = xs * (*g1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int n = nbase + i;
+            if (n < N) {
+                const float yg = (float)ga[i] * sg;
+                const float yu = (float)ua[i] * su;
+                h[(size_t)tok * N + n] = (uint16_t)relu2_gate_bits(yg, yu);
+            }
+        }
+    } else {
+        const v4i ta = -((red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]));
+        const float sc = xs * (*g0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int n = nbase + i;
+            if (n < N) y[(size_t)tok * N + n] = (float)ta[i] * sc;
+        }
+    }
+}
+
+bool ffn_fused_supported(int64_t M, int64_t K, int64_t N_ff) {
+    if (M < 1 || M > 4 || (256 % M) != 0) return false;
+    // Activation units must fit the register cache; rows must cover the
+    // K split with full 256-weight chunks.
+    if (M * (K / 16) > kFfnThreads * kFfnCache || M * (N_ff / 16) > kFfnThreads * kFfnCache)
+        return false;
+    return K / 256 >= 2 && N_ff / 256 >= 4;
+}
+
+hipError_t launch_ffn_fused(const uint16_t* x, int M, int K, const uint32_t* Wg,
+                            const float* gg, const uint32_t* Wu, const float* gu, int N_ff,
+                            const uint32_t* Wd, const float* gd, uint16_t* h, float* y,
+                            hipStream_t stream) {
+    const int blocks_a = (N_ff + 15) / 16;
+    hipLaunchKernelGGL(k_ffn_gemv<true>, dim3(blocks_a), dim3(kFfnThreads), (size_t)M * K,
+                       stream, x, M, K, Wg, gg, Wu, gu, N_ff, (float*)nullptr, h);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int blocks_b = (K + 15) / 16;
+    hipLaunchKernelGGL(k_ffn_gemv<false>, dim3(blocks_b), dim3(kFfnThreads), (size_t)M * N_ff,
+                       stream, h, M, N_ff, Wd, gd, (const uint32_t*)nullptr,
+                       (const float*)nullptr, K, y, (uint16_t*)nullptr);
+    return hipGetLastError();
+}
+
+}  // namespace bl

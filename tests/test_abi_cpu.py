@@ -95,6 +95,16 @@ def test_invalid_arguments_rejected_before_launch(L):
     assert L.bl_relu2_glu_quant(A, A, 0, 64, A, A, None) == E
     assert L.bl_relu2_glu_quant(A, MIS, 1, 64, A, A, None) == E
     assert L.bl_relu2_glu_quant(A, A, 1, 64, A, None, None) == E
+    # fused FFN step
+    WS = P(0x200000)  # 256-byte aligned
+    need = L.bl_ffn_relu2_workspace_bytes(4, 2560, 6912)
+    assert need >= 2 * 4 * 6912
+    assert L.bl_ffn_relu2_workspace_bytes(4, 100, 6912) == 0
+    assert L.bl_ffn_relu2(A, 4, 2560, A, A, A, A, 6912, A, A, A, WS, need - 1, None) == E
+    assert L.bl_ffn_relu2(A, 4, 2560, A, A, A, A, 6912, A, A, A, P(0x200010), need, None) == E
+    assert L.bl_ffn_relu2(A, 4, 2560, A, A, None, A, 6912, A, A, A, WS, need, None) == E
+    assert L.bl_ffn_relu2(A, 4, 2560, A, A, A, A, 6900, A, A, A, WS, need, None) == E
+    assert L.bl_ffn_relu2(MIS, 4, 2560, A, A, A, A, 6912, A, A, A, WS, need, None) == E
     # pair
     assert L.bl_bitlinear_pair(A, A, 1, 64, A, A, 16, A, None, A, 16, A, None) == E
     assert L.bl_bitlinear_pair(A, A, 1, 64, A, A, 16, A, A, A, 0, A, None) == E
@@ -113,6 +123,8 @@ def test_no_device_status(L):
     assert L.bl_relu2_glu(A, A, 4, A, None) == D
     assert L.bl_relu2_glu_quant(A, A, 1, 64, A, A, None) == D
     assert L.bl_bitlinear_pair(A, A, 1, 64, A, A, 16, A, A, A, 16, A, None) == D
+    need = L.bl_ffn_relu2_workspace_bytes(1, 256, 1024)
+    assert L.bl_ffn_relu2(A, 1, 256, A, A, A, A, 1024, A, A, A, P(0x200000), need, None) == D
 
 
 def test_binding_fails_loudly_without_gpu():

@@ -422,3 +422,50 @@ def test_ffn_block_fused_path_equals_unfused():
         ry = bl.bitlinear(rq, rs, *dev["down"])
         assert torch.equal(hq, rq) and torch.equal(hs, rs)
         assert torch.equal(y.view(torch.int32), ry.view(torch.int32))
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 16, 40])
+@pytest.mark.parametrize("K,N_ff", [(2560, 6912), (3200, 8640), (512, 1024)])
+def test_ffn_relu2_matches_unfused_sequence(M, K, N_ff):
+    """bl_ffn_relu2 (two launches for M <= 4, four otherwise) gives the bits
+    of quantize_acts -> bitlinear(gate, up) -> relu2_glu -> quantize_acts ->
+    bitlinear(down); the unfused sequence is checked against the oracle by
+    the stage-wise block test."""
+    wid = 70
+    Wg, Wu = wl.weights(wid, 0, N_ff, K), wl.weights(wid, 1, N_ff, K)
+    Wd = wl.weights(wid, 2, K, N_ff)
+    (pg, gg), (pu, gu), (pd, gd) = gpu_weights(Wg), gpu_weights(Wu), gpu_weights(Wd)
+    x = dev_bf16(wl.activations(wid, M, M, K))
+    y = bl.ffn_relu2(x, pg, gg, pu, gu, pd, gd)
+    xq, xs = bl.quantize_acts(x)
+    h = bl.relu2_glu(bl.bitlinear(xq, xs, pg, gg), bl.bitlinear(xq, xs, pu, gu))
+    hq, hs = bl.quantize_acts(h)
+    ref = bl.bitlinear(hq, hs, pd, gd)
+    assert torch.equal(y.view(torch.int32), ref.view(torch.int32))
+    # Second call on the same workspace: no state carried over.
+    ws = bl.ffn_relu2_workspace(M, K, N_ff, DEV)
+    y2 = bl.ffn_relu2(x, pg, gg, pu, gu, pd, gd, workspace=ws)
+    y3 = bl.ffn_relu2(x, pg, gg, pu, gu, pd, gd, workspace=ws)
+    assert torch.equal(y2.view(torch.int32), ref.view(torch.int32))
+    assert torch.equal(y3.view(torch.int32), ref.view(torch.int32))
+
+
+def test_ffn_relu2_oracle_end_to_end_small():
+    """Fused step against the oracle on its own end-to-end path; the down
+    input codes can flip by one at rounding boundaries of y_gate, y_up
+    (fp32 within 1e-6), so the check counts flips and bounds y."""
+    wid, M, K, N_ff = 71, 4, 512, 1024
+    Wg, Wu, Wd = wl.weights(wid, 0, N_ff, K), wl.weights(wid, 1, N_ff, K), wl.weights(wid, 2, K, N_ff)
+    xb = wl.activations(wid, 0, M, K)
+    (pg, gg), (pu, gu), (pd, gd) = gpu_weights(Wg), gpu_weights(Wu), gpu_weights(Wd)
+    y = bl.ffn_relu2(dev_bf16(xb), pg, gg, pu, gu, pd, gd).cpu().numpy()
+    _, g_g, q_g = oracle.quantize_weights(Wg)
+    _, g_u, q_u = oracle.quantize_weights(Wu)
+    _, g_d, q_d = oracle.quantize_weights(Wd)
+    xq, xs = oracle.act_quant(xb)
+    yg, _ = oracle.bitlinear(xq, xs, q_g, g_g)
+    yu, _ = oracle.bitlinear(xq, xs, q_u, g_u)
+    hq, hs = oracle.act_quant(oracle.relu2_glu(yg, yu))
+    y_ref, _ = oracle.bitlinear(hq, hs, q_d, g_d)
+    rel = np.linalg.norm(y - y_ref) / np.linalg.norm(y_ref)
+    assert rel < 1e-3, rel
