@@ -10,8 +10,8 @@
 //
 // y = x_q . q^T with v_mfma_i32_32x32x32_i8: A = activation tile (rows =
 // tokens), B = weight tile (rows = output features), both k-contiguous.
-// Workgroup: 256 threads = 4 waves in a 2 x 2 grid over a BM x BN tile; K step
-// 128. A STAGES-deep LDS ring is filled with global_load_lds_dwordx4 (each
+// Workgroup: WGM x WGN waves over a BM x BN tile, each wave a (BM/WGM) x
+// (BN/WGN) block of 32 x 32 MFMA tiles; K step 128. A STAGES-deep LDS ring is filled with global_load_lds_dwordx4 (each
 // lane's 16 bytes land directly in LDS, no register staging): per stage the
 // activation tile (BM x 128 B) and the PACKED weight tile (BN x 32 B, 2 bits
 // per weight). Loads for stage kt+STAGES-1 are issued before computing stage
@@ -151,20 +151,18 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_gemm(
     // Fragment reads from LDS stage `kt % STAGES`.
     auto read_b = [&](uint4* bp, int kt) {
         const uint8_t* Bs = smem + (kt % STAGES) * STAGE + A_STAGE;
-        // Last stage of a K that is not a multiple of 128: the upper 64 k
-        // (lane group 1) lie past K, so that group's codes become zeros.
-        const uint32_t keep = (k_tail && kt == KT - 1 && fg) ? 0u : 0xFFFFFFFFu;
-        const uint32_t fill = 0x55555555u & ~keep;  // code 1 = weight 0
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int r = wn0 + 32 * j + fr;
-            uint4 v = *reinterpret_cast<const uint4*>(Bs + r * kBRow + 16 * (fg ^ swz_b(r)));
-            v.x = (v.x & keep) | fill;
-            v.y = (v.y & keep) | fill;
-            v.z = (v.z & keep) | fill;
-            v.w = (v.w & keep) | fill;
-            bp[j] = v;
+            bp[j] = *reinterpret_cast<const uint4*>(Bs + r * kBRow + 16 * (fg ^ swz_b(r)));
         }
+    };
+    // Last stage of a K that is not a multiple of 128: the upper 64 k (lane
+    // group 1) lie past K, so that group's codes are replaced by code 1
+    // (weight 0) when they are expanded. Applied at expansion, not at the
+    // LDS read, so the read need not complete right after the barrier.
+    auto keep_mask = [&](int kt) -> uint32_t {
+        return (k_tail && kt == KT - 1 && fg) ? 0u : 0xFFFFFFFFu;
     };
     auto read_a = [&](v4i* af, int kt, int s) {
         const uint8_t* As = smem + (kt % STAGES) * STAGE;
@@ -174,11 +172,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_gemm(
             af[i] = *reinterpret_cast<const v4i*>(As + r * kARow + 16 * ((4 * fg + s) ^ swz_a(r)));
         }
     };
-    auto expand = [&](v4i* bf, const uint4* bp, int s) {
+    auto expand = [&](v4i* bf, const uint4* bp, int s, uint32_t keep) {
+        const uint32_t fill = 0x55555555u & ~keep;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const uint32_t w = s == 0 ? bp[j].x : s == 1 ? bp[j].y : s == 2 ? bp[j].z : bp[j].w;
-            bf[j] = expand_word_neg(w);
+            bf[j] = expand_word_neg((w & keep) | fill);
         }
     };
 
@@ -211,7 +210,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_gemm(
     v4i af[TM], an[TM], bf[TN], bfn[TN];
     read_b(bp, 0);
     read_a(af, 0, 0);
-    expand(bf, bp, 0);
+    expand(bf, bp, 0, keep_mask(0));
 
     for (int kt = 0; kt < KT; ++kt) {
         const bool more = kt + 1 < KT;
@@ -220,10 +219,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_gemm(
             // Next fragments: same step for s < 3, else the first of kt+1.
             if (s < 3) {
                 read_a(an, kt, s + 1);
-                expand(bfn, bp, s + 1);
+                expand(bfn, bp, s + 1, keep_mask(kt));
             } else if (more) {
                 read_a(an, kt + 1, 0);
-                expand(bfn, bpn, 0);
+                expand(bfn, bpn, 0, keep_mask(kt + 1));
             }
 #pragma unroll
             for (int i = 0; i < TM; ++i)
@@ -231,6 +230,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_gemm(
                 for (int j = 0; j < TN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j],
                                                                       0, 0, 0);
+            // The next sub-step's LDS fragment reads go first, so they have a
+            // whole sub-step of MFMAs to land; the expansion arithmetic is
+            // interleaved with the MFMAs.
+            __builtin_amdgcn_sched_group_barrier(0x100, TM, 0);
+#pragma unroll
+            for (int q = 0; q < TM * TN; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            }
             if (s == 1 && more) {
                 // Stage kt+1 landed once the stages issued after it are the
                 // only loads outstanding.
@@ -307,10 +315,20 @@ hipError_t launch_gemm(const int8_t* xq, const float* xs, int M, int K, const ui
         return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
     };
     constexpr int kCUs = 256;
-    if (tiles(256, 256) >= kCUs)
-        return launch_gemm_tile<256, 256, 4, 2, 3, 2>(xq, xs, M, K, Wp, gamma, N, y, acc, stream);
-    if (tiles(256, 128) >= kCUs)
-        return launch_gemm_tile<256, 128, 4, 2, 3, 2>(xq, xs, M, K, Wp, gamma, N, y, acc, stream);
+    // 128 x 512 tiles, one 8-wave workgroup per CU, each wave all 128 rows by
+    // its own 64 columns (no weight column is expanded twice): fastest per
+    // tile, chosen when its grid fills at least 95% of whole rounds of the
+    // 256 CUs.
+    const int64_t t512 = tiles(128, 512);
+    const int64_t rounds512 = (t512 + kCUs - 1) / kCUs;
+    if (t512 >= kCUs && t512 * 20 >= rounds512 * kCUs * 19)
+        return launch_gemm_tile<128, 512, 1, 8, 3, 2>(xq, xs, M, K, Wp, gamma, N, y, acc, stream);
+    // Otherwise 128 x 256 tiles, two 4-wave workgroups per CU (72 KB of LDS
+    // each): the pair is not tied by barriers, so one workgroup's barrier
+    // waits and output stores overlap the other's MFMAs, and a partial last
+    // round leaves fewer CUs idle.
+    if (tiles(128, 256) >= kCUs)
+        return launch_gemm_tile<128, 256, 1, 4, 3, 2>(xq, xs, M, K, Wp, gamma, N, y, acc, stream);
     if (tiles(128, 128) >= kCUs)
         return launch_gemm_tile<128, 128, 2, 2, 3, 2>(xq, xs, M, K, Wp, gamma, N, y, acc, stream);
     return launch_gemm_tile<64, 128, 2, 2, 3, 2>(xq, xs, M, K, Wp, gamma, N, y, acc, stream);

@@ -208,6 +208,35 @@ def test_gemm_parity(M, K, N):
     assert_y_close(y.cpu().numpy(), y_ref, "gemm")
 
 
+# Grids of at least 256 tiles select the large prefill tiles (128 x 512 with
+# one workgroup per CU, 128 x 256 with two); these shapes are ragged in M and
+# N, and K = 320 / 192 ends in a half (64-deep) K step.
+LARGE_TILE_CASES = [(2000, 320, 4000), (2000, 192, 8000), (2048, 384, 8192), (1935, 448, 5000)]
+
+
+@pytest.mark.parametrize("M,K,N", LARGE_TILE_CASES)
+def test_gemm_large_tiles_ragged(M, K, N):
+    q, xq, xs, g = _product_case(M, K, N, 58)
+    y, acc = bl.bitlinear(torch.from_numpy(xq).to(DEV), dev_f32(xs), dev_packed(oracle.pack(q)),
+                          dev_f32([g]), return_acc=True, path=2)
+    # Every int32 sum: an fp64 product of the integer operands is exact here
+    # (|acc| <= 127 * K < 2^53).
+    ref64 = torch.from_numpy(xq).to(DEV, torch.float64) @ torch.from_numpy(q).to(
+        DEV, torch.float64).t().contiguous()
+    assert torch.equal(acc.to(torch.float64), ref64)
+    # Oracle on a sample of tokens (first, last and every row-tile edge), all
+    # output features.
+    rng = np.random.default_rng(M + N)
+    edges = [m for t in range(0, M, 128) for m in (t, min(t + 127, M - 1))]
+    ms = np.unique(np.concatenate([rng.choice(M, 8, replace=False), edges[:6], edges[-6:]]))
+    y_ref, acc_ref = oracle.bitlinear(xq[ms], xs[ms], q, g)
+    idx = torch.from_numpy(ms).to(DEV)
+    assert np.array_equal(acc[idx].cpu().numpy(), acc_ref)
+    assert_y_close(y[idx].cpu().numpy(), y_ref, "gemm large tiles")
+    sc = (dev_f32(xs) * dev_f32([g])).view(-1, 1)
+    assert torch.equal(y, acc.to(torch.float32) * sc)
+
+
 def test_gemv_and_gemm_agree_bitwise():
     for M, K, N in [(1, 2560, 6912), (16, 6912, 2560), (4, 3200, 8640)]:
         q, xq, xs, g = _product_case(M, K, N, 55)
