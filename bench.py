@@ -6,15 +6,24 @@ Headline (`value`): decode packed-weight GB/s of a 2B4T-shaped FFN stack
 and 16 tokens. One step runs, for each M and each of L layers, one
 bl_ffn_relu2 call: per-token act quant -> gate and up BitLinears ->
 relu(gate)^2 * up -> act quant -> down BitLinear (two launches for M <= 4,
-four for M = 16). The L layers hold distinct copies of the packed weights (identical
-content, distinct addresses) whose total exceeds twice the 256 MB Infinity
-Cache, so every BitLinear streams its weights from HBM. Weights are quantised
-once before the timed region (offline in the method); that pass is timed and
-reported separately. The step is captured in a HIP graph and replayed.
+four for M = 16). The L layers hold distinct copies of the packed weights
+(identical content, distinct addresses) whose total exceeds twice the 256 MB
+Infinity Cache, so every BitLinear streams its weights from HBM. Weights are
+quantised once before the timed region (offline in the method); that pass is
+timed and reported separately. The step is captured in a HIP graph and
+replayed.
 
-Also reported: the roofline of the decode weight-stream kernel (HIP-event
-timing of a graph of its launches), per-M rates, the prefill GEMM at M = 4096 (int8 TOPS against the MFMA
-peak), and the CPU oracle timed on a bounded sample of the decode step.
+Also reported, each with its roofline (achieved vs. the published peak,
+HIP-event timing on the launching stream, HBM bytes per launch from the
+committed rocprofv3 counter summary when the kernel sources are unchanged):
+  - the decode weight-stream kernel of the headline step;
+  - 70B-class decode (8192 -> 28672 and 28672 -> 8192) at M = 1 (GEMV) and
+    M = 64 (GEMM), over rotated weight copies;
+  - prefill GEMMs: M = 4096 on 2560 <-> 6912 and M = 2048 on the 70B shapes
+    (int8 TOPS against the matrix-core peak);
+  - measured ceilings of own-code calibration kernels (a read-only 16-byte
+    HBM stream and an int8 matrix-core loop);
+  - the CPU oracle timed on a bounded sample of the decode step.
 
     python bench.py [--steps K] [--warmup W] [--layers L]
 """
@@ -36,6 +45,9 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
 I8_PEAK_TOPS = 5000.0       # MI355X dense int8 MFMA, published
 DECODE_WORKLOAD = 2         # 2B4T-shaped FFN at decode
 PREFILL_WORKLOAD = 3        # one 4096-token sequence
+LARGE_WORKLOAD = 5          # 70B-class shapes
+LARGE_COPIES = 5            # 5 x 2 x 58.7 MB of packed weights > 2 x 256 MB
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
 
 
 def parse_args():
@@ -49,6 +61,7 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="CPU-oracle sample budget (0 disables the leg)")
     p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-large", action="store_true", help="skip the 70B-class legs")
     p.add_argument("--no-graph", action="store_true", help="time eager launches instead")
     return p.parse_args()
 
@@ -206,6 +219,31 @@ def main():
     packed_per_step = packed_per_layer * L * len(Ms)
     value = packed_per_step / (ms_per_step * 1e-3) / 1e9
 
+    from ternary_weight_linear_quant_amd import counters
+    traffic = counters.load_traffic(COUNTERS_FILE)
+
+    def replay_stats(gr, reps, launches):
+        """Per-launch time (us) of a graph of `launches` kernel launches: mean
+        over `reps` replays timed as one, and p10 / median / p90 over replays
+        timed one by one (HIP events on the replaying stream)."""
+        mean_ms = time_graph(gr, reps)
+        per = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            gr.replay()
+            b.record()
+            per.append((a, b))
+        torch.cuda.synchronize()
+        us = sorted(1e3 * a.elapsed_time(b) / launches for a, b in per)
+        q = lambda f: us[min(len(us) - 1, int(round(f * (len(us) - 1))))]
+        return {"mean_us": round(1e3 * mean_ms / launches, 3), "p10_us": round(q(0.1), 3),
+                "median_us": round(q(0.5), 3), "p90_us": round(q(0.9), 3),
+                "replays": reps, "launches_per_replay": launches,
+                "note": "mean over replays timed as one; percentiles over replays timed one "
+                        "by one (each includes its own event overhead)"}
+
     # Per token count, and the roofline of the weight-streaming kernel: the
     # M = 1 pass is nothing but k_ffn_gemv launches (gate/up + down per
     # layer), replayed from its own HIP graph and timed with HIP events on
@@ -217,22 +255,25 @@ def main():
         per_M[f"M{M}"] = {"ms": round(ms, 4), "launches_per_layer": 2 if M <= 4 else 4,
                           "packed_GBps": round(packed_per_layer * L / (ms * 1e-3) / 1e9, 1)}
         if M == 1:
-            ms1 = ms
+            stats1 = replay_stats(gm, 20, 2 * L)
         del gm
     Kd, Nd = shapes["down"]
     M = 1
     bytes_a = 2 * (Nff * Kin // 4 + 4) + 2 * M * Kin + 2 * M * Nff
     bytes_b = Nd * Kd // 4 + 4 + 2 * M * Kd + 4 * M * Nd
-    launches = 2 * L
-    achieved = (bytes_a + bytes_b) * L / (ms1 * 1e-3) / 1e9
+    alg_per_launch = (bytes_a + bytes_b) / 2
+    achieved = alg_per_launch / (stats1["mean_us"] * 1e-6) / 1e9
     roofline = {
         "bound": "hbm",
         "kernel": "k_ffn_gemv (decode weight stream: gate/up+gating and act-quant+down "
                   "launches of the M=1 pass)",
         "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-        "launches": launches, "avg_us": round(1e3 * ms1 / launches, 3),
-        "alg_bytes_per_launch": round((bytes_a + bytes_b) / 2),
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": traffic.get("ffn_2b4t_m1"),
+        "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled "
+                        "by a copy kernel)",
+        "alg_bytes_per_launch": round(alg_per_launch),
+        "launches": 2 * L, "avg_us": stats1["mean_us"], "per_launch": stats1,
         "timing": "HIP graph of the M=1 pass (k_ffn_gemv launches only), HIP events on "
                   "the replay stream",
     }
@@ -242,22 +283,24 @@ def main():
     print(f"decode: {value:.1f} GB/s per step, weight-stream kernel {achieved:.1f} GB/s "
           f"({roofline['avg_us']} us/launch), per M {per_M}", file=sys.stderr, flush=True)
 
-    # ------------------------------------------------ prefill GEMM leg ----
-    prefill = None
-    if not args.no_prefill:
-        _, pprojs, pMs = wl.WORKLOADS[PREFILL_WORKLOAD]
-        Mp = pMs[0]
+    def prepare(wid, idx, N, K, copies=1):
+        W = torch.from_numpy(wl.weights(wid, idx, N, K)).to(dev)
+        pk, g = bl.quantize_weights(W)
+        del W
+        return [(pk, g)] + [(pk.clone(), g.clone()) for _ in range(copies - 1)]
+
+    def gemm_leg(label, wid, M, legs_w, reps):
+        """Prefill GEMMs at M tokens: act quant then BitLinear per projection;
+        GEMM launches timed one by one with HIP events."""
         legs = []
-        for i, (name, K, N) in enumerate(pprojs):
-            W = torch.from_numpy(wl.weights(PREFILL_WORKLOAD, i, N, K)).to(dev)
-            pk, g = bl.quantize_weights(W)
-            del W
-            x = bf16_dev(wl.activations(PREFILL_WORKLOAD, i, Mp, K))
+        for i, (name, K, N) in enumerate(legs_w):
+            pk, g = prepare(wid, i, N, K)[0]
+            x = bf16_dev(wl.activations(wid, i, M, K))
             xq, xs = bl.quantize_acts(x)
-            y = torch.empty((Mp, N), dtype=torch.float32, device=dev)
+            y = torch.empty((M, N), dtype=torch.float32, device=dev)
             legs.append((name, K, N, x, xq, xs, pk, g, y))
 
-        def prefill_step(timer=None):
+        def step(timer=None):
             for name, K, N, x, xq, xs, pk, g, y in legs:
                 if timer is None:
                     bl.quantize_acts(x, out=(xq, xs))
@@ -266,49 +309,150 @@ def main():
                     timer.run("act_quant", lambda: bl.quantize_acts(x, out=(xq, xs)))
                     timer.run(("gemm", name), lambda: bl.bitlinear(xq, xs, pk, g, out=y))
 
-        prefill_step()
-        torch.cuda.synchronize()
-        for _ in range(args.warmup):
-            prefill_step()
+        for _ in range(1 + args.warmup):
+            step()
         torch.cuda.synchronize()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
-        reps = max(5, args.steps)
         a.record()
         for _ in range(reps):
-            prefill_step()
+            step()
         b.record()
         torch.cuda.synchronize()
         p_ms = a.elapsed_time(b) / reps
-        ops = sum(2 * Mp * N * K for _, K, N, *_ in legs)
+        ops = sum(2 * M * N * K for _, K, N, *_ in legs)
         tp = Timer(torch)
         for _ in range(reps):
-            prefill_step(tp)
+            step(tp)
         torch.cuda.synchronize()
         per = {}
         gemm_ms = 0.0
-        gemm_n = 0
         for name, K, N, *_ in legs:
             ms = tp.total_ms(("gemm", name))
             n = tp.count(("gemm", name))
             gemm_ms += ms
-            gemm_n += n
-            per[name] = {"M": Mp, "K": K, "N": N, "avg_us": round(1e3 * ms / n, 2),
-                         "TOPS": round(2 * Mp * N * K * n / (ms * 1e-3) / 1e12, 1)}
-        gemm_tops = ops * reps / (gemm_ms * 1e-3) / 1e12
-        prefill = {
-            "workload": "prefill_4096 (M=4096; up 2560->6912, down 6912->2560)",
+            per[name] = {"M": M, "K": K, "N": N, "avg_us": round(1e3 * ms / n, 2),
+                         "TOPS": round(2 * M * N * K * n / (ms * 1e-3) / 1e12, 1)}
+        tops = ops * reps / (gemm_ms * 1e-3) / 1e12
+        out = {
             "ms_per_step": round(p_ms, 4),
             "step_TOPS": round(ops / (p_ms * 1e-3) / 1e12, 1),
-            "roofline": {"bound": "mfma", "kernel": "k_gemm", "achieved": round(gemm_tops, 1),
-                         "peak": I8_PEAK_TOPS, "unit": "TOPS",
-                         "frac": round(gemm_tops / I8_PEAK_TOPS, 4), "traffic": None,
+            "roofline": {"bound": "mfma", "kernel": "k_gemm", "achieved": round(tops, 1),
+                         "peak": I8_PEAK_TOPS, "unit": "TFLOP/s (int8 TOPS)",
+                         "frac": round(tops / I8_PEAK_TOPS, 4),
+                         "traffic": traffic.get(label),
+                         "traffic_unit": "HBM bytes per launch",
                          "per_projection": per},
             "act_quant_avg_us": round(1e3 * tp.total_ms("act_quant") / tp.count("act_quant"), 2),
         }
         del legs
         torch.cuda.empty_cache()
-        print(f"prefill: GEMM {gemm_tops:.1f} TOPS", file=sys.stderr, flush=True)
+        print(f"{label}: GEMM {tops:.1f} TOPS", file=sys.stderr, flush=True)
+        return out
+
+    # ------------------------------------------------ prefill GEMM leg ----
+    prefill = None
+    if not args.no_prefill:
+        _, pprojs, pMs = wl.WORKLOADS[PREFILL_WORKLOAD]
+        prefill = {"workload": "prefill_4096 (M=4096; up 2560->6912, down 6912->2560)"}
+        prefill.update(gemm_leg("gemm_prefill_4096", PREFILL_WORKLOAD, pMs[0], pprojs,
+                                max(5, args.steps)))
+
+    # ------------------------------------------- 70B-class shapes ----
+    large = None
+    ceilings = None
+    if not args.no_large:
+        _, lprojs, lMs = wl.WORKLOADS[LARGE_WORKLOAD]
+        wts = {name: prepare(LARGE_WORKLOAD, i, N, K, LARGE_COPIES)
+               for i, (name, K, N) in enumerate(lprojs)}
+        large = {"workload": "70b_class (hidden 8192, FFN 28672; up 8192->28672, "
+                             "down 28672->8192)", "weight_copies": LARGE_COPIES}
+        for M in (1, 64):
+            io = {}
+            for i, (name, K, N) in enumerate(lprojs):
+                xq, xs = bl.quantize_acts(bf16_dev(wl.activations(LARGE_WORKLOAD, i, M, K)))
+                io[name] = (xq, xs, torch.empty((M, N), dtype=torch.float32, device=dev))
+
+            def rotation(M=M, io=io):
+                for c in range(LARGE_COPIES):
+                    for name, K, N in lprojs:
+                        xq, xs, y = io[name]
+                        bl.bitlinear(xq, xs, *wts[name][c], out=y)
+
+            rotation()
+            torch.cuda.synchronize()
+            gr = capture(rotation)
+            launches = LARGE_COPIES * len(lprojs)
+            st = replay_stats(gr, 20, launches)
+            del gr
+            packed = sum(N * K // 4 for _, K, N in lprojs) / len(lprojs)
+            alg = sum(N * K // 4 + 4 + M * K + 4 * M + 4 * M * N for _, K, N in lprojs) \
+                / len(lprojs)
+            ops = sum(2 * M * N * K for _, K, N in lprojs) / len(lprojs)
+            t = st["mean_us"] * 1e-6
+            leg = {
+                "kernel": "k_gemv" if M <= 16 else "k_gemm",
+                "packed_GBps": round(packed / t / 1e9, 1),
+                "roofline": {"bound": "hbm", "achieved": round(alg / t / 1e9, 1),
+                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(alg / t / 1e9 / HBM_PEAK_GBS, 4),
+                             "traffic": traffic.get("gemv_70b_m1" if M == 1
+                                                    else "gemm_decode_70b_m64"),
+                             "traffic_unit": "HBM bytes per launch",
+                             "alg_bytes_per_launch": round(alg)},
+                "per_launch": st,
+                "timing": "HIP graph of the rotation (up and down over the weight copies), "
+                          "HIP events on the replay stream",
+            }
+            if M > 16:
+                leg["mfma"] = {"achieved_TOPS": round(ops / t / 1e12, 1),
+                               "frac": round(ops / t / 1e12 / I8_PEAK_TOPS, 4)}
+            large[f"decode_M{M}"] = leg
+            print(f"70b decode M={M}: {leg['packed_GBps']} GB/s packed, "
+                  f"{st['mean_us']} us/launch", file=sys.stderr, flush=True)
+
+        # Measured ceilings: a read-only 16-byte stream over the same rotated
+        # packed weights, and the int8 matrix-core loop.
+        sink = torch.zeros(4, dtype=torch.int32, device=dev)
+        bufs_r = [w[0] for name in wts for w in wts[name]]
+
+        def read_all():
+            for buf in bufs_r:
+                bl.calib_read(buf, sink)
+
+        read_all()
+        gr = capture(read_all)
+        st = replay_stats(gr, 10, len(bufs_r))
+        del gr
+        nbytes = bufs_r[0].numel() * 4
+        msink = bl.calib_mfma_sink(dev)
+        iters = 4000
+        bl.calib_mfma_i8(iters, msink)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(5):
+            mops = bl.calib_mfma_i8(iters, msink)
+        b.record()
+        torch.cuda.synchronize()
+        mfma_tops = mops * 5 / (a.elapsed_time(b) * 1e-3) / 1e12
+        ceilings = {
+            "hbm_read_stream": {"kernel": "k_calib_read", "bytes_per_launch": nbytes,
+                                "GBps": round(nbytes / (st["mean_us"] * 1e-6) / 1e9, 1),
+                                "frac_of_peak": round(nbytes / (st["mean_us"] * 1e-6) / 1e9
+                                                      / HBM_PEAK_GBS, 4),
+                                "per_launch": st},
+            "i8_mfma_loop": {"kernel": "k_calib_mfma (v_mfma_i32_32x32x32_i8, 8 waves/CU)",
+                             "TOPS": round(mfma_tops, 1),
+                             "frac_of_peak": round(mfma_tops / I8_PEAK_TOPS, 4)},
+        }
+        print(f"ceilings: read {ceilings['hbm_read_stream']['GBps']} GB/s, "
+              f"mfma {mfma_tops:.0f} TOPS", file=sys.stderr, flush=True)
+        del wts, bufs_r
+        torch.cuda.empty_cache()
+        large["prefill_M2048"] = gemm_leg("gemm_prefill_70b", LARGE_WORKLOAD, 2048, lprojs,
+                                          max(3, args.steps // 4))
 
     # ------------------------------------------------ CPU oracle leg ----
     cpu_baseline = None
@@ -367,6 +511,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu_baseline,
         "prefill": prefill,
+        "large_70b": large,
+        "ceilings": ceilings,
         "weight_prep": {"matrices": list(base), "ms_total": round(wp_ms, 3),
                         "fp32_read_GBps": round(wp_bytes / (wp_ms * 1e-3) / 1e9, 1)},
         "device": {"name": props.name, "cus": props.multi_processor_count,

@@ -206,6 +206,31 @@ int bl_ffn_relu2(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate
                  int64_t N_ff, const uint32_t* W_down, const float* gamma_down, float* y,
                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Calibration kernels ------------------------------------------------
+ * Measured ceilings for the roofline of the kernels above; they compute
+ * nothing of the method. Same conventions as above. */
+
+/* Reads `bytes` bytes at `src` once with 16-byte loads and discards them (a
+ * read-only HBM stream). bytes >= 16, bytes % 16 == 0, src 16-byte aligned;
+ * sink: >= 4 bytes of device memory, written only for one data pattern. */
+int bl_calib_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
+/* Copies `bytes` bytes from src to dst with 16-byte loads and stores. Same
+ * size and alignment rules as bl_calib_read for both pointers; the ranges
+ * must not overlap. */
+int bl_calib_copy(void* dst, const void* src, size_t bytes, void* stream);
+
+/* Number of int8 operations (2 per multiply-add) one bl_calib_mfma_i8 call
+ * performs for `iters` (0 if iters is out of range), and the int32 elements
+ * of the sink it writes. Host-only. */
+int64_t bl_calib_mfma_i8_ops(int64_t iters);
+size_t bl_calib_mfma_i8_sink_elems(void);
+
+/* Runs a fixed grid of waves, each issuing `iters` rounds of 8 independent
+ * 32x32x32 int8 matrix-core instructions on register operands, and writes
+ * one int32 per lane to sink. 1 <= iters <= 2^24. */
+int bl_calib_mfma_i8(int64_t iters, int32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

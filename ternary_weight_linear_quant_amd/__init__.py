@@ -42,6 +42,11 @@ _SIGNATURES = {
     "bl_relu2_glu_quant": ([_P, _P, _I, _I, _P, _P, _P], ctypes.c_int),
     "bl_ffn_relu2_workspace_bytes": ([_I, _I, _I], _S),
     "bl_ffn_relu2": ([_P, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _S, _P], ctypes.c_int),
+    "bl_calib_read": ([_P, _S, _P, _P], ctypes.c_int),
+    "bl_calib_copy": ([_P, _P, _S, _P], ctypes.c_int),
+    "bl_calib_mfma_i8_ops": ([_I], _I),
+    "bl_calib_mfma_i8_sink_elems": ([], _S),
+    "bl_calib_mfma_i8": ([_I, _P, _P], ctypes.c_int),
 }
 
 
@@ -256,3 +261,47 @@ def ffn_relu2(x, W_gate, gamma_gate, W_up, gamma_up, W_down, gamma_down, workspa
                               _dev(workspace, torch.uint8, "workspace"),
                               workspace.numel(), _stream_ptr(x)), "bl_ffn_relu2")
     return y
+
+
+# ---------------------------------------------------------- calibration ----
+# Measured ceilings (a read-only stream, a copy, an int8 matrix-core loop);
+# they compute nothing of the method.
+
+def _any_dev(t, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+        raise BitLinearError(f"{name} must be a contiguous CUDA (HIP) tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def calib_read(src, sink):
+    """Reads every byte of `src` once (bl_calib_read); sink: int32 device tensor."""
+    torch = _torch()
+    _check(lib().bl_calib_read(_any_dev(src, "src"), src.numel() * src.element_size(),
+                               _dev(sink, torch.int32, "sink"), _stream_ptr(src)),
+           "bl_calib_read")
+
+
+def calib_copy(dst, src):
+    """dst[:] = src bytewise (bl_calib_copy); equal byte sizes required."""
+    nb = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nb:
+        raise BitLinearError("calib_copy: dst and src sizes differ")
+    _check(lib().bl_calib_copy(_any_dev(dst, "dst"), _any_dev(src, "src"), nb,
+                               _stream_ptr(src)), "bl_calib_copy")
+
+
+def calib_mfma_sink(device=None):
+    torch = _torch()
+    return torch.empty(lib().bl_calib_mfma_i8_sink_elems(), dtype=torch.int32, device=device)
+
+
+def calib_mfma_i8(iters: int, sink) -> int:
+    """Runs the int8 matrix-core loop (bl_calib_mfma_i8); returns its op count."""
+    torch = _torch()
+    L = lib()
+    if sink.numel() < L.bl_calib_mfma_i8_sink_elems():
+        raise BitLinearError("calib_mfma_i8: sink too small")
+    _check(L.bl_calib_mfma_i8(iters, _dev(sink, torch.int32, "sink"), _stream_ptr(sink)),
+           "bl_calib_mfma_i8")
+    return L.bl_calib_mfma_i8_ops(iters)

@@ -1,0 +1,356 @@
+"""HBM byte counters of the BitLinear kernels, scaled by a plain copy kernel.
+
+Two parts:
+
+``python -m ternary_weight_linear_quant_amd.counters run``
+    The workload that ``rocprofv3 --pmc FETCH_SIZE`` and, in a second pass,
+    ``rocprofv3 --pmc WRITE_SIZE`` profile: a copy of a known byte count (the
+    calibration), then the kernels whose roofline the benchmark reports, each
+    phase on the benchmark's shapes and weight rotation. Phases are separated
+    by one-block marker copies so every dispatch can be attributed to its
+    phase without knowing how many kernels a call launches.
+
+``python -m ternary_weight_linear_quant_amd.counters trace PROF_DIR``
+    Formats a ``rocprofv3 --kernel-trace --stats`` run (``*_kernel_stats.csv``
+    and ``*_kernel_trace.csv`` under PROF_DIR) as a Markdown table: per kernel
+    the call count and average duration, and per launch shape the median,
+    p10 and p90.
+
+``python -m ternary_weight_linear_quant_amd.counters summarize FETCH_DIR WRITE_DIR``
+    Reads the two passes' ``*counter_collection.csv``, scales each counter by
+    (known bytes / counter reading) of the calibration copy, and prints a
+    Markdown summary whose JSON block the benchmark reads: HBM bytes per
+    launch per phase, next to the SHA-256 of the sources each phase's kernels
+    are built from (a changed source voids the figure).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "ternary_weight_linear_quant_amd", "csrc")
+
+COPY_BYTES = 256 << 20          # calibration copy size
+COPY_CALLS = 3
+MARKER_BYTES = 16 * 256         # one block: a marker dispatch
+LAYERS_2B4T = 40                # weight copies, as in the benchmark
+COPIES_70B = 5                  # 5 x 2 x 58.7 MB > 2 x the 256 MB Infinity Cache
+
+# phase label -> (sources its kernels are built from, what one launch is)
+PHASES = {
+    "ffn_2b4t_m1": (["ffn.hip", "common.hpp"],
+                    "bl_ffn_relu2 at M=1 on 2560->6912->2560 weights, 40 rotated layers "
+                    "(k_ffn_gemv: gate/up+gating and act-quant+down launches)"),
+    "gemv_70b_m1": (["gemv.hip", "common.hpp"],
+                    "bl_bitlinear at M=1 on 8192->28672 and 28672->8192, 5 rotated copies (k_gemv)"),
+    "gemm_decode_70b_m64": (["gemm.hip", "common.hpp"],
+                            "bl_bitlinear at M=64 on the 70B shapes, 5 rotated copies (k_gemm)"),
+    "gemm_prefill_4096": (["gemm.hip", "common.hpp"],
+                          "bl_bitlinear at M=4096 on 2560->6912 and 6912->2560 (k_gemm)"),
+    "gemm_prefill_70b": (["gemm.hip", "common.hpp"],
+                         "bl_bitlinear at M=2048 on 8192->28672 and 28672->8192 (k_gemm)"),
+}
+PHASE_ORDER = ["copy_calibration"] + list(PHASES)
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+# ------------------------------------------------------------------ run ----
+
+def run():
+    import numpy as np
+    import torch
+
+    sys.path.insert(0, ROOT)
+    import ternary_weight_linear_quant_amd as bl
+    from ternary_weight_linear_quant_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    bl.lib()
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev) \
+            .view(torch.bfloat16)
+
+    def weights(wid, idx, N, K, copies):
+        W = torch.from_numpy(wl.weights(wid, idx, N, K)).to(dev)
+        pk, g = bl.quantize_weights(W)
+        del W
+        return [(pk.clone(), g.clone()) for _ in range(copies)]
+
+    print("setup", flush=True)
+    msrc = torch.zeros(MARKER_BYTES // 4, dtype=torch.int32, device=dev)
+    mdst = torch.zeros_like(msrc)
+    csrc = torch.ones(COPY_BYTES // 4, dtype=torch.int32, device=dev)
+    cdst = torch.zeros_like(csrc)
+
+    _, p2, _ = wl.WORKLOADS[2]
+    sh2 = {name: (K, N) for name, K, N in p2}
+    w2 = {name: weights(2, i, N, K, LAYERS_2B4T) for i, (name, K, N) in enumerate(p2)}
+    Kin, Nff = sh2["gate"]
+    x2 = bf16(wl.activations(2, 9, 1, Kin))
+    y2 = torch.empty((1, Kin), dtype=torch.float32, device=dev)
+    ws2 = bl.ffn_relu2_workspace(1, Kin, Nff, dev)
+
+    _, p5, _ = wl.WORKLOADS[5]
+    w5 = {name: weights(5, i, N, K, COPIES_70B) for i, (name, K, N) in enumerate(p5)}
+    q5 = {}
+    for M in (1, 64, 2048):
+        for i, (name, K, N) in enumerate(p5):
+            xq, xs = bl.quantize_acts(bf16(wl.activations(5, i, M, K)))
+            q5[(M, name)] = (xq, xs, torch.empty((M, N), dtype=torch.float32, device=dev))
+
+    _, p3, M3 = wl.WORKLOADS[3]
+    q3 = []
+    for i, (name, K, N) in enumerate(p3):
+        pk, g = weights(3, i, N, K, 1)[0]
+        xq, xs = bl.quantize_acts(bf16(wl.activations(3, i, M3[0], K)))
+        q3.append((xq, xs, pk, g, torch.empty((M3[0], N), dtype=torch.float32, device=dev)))
+    torch.cuda.synchronize()
+
+    def marker():
+        torch.cuda.synchronize()
+        bl.calib_copy(mdst, msrc)
+        torch.cuda.synchronize()
+
+    def phase(name, fn):
+        marker()
+        fn()
+        torch.cuda.synchronize()
+        print("phase", name, flush=True)
+
+    def copy_cal():
+        for _ in range(COPY_CALLS):
+            bl.calib_copy(cdst, csrc)
+
+    def ffn():
+        for lay in range(LAYERS_2B4T):
+            bl.ffn_relu2(x2, *w2["gate"][lay], *w2["up"][lay], *w2["down"][lay],
+                         workspace=ws2, out=y2)
+
+    def rotate70(M):
+        def fn():
+            for c in range(COPIES_70B):
+                for name, _, _ in p5:
+                    xq, xs, y = q5[(M, name)]
+                    bl.bitlinear(xq, xs, *w5[name][c], out=y)
+        return fn
+
+    def prefill4096():
+        for xq, xs, pk, g, y in q3:
+            bl.bitlinear(xq, xs, pk, g, out=y)
+
+    def prefill70():
+        for name, _, _ in p5:
+            xq, xs, y = q5[(2048, name)]
+            bl.bitlinear(xq, xs, *w5[name][0], out=y)
+
+    phase("copy_calibration", copy_cal)
+    phase("ffn_2b4t_m1", ffn)
+    phase("gemv_70b_m1", rotate70(1))
+    phase("gemm_decode_70b_m64", rotate70(64))
+    phase("gemm_prefill_4096", prefill4096)
+    phase("gemm_prefill_70b", prefill70)
+    marker()
+    print("done", flush=True)
+
+
+# ------------------------------------------------------------ summarize ----
+
+def _read_pass(d, counter):
+    """Library dispatches of one pass, in dispatch order: (name, grid, value)."""
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    rows = {}
+    for f in files:
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                name = r["Kernel_Name"]
+                if name.startswith("void "):      # templates demangle with a return type
+                    name = name[5:]
+                if r["Counter_Name"] != counter or not name.startswith("bl::"):
+                    continue
+                key = (int(r["Process_Id"]), int(r["Dispatch_Id"]))
+                rows[key] = (name, int(r["Grid_Size"]), float(r["Counter_Value"]))
+    return [rows[k] for k in sorted(rows)]
+
+
+def _phases(disp):
+    """Split dispatches at the one-block marker copies."""
+    out, cur = [], None
+    for name, grid, val in disp:
+        if name.startswith("bl::k_calib_copy") and grid <= 256:
+            if cur is not None:
+                out.append(cur)
+            cur = []
+        elif cur is not None:
+            cur.append((name, grid, val))
+    if len(out) != len(PHASE_ORDER):
+        raise SystemExit(f"expected {len(PHASE_ORDER)} phases, found {len(out)}")
+    return dict(zip(PHASE_ORDER, out))
+
+
+def _short(name):
+    return name.split("(")[0].replace("bl::", "")
+
+
+def summarize(fetch_dir, write_dir, cmd_fetch, cmd_write):
+    fetch = _phases(_read_pass(fetch_dir, "FETCH_SIZE"))
+    write = _phases(_read_pass(write_dir, "WRITE_SIZE"))
+    cal_f = [v for _, _, v in fetch["copy_calibration"]]
+    cal_w = [v for _, _, v in write["copy_calibration"]]
+    known_kib = COPY_BYTES / 1024
+    f_fetch = known_kib / (sum(cal_f) / len(cal_f))
+    f_write = known_kib / (sum(cal_w) / len(cal_w))
+    result = {
+        "calibration": {"kernel": "k_calib_copy", "bytes": COPY_BYTES, "calls": COPY_CALLS,
+                        "fetch_kib_avg": round(sum(cal_f) / len(cal_f), 1),
+                        "write_kib_avg": round(sum(cal_w) / len(cal_w), 1),
+                        "fetch_factor": round(f_fetch, 5), "write_factor": round(f_write, 5)},
+        "phases": {},
+    }
+    lines = [
+        "# HBM traffic of the BitLinear kernels (rocprofv3 FETCH_SIZE / WRITE_SIZE)",
+        "",
+        "Commands (from the repository root, one pass each):",
+        "",
+        "```",
+        cmd_fetch,
+        cmd_write,
+        f"python -m ternary_weight_linear_quant_amd.counters summarize {fetch_dir} {write_dir}",
+        "```",
+        "",
+        f"Calibration: k_calib_copy of {COPY_BYTES} B read {result['calibration']['fetch_kib_avg']} "
+        f"KiB (FETCH_SIZE) and wrote {result['calibration']['write_kib_avg']} KiB (WRITE_SIZE) per "
+        f"dispatch against {known_kib:.0f} KiB moved each way, so the readings below are scaled by "
+        f"{f_fetch:.4f} (fetch) and {f_write:.4f} (write).",
+        "",
+        "| phase | kernel | dispatches | FETCH KiB/disp | WRITE KiB/disp | scaled HBM bytes/launch |",
+        "|---|---|---|---|---|---|",
+    ]
+    for label in PHASES:
+        files, what = PHASES[label]
+        fd, wd = fetch[label], write[label]
+        if len(fd) != len(wd):
+            raise SystemExit(f"{label}: {len(fd)} fetch vs {len(wd)} write dispatches")
+        per = {}
+        for (n, _, fv), (_, _, wv) in zip(fd, wd):
+            e = per.setdefault(_short(n), [0, 0.0, 0.0])
+            e[0] += 1
+            e[1] += fv
+            e[2] += wv
+        tot_f = sum(v for _, _, v in fd)
+        tot_w = sum(v for _, _, v in wd)
+        traffic = (tot_f * f_fetch + tot_w * f_write) * 1024 / len(fd)
+        for k, (c, fv, wv) in per.items():
+            lines.append(f"| {label} | {k} | {c} | {fv / c:.1f} | {wv / c:.1f} | "
+                         f"{(fv * f_fetch + wv * f_write) * 1024 / c:.0f} |")
+        result["phases"][label] = {
+            "what": what, "dispatches": len(fd),
+            "kernels": {k: {"dispatches": c, "fetch_kib": round(fv / c, 1),
+                            "write_kib": round(wv / c, 1)} for k, (c, fv, wv) in per.items()},
+            "traffic_bytes_per_launch": round(traffic),
+            "sources": files, "source_sha256": source_hash(files),
+        }
+    lines += ["", "Machine-readable (read by bench.py; a figure is void once the hash of "
+              "its sources differs):", "", "```json", json.dumps(result, indent=1), "```", ""]
+    return "\n".join(lines)
+
+
+def trace(prof_dir, cmd, desc):
+    def one(pattern):
+        f = glob.glob(os.path.join(prof_dir, "**", pattern), recursive=True)
+        if not f:
+            raise SystemExit(f"no {pattern} under {prof_dir}")
+        with open(f[0], newline="") as fh:
+            return list(csv.DictReader(fh))
+    stats, tr = one("*kernel_stats.csv"), one("*kernel_trace.csv")
+    lines = [f"# rocprofv3 kernel statistics: {desc}", "",
+             "Command (from the repository root, one MI355X):", "", "```", cmd,
+             f"python -m ternary_weight_linear_quant_amd.counters trace {prof_dir}", "```", "",
+             "Durations exclude launch gaps; the profiler serialises dispatches.", "",
+             "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| `{r['Name'].split('(')[0]}` | {r['Calls']} | "
+                     f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
+    per = {}
+    for r in tr:
+        n = r["Kernel_Name"].split("(")[0]
+        if "bl::" not in n:
+            continue
+        wg = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+        per.setdefault((n, wg), []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines += ["", "Per launch shape (workgroups per launch):", "",
+              "| kernel | workgroups | launches | median us | p10 us | p90 us |",
+              "|---|---|---|---|---|---|"]
+    for (n, wg), v in sorted(per.items()):
+        v = sorted(v)
+        lines.append(f"| `{n}` | {wg} | {len(v)} | {v[len(v) // 2]:.2f} | "
+                     f"{v[len(v) // 10]:.2f} | {v[9 * len(v) // 10]:.2f} |")
+    return "\n".join(lines) + "\n"
+
+
+def load_traffic(path):
+    """{phase: bytes per launch} for the phases whose sources are unchanged."""
+    try:
+        text = open(path).read()
+    except OSError:
+        return {}
+    try:
+        block = text.split("```json", 1)[1].split("```", 1)[0]
+        data = json.loads(block)
+    except (IndexError, ValueError):
+        return {}
+    out = {}
+    for label, ph in data.get("phases", {}).items():
+        try:
+            if source_hash(ph["sources"]) == ph["source_sha256"]:
+                out[label] = ph["traffic_bytes_per_launch"]
+        except (OSError, KeyError):
+            continue
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    sub.add_parser("run")
+    t = sub.add_parser("trace")
+    t.add_argument("prof_dir")
+    t.add_argument("--cmd", dest="trace_cmd", default="rocprofv3 --kernel-trace --stats -d <PROF_DIR> -o bench "
+                   "--output-format csv -- python3 bench.py --steps 3 --warmup 1 --cpu-seconds 0")
+    t.add_argument("--desc", default="bench.py, all legs")
+    s = sub.add_parser("summarize")
+    s.add_argument("fetch_dir")
+    s.add_argument("write_dir")
+    s.add_argument("--cmd-fetch", default="rocprofv3 --pmc FETCH_SIZE --output-format csv "
+                   "-d <FETCH_DIR> -- python3 -m ternary_weight_linear_quant_amd.counters run")
+    s.add_argument("--cmd-write", default="rocprofv3 --pmc WRITE_SIZE --output-format csv "
+                   "-d <WRITE_DIR> -- python3 -m ternary_weight_linear_quant_amd.counters run")
+    a = ap.parse_args()
+    if a.cmd == "run":
+        run()
+    elif a.cmd == "trace":
+        print(trace(a.prof_dir, a.trace_cmd, a.desc), end="")
+    else:
+        print(summarize(a.fetch_dir, a.write_dir, a.cmd_fetch, a.cmd_write))
+
+
+if __name__ == "__main__":
+    main()

@@ -232,4 +232,33 @@ int bl_relu2_glu(const float* gate, const float* up, int64_t count, uint16_t* h,
     return hip_status(bl::launch_relu2_glu(gate, up, count, h, as_stream(stream)));
 }
 
+int bl_calib_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+    if (!src || !sink || bytes < 16 || (bytes % 16) != 0 || !aligned16(src))
+        return BL_ERR_INVALID_ARG;
+    if (int st = device_status()) return st;
+    return hip_status(bl::launch_calib_read(src, bytes, sink, as_stream(stream)));
+}
+
+int bl_calib_copy(void* dst, const void* src, size_t bytes, void* stream) {
+    if (!src || !dst || bytes < 16 || (bytes % 16) != 0 || !aligned16(src) || !aligned16(dst))
+        return BL_ERR_INVALID_ARG;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+    if (a < b + bytes && b < a + bytes) return BL_ERR_INVALID_ARG;
+    if (int st = device_status()) return st;
+    return hip_status(bl::launch_calib_copy(dst, src, bytes, as_stream(stream)));
+}
+
+int64_t bl_calib_mfma_i8_ops(int64_t iters) {
+    if (iters < 1 || iters > (int64_t{1} << 24)) return 0;
+    return bl::calib_mfma_ops(iters);
+}
+
+size_t bl_calib_mfma_i8_sink_elems(void) { return (size_t)bl::kCalibMfmaBlocks * 256; }
+
+int bl_calib_mfma_i8(int64_t iters, int32_t* sink, void* stream) {
+    if (!sink || iters < 1 || iters > (int64_t{1} << 24)) return BL_ERR_INVALID_ARG;
+    if (int st = device_status()) return st;
+    return hip_status(bl::launch_calib_mfma((int)iters, sink, as_stream(stream)));
+}
+
 }  // extern "C"

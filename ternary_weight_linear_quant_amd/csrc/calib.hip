@@ -1,0 +1,110 @@
+// Calibration kernels: the measured ceilings that the BitLinear kernels are
+// compared against, written with the same load widths and matrix
+// instructions. Not part of the method.
+//
+//   k_calib_read  read-only HBM stream with 16-byte loads (the practical
+//                 bandwidth ceiling of the decode GEMV),
+//   k_calib_copy  plain 16-byte copy of a known byte count (the reference
+//                 for scaling hardware byte counters to bytes),
+//   k_calib_mfma  back-to-back independent v_mfma_i32_32x32x32_i8 on register
+//                 operands (the practical int8 matrix-core ceiling of the
+//                 prefill GEMM).
+#include "launch.hpp"
+
+namespace bl {
+
+namespace {
+
+constexpr int kCalibThreads = 256;
+constexpr int kCalibMaxBlocks = 4096;
+constexpr int kMfmaAcc = 8;  // independent accumulators per wave
+
+typedef int v4i_c __attribute__((ext_vector_type(4)));
+typedef int v16i_c __attribute__((ext_vector_type(16)));
+
+int stream_blocks(size_t n16) {
+    const size_t b = (n16 + kCalibThreads - 1) / kCalibThreads;
+    return (int)(b < (size_t)kCalibMaxBlocks ? b : (size_t)kCalibMaxBlocks);
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(kCalibThreads) void k_calib_read(const uint4* __restrict__ src,
+                                                              size_t n16,
+                                                              uint32_t* __restrict__ sink) {
+    uint32_t acc = 0;
+    const size_t stride = (size_t)gridDim.x * kCalibThreads;
+    for (size_t i = (size_t)blockIdx.x * kCalibThreads + threadIdx.x; i < n16; i += stride) {
+        const uint4 v = src[i];
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    // Keeps the loads live; the store happens only for one bit pattern.
+    if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
+__global__ __launch_bounds__(kCalibThreads) void k_calib_copy(uint4* __restrict__ dst,
+                                                              const uint4* __restrict__ src,
+                                                              size_t n16) {
+    const size_t stride = (size_t)gridDim.x * kCalibThreads;
+    for (size_t i = (size_t)blockIdx.x * kCalibThreads + threadIdx.x; i < n16; i += stride)
+        dst[i] = src[i];
+}
+
+// Operands: pseudo-random int8 activations against ternary bytes, the value
+// mix of the prefill GEMM.
+__global__ __launch_bounds__(kCalibThreads) void k_calib_mfma(int iters, int32_t* __restrict__ sink) {
+    const uint32_t t = blockIdx.x * kCalibThreads + threadIdx.x;
+    uint32_t h = t * 0x9E3779B1u + 0x7F4A7C15u;
+    v4i_c a, b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        h ^= h >> 15; h *= 0x2C1B3C6Du; h ^= h >> 12;
+        a[i] = (int)(h & 0x7F7F7F7Fu);
+        const uint32_t c = (h >> 3) & 0x03030303u;            // codes 0..3
+        b[i] = (int)(((c | 0x80808080u) - 0x01010101u) ^ 0x80808080u);  // -1, 0, 1, 2
+    }
+    v16i_c acc[kMfmaAcc];
+#pragma unroll
+    for (int j = 0; j < kMfmaAcc; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[j][v] = 0;
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int j = 0; j < kMfmaAcc; ++j)
+            acc[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc[j], 0, 0, 0);
+    }
+    int32_t s = 0;
+#pragma unroll
+    for (int j = 0; j < kMfmaAcc; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s += acc[j][v];
+    sink[t] = s;
+}
+
+hipError_t launch_calib_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {
+    const size_t n16 = bytes / 16;
+    hipLaunchKernelGGL(k_calib_read, dim3(stream_blocks(n16)), dim3(kCalibThreads), 0, stream,
+                       static_cast<const uint4*>(src), n16, sink);
+    return hipGetLastError();
+}
+
+hipError_t launch_calib_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+    const size_t n16 = bytes / 16;
+    hipLaunchKernelGGL(k_calib_copy, dim3(stream_blocks(n16)), dim3(kCalibThreads), 0, stream,
+                       static_cast<uint4*>(dst), static_cast<const uint4*>(src), n16);
+    return hipGetLastError();
+}
+
+hipError_t launch_calib_mfma(int iters, int32_t* sink, hipStream_t stream) {
+    hipLaunchKernelGGL(k_calib_mfma, dim3(kCalibMfmaBlocks), dim3(kCalibThreads), 0, stream,
+                       iters, sink);
+    return hipGetLastError();
+}
+
+int64_t calib_mfma_ops(int64_t iters) {
+    // 2 ops per multiply-add; 32*32*32 per instruction; kMfmaAcc per
+    // iteration per wave; 4 waves per block.
+    return iters * (int64_t)kMfmaAcc * 2 * 32 * 32 * 32 * (kCalibThreads / 64) * kCalibMfmaBlocks;
+}
+
+}  // namespace bl

@@ -42,4 +42,11 @@ hipError_t launch_ffn_fused(const uint16_t* x, int M, int K, const uint32_t* Wg,
                             const uint32_t* Wd, const float* gd, uint16_t* h, float* y,
                             hipStream_t stream);
 
+// Calibration kernels (measured ceilings; not part of the method).
+constexpr int kCalibMfmaBlocks = 512;        // 256-thread blocks of the MFMA loop
+hipError_t launch_calib_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
+hipError_t launch_calib_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+hipError_t launch_calib_mfma(int iters, int32_t* sink, hipStream_t stream);
+int64_t calib_mfma_ops(int64_t iters);
+
 }  // namespace bl

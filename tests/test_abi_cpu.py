@@ -112,6 +112,23 @@ def test_invalid_arguments_rejected_before_launch(L):
     assert L.bl_bitlinear_pair(A, A, 1, 64, MIS, A, 16, A, A, A, 16, A, None) == E
 
 
+def test_calibration_arguments(L):
+    E = bl.BL_ERR_INVALID_ARG
+    assert L.bl_calib_read(A, 8, A, None) == E
+    assert L.bl_calib_read(A, 24, A, None) == E
+    assert L.bl_calib_read(MIS, 32, A, None) == E
+    assert L.bl_calib_read(None, 32, A, None) == E
+    assert L.bl_calib_copy(A, A, 32, None) == E                  # overlapping
+    assert L.bl_calib_copy(P(0x100010), A, 32, None) == E       # overlapping
+    assert L.bl_calib_copy(P(0x200000), MIS, 32, None) == E
+    assert L.bl_calib_mfma_i8(0, A, None) == E
+    assert L.bl_calib_mfma_i8((1 << 24) + 1, A, None) == E
+    assert L.bl_calib_mfma_i8_ops(0) == 0
+    # 8 instructions x 32*32*32 multiply-adds x 2 ops x 4 waves x blocks
+    blocks = L.bl_calib_mfma_i8_sink_elems() // 256
+    assert L.bl_calib_mfma_i8_ops(10) == 10 * 8 * 2 * 32 ** 3 * 4 * blocks
+
+
 def test_no_device_status(L):
     import torch
     if torch.cuda.device_count() > 0:

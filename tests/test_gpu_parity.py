@@ -498,3 +498,24 @@ def test_ffn_relu2_oracle_end_to_end_small():
     y_ref, _ = oracle.bitlinear(hq, hs, q_d, g_d)
     rel = np.linalg.norm(y - y_ref) / np.linalg.norm(y_ref)
     assert rel < 1e-3, rel
+
+
+# --------------------------------------------------------- calibration ----
+
+def test_calibration_kernels():
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (1 << 20,), dtype=torch.int32, device=DEV)
+    dst = torch.zeros_like(src)
+    bl.calib_copy(dst, src)
+    assert torch.equal(dst, src)
+    tail = torch.zeros(1000 + 4, dtype=torch.int32, device=DEV)  # 16-byte multiple
+    bl.calib_copy(tail, src[:1004].clone())
+    assert torch.equal(tail, src[:1004])
+    sink = torch.zeros(4, dtype=torch.int32, device=DEV)
+    bl.calib_read(src, sink)
+    ms = bl.calib_mfma_sink(DEV)
+    ops = bl.calib_mfma_i8(3, ms)
+    first = ms.clone()
+    assert ops == 3 * 8 * 2 * 32 ** 3 * 4 * (ms.numel() // 256)
+    bl.calib_mfma_i8(3, ms)
+    torch.cuda.synchronize()
+    assert torch.equal(first, ms) and int(first.abs().max()) > 0
