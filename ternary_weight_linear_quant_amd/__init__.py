@@ -155,16 +155,19 @@ def quantize_acts(x, rms_gain=None, rms_eps: float = 1e-5, out=None):
 
 
 def bitlinear(x_q, x_scale, W_packed, gamma, return_acc: bool = False, path: int = 0,
-              out=None):
+              out=None, acc_out=None):
     """y[m][n] = (x_q . q^T)[m][n] * x_scale[m] * gamma -> fp32 [M][N].
-    path: 0 auto, 1 GEMV, 2 GEMM. Calls bl_bitlinear_path."""
+    path: 0 auto, 1 GEMV, 2 GEMM. acc_out: optional int32 [M][N] buffer for the
+    exact sums (returned with y, as with return_acc). Calls bl_bitlinear_path."""
     torch = _torch()
     M, K = x_q.shape
     N = W_packed.shape[0]
     if W_packed.shape[1] * 16 != K:
         raise BitLinearError("W_packed shape does not match K")
     y = torch.empty((M, N), dtype=torch.float32, device=x_q.device) if out is None else out
-    acc = torch.empty((M, N), dtype=torch.int32, device=x_q.device) if return_acc else None
+    acc = acc_out
+    if acc is None and return_acc:
+        acc = torch.empty((M, N), dtype=torch.int32, device=x_q.device)
     _check(lib().bl_bitlinear_path(_dev(x_q, torch.int8, "x_q"),
                                    _dev(x_scale, torch.float32, "x_scale"), M, K,
                                    _dev(W_packed, torch.int32, "W_packed"),
@@ -172,7 +175,7 @@ def bitlinear(x_q, x_scale, W_packed, gamma, return_acc: bool = False, path: int
                                    _dev(y, torch.float32, "y"),
                                    None if acc is None else _dev(acc, torch.int32, "acc"),
                                    int(path), _stream_ptr(x_q)), "bl_bitlinear")
-    return (y, acc) if return_acc else y
+    return (y, acc) if acc is not None else y
 
 
 def relu2_glu(gate, up, out=None):

@@ -25,6 +25,7 @@
 // these reads are free of bank conflicts.
 //
 // Roofline: MFMA (int8). Algorithmic work per call = 2*M*N*K operations.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -44,13 +45,33 @@ constexpr int kBRow = kBK / 4;      // packed weight bytes per row per stage
 __device__ __forceinline__ int swz_a(int r) { return (r ^ ((r >> 3) & 3)) & 7; }
 __device__ __forceinline__ int swz_b(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
 
+// Wait until at most `stages` (wave-uniform, 0..S) pipeline stages of LOADS
+// vector memory instructions each are still outstanding (they complete in
+// issue order).
+template <int LOADS, int S>
+__device__ __forceinline__ void wait_stages(int stages) {
+    static_assert(LOADS * S < 64, "vmcnt range");
+    if constexpr (S == 0) {
+        BL_WAIT_VMCNT(0);
+    } else {
+        if (stages >= S) {
+            BL_WAIT_VMCNT(S * LOADS);
+        } else {
+            wait_stages<LOADS, S - 1>(stages);
+        }
+    }
+}
+
 // WPE: waves per SIMD the register allocation must allow (2 lets two
 // workgroups share a CU so that one's barrier gaps are filled by the other).
-template <int BM, int BN, int WGM, int WGN, int STAGES, int WPE>
+// SPLIT: the K steps are divided among gridDim.y workgroups per tile (kt_split
+// steps each); each adds its exact int32 partial sums into y, which holds
+// int32 zeros beforehand, and k_splitk_finalize rescales them afterwards.
+template <int BM, int BN, int WGM, int WGN, int STAGES, int WPE, bool SPLIT>
 __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_gemm(
     const int8_t* __restrict__ xq, const float* __restrict__ xs, int M, int K,
     const uint32_t* __restrict__ Wp, const float* __restrict__ gamma_p, int N,
-    float* __restrict__ y, int32_t* __restrict__ acc_out) {
+    float* __restrict__ y, int32_t* __restrict__ acc_out, int kt_split) {
     constexpr int NW = WGM * WGN;               // waves per workgroup
     constexpr int WM = BM / WGM, WN = BN / WGN;  // wave tile
     constexpr int TM = WM / 32, TN = WN / 32;
@@ -93,6 +114,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_gemm(
 
     const int KT = (K + kBK - 1) / kBK;
     const bool k_tail = (K % kBK) != 0;  // last stage holds 64 valid k
+    // This workgroup's K steps: global step kt0 + kt for local kt < NK (>= 1).
+    const int kt0 = SPLIT ? (int)blockIdx.y * kt_split : 0;
+    const int NK = SPLIT ? min(kt_split, KT - kt0) : KT;
 
     // Per-lane global sources for the stage loads (k offset added per stage).
     // A instruction i of this wave: rows 8i + lane/8 of the wave's A_ROWS;
@@ -119,8 +143,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_gemm(
 
     auto issue = [&](int kt) {
         const uint32_t st = smem_base + (uint32_t)((kt % STAGES) * STAGE);
-        const int k0 = kt * kBK;
-        const bool tail = k_tail && kt == KT - 1;
+        const int k0 = (kt0 + kt) * kBK;
+        const bool tail = k_tail && kt0 + kt == KT - 1;
 #pragma unroll
         for (int i = 0; i < A_INSTR; ++i) {
             int c = a_chunk[i];
@@ -162,7 +186,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_gemm(
     // (weight 0) when they are expanded. Applied at expansion, not at the
     // LDS read, so the read need not complete right after the barrier.
     auto keep_mask = [&](int kt) -> uint32_t {
-        return (k_tail && kt == KT - 1 && fg) ? 0u : 0xFFFFFFFFu;
+        return (k_tail && kt0 + kt == KT - 1 && fg) ? 0u : 0xFFFFFFFFu;
     };
     auto read_a = [&](v4i* af, int kt, int s) {
         const uint8_t* As = smem + (kt % STAGES) * STAGE;
@@ -192,17 +216,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_gemm(
     static_assert(STAGES >= 3, "pipeline depth");
 #pragma unroll
     for (int st = 0; st < STAGES - 1; ++st)
-        if (st < KT) issue(st);
+        if (st < NK) issue(st);
     // Stage 0 landed: STAGES-2 later stages may still be in flight.
     {
-        const int after = min(STAGES - 2, KT - 1);
-        if (after >= 2) {
-            if (b_loader) BL_WAIT_VMCNT(LOADS_B * 2); else BL_WAIT_VMCNT(LOADS_A * 2);
-        } else if (after == 1) {
-            if (b_loader) BL_WAIT_VMCNT(LOADS_B); else BL_WAIT_VMCNT(LOADS_A);
-        } else {
-            BL_WAIT_VMCNT(0);
-        }
+        const int after = min(STAGES - 2, NK - 1);
+        if (b_loader) wait_stages<LOADS_B, STAGES - 2>(after);
+        else wait_stages<LOADS_A, STAGES - 2>(after);
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
     }
@@ -212,8 +231,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_gemm(
     read_a(af, 0, 0);
     expand(bf, bp, 0, keep_mask(0));
 
-    for (int kt = 0; kt < KT; ++kt) {
-        const bool more = kt + 1 < KT;
+    for (int kt = 0; kt < NK; ++kt) {
+        const bool more = kt + 1 < NK;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             // Next fragments: same step for s < 3, else the first of kt+1.
@@ -242,15 +261,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_gemm(
             if (s == 1 && more) {
                 // Stage kt+1 landed once the stages issued after it are the
                 // only loads outstanding.
-                const int after = min(STAGES - 3, KT - 2 - kt);
-                if (after >= 1) {
-                    if (b_loader) BL_WAIT_VMCNT(LOADS_B); else BL_WAIT_VMCNT(LOADS_A);
-                } else {
-                    BL_WAIT_VMCNT(0);
-                }
+                const int after = min(STAGES - 3, NK - 2 - kt);
+                if (b_loader) wait_stages<LOADS_B, STAGES - 3>(after);
+                else wait_stages<LOADS_A, STAGES - 3>(after);
                 __builtin_amdgcn_s_barrier();
                 asm volatile("" ::: "memory");
-                if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
+                if (kt + STAGES - 1 < NK) issue(kt + STAGES - 1);
                 read_b(bpn, kt + 1);
             }
 #pragma unroll
@@ -265,6 +281,27 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_gemm(
 
     // Epilogue. C layout of the 32x32 MFMA: lane l, register v holds row
     // 8*(v/4) + 4*(l/32) + v%4 (token) and column l%32 (output feature).
+    if constexpr (SPLIT) {
+        int32_t* yi = reinterpret_cast<int32_t*>(y);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int m = m0 + wm0 + 32 * i + 8 * (v / 4) + 4 * (lane / 32) + (v % 4);
+                if (m < M) {
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) {
+                        const int n = n0 + wn0 + 32 * j + (lane % 32);
+                        if (n < N)
+                            __hip_atomic_fetch_add(yi + (size_t)m * N + n, -acc[i][j][v],
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        return;
+    }
     const float gm = *gamma_p;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -290,22 +327,84 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_gemm(
     }
 }
 
-template <int BM, int BN, int WGM, int WGN, int STAGES, int WPE>
+// Split-K helpers: int32 zeros into y before the partial sums are added, and
+// the fp32 rescale in place afterwards (y[m][n] = acc * (x_scale[m] * gamma),
+// the same product and rounding as the direct epilogue).
+__global__ __launch_bounds__(256) void k_splitk_zero(int32_t* __restrict__ y, size_t total) {
+    const size_t stride = (size_t)gridDim.x * 256;
+    const size_t i0 = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if ((reinterpret_cast<uintptr_t>(y) & 15) == 0) {
+        int4* y4 = reinterpret_cast<int4*>(y);
+        for (size_t i = i0; i < total / 4; i += stride) y4[i] = make_int4(0, 0, 0, 0);
+        for (size_t i = total / 4 * 4 + i0; i < total; i += stride) y[i] = 0;
+    } else {
+        for (size_t i = i0; i < total; i += stride) y[i] = 0;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_splitk_finalize(float* __restrict__ y,
+                                                         const float* __restrict__ xs,
+                                                         const float* __restrict__ gamma_p,
+                                                         int32_t* __restrict__ acc_out, int N,
+                                                         size_t total) {
+    const float gm = *gamma_p;
+    const size_t stride = (size_t)gridDim.x * 256;
+    const size_t i0 = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const bool vec = (N % 4) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0 &&
+                     (reinterpret_cast<uintptr_t>(acc_out) & 15) == 0;
+    if (vec) {
+        // Four consecutive elements of one row.
+        for (size_t i = i0; i < total / 4; i += stride) {
+            const int4 a = reinterpret_cast<const int4*>(y)[i];
+            const float sc = xs[(4 * i) / (size_t)N] * gm;
+            reinterpret_cast<float4*>(y)[i] =
+                make_float4((float)a.x * sc, (float)a.y * sc, (float)a.z * sc, (float)a.w * sc);
+            if (acc_out) reinterpret_cast<int4*>(acc_out)[i] = a;
+        }
+        return;
+    }
+    for (size_t i = i0; i < total; i += stride) {
+        const int32_t a = reinterpret_cast<const int32_t*>(y)[i];
+        y[i] = (float)a * (xs[i / (size_t)N] * gm);
+        if (acc_out) acc_out[i] = a;
+    }
+}
+
+template <int BM, int BN, int WGM, int WGN, int STAGES, int WPE, bool SPLIT = false>
 static hipError_t launch_gemm_tile(const int8_t* xq, const float* xs, int M, int K,
                                    const uint32_t* Wp, const float* gamma, int N, float* y,
-                                   int32_t* acc, hipStream_t stream) {
+                                   int32_t* acc, hipStream_t stream, int splits = 1) {
     constexpr size_t lds = (size_t)STAGES * (BM * kARow + BN * kBRow);
+    auto kern = &k_gemm<BM, BN, WGM, WGN, STAGES, WPE, SPLIT>;
     static bool attr_set = false;
     if (lds > 64 * 1024 && !attr_set) {
-        hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&k_gemm<BM, BN, WGM, WGN, STAGES, WPE>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const int blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    hipLaunchKernelGGL((k_gemm<BM, BN, WGM, WGN, STAGES, WPE>), dim3(blocks), dim3(64 * WGM * WGN),
-                       lds, stream, xq, xs, M, K, Wp, gamma, N, y, acc);
+    const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const int KT = (K + kBK - 1) / kBK;
+    if (!SPLIT) {
+        hipLaunchKernelGGL(kern, dim3(tiles), dim3(64 * WGM * WGN), lds, stream, xq, xs, M, K,
+                           Wp, gamma, N, y, acc, KT);
+        return hipGetLastError();
+    }
+    // Even split of the K steps; every split gets at least one step.
+    const int per = (KT + splits - 1) / splits;
+    const int used = (KT + per - 1) / per;
+    const size_t total = (size_t)M * N;
+    const int blocks = (int)std::min<size_t>((total / 4 + 255) / 256 + 1, 2048);
+    hipLaunchKernelGGL(k_splitk_zero, dim3(blocks), dim3(256), 0, stream,
+                       reinterpret_cast<int32_t*>(y), total);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(tiles, used), dim3(64 * WGM * WGN), lds, stream, xq, xs, M, K,
+                       Wp, gamma, N, y, acc, per);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_splitk_finalize, dim3(blocks), dim3(256), 0, stream, y, xs, gamma, acc,
+                       N, total);
     return hipGetLastError();
 }
 
@@ -331,7 +430,18 @@ hipError_t launch_gemm(const int8_t* xq, const float* xs, int M, int K, const ui
         return launch_gemm_tile<128, 256, 1, 4, 3, 2>(xq, xs, M, K, Wp, gamma, N, y, acc, stream);
     if (tiles(128, 128) >= kCUs)
         return launch_gemm_tile<128, 128, 2, 2, 3, 2>(xq, xs, M, K, Wp, gamma, N, y, acc, stream);
-    return launch_gemm_tile<64, 128, 2, 2, 3, 2>(xq, xs, M, K, Wp, gamma, N, y, acc, stream);
+    // Few tiles (few tokens, or few output features): 64 x 128 tiles, two
+    // 4-wave workgroups per CU with six stages in flight each, and the K
+    // steps split across workgroups until the grid covers every CU (each
+    // split keeps at least 8 steps). The partial sums are integers, so their
+    // order of addition does not change a bit of the result.
+    const int64_t t64 = tiles(64, 128);
+    const int KT = (K + kBK - 1) / kBK;
+    const int splits = (int)std::min<int64_t>((kCUs + t64 - 1) / t64, std::max(1, KT / 8));
+    if (splits > 1)
+        return launch_gemm_tile<64, 128, 1, 4, 6, 2, true>(xq, xs, M, K, Wp, gamma, N, y, acc,
+                                                           stream, splits);
+    return launch_gemm_tile<64, 128, 1, 4, 6, 2>(xq, xs, M, K, Wp, gamma, N, y, acc, stream);
 }
 
 }  // namespace bl

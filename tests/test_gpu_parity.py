@@ -237,6 +237,32 @@ def test_gemm_large_tiles_ragged(M, K, N):
     assert torch.equal(y, acc.to(torch.float32) * sc)
 
 
+# Few tiles split K across workgroups whose int32 partial sums are added into
+# y; y starts with garbage here (NaN bits) to show it is cleared first.
+SPLIT_K_CASES = [(64, 8192, 700), (64, 28672, 260), (33, 6912, 1000), (512, 3200, 3200),
+                 (100, 2560, 300), (300, 8640, 129)]
+
+
+@pytest.mark.parametrize("M,K,N", SPLIT_K_CASES)
+def test_gemm_split_k(M, K, N):
+    q, xq, xs, g = _product_case(M, K, N, 59)
+    args = (torch.from_numpy(xq).to(DEV), dev_f32(xs), dev_packed(oracle.pack(q)), dev_f32([g]))
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    acc = torch.full((M, N), -7, dtype=torch.int32, device=DEV)
+    for _ in range(2):
+        bl.bitlinear(*args, out=y, acc_out=acc, path=2)
+        ref64 = args[0].to(torch.float64) @ torch.from_numpy(q).to(DEV, torch.float64).t().contiguous()
+        assert torch.equal(acc.to(torch.float64), ref64)
+        sc = (args[1] * args[3]).view(-1, 1)
+        assert torch.equal(y, acc.to(torch.float32) * sc)
+    rng = np.random.default_rng(M * N)
+    ms = np.unique(np.concatenate([[0, M - 1], rng.choice(M, min(M, 6), replace=False)]))
+    y_ref, acc_ref = oracle.bitlinear(xq[ms], xs[ms], q, g)
+    idx = torch.from_numpy(ms).to(DEV)
+    assert np.array_equal(acc[idx].cpu().numpy(), acc_ref)
+    assert_y_close(y[idx].cpu().numpy(), y_ref, "split-K gemm")
+
+
 def test_gemv_and_gemm_agree_bitwise():
     for M, K, N in [(1, 2560, 6912), (16, 6912, 2560), (4, 3200, 8640)]:
         q, xq, xs, g = _product_case(M, K, N, 55)
