@@ -334,6 +334,7 @@ def main():
             per[name] = {"M": M, "K": K, "N": N, "avg_us": round(1e3 * ms / n, 2),
                          "TOPS": round(2 * M * N * K * n / (ms * 1e-3) / 1e12, 1)}
         tops = ops * reps / (gemm_ms * 1e-3) / 1e12
+        alg = sum(N * K // 4 + 4 + M * K + 4 * M + 4 * M * N for _, K, N, *_ in legs) / len(legs)
         out = {
             "ms_per_step": round(p_ms, 4),
             "step_TOPS": round(ops / (p_ms * 1e-3) / 1e12, 1),
@@ -341,7 +342,8 @@ def main():
                          "peak": I8_PEAK_TOPS, "unit": "TFLOP/s (int8 TOPS)",
                          "frac": round(tops / I8_PEAK_TOPS, 4),
                          "traffic": traffic.get(label),
-                         "traffic_unit": "HBM bytes per launch",
+                         "traffic_unit": "HBM bytes per bl_bitlinear call",
+                         "alg_bytes_per_call": round(alg),
                          "per_projection": per},
             "act_quant_avg_us": round(1e3 * tp.total_ms("act_quant") / tp.count("act_quant"), 2),
         }
@@ -398,8 +400,8 @@ def main():
                              "frac": round(alg / t / 1e9 / HBM_PEAK_GBS, 4),
                              "traffic": traffic.get("gemv_70b_m1" if M == 1
                                                     else "gemm_decode_70b_m64"),
-                             "traffic_unit": "HBM bytes per launch",
-                             "alg_bytes_per_launch": round(alg)},
+                             "traffic_unit": "HBM bytes per bl_bitlinear call",
+                             "alg_bytes_per_call": round(alg)},
                 "per_launch": st,
                 "timing": "HIP graph of the rotation (up and down over the weight copies), "
                           "HIP events on the replay stream",

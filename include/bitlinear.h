@@ -133,7 +133,10 @@ int bl_quantize_acts(const uint16_t* x, int64_t M, int64_t K,
  *   acc        out  optional int32 [M][N]: acc[m][n] = sum_k q[n][k]*x_q[m][k],
  *                   exact (|acc| <= 127*K). NULL to skip.
  * Small M runs a weight-streaming GEMV, large M an int8 MFMA GEMM; both give
- * identical bits. */
+ * identical bits. When the GEMM grid is small (few tokens or few output
+ * features) the K dimension is split across workgroups: the call then
+ * enqueues three kernels and y's memory holds int32 partial sums until the
+ * last one has rescaled them, so y must not alias any input. */
 int bl_bitlinear(const int8_t* x_q, const float* x_scale, int64_t M, int64_t K,
                  const uint32_t* W_packed, const float* gamma, int64_t N,
                  float* y, int32_t* acc, void* stream);

@@ -42,19 +42,27 @@ MARKER_BYTES = 16 * 256         # one block: a marker dispatch
 LAYERS_2B4T = 40                # weight copies, as in the benchmark
 COPIES_70B = 5                  # 5 x 2 x 58.7 MB > 2 x the 256 MB Infinity Cache
 
-# phase label -> (sources its kernels are built from, what one launch is)
+# phase label -> (sources its kernels are built from, what the phase runs,
+# roofline units in the phase, what one unit is). HBM bytes are reported per
+# unit, the unit of the matching roofline in bench.py.
 PHASES = {
     "ffn_2b4t_m1": (["ffn.hip", "common.hpp"],
-                    "bl_ffn_relu2 at M=1 on 2560->6912->2560 weights, 40 rotated layers "
-                    "(k_ffn_gemv: gate/up+gating and act-quant+down launches)"),
+                    "bl_ffn_relu2 at M=1 on 2560->6912->2560 weights, 40 rotated layers",
+                    2 * LAYERS_2B4T,
+                    "k_ffn_gemv launch (gate/up+gating, or act-quant+down)"),
     "gemv_70b_m1": (["gemv.hip", "common.hpp"],
-                    "bl_bitlinear at M=1 on 8192->28672 and 28672->8192, 5 rotated copies (k_gemv)"),
+                    "bl_bitlinear at M=1 on 8192->28672 and 28672->8192, 5 rotated copies",
+                    2 * COPIES_70B, "k_gemv launch"),
     "gemm_decode_70b_m64": (["gemm.hip", "common.hpp"],
-                            "bl_bitlinear at M=64 on the 70B shapes, 5 rotated copies (k_gemm)"),
+                            "bl_bitlinear at M=64 on the 70B shapes, 5 rotated copies",
+                            2 * COPIES_70B,
+                            "bl_bitlinear call (split K: zero, k_gemm, finalize)"),
     "gemm_prefill_4096": (["gemm.hip", "common.hpp"],
-                          "bl_bitlinear at M=4096 on 2560->6912 and 6912->2560 (k_gemm)"),
+                          "bl_bitlinear at M=4096 on 2560->6912 and 6912->2560", 2,
+                          "bl_bitlinear call (k_gemm)"),
     "gemm_prefill_70b": (["gemm.hip", "common.hpp"],
-                         "bl_bitlinear at M=2048 on 8192->28672 and 28672->8192 (k_gemm)"),
+                         "bl_bitlinear at M=2048 on 8192->28672 and 28672->8192", 2,
+                         "bl_bitlinear call (k_gemm)"),
 }
 PHASE_ORDER = ["copy_calibration"] + list(PHASES)
 
@@ -238,11 +246,11 @@ def summarize(fetch_dir, write_dir, cmd_fetch, cmd_write):
         f"dispatch against {known_kib:.0f} KiB moved each way, so the readings below are scaled by "
         f"{f_fetch:.4f} (fetch) and {f_write:.4f} (write).",
         "",
-        "| phase | kernel | dispatches | FETCH KiB/disp | WRITE KiB/disp | scaled HBM bytes/launch |",
+        "| phase | kernel | dispatches | FETCH KiB/disp | WRITE KiB/disp | scaled HBM bytes/disp |",
         "|---|---|---|---|---|---|",
     ]
     for label in PHASES:
-        files, what = PHASES[label]
+        files, what, units, unit = PHASES[label]
         fd, wd = fetch[label], write[label]
         if len(fd) != len(wd):
             raise SystemExit(f"{label}: {len(fd)} fetch vs {len(wd)} write dispatches")
@@ -254,17 +262,20 @@ def summarize(fetch_dir, write_dir, cmd_fetch, cmd_write):
             e[2] += wv
         tot_f = sum(v for _, _, v in fd)
         tot_w = sum(v for _, _, v in wd)
-        traffic = (tot_f * f_fetch + tot_w * f_write) * 1024 / len(fd)
+        traffic = (tot_f * f_fetch + tot_w * f_write) * 1024 / units
         for k, (c, fv, wv) in per.items():
             lines.append(f"| {label} | {k} | {c} | {fv / c:.1f} | {wv / c:.1f} | "
                          f"{(fv * f_fetch + wv * f_write) * 1024 / c:.0f} |")
         result["phases"][label] = {
-            "what": what, "dispatches": len(fd),
+            "what": what, "dispatches": len(fd), "units": units, "unit": unit,
             "kernels": {k: {"dispatches": c, "fetch_kib": round(fv / c, 1),
                             "write_kib": round(wv / c, 1)} for k, (c, fv, wv) in per.items()},
-            "traffic_bytes_per_launch": round(traffic),
+            "traffic_bytes_per_unit": round(traffic),
             "sources": files, "source_sha256": source_hash(files),
         }
+    lines += ["", "| phase | roofline unit | units | scaled HBM bytes per unit |", "|---|---|---|---|"]
+    for label, ph in result["phases"].items():
+        lines.append(f"| {label} | {ph['unit']} | {ph['units']} | {ph['traffic_bytes_per_unit']} |")
     lines += ["", "Machine-readable (read by bench.py; a figure is void once the hash of "
               "its sources differs):", "", "```json", json.dumps(result, indent=1), "```", ""]
     return "\n".join(lines)
@@ -320,7 +331,7 @@ def load_traffic(path):
     for label, ph in data.get("phases", {}).items():
         try:
             if source_hash(ph["sources"]) == ph["source_sha256"]:
-                out[label] = ph["traffic_bytes_per_launch"]
+                out[label] = ph["traffic_bytes_per_unit"]
         except (OSError, KeyError):
             continue
     return out

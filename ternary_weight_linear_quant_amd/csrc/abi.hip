@@ -56,6 +56,12 @@ FfnWorkspace ffn_layout(int64_t M, int64_t K, int64_t N) {
     return w;
 }
 
+// True when the byte ranges [a, a+na) and [b, b+nb) intersect.
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
 bool ffn_shapes_ok(int64_t M, int64_t K, int64_t N) {
     return shape_ok(M, K) && shape_ok(M, N) && shape_ok(N, K) && shape_ok(K, N) &&
            M <= (int64_t{1} << 31) / N;
@@ -121,6 +127,15 @@ int bl_bitlinear_path(const int8_t* x_q, const float* x_scale, int64_t M, int64_
     if (M > (int64_t{1} << 31) / N) return BL_ERR_INVALID_ARG;  // M*N < 2^31
     if (!aligned16(x_q) || !aligned16(W_packed)) return BL_ERR_INVALID_ARG;
     if (path < 0 || path > 2) return BL_ERR_INVALID_ARG;
+    // The outputs may not alias an input (y holds partial sums mid-call).
+    const size_t ny = (size_t)(M * N) * 4;
+    if (overlaps(y, ny, x_q, (size_t)(M * K)) || overlaps(y, ny, x_scale, (size_t)M * 4) ||
+        overlaps(y, ny, W_packed, (size_t)(N * K) / 4) || overlaps(y, ny, gamma, 4))
+        return BL_ERR_INVALID_ARG;
+    if (acc && (overlaps(acc, ny, y, ny) || overlaps(acc, ny, x_q, (size_t)(M * K)) ||
+                overlaps(acc, ny, x_scale, (size_t)M * 4) ||
+                overlaps(acc, ny, W_packed, (size_t)(N * K) / 4) || overlaps(acc, ny, gamma, 4)))
+        return BL_ERR_INVALID_ARG;
     const bool gemv_ok = bl::gemv_supported(M, K);
     if (path == 1 && !gemv_ok) return BL_ERR_INVALID_ARG;
     if (int s = device_status()) return s;

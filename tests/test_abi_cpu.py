@@ -58,26 +58,34 @@ def test_host_helpers(L):
 P = ctypes.c_void_p
 A = P(0x100000)        # aligned fake address, never dereferenced
 MIS = P(0x100001)      # misaligned
+# Distinct, non-overlapping fake buffers for the product's operands.
+X, S, W, G, Y = (P(0x1000000 * i) for i in range(1, 6))
 
 
 def test_invalid_arguments_rejected_before_launch(L):
     E = bl.BL_ERR_INVALID_ARG
     # null pointers
-    assert L.bl_bitlinear(None, A, 1, 64, A, A, 16, A, None, None) == E
-    assert L.bl_bitlinear(A, A, 1, 64, A, A, 16, None, None, None) == E
+    assert L.bl_bitlinear(None, S, 1, 64, W, G, 16, Y, None, None) == E
+    assert L.bl_bitlinear(X, S, 1, 64, W, G, 16, None, None, None) == E
     # shapes
-    assert L.bl_bitlinear(A, A, 0, 64, A, A, 16, A, None, None) == E
-    assert L.bl_bitlinear(A, A, 1, 100, A, A, 16, A, None, None) == E
-    assert L.bl_bitlinear(A, A, 1, 32, A, A, 16, A, None, None) == E
-    assert L.bl_bitlinear(A, A, 1, 64, A, A, 0, A, None, None) == E
-    assert L.bl_bitlinear(A, A, 1 << 20, 1 << 12, A, A, 16, A, None, None) == E
+    assert L.bl_bitlinear(X, S, 0, 64, W, G, 16, Y, None, None) == E
+    assert L.bl_bitlinear(X, S, 1, 100, W, G, 16, Y, None, None) == E
+    assert L.bl_bitlinear(X, S, 1, 32, W, G, 16, Y, None, None) == E
+    assert L.bl_bitlinear(X, S, 1, 64, W, G, 0, Y, None, None) == E
+    assert L.bl_bitlinear(X, S, 1 << 20, 1 << 12, W, G, 16, Y, None, None) == E
     # alignment
-    assert L.bl_bitlinear(MIS, A, 1, 64, A, A, 16, A, None, None) == E
-    assert L.bl_bitlinear(A, A, 1, 64, MIS, A, 16, A, None, None) == E
+    assert L.bl_bitlinear(P(0x1000001), S, 1, 64, W, G, 16, Y, None, None) == E
+    assert L.bl_bitlinear(X, S, 1, 64, P(0x3000001), G, 16, Y, None, None) == E
+    # outputs aliasing inputs
+    assert L.bl_bitlinear(A, P(0x200000), 1, 64, P(0x300000), P(0x400000), 16, A, None, None) == E
+    assert L.bl_bitlinear(P(0x100000), P(0x200000), 1, 64, P(0x300000), P(0x400000), 16,
+                          P(0x500000), P(0x500020), None) == E
+    assert L.bl_bitlinear(P(0x100000), P(0x200000), 1, 64, P(0x300000), P(0x400000), 16,
+                          P(0x3000F0), None, None) == E
     # path selection
-    assert L.bl_bitlinear_path(A, A, 1, 64, A, A, 16, A, None, 3, None) == E
-    assert L.bl_bitlinear_path(A, A, 17, 64, A, A, 16, A, None, 1, None) == E
-    assert L.bl_bitlinear_path(A, A, 16, 16384, A, A, 16, A, None, 1, None) == E
+    assert L.bl_bitlinear_path(X, S, 1, 64, W, G, 16, Y, None, 3, None) == E
+    assert L.bl_bitlinear_path(X, S, 17, 64, W, G, 16, Y, None, 1, None) == E
+    assert L.bl_bitlinear_path(X, S, 16, 16384, W, G, 16, Y, None, 1, None) == E
     # weight quantisation
     assert L.bl_quantize_weights(A, 16, 64, A, A, A, 8 * 15, None) == E
     assert L.bl_quantize_weights(A, 16, 64, A, A, P(0x100004), 8 * 16, None) == E
@@ -134,7 +142,7 @@ def test_no_device_status(L):
     if torch.cuda.device_count() > 0:
         pytest.skip("a GPU is visible; this checks the no-device path")
     D = bl.BL_ERR_NO_DEVICE
-    assert L.bl_bitlinear(A, A, 1, 64, A, A, 16, A, None, None) == D
+    assert L.bl_bitlinear(X, S, 1, 64, W, G, 16, Y, None, None) == D
     assert L.bl_quantize_acts(A, 1, 64, None, 0.0, A, A, None) == D
     assert L.bl_quantize_weights(A, 16, 64, A, A, A, 8 * 16, None) == D
     assert L.bl_relu2_glu(A, A, 4, A, None) == D
