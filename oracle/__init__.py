@@ -60,6 +60,11 @@ def _load():
         "oracle_addsub_matmul": ([P, I, I, P, I, P], None),
         "oracle_epilogue": ([P, I, I, P, F, P], None),
         "oracle_relu2_glu": ([P, P, I, P], None),
+        "oracle_binarize": ([P, I, I, P], None),
+        "oracle_pack_binary": ([P, I, I, I, P], None),
+        "oracle_unpack_binary": ([P, I, I, I, P], None),
+        "oracle_pack_base3": ([P, I, I, I, P], None),
+        "oracle_unpack_base3": ([P, I, I, I, P], None),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -189,3 +194,64 @@ def relu2_glu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
     h = np.empty(g.shape, np.uint16)
     _load().oracle_relu2_glu(_p(g), _p(u), g.size, _p(h))
     return h
+
+
+# ------------------------------------------------- other weight formats ----
+
+def binary_row_words(K: int) -> int:
+    """uint32 words per row of 1-bit weights: 16-byte rows, 128 weights each."""
+    return 4 * ((K + 127) // 128)
+
+
+def base3_row_bytes(K: int) -> int:
+    """Bytes per row of base-3 weights: ceil(K/5) rounded up to 16."""
+    return 16 * (((K + 4) // 5 + 15) // 16)
+
+
+def binarize(W: np.ndarray) -> np.ndarray:
+    W = _c(W, np.float32)
+    N, K = W.shape
+    q = np.empty((N, K), np.int8)
+    _load().oracle_binarize(_p(W), N, K, _p(q))
+    return q
+
+
+def pack_binary(q: np.ndarray) -> np.ndarray:
+    q = _c(q, np.int8)
+    N, K = q.shape
+    rw = binary_row_words(K)
+    out = np.empty((N, rw), np.uint32)
+    _load().oracle_pack_binary(_p(q), N, K, rw, _p(out))
+    return out
+
+
+def unpack_binary(packed: np.ndarray, K: int) -> np.ndarray:
+    packed = _c(packed, np.uint32)
+    N = packed.shape[0]
+    q = np.empty((N, K), np.int8)
+    _load().oracle_unpack_binary(_p(packed), N, K, packed.shape[1], _p(q))
+    return q
+
+
+def quantize_weights_binary(W: np.ndarray):
+    """(1-bit packed uint32 [N][row words], gamma fp32, codes int8 [N][K])."""
+    g = absmean_gamma(W)
+    q = binarize(W)
+    return pack_binary(q), g, q
+
+
+def pack_base3(q: np.ndarray) -> np.ndarray:
+    q = _c(q, np.int8)
+    N, K = q.shape
+    rb = base3_row_bytes(K)
+    out = np.empty((N, rb), np.uint8)
+    _load().oracle_pack_base3(_p(q), N, K, rb, _p(out))
+    return out
+
+
+def unpack_base3(packed: np.ndarray, K: int) -> np.ndarray:
+    packed = _c(packed, np.uint8)
+    N = packed.shape[0]
+    q = np.empty((N, K), np.int8)
+    _load().oracle_unpack_base3(_p(packed), N, K, packed.shape[1], _p(q))
+    return q

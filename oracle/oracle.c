@@ -92,6 +92,71 @@ void oracle_unpack(const uint32_t* packed, int64_t N, int64_t K, int8_t* q) {
     }
 }
 
+/* Binary weights, the original BitNet's {-1, +1} [P3d]: sign of the latent
+ * weight, with W >= 0 (both zeros included) giving +1. */
+void oracle_binarize(const float* W, int64_t N, int64_t K, int8_t* q) {
+    for (int64_t i = 0; i < N * K; ++i) q[i] = (int8_t)(W[i] >= 0.0f ? 1 : -1);
+}
+
+/* One bit per weight: bit 1 for +1, 0 for -1. Row n is row_words uint32
+ * words; weight k sits in word k/32 at bit 8*(i%4) + i/4, i = k%32. Bits at
+ * k >= K are 0. */
+void oracle_pack_binary(const int8_t* q, int64_t N, int64_t K, int64_t row_words,
+                        uint32_t* packed) {
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t j = 0; j < row_words; ++j) {
+            uint32_t w = 0;
+            for (int i = 0; i < 32; ++i) {
+                int64_t k = 32 * j + i;
+                if (k < K && q[n * K + k] > 0) w |= 1u << (8 * (i % 4) + i / 4);
+            }
+            packed[n * row_words + j] = w;
+        }
+    }
+}
+
+void oracle_unpack_binary(const uint32_t* packed, int64_t N, int64_t K, int64_t row_words,
+                          int8_t* q) {
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            int i = (int)(k % 32);
+            uint32_t bit = (packed[n * row_words + k / 32] >> (8 * (i % 4) + i / 4)) & 1u;
+            q[n * K + k] = (int8_t)(bit ? 1 : -1);
+        }
+}
+
+/* Five ternary weights per byte, near the log2(3) bound [P3b]: byte j of row
+ * n is the base-3 number sum_{i<5} c_i * 3^i with c_i = q[n][5j+i] + 1 (the
+ * least significant digit first); positions k >= K count as weight 0 (c = 1).
+ * A row is row_bytes bytes; bytes past ceil(K/5) are 121 (five zeros). */
+void oracle_pack_base3(const int8_t* q, int64_t N, int64_t K, int64_t row_bytes,
+                       uint8_t* packed) {
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t j = 0; j < row_bytes; ++j) {
+            int v = 0, p3 = 1;
+            for (int i = 0; i < 5; ++i) {
+                int64_t k = 5 * j + i;
+                int c = k < K ? q[n * K + k] + 1 : 1;
+                v += c * p3;
+                p3 *= 3;
+            }
+            packed[n * row_bytes + j] = (uint8_t)v;
+        }
+    }
+}
+
+void oracle_unpack_base3(const uint8_t* packed, int64_t N, int64_t K, int64_t row_bytes,
+                         int8_t* q) {
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t j = 0; 5 * j < K; ++j) {
+            int v = packed[n * row_bytes + j];
+            for (int i = 0; i < 5 && 5 * j + i < K; ++i) {
+                q[n * K + 5 * j + i] = (int8_t)(v % 3 - 1);
+                v /= 3;
+            }
+        }
+}
+
 /* 8-bit activations [P1], per token by absmax into [-127, 127]. */
 void oracle_act_quant(const uint16_t* x, int64_t M, int64_t K,
                       const uint16_t* gain, float rms_eps,

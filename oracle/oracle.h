@@ -21,6 +21,9 @@
  *        bound; practical storage puts a ternary value in two bits.
  *   [P3c] same page, section "Mnożenie? Jakie mnożenie": times +1 is an add,
  *        times -1 a subtract, times 0 is skipped.
+ *   [P3d] same page, section "Dlaczego akurat ternarne, a nie czyste
+ *        zero-jeden" (the paragraph after the 1.58-bit count): the original
+ *        BitNet used binary weights, only -1 and +1.
  *   [P5] juhe.plus (Habr repost), section «Когда - три лучше двух»: with
  *        ternary weights y = W·x reduces to sums of the inputs where the
  *        weight is +1 minus sums where it is -1.
@@ -41,6 +44,11 @@
  *     words; weight k sits in word k/16 at bits 8*(i%4) + 2*(i/4), i = k%16.
  *   - epilogue y = acc * scale * gamma evaluated in fp64, rounded to fp32.
  *   - FFN glue h = bf16_rne((relu(g)*relu(g)) * u) in fp32.
+ *   - binary weights: q = +1 where W >= 0, else -1, with the same absmean
+ *     gamma; 1 bit per weight (word k/32, bit 8*(i%4) + i/4), rows padded to
+ *     16 bytes with 0 bits.
+ *   - 1.6-bit storage: five weights per byte as a base-3 number, least
+ *     significant digit first (c = q + 1), rows padded to 16 bytes with 121.
  */
 #ifndef BITLINEAR_ORACLE_H
 #define BITLINEAR_ORACLE_H
@@ -89,6 +97,19 @@ void oracle_epilogue(const int32_t* acc, int64_t M, int64_t N,
 /* h = bf16_rne((r*r)*u), r = g > 0 ? g : 0, fp32 arithmetic. */
 void oracle_relu2_glu(const float* g, const float* u, int64_t count,
                       uint16_t* h);
+
+/* Binary codes q = (W >= 0) ? +1 : -1.  [P3d] */
+void oracle_binarize(const float* W, int64_t N, int64_t K, int8_t* q);
+/* 1-bit packing of codes in {-1, +1}; rows of row_words words.  [P3d] */
+void oracle_pack_binary(const int8_t* q, int64_t N, int64_t K, int64_t row_words,
+                        uint32_t* packed);
+void oracle_unpack_binary(const uint32_t* packed, int64_t N, int64_t K, int64_t row_words,
+                          int8_t* q);
+/* Base-3 packing, five ternary codes per byte; rows of row_bytes bytes. [P3b] */
+void oracle_pack_base3(const int8_t* q, int64_t N, int64_t K, int64_t row_bytes,
+                       uint8_t* packed);
+void oracle_unpack_base3(const uint8_t* packed, int64_t N, int64_t K, int64_t row_bytes,
+                         int8_t* q);
 
 #ifdef __cplusplus
 }

@@ -491,3 +491,102 @@ def test_outlier_columns_shared_across_tokens():
     assert len(cols) == 3
     big = np.abs(x).max(axis=0)
     assert set(np.argsort(big)[-3:].tolist()) == set(cols.tolist())
+
+
+# ------------------------------------------------- binary weights (1 bit) ----
+# inferownia.pl, "BitNet b1.58: era 1-bitowych LLM-ów", section "Dlaczego
+# akurat ternarne, a nie czyste zero-jeden": the original BitNet used binary
+# weights, -1 and +1 only. Readings: sign with W >= 0 -> +1, the same absmean
+# gamma, one bit per weight.
+
+def test_binarize_sign_rule_and_zeros():
+    W = np.array([[-1.5, -1e-30, -0.0, 0.0, 1e-30, 2.0, -np.float32(1e-45), 7.0]], np.float32)
+    assert oracle.binarize(W).tolist() == [[-1, -1, 1, 1, 1, 1, -1, 1]]
+
+
+def test_binary_codes_and_gamma():
+    rng = np.random.default_rng(71)
+    W = (0.02 * rng.standard_normal((40, 256))).astype(np.float32)
+    pk, g, q = oracle.quantize_weights_binary(W)
+    assert set(np.unique(q)) <= {-1, 1}
+    assert np.array_equal(q == 1, W >= 0)
+    assert g == oracle.absmean_gamma(W)
+
+
+def test_pack_binary_hand_words():
+    K = 128
+    def word0(q):
+        return int(oracle.pack_binary(np.array([q], np.int8))[0, 0])
+    alt = [1 if k % 2 == 0 else -1 for k in range(K)]
+    assert word0(alt) == 0x00FF00FF          # even k: bytes 0 and 2 (i%4 in {0,2})
+    assert word0([1] * K) == 0xFFFFFFFF
+    assert word0([-1] * K) == 0
+    for k, w in [(0, 0x1), (4, 0x2), (1, 0x100), (3, 0x1000000), (31, 0x80000000)]:
+        q = [-1] * K
+        q[k] = 1
+        assert word0(q) == w, k
+
+
+def test_pack_binary_layout_property_and_roundtrip():
+    rng = np.random.default_rng(72)
+    for K in (64, 128, 192, 8640):
+        q = np.where(rng.random((5, K)) < 0.5, 1, -1).astype(np.int8)
+        pk = oracle.pack_binary(q)
+        assert pk.shape == (5, oracle.binary_row_words(K))
+        assert pk.shape[1] * 4 % 16 == 0 and pk.shape[1] * 32 >= K
+        assert np.array_equal(oracle.unpack_binary(pk, K), q)
+        # (w >> p) & 0x01010101 holds the bits of k = 32j+4p .. 32j+4p+3
+        for j in range(K // 32):
+            w = int(pk[0, j])
+            for p in range(8):
+                v = (w >> p) & 0x01010101
+                for b in range(4):
+                    assert ((v >> (8 * b)) & 1) == int(q[0, 32 * j + 4 * p + b] > 0)
+        # padding bits (k >= K; every K here is a multiple of 32) are zero
+        assert (pk[:, K // 32:] == 0).all()
+
+
+def test_binary_product_invariant():
+    # x = all ones: acc = (#+1) - (#-1) per row.
+    rng = np.random.default_rng(73)
+    q = np.where(rng.random((7, 192)) < 0.3, 1, -1).astype(np.int8)
+    acc = oracle.int_matmul(np.ones((1, 192), np.int8), q)
+    assert np.array_equal(acc[0], 2 * (q == 1).sum(1) - 192)
+
+
+# ------------------------------------------- base-3 storage (1.6 bits) ----
+# inferownia.pl, section "Skąd te 1,58 bita": log2(3) bits carry one ternary
+# weight; five of them fit one byte (3^5 = 243 <= 256).
+
+def test_base3_hand_bytes():
+    def bytes_of(q):
+        return oracle.pack_base3(np.array([q], np.int8))[0].tolist()
+    assert bytes_of([0] * 5)[:2] == [121, 121]           # 1+3+9+27+81
+    assert bytes_of([1] * 5)[0] == 242
+    assert bytes_of([-1] * 5)[0] == 0
+    assert bytes_of([-1, 0, 1, -1, 0])[0] == 102         # 0 + 3 + 18 + 0 + 81
+    assert bytes_of([-1, 0, 1, -1, 0, 1, 1])[:3] == [102, 125, 121]   # tail: 2+6+9+27+81
+    assert bytes_of([1, -1, -1, -1, -1])[0] == 2         # least significant digit first
+
+
+def test_base3_exhaustive_bijection():
+    import itertools
+    combos = np.array(list(itertools.product([-1, 0, 1], repeat=5)), np.int8)  # 243 rows
+    pk = oracle.pack_base3(combos)
+    vals = pk[:, 0].astype(int)
+    assert sorted(vals.tolist()) == list(range(243))
+    assert np.array_equal(oracle.unpack_base3(pk, 5), combos)
+    assert (pk[:, 1:] == 121).all()
+
+
+def test_base3_rows_padding_and_density():
+    rng = np.random.default_rng(74)
+    for K in (64, 2560, 6912, 8192, 28672, 3200, 8640):
+        rb = oracle.base3_row_bytes(K)
+        assert rb % 16 == 0 and 5 * rb >= K and rb - (K + 4) // 5 < 16
+        assert K < 1000 or 8 * rb / K <= 1.65   # at the workloads' K
+        q = rng.integers(-1, 2, size=(3, K), dtype=np.int8)
+        pk = oracle.pack_base3(q)
+        assert pk.shape == (3, rb) and int(pk.max()) <= 242
+        assert np.array_equal(oracle.unpack_base3(pk, K), q)
+        assert (pk[:, (K + 4) // 5:] == 121).all()
