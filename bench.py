@@ -413,6 +413,61 @@ def main():
             print(f"70b decode M={M}: {leg['packed_GBps']} GB/s packed, "
                   f"{st['mean_us']} us/launch", file=sys.stderr, flush=True)
 
+        # The same decode (M = 1) from the denser formats: five ternary weights
+        # per byte repacked from the 2-bit copies, and 1-bit binary weights of
+        # the same latent matrices.
+        io1 = {}
+        for i, (name, K, N) in enumerate(lprojs):
+            xq, xs = bl.quantize_acts(bf16_dev(wl.activations(LARGE_WORKLOAD, i, 1, K)))
+            io1[name] = (xq, xs, torch.empty((1, N), dtype=torch.float32, device=dev))
+        fmt_w = {"base3": {name: [(bl.pack_base3(pk, K), g) for pk, g in wts[name]]
+                           for name, K, N in lprojs}}
+        binw = {}
+        for i, (name, K, N) in enumerate(lprojs):
+            W = torch.from_numpy(wl.weights(LARGE_WORKLOAD, i, N, K)).to(dev)
+            bits, gb = bl.quantize_weights_binary(W)
+            del W
+            binw[name] = [(bits, gb)] + [(bits.clone(), gb.clone())
+                                         for _ in range(LARGE_COPIES - 1)]
+        fmt_w["binary"] = binw
+        fmt_fn = {"base3": bl.bitlinear_base3, "binary": bl.bitlinear_binary}
+        for fmt, wsets in fmt_w.items():
+            def rotation_f(fmt=fmt, wsets=wsets):
+                for c in range(LARGE_COPIES):
+                    for name, K, N in lprojs:
+                        xq, xs, y = io1[name]
+                        fmt_fn[fmt](xq, xs, *wsets[name][c], out=y)
+
+            rotation_f()
+            torch.cuda.synchronize()
+            gr = capture(rotation_f)
+            st = replay_stats(gr, 20, LARGE_COPIES * len(lprojs))
+            del gr
+            t = st["mean_us"] * 1e-6
+            wbytes = sum(wsets[name][0][0].numel() * wsets[name][0][0].element_size()
+                         for name, _, _ in lprojs) / len(lprojs)
+            alg = sum(wsets[name][0][0].numel() * wsets[name][0][0].element_size()
+                      + 4 + K + 4 + 4 * N for name, K, N in lprojs) / len(lprojs)
+            weights = sum(N * K for _, K, N in lprojs) / len(lprojs)
+            large[f"decode_M1_{fmt}"] = {
+                "kernel": f"k_gemv ({'five ternary weights per byte' if fmt == 'base3' else '1 bit per +-1 weight'})",
+                "bits_per_weight": round(8 * wbytes / weights, 4),
+                "packed_GBps": round(wbytes / t / 1e9, 1),
+                "weights_per_s": round(weights / t / 1e12, 3),
+                "weights_unit": "T weights/s",
+                "roofline": {"bound": "hbm", "achieved": round(alg / t / 1e9, 1),
+                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(alg / t / 1e9 / HBM_PEAK_GBS, 4),
+                             "traffic": None, "alg_bytes_per_launch": round(alg)},
+                "per_launch": st,
+            }
+            print(f"70b decode M=1 {fmt}: {large[f'decode_M1_{fmt}']['packed_GBps']} GB/s packed, "
+                  f"{large[f'decode_M1_{fmt}']['weights_per_s']} T weights/s", file=sys.stderr,
+                  flush=True)
+        large["decode_M1"]["weights_per_s"] = round(
+            sum(N * K for _, K, N in lprojs) / len(lprojs) / (large["decode_M1"]["per_launch"]["mean_us"] * 1e-6) / 1e12, 3)
+        del fmt_w, binw, io1
+
         # Measured ceilings: a read-only 16-byte stream over the same rotated
         # packed weights, and the int8 matrix-core loop.
         sink = torch.zeros(4, dtype=torch.int32, device=dev)

@@ -209,6 +209,59 @@ int bl_ffn_relu2(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate
                  int64_t N_ff, const uint32_t* W_down, const float* gamma_down, float* y,
                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Other weight formats (decode) ----------------------------------------
+ * Two storage formats besides the 2-bit one, each with its own decode
+ * product for M <= 16 tokens (the weight-streaming GEMV; the prefill GEMM
+ * takes the 2-bit format). Same conventions and shape rules as above; the
+ * product additionally needs M * k_extent(K) <= 128 KiB of activations
+ * (k_extent: K rounded up to the format's row). */
+
+/* Bytes of a matrix of 1-bit weights: N * 16*ceil(K/128); of base-3 weights:
+ * N * 16*ceil(ceil(K/5)/16). 0 if the shape is invalid. Host-only. */
+size_t bl_packed_bytes_binary(int64_t N, int64_t K);
+size_t bl_packed_bytes_base3(int64_t N, int64_t K);
+
+/* Binary weights, the original BitNet's {-1, +1}. Source: inferownia.pl
+ * page above, section "Dlaczego akurat ternarne, a nie czyste zero-jeden"
+ * (the earlier BitNet used only -1 and +1 weights).
+ *
+ *   W          in   fp32 [N][K] latent weights (as bl_quantize_weights).
+ *   W_bits     out  uint32 rows of 4*ceil(K/128) words (bl_packed_bytes_binary
+ *                   bytes). q = +1 where W >= 0 (either zero), else -1; bit 1
+ *                   for +1 in word k/32 at bit 8*(i%4) + i/4, i = k % 32, so
+ *                   (word >> p) & 0x01010101 holds the bits of weights
+ *                   32j+4p .. 32j+4p+3. Bits past K are 0.
+ *   gamma      out  one fp32 (device): the same absmean gamma as
+ *                   bl_quantize_weights (mean |W| over the whole matrix).
+ *   workspace  tmp  >= bl_quantize_weights_workspace_bytes(N,K) bytes, 8-byte
+ *                   aligned. */
+int bl_quantize_weights_binary(const float* W, int64_t N, int64_t K, uint32_t* W_bits,
+                               float* gamma, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* Five ternary weights per byte (1.6 bits per weight), repacked from the
+ * 2-bit format so both hold the same codes. Source: inferownia.pl page
+ * above, section "Skąd te 1,58 bita" (log2(3) = 1.58 bits carry a ternary
+ * weight).
+ *
+ *   W_packed   in   2-bit weights [N][K/16] from bl_quantize_weights.
+ *   W3         out  uint8 rows of 16*ceil(ceil(K/5)/16) bytes: byte j is
+ *                   sum_{i<5} c_i 3^i with c_i = q[5j+i] + 1 (least
+ *                   significant digit first); positions past K count as
+ *                   weight 0, so padding bytes are 121. 16-byte aligned. */
+int bl_pack_base3(const uint32_t* W_packed, int64_t N, int64_t K, uint8_t* W3, void* stream);
+
+/* y = (x_q . q^T) * x_scale * gamma for 1-bit (bl_bitlinear_binary) or
+ * base-3 (bl_bitlinear_base3) weights, M <= 16: same outputs, bits and
+ * arguments as bl_bitlinear for the same codes. Sources as bl_bitlinear,
+ * plus the format's passage above. */
+int bl_bitlinear_binary(const int8_t* x_q, const float* x_scale, int64_t M, int64_t K,
+                        const uint32_t* W_bits, const float* gamma, int64_t N, float* y,
+                        int32_t* acc, void* stream);
+int bl_bitlinear_base3(const int8_t* x_q, const float* x_scale, int64_t M, int64_t K,
+                       const uint8_t* W3, const float* gamma, int64_t N, float* y,
+                       int32_t* acc, void* stream);
+
 /* ---- Calibration kernels ------------------------------------------------
  * Measured ceilings for the roofline of the kernels above; they compute
  * nothing of the method. Same conventions as above. */

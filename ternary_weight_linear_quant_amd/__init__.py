@@ -42,6 +42,12 @@ _SIGNATURES = {
     "bl_relu2_glu_quant": ([_P, _P, _I, _I, _P, _P, _P], ctypes.c_int),
     "bl_ffn_relu2_workspace_bytes": ([_I, _I, _I], _S),
     "bl_ffn_relu2": ([_P, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _S, _P], ctypes.c_int),
+    "bl_packed_bytes_binary": ([_I, _I], _S),
+    "bl_packed_bytes_base3": ([_I, _I], _S),
+    "bl_quantize_weights_binary": ([_P, _I, _I, _P, _P, _P, _S, _P], ctypes.c_int),
+    "bl_pack_base3": ([_P, _I, _I, _P, _P], ctypes.c_int),
+    "bl_bitlinear_binary": ([_P, _P, _I, _I, _P, _P, _I, _P, _P, _P], ctypes.c_int),
+    "bl_bitlinear_base3": ([_P, _P, _I, _I, _P, _P, _I, _P, _P, _P], ctypes.c_int),
     "bl_calib_read": ([_P, _S, _P, _P], ctypes.c_int),
     "bl_calib_copy": ([_P, _P, _S, _P], ctypes.c_int),
     "bl_calib_mfma_i8_ops": ([_I], _I),
@@ -264,6 +270,74 @@ def ffn_relu2(x, W_gate, gamma_gate, W_up, gamma_up, W_down, gamma_down, workspa
                               _dev(workspace, torch.uint8, "workspace"),
                               workspace.numel(), _stream_ptr(x)), "bl_ffn_relu2")
     return y
+
+
+# ------------------------------------------------- other weight formats ----
+# 1 bit per {-1, +1} weight (the original BitNet's binary weights) and five
+# ternary weights per byte (1.6 bits); decode products for M <= 16.
+
+def quantize_weights_binary(W, workspace=None):
+    """W fp32 [N][K] -> (W_bits int32 [N][4*ceil(K/128)] holding uint32 words,
+    gamma fp32 [1]). Calls bl_quantize_weights_binary."""
+    torch = _torch()
+    N, K = W.shape
+    L = lib()
+    nbytes = L.bl_packed_bytes_binary(N, K)
+    if nbytes == 0:
+        raise BitLinearError("invalid weight shape")
+    bits = torch.empty((N, nbytes // (4 * N)), dtype=torch.int32, device=W.device)
+    gamma = torch.empty(1, dtype=torch.float32, device=W.device)
+    ws_bytes = L.bl_quantize_weights_workspace_bytes(N, K)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 8) // 8, dtype=torch.float64, device=W.device)
+    _check(L.bl_quantize_weights_binary(_dev(W, torch.float32, "W"), N, K,
+                                        _dev(bits, torch.int32, "W_bits"),
+                                        _dev(gamma, torch.float32, "gamma"),
+                                        _dev(workspace, workspace.dtype, "workspace"),
+                                        workspace.numel() * workspace.element_size(),
+                                        _stream_ptr(W)), "bl_quantize_weights_binary")
+    return bits, gamma
+
+
+def pack_base3(W_packed, K: int):
+    """2-bit packed [N][K/16] -> uint8 [N][16*ceil(ceil(K/5)/16)], five ternary
+    weights per byte. Calls bl_pack_base3."""
+    torch = _torch()
+    N = W_packed.shape[0]
+    L = lib()
+    nbytes = L.bl_packed_bytes_base3(N, K)
+    if nbytes == 0 or W_packed.shape[1] * 16 != K:
+        raise BitLinearError("invalid weight shape")
+    out = torch.empty((N, nbytes // N), dtype=torch.uint8, device=W_packed.device)
+    _check(L.bl_pack_base3(_dev(W_packed, torch.int32, "W_packed"), N, K,
+                           _dev(out, torch.uint8, "W3"), _stream_ptr(W_packed)), "bl_pack_base3")
+    return out
+
+
+def _other_product(fn, name, x_q, x_scale, W, wdtype, gamma, N, return_acc, out):
+    torch = _torch()
+    M, K = x_q.shape
+    y = torch.empty((M, N), dtype=torch.float32, device=x_q.device) if out is None else out
+    acc = torch.empty((M, N), dtype=torch.int32, device=x_q.device) if return_acc else None
+    _check(fn(_dev(x_q, torch.int8, "x_q"), _dev(x_scale, torch.float32, "x_scale"), M, K,
+              _dev(W, wdtype, "W"), _dev(gamma, torch.float32, "gamma"), N,
+              _dev(y, torch.float32, "y"),
+              None if acc is None else _dev(acc, torch.int32, "acc"), _stream_ptr(x_q)), name)
+    return (y, acc) if return_acc else y
+
+
+def bitlinear_binary(x_q, x_scale, W_bits, gamma, return_acc: bool = False, out=None):
+    """BitLinear with 1-bit weights (M <= 16). Calls bl_bitlinear_binary."""
+    torch = _torch()
+    return _other_product(lib().bl_bitlinear_binary, "bl_bitlinear_binary", x_q, x_scale,
+                          W_bits, torch.int32, gamma, W_bits.shape[0], return_acc, out)
+
+
+def bitlinear_base3(x_q, x_scale, W3, gamma, return_acc: bool = False, out=None):
+    """BitLinear with base-3 weights (M <= 16). Calls bl_bitlinear_base3."""
+    torch = _torch()
+    return _other_product(lib().bl_bitlinear_base3, "bl_bitlinear_base3", x_q, x_scale, W3,
+                          torch.uint8, gamma, W3.shape[0], return_acc, out)
 
 
 # ---------------------------------------------------------- calibration ----

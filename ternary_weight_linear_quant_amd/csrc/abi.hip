@@ -247,6 +247,87 @@ int bl_relu2_glu(const float* gate, const float* up, int64_t count, uint16_t* h,
     return hip_status(bl::launch_relu2_glu(gate, up, count, h, as_stream(stream)));
 }
 
+size_t bl_packed_bytes_binary(int64_t N, int64_t K) {
+    if (!shape_ok(N, K)) return 0;
+    return (size_t)N * (size_t)bl::packed_row_bytes_binary(K);
+}
+
+size_t bl_packed_bytes_base3(int64_t N, int64_t K) {
+    if (!shape_ok(N, K)) return 0;
+    return (size_t)N * (size_t)bl::packed_row_bytes_base3(K);
+}
+
+int bl_quantize_weights_binary(const float* W, int64_t N, int64_t K, uint32_t* W_bits,
+                               float* gamma, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    if (!W || !W_bits || !gamma || !workspace) return BL_ERR_INVALID_ARG;
+    if (!shape_ok(N, K)) return BL_ERR_INVALID_ARG;
+    if (!aligned16(W) || !aligned16(W_bits)) return BL_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 7u) != 0) return BL_ERR_INVALID_ARG;
+    if (workspace_bytes < bl_quantize_weights_workspace_bytes(N, K)) return BL_ERR_INVALID_ARG;
+    if (int s = device_status()) return s;
+    return hip_status(bl::launch_quantize_weights_binary(
+        W, N, K, W_bits, bl::packed_row_bytes_binary(K) / 4, gamma,
+        static_cast<double*>(workspace), as_stream(stream)));
+}
+
+int bl_pack_base3(const uint32_t* W_packed, int64_t N, int64_t K, uint8_t* W3, void* stream) {
+    if (!W_packed || !W3) return BL_ERR_INVALID_ARG;
+    if (!shape_ok(N, K)) return BL_ERR_INVALID_ARG;
+    if (!aligned16(W_packed) || !aligned16(W3)) return BL_ERR_INVALID_ARG;
+    if (overlaps(W3, bl_packed_bytes_base3(N, K), W_packed, (size_t)(N * K) / 4))
+        return BL_ERR_INVALID_ARG;
+    if (int s = device_status()) return s;
+    return hip_status(bl::launch_pack_base3(W_packed, N, K, W3, bl::packed_row_bytes_base3(K),
+                                            as_stream(stream)));
+}
+
+namespace {
+
+// Validation shared by the decode products of the other weight formats.
+int other_format_args(const int8_t* x_q, const float* x_scale, int64_t M, int64_t K,
+                      const void* W, size_t w_bytes, const float* gamma, int64_t N, float* y,
+                      int32_t* acc, bool fits) {
+    if (!x_q || !x_scale || !W || !gamma || !y) return BL_ERR_INVALID_ARG;
+    if (!shape_ok(M, K) || !shape_ok(N, K)) return BL_ERR_INVALID_ARG;
+    if (M > (int64_t{1} << 31) / N) return BL_ERR_INVALID_ARG;
+    if (!aligned16(x_q) || !aligned16(W)) return BL_ERR_INVALID_ARG;
+    if (!fits) return BL_ERR_INVALID_ARG;
+    const size_t ny = (size_t)(M * N) * 4;
+    if (overlaps(y, ny, x_q, (size_t)(M * K)) || overlaps(y, ny, x_scale, (size_t)M * 4) ||
+        overlaps(y, ny, W, w_bytes) || overlaps(y, ny, gamma, 4))
+        return BL_ERR_INVALID_ARG;
+    if (acc && (overlaps(acc, ny, y, ny) || overlaps(acc, ny, x_q, (size_t)(M * K)) ||
+                overlaps(acc, ny, x_scale, (size_t)M * 4) || overlaps(acc, ny, W, w_bytes) ||
+                overlaps(acc, ny, gamma, 4)))
+        return BL_ERR_INVALID_ARG;
+    return device_status();
+}
+
+}  // namespace
+
+int bl_bitlinear_binary(const int8_t* x_q, const float* x_scale, int64_t M, int64_t K,
+                        const uint32_t* W_bits, const float* gamma, int64_t N, float* y,
+                        int32_t* acc, void* stream) {
+    const bool fits = shape_ok(M, K) && bl::gemv_binary_supported(M, K);
+    if (int s = other_format_args(x_q, x_scale, M, K, W_bits, bl_packed_bytes_binary(N, K),
+                                  gamma, N, y, acc, fits))
+        return s;
+    return hip_status(bl::launch_gemv_binary(x_q, x_scale, (int)M, (int)K, W_bits, gamma, (int)N,
+                                             y, acc, as_stream(stream)));
+}
+
+int bl_bitlinear_base3(const int8_t* x_q, const float* x_scale, int64_t M, int64_t K,
+                       const uint8_t* W3, const float* gamma, int64_t N, float* y, int32_t* acc,
+                       void* stream) {
+    const bool fits = shape_ok(M, K) && bl::gemv_base3_supported(M, K);
+    if (int s = other_format_args(x_q, x_scale, M, K, W3, bl_packed_bytes_base3(N, K), gamma,
+                                  N, y, acc, fits))
+        return s;
+    return hip_status(bl::launch_gemv_base3(x_q, x_scale, (int)M, (int)K, W3, gamma, (int)N, y,
+                                            acc, as_stream(stream)));
+}
+
 int bl_calib_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
     if (!src || !sink || bytes < 16 || (bytes % 16) != 0 || !aligned16(src))
         return BL_ERR_INVALID_ARG;

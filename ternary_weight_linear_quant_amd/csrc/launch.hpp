@@ -42,6 +42,24 @@ hipError_t launch_ffn_fused(const uint16_t* x, int M, int K, const uint32_t* Wg,
                             const uint32_t* Wd, const float* gd, uint16_t* h, float* y,
                             hipStream_t stream);
 
+// Other weight formats (decode GEMV only): 1 bit per {-1, +1} weight and
+// five ternary weights per byte.
+int64_t packed_row_bytes_binary(int64_t K);
+int64_t packed_row_bytes_base3(int64_t K);
+bool gemv_binary_supported(int64_t M, int64_t K);
+bool gemv_base3_supported(int64_t M, int64_t K);
+hipError_t launch_quantize_weights_binary(const float* W, int64_t N, int64_t K, uint32_t* packed,
+                                          int64_t row_words, float* gamma, double* rowsums,
+                                          hipStream_t stream);
+hipError_t launch_pack_base3(const uint32_t* packed2, int64_t N, int64_t K, uint8_t* out,
+                             int64_t row_bytes, hipStream_t stream);
+hipError_t launch_gemv_binary(const int8_t* xq, const float* xs, int M, int K,
+                              const uint32_t* Wb, const float* gamma, int N, float* y,
+                              int32_t* acc, hipStream_t stream);
+hipError_t launch_gemv_base3(const int8_t* xq, const float* xs, int M, int K, const uint8_t* W3,
+                             const float* gamma, int N, float* y, int32_t* acc,
+                             hipStream_t stream);
+
 // Calibration kernels (measured ceilings; not part of the method).
 constexpr int kCalibMfmaBlocks = 512;        // 256-thread blocks of the MFMA loop
 hipError_t launch_calib_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);

@@ -34,14 +34,25 @@ __global__ __launch_bounds__(64) void k_absmean_rowsum(
     R[n] = s;
 }
 
-// gamma = (float)((sum_n R[n], n increasing) / (N*K)). One thread.
-__global__ __launch_bounds__(64) void k_gamma_finalize(
+// gamma = (float)((sum_n R[n], n increasing) / (N*K)). The row sums are
+// staged through LDS by the whole block in coalesced tiles; thread 0 adds
+// them in order (the chain, not the loads, is then the critical path).
+__global__ __launch_bounds__(256) void k_gamma_finalize(
     const double* __restrict__ R, int64_t N, int64_t K, float* __restrict__ gamma) {
-    if (threadIdx.x != 0) return;
+    constexpr int kTile = 2048;
+    __shared__ double tile[kTile];
     double s = 0.0;
+    for (int64_t base = 0; base < N; base += kTile) {
+        const int cnt = (int)((N - base) < kTile ? (N - base) : kTile);
+        for (int i = threadIdx.x; i < cnt; i += blockDim.x) tile[i] = R[base + i];
+        __syncthreads();
+        if (threadIdx.x == 0) {
 #pragma unroll 8
-    for (int64_t n = 0; n < N; ++n) s += R[n];
-    *gamma = (float)(s / (double)(N * K));
+            for (int i = 0; i < cnt; ++i) s += tile[i];
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *gamma = (float)(s / (double)(N * K));
 }
 
 // One thread per packed word: 16 consecutive weights of one row.
@@ -83,7 +94,7 @@ hipError_t launch_quantize_weights(const float* W, int64_t N, int64_t K, uint32_
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_gamma_finalize, dim3(1), dim3(64), 0, stream, rowsums, N, K, gamma);
+    hipLaunchKernelGGL(k_gamma_finalize, dim3(1), dim3(256), 0, stream, rowsums, N, K, gamma);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     {
@@ -93,6 +104,92 @@ hipError_t launch_quantize_weights(const float* W, int64_t N, int64_t K, uint32_
         hipLaunchKernelGGL(k_ternarize_pack, dim3((unsigned)blocks), dim3(threads), 0, stream,
                            W, words, gamma, packed);
     }
+    return hipGetLastError();
+}
+
+// Binary weights of the original BitNet (inferownia.pl page above, section
+// "Dlaczego akurat ternarne, a nie czyste zero-jeden": only -1 and +1): the
+// sign of the latent weight, W >= 0 (either zero) giving +1, stored at one
+// bit per weight -- word k/32 of the row, bit 8*(i%4) + i/4 for i = k%32, so
+// that (w >> p) & 0x01010101 holds four consecutive weights. Rows are
+// row_words words (16-byte multiples); bits past K are 0. One thread per
+// word.
+__global__ __launch_bounds__(256) void k_binarize_pack(
+    const float* __restrict__ W, int64_t N, int64_t K, int64_t row_words,
+    uint32_t* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= N * row_words) return;
+    const int64_t n = i / row_words, j = i - n * row_words;
+    uint32_t word = 0;
+    if (32 * j < K) {  // K % 64 == 0: a word is wholly inside or past the row
+        const float4* src = reinterpret_cast<const float4*>(W + n * K + 32 * j);
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+            const float4 f = src[v];
+            const float e[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int b = 4 * v + t;  // weight index within the word
+                if (e[t] >= 0.0f) word |= 1u << (8 * (b % 4) + b / 4);
+            }
+        }
+    }
+    out[i] = word;
+}
+
+// Ternary codes at five per byte (same page, section "Skąd te 1,58 bita":
+// log2(3) bits carry a ternary value): byte j of a row is the base-3 number
+// sum_{i<5} c_i 3^i of codes c = q + 1 at k = 5j + i (least significant
+// digit first), read from the 2-bit packing; positions k >= K count as
+// weight 0 (c = 1), so padding bytes are 121. One thread per output byte.
+__global__ __launch_bounds__(256) void k_pack_base3(
+    const uint32_t* __restrict__ P2, int64_t N, int64_t K, int64_t row_bytes,
+    uint8_t* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= N * row_bytes) return;
+    const int64_t n = i / row_bytes, j = i - n * row_bytes;
+    const uint32_t* row = P2 + n * (K / 16);
+    int v = 0;
+#pragma unroll
+    for (int d = 4; d >= 0; --d) {  // Horner, most significant digit first
+        const int64_t k = 5 * j + d;
+        int c = 1;
+        if (k < K) {
+            const int t = (int)(k % 16);
+            c = (int)((row[k / 16] >> (8 * (t % 4) + 2 * (t / 4))) & 3u);
+        }
+        v = 3 * v + c;
+    }
+    out[i] = (uint8_t)v;
+}
+
+hipError_t launch_quantize_weights_binary(const float* W, int64_t N, int64_t K, uint32_t* packed,
+                                          int64_t row_words, float* gamma, double* rowsums,
+                                          hipStream_t stream) {
+    {
+        const int threads = 64;
+        const int64_t blocks = (N + threads - 1) / threads;
+        hipLaunchKernelGGL(k_absmean_rowsum, dim3((unsigned)blocks), dim3(threads), 0, stream,
+                           W, N, K, rowsums);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_gamma_finalize, dim3(1), dim3(256), 0, stream, rowsums, N, K, gamma);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int threads = 256;
+    const int64_t blocks = (N * row_words + threads - 1) / threads;
+    hipLaunchKernelGGL(k_binarize_pack, dim3((unsigned)blocks), dim3(threads), 0, stream, W, N, K,
+                       row_words, packed);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_base3(const uint32_t* packed2, int64_t N, int64_t K, uint8_t* out,
+                             int64_t row_bytes, hipStream_t stream) {
+    const int threads = 256;
+    const int64_t blocks = (N * row_bytes + threads - 1) / threads;
+    hipLaunchKernelGGL(k_pack_base3, dim3((unsigned)blocks), dim3(threads), 0, stream, packed2, N,
+                       K, row_bytes, out);
     return hipGetLastError();
 }
 

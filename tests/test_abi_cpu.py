@@ -120,6 +120,27 @@ def test_invalid_arguments_rejected_before_launch(L):
     assert L.bl_bitlinear_pair(A, A, 1, 64, MIS, A, 16, A, A, A, 16, A, None) == E
 
 
+def test_other_formats_host_side(L):
+    E = bl.BL_ERR_INVALID_ARG
+    assert L.bl_packed_bytes_binary(16, 8640) == 16 * 16 * 68
+    assert L.bl_packed_bytes_binary(16, 8192) == 16 * 8192 // 8
+    assert L.bl_packed_bytes_base3(16, 6912) == 16 * 1392
+    assert L.bl_packed_bytes_base3(16, 2560) == 16 * 512
+    assert L.bl_packed_bytes_base3(16, 100) == 0
+    ws = L.bl_quantize_weights_workspace_bytes(16, 64)
+    assert L.bl_quantize_weights_binary(None, 16, 64, W, G, S, ws, None) == E
+    assert L.bl_quantize_weights_binary(X, 16, 48, W, G, S, ws, None) == E
+    assert L.bl_quantize_weights_binary(X, 16, 64, W, G, S, ws - 1, None) == E
+    assert L.bl_pack_base3(W, 16, 64, P(0x3000010), None) == E               # overlapping
+    assert L.bl_pack_base3(W, 16, 64, P(0x6000001), None) == E               # misaligned
+    for f in (L.bl_bitlinear_binary, L.bl_bitlinear_base3):
+        assert f(X, S, 17, 64, W, G, 16, Y, None, None) == E                  # M > 16
+        assert f(X, S, 16, 16384, W, G, 16, Y, None, None) == E               # LDS bound
+        assert f(X, S, 1, 64, W, G, 16, P(0x3000000), None, None) == E        # y aliases W
+        assert f(X, S, 1, 100, W, G, 16, Y, None, None) == E
+        assert f(None, S, 1, 64, W, G, 16, Y, None, None) == E
+
+
 def test_calibration_arguments(L):
     E = bl.BL_ERR_INVALID_ARG
     assert L.bl_calib_read(A, 8, A, None) == E
@@ -148,6 +169,9 @@ def test_no_device_status(L):
     assert L.bl_relu2_glu(A, A, 4, A, None) == D
     assert L.bl_relu2_glu_quant(A, A, 1, 64, A, A, None) == D
     assert L.bl_bitlinear_pair(A, A, 1, 64, A, A, 16, A, A, A, 16, A, None) == D
+    assert L.bl_bitlinear_binary(X, S, 1, 64, W, G, 16, Y, None, None) == D
+    assert L.bl_bitlinear_base3(X, S, 1, 64, W, G, 16, Y, None, None) == D
+    assert L.bl_pack_base3(W, 16, 64, P(0x6000000), None) == D
     need = L.bl_ffn_relu2_workspace_bytes(1, 256, 1024)
     assert L.bl_ffn_relu2(A, 1, 256, A, A, A, A, 1024, A, A, A, P(0x200000), need, None) == D
 

@@ -545,3 +545,94 @@ def test_calibration_kernels():
     bl.calib_mfma_i8(3, ms)
     torch.cuda.synchronize()
     assert torch.equal(first, ms) and int(first.abs().max()) > 0
+
+
+# ------------------------------------------------- other weight formats ----
+# 1-bit {-1, +1} weights and five ternary weights per byte: packers bit-exact
+# against the oracle's packing of the oracle's codes, decode products exact in
+# int32 and within 1e-6 in fp32, and (base 3) bit-identical to the 2-bit path
+# on the same codes.
+
+FORMAT_CASES = [(1, 64, 16), (3, 192, 70), (1, 2560, 300), (16, 6912, 257), (5, 8640, 40),
+                (2, 3200, 33), (1, 28672, 48), (4, 8192, 100)]
+
+
+def _latent(rng, N, K):
+    W = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
+    W[0, :8] = [0.0, -0.0, 1e-30, -1e-30, 0.0, -0.0, 0.0, -0.0]   # signs of zeros
+    return W
+
+
+@pytest.mark.parametrize("M,K,N", FORMAT_CASES)
+def test_binary_weights_parity(M, K, N):
+    rng = np.random.default_rng(M * 1000 + K + N)
+    W = _latent(rng, N, K)
+    bits_ref, g_ref, q = oracle.quantize_weights_binary(W)
+    bits, g = bl.quantize_weights_binary(dev_f32(W))
+    assert g.item() == float(g_ref)
+    assert np.array_equal(bits.cpu().numpy().view(np.uint32), bits_ref)
+    xq, xs = oracle.act_quant(wl.activations(61, 0, M, K))
+    y, acc = bl.bitlinear_binary(torch.from_numpy(xq).to(DEV), dev_f32(xs), bits, g,
+                                 return_acc=True)
+    y_ref, acc_ref = oracle.bitlinear(xq, xs, q, g_ref)
+    assert np.array_equal(acc.cpu().numpy(), acc_ref)
+    assert_y_close(y.cpu().numpy(), y_ref, "binary")
+
+
+@pytest.mark.parametrize("M,K,N", FORMAT_CASES)
+def test_base3_weights_parity(M, K, N):
+    rng = np.random.default_rng(M * 2000 + K + N)
+    q = rand_codes(rng, N, K)
+    q[0] = 0
+    q[-1] = 1
+    pk = dev_packed(oracle.pack(q))
+    w3 = bl.pack_base3(pk, K)
+    assert np.array_equal(w3.cpu().numpy(), oracle.pack_base3(q))
+    xq, xs = oracle.act_quant(wl.activations(62, 0, M, K))
+    xq_d, xs_d, g = torch.from_numpy(xq).to(DEV), dev_f32(xs), dev_f32([0.0159])
+    y, acc = bl.bitlinear_base3(xq_d, xs_d, w3, g, return_acc=True)
+    y_ref, acc_ref = oracle.bitlinear(xq, xs, q, np.float32(0.0159))
+    assert np.array_equal(acc.cpu().numpy(), acc_ref)
+    assert_y_close(y.cpu().numpy(), y_ref, "base3")
+    y2, acc2 = bl.bitlinear(xq_d, xs_d, pk, g, return_acc=True, path=1)
+    assert torch.equal(acc, acc2) and torch.equal(y.view(torch.int32), y2.view(torch.int32))
+
+
+@pytest.mark.parametrize("idx", [0, 1])
+def test_other_formats_70b_full_size(idx):
+    """70B-class matrices at full size, M = 1: base 3 repacked from the
+    workload's 2-bit weights gives the 2-bit path's bits; binary weights of the
+    same latent matrix against the oracle on sampled rows."""
+    q_ref, g_ref, pk, g = workload_weights(5, idx)
+    _, K, N = wl.WORKLOADS[5][1][idx]
+    x = wl.activations(5, idx, 1, K)
+    xq, xs = bl.quantize_acts(dev_bf16(x))
+    w3 = bl.pack_base3(pk, K)
+    rows = np.sort(np.random.default_rng(idx).choice(N, 64, replace=False))
+    assert np.array_equal(w3[torch.from_numpy(rows).to(DEV)].cpu().numpy(),
+                          oracle.pack_base3(q_ref[rows]))
+    y3, a3 = bl.bitlinear_base3(xq, xs, w3, g, return_acc=True)
+    y2, a2 = bl.bitlinear(xq, xs, pk, g, return_acc=True)
+    assert torch.equal(a3, a2) and torch.equal(y3.view(torch.int32), y2.view(torch.int32))
+    W = wl.weights(5, idx, N, K)
+    bits, gb = bl.quantize_weights_binary(dev_f32(W))
+    assert gb.item() == float(g_ref)
+    qb = oracle.binarize(W[rows])
+    del W
+    assert np.array_equal(bits[torch.from_numpy(rows).to(DEV)].cpu().numpy().view(np.uint32),
+                          oracle.pack_binary(qb))
+    yb, ab = bl.bitlinear_binary(xq, xs, bits, gb, return_acc=True)
+    yr, ar = oracle.bitlinear(xq.cpu().numpy(), xs.cpu().numpy(), qb, g_ref)
+    idx_t = torch.from_numpy(rows).to(DEV)
+    assert np.array_equal(ab[:, idx_t].cpu().numpy(), ar)
+    assert_y_close(yb[:, idx_t].cpu().numpy(), yr, "binary 70B")
+
+
+def test_other_formats_reject_prefill_sizes():
+    q = np.zeros((16, 64), np.int8)
+    pk = dev_packed(oracle.pack(q))
+    w3 = bl.pack_base3(pk, 64)
+    xq = torch.zeros((17, 64), dtype=torch.int8, device=DEV)
+    xs = torch.ones(17, device=DEV)
+    with pytest.raises(bl.BitLinearError):
+        bl.bitlinear_base3(xq, xs, w3, dev_f32([1.0]))
