@@ -458,7 +458,9 @@ def main():
                 "roofline": {"bound": "hbm", "achieved": round(alg / t / 1e9, 1),
                              "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": round(alg / t / 1e9 / HBM_PEAK_GBS, 4),
-                             "traffic": None, "alg_bytes_per_launch": round(alg)},
+                             "traffic": traffic.get(f"gemv_70b_m1_{fmt}"),
+                             "traffic_unit": "HBM bytes per launch",
+                             "alg_bytes_per_launch": round(alg)},
                 "per_launch": st,
             }
             print(f"70b decode M=1 {fmt}: {large[f'decode_M1_{fmt}']['packed_GBps']} GB/s packed, "

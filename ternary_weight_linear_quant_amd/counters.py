@@ -53,6 +53,12 @@ PHASES = {
     "gemv_70b_m1": (["gemv.hip", "common.hpp"],
                     "bl_bitlinear at M=1 on 8192->28672 and 28672->8192, 5 rotated copies",
                     2 * COPIES_70B, "k_gemv launch"),
+    "gemv_70b_m1_base3": (["gemv.hip", "common.hpp"],
+                          "bl_bitlinear_base3 at M=1 on the 70B shapes, 5 rotated copies",
+                          2 * COPIES_70B, "k_gemv launch (five ternary weights per byte)"),
+    "gemv_70b_m1_binary": (["gemv.hip", "common.hpp"],
+                           "bl_bitlinear_binary at M=1 on the 70B shapes, 5 rotated copies",
+                           2 * COPIES_70B, "k_gemv launch (1 bit per +-1 weight)"),
     "gemm_decode_70b_m64": (["gemm.hip", "common.hpp"],
                             "bl_bitlinear at M=64 on the 70B shapes, 5 rotated copies",
                             2 * COPIES_70B,
@@ -120,6 +126,14 @@ def run():
             xq, xs = bl.quantize_acts(bf16(wl.activations(5, i, M, K)))
             q5[(M, name)] = (xq, xs, torch.empty((M, N), dtype=torch.float32, device=dev))
 
+    w5b3 = {name: [(bl.pack_base3(pk, K), g) for pk, g in w5[name]] for name, K, N in p5}
+    w5bin = {}
+    for i, (name, K, N) in enumerate(p5):
+        W = torch.from_numpy(wl.weights(5, i, N, K)).to(dev)
+        bits, gb = bl.quantize_weights_binary(W)
+        del W
+        w5bin[name] = [(bits.clone(), gb.clone()) for _ in range(COPIES_70B)]
+
     _, p3, M3 = wl.WORKLOADS[3]
     q3 = []
     for i, (name, K, N) in enumerate(p3):
@@ -156,6 +170,14 @@ def run():
                     bl.bitlinear(xq, xs, *w5[name][c], out=y)
         return fn
 
+    def rotate70_fmt(fn, wset):
+        def run_fmt():
+            for c in range(COPIES_70B):
+                for name, _, _ in p5:
+                    xq, xs, y = q5[(1, name)]
+                    fn(xq, xs, *wset[name][c], out=y)
+        return run_fmt
+
     def prefill4096():
         for xq, xs, pk, g, y in q3:
             bl.bitlinear(xq, xs, pk, g, out=y)
@@ -168,6 +190,8 @@ def run():
     phase("copy_calibration", copy_cal)
     phase("ffn_2b4t_m1", ffn)
     phase("gemv_70b_m1", rotate70(1))
+    phase("gemv_70b_m1_base3", rotate70_fmt(bl.bitlinear_base3, w5b3))
+    phase("gemv_70b_m1_binary", rotate70_fmt(bl.bitlinear_binary, w5bin))
     phase("gemm_decode_70b_m64", rotate70(64))
     phase("gemm_prefill_4096", prefill4096)
     phase("gemm_prefill_70b", prefill70)

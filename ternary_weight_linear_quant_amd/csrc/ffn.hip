@@ -9,10 +9,12 @@
 //
 // Launch A: every workgroup quantises the layer input x (bf16 [M][K]) per
 //   token into LDS itself, then computes 16 rows of BOTH the gate and the up
-//   projection (waves 0-1 gate, 2-3 up, K split two ways) and writes
+//   projection (KS waves each, splitting K) and writes
 //   h = bf16(relu(y_gate)^2 * y_up) for those rows.
 // Launch B: every workgroup quantises h per token into LDS itself and
-//   computes 16 rows of the down projection (K split four ways) into y.
+//   computes 16 rows of the down projection (KS waves splitting K) into y.
+// The K split is chosen so that every wave's weight chunks are in flight at
+// once (a few chunks per wave).
 // Each step uses exactly the arithmetic of bl_quantize_acts, bl_bitlinear
 // and bl_relu2_glu, so the output bits equal the unfused sequence. The
 // per-workgroup quantisation re-reads the M tokens from L2 in every
@@ -31,8 +33,9 @@
 
 namespace bl {
 
-constexpr int kFfnThreads = 256;
-constexpr int kFfnCache = 8;  // 16-value activation units cached per thread
+constexpr int kFfnMaxThreads = 1024;
+constexpr int kFfnMinThreads = 256;
+constexpr int kFfnCache = 8;  // 16-value activation units cached per thread (at 256 threads)
 constexpr int kFfnR = 4;      // weight chunks in flight per lane
 
 // lgkmcnt(0) only: LDS traffic done, vector loads may stay in flight.
@@ -50,22 +53,25 @@ __device__ __forceinline__ uint32_t relu2_gate_bits(float g, float u) {
     return f32_to_bf16_rne(sq * u);
 }
 
-template <bool GLU>
-__global__ __launch_bounds__(kFfnThreads) void k_ffn_gemv(
+template <bool GLU, int KS>
+__global__ __launch_bounds__(64 * (GLU ? 2 : 1) * KS) void k_ffn_gemv(
     const uint16_t* __restrict__ xin, int M, int K, const uint32_t* __restrict__ W0,
     const float* __restrict__ g0, const uint32_t* __restrict__ W1,
     const float* __restrict__ g1, int N, float* __restrict__ y, uint16_t* __restrict__ h) {
-    constexpr int KS = GLU ? 2 : 4;
+    constexpr int NW = (GLU ? 2 : 1) * KS;  // waves
+    constexpr int NT = 64 * NW;             // threads
+    constexpr int CACHE = kFfnCache * kFfnMinThreads / NT;
+    static_assert(NT >= kFfnMinThreads && NT <= kFfnMaxThreads && CACHE >= 1, "block shape");
     extern __shared__ __align__(16) uint8_t smem[];  // int8 activations, token-minor
-    __shared__ v4i red[4][kWave];
-    __shared__ float s_amax[4][16];
+    __shared__ v4i red[NW][kWave];
+    __shared__ float s_amax[NW][16];
     __shared__ float s_scale[16];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int lane = tid % kWave;
-    const int mat = GLU ? wave / 2 : 0;
-    const int ks = GLU ? wave % 2 : wave;
+    const int mat = GLU ? wave / KS : 0;
+    const int ks = wave % KS;
     const uint32_t* W = (GLU && mat) ? W1 : W0;
     const int r = lane % 16, g = lane / 16;
     const int row0 = blockIdx.x * 16;
@@ -79,10 +85,10 @@ __global__ __launch_bounds__(kFfnThreads) void k_ffn_gemv(
     //    units of thread t all belong to token t % M (M divides 256).
     const int U = M * (K / 16);
     const int mt = tid % M;
-    uint4 xa[kFfnCache], xb[kFfnCache];
+    uint4 xa[CACHE], xb[CACHE];
 #pragma unroll
-    for (int i = 0; i < kFfnCache; ++i) {
-        const int u = tid + kFfnThreads * i;
+    for (int i = 0; i < CACHE; ++i) {
+        const int u = tid + NT * i;
         if (u < U) {
             const uint4* src = reinterpret_cast<const uint4*>(xin + (size_t)mt * K + 16 * (u / M));
             xa[i] = src[0];
@@ -100,8 +106,8 @@ __global__ __launch_bounds__(kFfnThreads) void k_ffn_gemv(
     // 3. Per-token absmax (exact, order-free) of the cached units.
     float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kFfnCache; ++i) {
-        if (tid + kFfnThreads * i < U) {
+    for (int i = 0; i < CACHE; ++i) {
+        if (tid + NT * i < U) {
             const uint32_t w8[8] = {xa[i].x, xa[i].y, xa[i].z, xa[i].w,
                                     xb[i].x, xb[i].y, xb[i].z, xb[i].w};
 #pragma unroll
@@ -117,15 +123,17 @@ __global__ __launch_bounds__(kFfnThreads) void k_ffn_gemv(
         if (o >= M) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
     if (lane < M) s_amax[wave][lane] = amax;
     lds_barrier();
-    float a = fmaxf(fmaxf(s_amax[0][mt], s_amax[1][mt]), fmaxf(s_amax[2][mt], s_amax[3][mt]));
+    float a = s_amax[0][mt];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) a = fmaxf(a, s_amax[w][mt]);
     a = a > 1e-5f ? a : 1e-5f;
     const float inv = 127.0f / a;
     if (tid < M) s_scale[tid] = a / 127.0f;
 
     // 4. Codes into LDS slot u (chunk u / M of token u % M).
 #pragma unroll
-    for (int i = 0; i < kFfnCache; ++i) {
-        const int u = tid + kFfnThreads * i;
+    for (int i = 0; i < CACHE; ++i) {
+        const int u = tid + NT * i;
         if (u < U) {
             const uint32_t w8[8] = {xa[i].x, xa[i].y, xa[i].z, xa[i].w,
                                     xb[i].x, xb[i].y, xb[i].z, xb[i].w};
@@ -191,9 +199,15 @@ __global__ __launch_bounds__(kFfnThreads) void k_ffn_gemv(
     if (wave != 0 || !tok_ok) return;
     const float xs = s_scale[tok];
     const int nbase = row0 + 4 * (lane / 16);
-    if (GLU) {
-        const v4i ga = -(red[0][lane] + red[1][lane]);
-        const v4i ua = -(red[2][lane] + red[3][lane]);
+    if constexpr (GLU) {
+        v4i ga = red[0][lane], ua = red[KS][lane];
+#pragma unroll
+        for (int w = 1; w < KS; ++w) {
+            ga += red[w][lane];
+            ua += red[KS + w][lane];
+        }
+        ga = -ga;
+        ua = -ua;
         const float sg = xs * (*g0), su = xs * (*g1);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -205,7 +219,10 @@ __global__ __launch_bounds__(kFfnThreads) void k_ffn_gemv(
             }
         }
     } else {
-        const v4i ta = -((red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]));
+        v4i ta = red[0][lane];
+#pragma unroll
+        for (int w = 1; w < KS; ++w) ta += red[w][lane];
+        ta = -ta;
         const float sc = xs * (*g0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -215,28 +232,39 @@ __global__ __launch_bounds__(kFfnThreads) void k_ffn_gemv(
     }
 }
 
+// Launch shapes (measured on the 2B4T FFN): A (gate + up) with 2 waves per
+// matrix splitting K; B (down, few output rows, long K) with 8 waves so that
+// every wave's chunks are in flight at once, or 4 for hidden sizes under
+// 2048.
+constexpr int kKsA = 2, kKsB = 8, kKsBSmall = 4;
+
 bool ffn_fused_supported(int64_t M, int64_t K, int64_t N_ff) {
     if (M < 1 || M > 4 || (256 % M) != 0) return false;
-    // Activation units must fit the register cache; rows must cover the
-    // K split with full 256-weight chunks.
-    if (M * (K / 16) > kFfnThreads * kFfnCache || M * (N_ff / 16) > kFfnThreads * kFfnCache)
+    // Activation units must fit the register cache; every K-split wave needs
+    // at least one full 256-weight chunk.
+    if (M * (K / 16) > kFfnMinThreads * kFfnCache || M * (N_ff / 16) > kFfnMinThreads * kFfnCache)
         return false;
-    return K / 256 >= 2 && N_ff / 256 >= 4;
+    return K / 256 >= kKsA && N_ff / 256 >= kKsBSmall;
 }
 
 hipError_t launch_ffn_fused(const uint16_t* x, int M, int K, const uint32_t* Wg,
                             const float* gg, const uint32_t* Wu, const float* gu, int N_ff,
                             const uint32_t* Wd, const float* gd, uint16_t* h, float* y,
                             hipStream_t stream) {
-    const int blocks_a = (N_ff + 15) / 16;
-    hipLaunchKernelGGL(k_ffn_gemv<true>, dim3(blocks_a), dim3(kFfnThreads), (size_t)M * K,
-                       stream, x, M, K, Wg, gg, Wu, gu, N_ff, (float*)nullptr, h);
+    hipLaunchKernelGGL((k_ffn_gemv<true, kKsA>), dim3((N_ff + 15) / 16), dim3(64 * 2 * kKsA),
+                       (size_t)M * K, stream, x, M, K, Wg, gg, Wu, gu, N_ff, (float*)nullptr, h);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int blocks_b = (K + 15) / 16;
-    hipLaunchKernelGGL(k_ffn_gemv<false>, dim3(blocks_b), dim3(kFfnThreads), (size_t)M * N_ff,
-                       stream, h, M, N_ff, Wd, gd, (const uint32_t*)nullptr,
-                       (const float*)nullptr, K, y, (uint16_t*)nullptr);
+    if (N_ff / 256 >= kKsB) {
+        hipLaunchKernelGGL((k_ffn_gemv<false, kKsB>), dim3((K + 15) / 16), dim3(64 * kKsB),
+                           (size_t)M * N_ff, stream, h, M, N_ff, Wd, gd, (const uint32_t*)nullptr,
+                           (const float*)nullptr, K, y, (uint16_t*)nullptr);
+    } else {
+        hipLaunchKernelGGL((k_ffn_gemv<false, kKsBSmall>), dim3((K + 15) / 16),
+                           dim3(64 * kKsBSmall), (size_t)M * N_ff, stream, h, M, N_ff, Wd, gd,
+                           (const uint32_t*)nullptr, (const float*)nullptr, K, y,
+                           (uint16_t*)nullptr);
+    }
     return hipGetLastError();
 }
 

@@ -24,8 +24,9 @@
 // group in the output stream, the five weight bytes already shifted into
 // place, so one 8-byte table read and two ORs place five weights.
 //
-// Layout of the work. A wave owns 16 weight rows (the MFMA A operand: lane
-// l -> row l % 16, k-group l / 16) and every KS-th 64-byte chunk of each row.
+// Layout of the work. A workgroup of KS waves owns 16 weight rows (the MFMA
+// A operand: lane l -> row l % 16, k-group l / 16); wave ks takes every
+// KS-th 64-byte chunk of each row.
 // Each lane loads 16 bytes of its row per chunk; the 4 lanes of a row cover
 // 64 contiguous bytes. The whole [M][K] int8 activation block is staged once
 // per workgroup in LDS by direct global-to-LDS loads issued before the weight
@@ -48,7 +49,6 @@
 
 namespace bl {
 
-constexpr int kGemvThreads = 256;
 constexpr int kGemvMaxM = 16;
 constexpr int64_t kGemvMaxXBytes = 128 * 1024;
 constexpr int kBase3TableBytes = 4 * 256 * 8;
@@ -136,8 +136,8 @@ struct Decoder<Base3> {
 // Table entry (a, b): the five negated weights of base-3 byte b (weight =
 // digit - 1, least significant digit first) as bytes a .. a+4 of 8. Bytes
 // above 242 (never written by the packer) decode to zeros.
-__device__ __forceinline__ void build_base3_table(uint2* tab, int tid) {
-    for (int e = tid; e < 1024; e += kGemvThreads) {
+__device__ __forceinline__ void build_base3_table(uint2* tab, int tid, int nthreads) {
+    for (int e = tid; e < 1024; e += nthreads) {
         const int a = e / 256;
         int b = e % 256;
         uint64_t v = 0;
@@ -167,15 +167,16 @@ struct GemvArgs {
     GemvMat mat[2];
 };
 
-// R: ring of chunk loads in flight per lane; WPE: waves per SIMD the register
-// allocation must allow (short rows want many waves, long rows a deep ring).
-template <class F, int RG, int R, int WPE>
-__global__ __launch_bounds__(kGemvThreads, WPE) void k_gemv(const int8_t* __restrict__ xq,
-                                                       const float* __restrict__ xs, int M,
-                                                       int K, GemvArgs args) {
-    constexpr int KS = 4 / RG;  // waves splitting K within a row group
+// KS: waves splitting K; R: ring of chunk loads in flight per lane; WPE:
+// waves per SIMD the register allocation must allow (short rows want many
+// waves, long rows a deep ring).
+template <class F, int KS, int R, int WPE>
+__global__ __launch_bounds__(64 * KS, WPE) void k_gemv(const int8_t* __restrict__ xq,
+                                                     const float* __restrict__ xs, int M, int K,
+                                                     GemvArgs args) {
+    constexpr int NT = 64 * KS;
     extern __shared__ __align__(16) uint8_t smem[];
-    __shared__ v4i red[4][kWave];
+    __shared__ v4i red[KS][kWave];
 
     const bool second = (int)blockIdx.x >= args.mat[0].blocks;
     const GemvMat P = second ? args.mat[1] : args.mat[0];
@@ -185,9 +186,9 @@ __global__ __launch_bounds__(kGemvThreads, WPE) void k_gemv(const int8_t* __rest
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int lane = tid % kWave;
-    const int rg = wave % RG, ks = wave / RG;
+    const int ks = wave;
     const int r = lane % 16, g = lane / 16;
-    const int row0 = lb * (16 * RG) + rg * 16;
+    const int row0 = lb * 16;
     const int row = min(row0 + r, N - 1);
     const int RB = F::row_bytes(K);   // bytes per packed row, a multiple of 16
     const int nfull = RB / 64;        // full 64-byte chunks per row
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(kGemvThreads, WPE) void k_gemv(const int8_t* __rest
     //    read 16 consecutive slots. Each DMA instruction fills 64 slots.
     const int total = M * (K / 16);
     const uint32_t xbase = lds_offset(smem);
-    for (int p0 = wave * kWave; p0 < total; p0 += kGemvThreads) {
+    for (int p0 = wave * kWave; p0 < total; p0 += NT) {
         const int p = p0 + lane;
         if (p < total) {
             const int j = p / M, t = p - j * M;
@@ -219,10 +220,10 @@ __global__ __launch_bounds__(kGemvThreads, WPE) void k_gemv(const int8_t* __rest
     // Slots of the padded K extent hold zeros; the base-3 table follows the
     // activations.
     const int xslots = M * (F::k_extent(K) / 16);
-    for (int p = total + tid; p < xslots; p += kGemvThreads)
+    for (int p = total + tid; p < xslots; p += NT)
         *reinterpret_cast<uint4*>(smem + 16 * p) = make_uint4(0, 0, 0, 0);
     uint2* tab = reinterpret_cast<uint2*>(smem + 16 * xslots);
-    if constexpr (F::kTable) build_base3_table(tab, tid);
+    if constexpr (F::kTable) build_base3_table(tab, tid, NT);
 
     // 3. Wait for this wave's activation DMA only (the weight loads, issued
     //    after it, may stay in flight) and its LDS stores, then make every
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(kGemvThreads, WPE) void k_gemv(const int8_t* __rest
         __syncthreads();
         if (ks != 0) return;
 #pragma unroll
-        for (int t = 1; t < KS; ++t) acc += red[rg + t * RG][lane];
+        for (int t = 1; t < KS; ++t) acc += red[t][lane];
     }
 
     // The weights were expanded negated: flip the exact sums back.
@@ -317,31 +318,39 @@ bool gemv_supported(int64_t M, int64_t K) { return gemv_fits<Ternary2>(M, K); }
 bool gemv_binary_supported(int64_t M, int64_t K) { return gemv_fits<Binary1>(M, K); }
 bool gemv_base3_supported(int64_t M, int64_t K) { return gemv_fits<Base3>(M, K); }
 
-template <class F, int RG, int R, int WPE>
+template <class F, int KS, int R, int WPE>
 static hipError_t launch_gemv_cfg(const int8_t* xq, const float* xs, int M, int K,
                                  const GemvArgs& args, hipStream_t stream) {
     const size_t lds = (size_t)M * F::k_extent(K) + (F::kTable ? kBase3TableBytes : 0);
     static bool attr_set = false;
     if (lds > 64 * 1024 && !attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv<F, RG, R, WPE>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv<F, KS, R, WPE>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)(kGemvMaxXBytes + kBase3TableBytes));
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     const int blocks = args.mat[0].blocks + args.mat[1].blocks;
-    hipLaunchKernelGGL((k_gemv<F, RG, R, WPE>), dim3(blocks), dim3(kGemvThreads), lds, stream, xq,
-                       xs, M, K, args);
+    hipLaunchKernelGGL((k_gemv<F, KS, R, WPE>), dim3(blocks), dim3(64 * KS), lds, stream, xq, xs,
+                       M, K, args);
     return hipGetLastError();
 }
 
-// Rows of more than 8 chunks per wave take the deep ring.
+// Four waves per row group, or eight when the grid has fewer than 512 row
+// groups (few output rows, as in a down projection) and rows of at least 16
+// chunks, so that the CUs hold enough waves; rows of more than 8 chunks per
+// wave take the deep ring.
 template <class F>
 static hipError_t launch_gemv_auto(const int8_t* xq, const float* xs, int M, int K,
                                    const GemvArgs& args, hipStream_t stream) {
-    const int chunks_per_wave = (F::row_bytes(K) / 64 + 3) / 4;
-    if (chunks_per_wave > 8) return launch_gemv_cfg<F, 1, 8, 1>(xq, xs, M, K, args, stream);
-    return launch_gemv_cfg<F, 1, 4, F::kWaves>(xq, xs, M, K, args, stream);
+    const int chunks = F::row_bytes(K) / 64;
+    const int groups = args.mat[0].blocks + args.mat[1].blocks;
+    if (groups < 512 && chunks >= 16) {
+        if ((chunks + 7) / 8 > 8) return launch_gemv_cfg<F, 8, 8, 2>(xq, xs, M, K, args, stream);
+        return launch_gemv_cfg<F, 8, 4, 4>(xq, xs, M, K, args, stream);
+    }
+    if ((chunks + 3) / 4 > 8) return launch_gemv_cfg<F, 4, 8, 1>(xq, xs, M, K, args, stream);
+    return launch_gemv_cfg<F, 4, 4, F::kWaves>(xq, xs, M, K, args, stream);
 }
 
 static GemvMat make_mat(const void* Wp, const float* gamma, int N, float* y, int32_t* acc,
