@@ -65,6 +65,8 @@ def _load():
         "oracle_unpack_binary": ([P, I, I, I, P], None),
         "oracle_pack_base3": ([P, I, I, I, P], None),
         "oracle_unpack_base3": ([P, I, I, I, P], None),
+        "oracle_pack_ste_t": ([P, I, I, I, P], None),
+        "oracle_ste_dx": ([P, I, I, P, I, F, P], None),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -255,3 +257,31 @@ def unpack_base3(packed: np.ndarray, K: int) -> np.ndarray:
     q = np.empty((N, K), np.int8)
     _load().oracle_unpack_base3(_p(packed), N, K, packed.shape[1], _p(q))
     return q
+
+
+# ------------------------------------------- straight-through backward ----
+
+def ste_t_row_bytes(N: int) -> int:
+    """Bytes per row of the transposed backward codes: ceil(N/4) rounded to 16."""
+    return 16 * (((N + 3) // 4 + 15) // 16)
+
+
+def pack_ste_t(q: np.ndarray) -> np.ndarray:
+    """Codes q [N][K] -> transposed uint8 [K][ste_t_row_bytes(N)], four n per byte."""
+    q = _c(q, np.int8)
+    N, K = q.shape
+    rb = ste_t_row_bytes(N)
+    out = np.empty((K, rb), np.uint8)
+    _load().oracle_pack_ste_t(_p(q), N, K, rb, _p(out))
+    return out
+
+
+def ste_dx(dy_bits: np.ndarray, q: np.ndarray, gamma) -> np.ndarray:
+    """dx fp32 [M][K] = gamma * dy . q for bf16 dy [M][N] (raw bits)."""
+    dy_bits = _c(dy_bits, np.uint16)
+    q = _c(q, np.int8)
+    M, N = dy_bits.shape
+    K = q.shape[1]
+    dx = np.empty((M, K), np.float32)
+    _load().oracle_ste_dx(_p(dy_bits), M, N, _p(q), K, float(np.float32(gamma)), _p(dx))
+    return dx

@@ -157,6 +157,43 @@ void oracle_unpack_base3(const uint8_t* packed, int64_t N, int64_t K, int64_t ro
         }
 }
 
+/* Backward-layout packing of the ternary codes for the straight-through
+ * estimator [P5b]: row k of qT holds q[n][k] for n = 0..N-1, four codes per
+ * byte, code c = q + 1 of n = 4j + i at bits 2i of byte j; positions n >= N
+ * are code 1 (weight 0). Rows are row_bytes bytes (padding bytes 0x55). */
+void oracle_pack_ste_t(const int8_t* q, int64_t N, int64_t K, int64_t row_bytes,
+                       uint8_t* qT) {
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t j = 0; j < row_bytes; ++j) {
+            unsigned v = 0;
+            for (int i = 0; i < 4; ++i) {
+                int64_t n = 4 * j + i;
+                unsigned c = n < N ? (unsigned)(q[n * K + k] + 1) : 1u;
+                v |= c << (2 * i);
+            }
+            qT[k * row_bytes + j] = (uint8_t)v;
+        }
+}
+
+/* Straight-through estimator, gradient with respect to the layer input
+ * [P5b]: the forward's rounding is treated as the identity, so
+ * dx[m][k] = gamma * sum_n dy[m][n] * q[n][k] (the transpose of the ternary
+ * product, rescaled by the weight scale). dy is bf16 [M][N]; the sum is taken
+ * in fp64 with n increasing, multiplied by gamma in fp64 and rounded once to
+ * fp32. */
+void oracle_ste_dx(const uint16_t* dy, int64_t M, int64_t N, const int8_t* q, int64_t K,
+                   float gamma, float* dx) {
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k) {
+            double s = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                int8_t w = q[n * K + k];
+                if (w) s += (double)w * (double)bf16_bits_to_float(dy[m * N + n]);
+            }
+            dx[m * K + k] = (float)(s * (double)gamma);
+        }
+}
+
 /* 8-bit activations [P1], per token by absmax into [-127, 127]. */
 void oracle_act_quant(const uint16_t* x, int64_t M, int64_t K,
                       const uint16_t* gain, float rms_eps,

@@ -24,6 +24,10 @@
  *   [P3d] same page, section "Dlaczego akurat ternarne, a nie czyste
  *        zero-jeden" (the paragraph after the 1.58-bit count): the original
  *        BitNet used binary weights, only -1 and +1.
+ *   [P5b] juhe.plus (Habr repost), the section on training that follows
+ *        BinaryConnect: sign() has no useful derivative, so the forward
+ *        uses the rounding and the backward passes the gradient straight
+ *        through as if there were none (straight-through estimator).
  *   [P5] juhe.plus (Habr repost), section «Когда - три лучше двух»: with
  *        ternary weights y = W·x reduces to sums of the inputs where the
  *        weight is +1 minus sums where it is -1.
@@ -49,6 +53,9 @@
  *     16 bytes with 0 bits.
  *   - 1.6-bit storage: five weights per byte as a base-3 number, least
  *     significant digit first (c = q + 1), rows padded to 16 bytes with 121.
+ *   - straight-through backward: dx = gamma * dy . q with dy in bf16, the
+ *     sum exact in fp64, rounded once to fp32; the transposed codes are
+ *     stored four per byte along n, rows padded to 16 bytes with 0x55.
  */
 #ifndef BITLINEAR_ORACLE_H
 #define BITLINEAR_ORACLE_H
@@ -110,6 +117,13 @@ void oracle_pack_base3(const int8_t* q, int64_t N, int64_t K, int64_t row_bytes,
                        uint8_t* packed);
 void oracle_unpack_base3(const uint8_t* packed, int64_t N, int64_t K, int64_t row_bytes,
                          int8_t* q);
+
+/* Transposed 2-bit codes for the backward pass, four n per byte.  [P5b] */
+void oracle_pack_ste_t(const int8_t* q, int64_t N, int64_t K, int64_t row_bytes,
+                       uint8_t* qT);
+/* dx = gamma * dy . q, dy bf16 [M][N], q [N][K], fp64 sum, one rounding. [P5b] */
+void oracle_ste_dx(const uint16_t* dy, int64_t M, int64_t N, const int8_t* q, int64_t K,
+                   float gamma, float* dx);
 
 #ifdef __cplusplus
 }

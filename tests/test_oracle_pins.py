@@ -590,3 +590,84 @@ def test_base3_rows_padding_and_density():
         assert pk.shape == (3, rb) and int(pk.max()) <= 242
         assert np.array_equal(oracle.unpack_base3(pk, K), q)
         assert (pk[:, (K + 4) // 5:] == 121).all()
+
+
+# ------------------------------------------- straight-through backward ----
+# juhe.plus (Habr repost), the section on training after BinaryConnect: the
+# forward rounds, the backward passes the gradient straight through. For the
+# input that is dx = gamma * dy . q (the forward's rounding treated as the
+# identity; the weight scale stays).
+
+def _bf16_bits(a):
+    return wl.f32_to_bf16_bits(np.asarray(a, np.float32))
+
+
+def test_pack_ste_t_bytes_and_layout():
+    q = np.zeros((5, 3), np.int8)
+    q[:4, 0] = [-1, 0, 1, -1]
+    q[:, 1] = 1
+    q[:, 2] = 0
+    t = oracle.pack_ste_t(q)
+    assert t.shape == (3, 16)
+    assert t[0, 0] == 0x24                  # codes 0,1,2,0 at bits 0,2,4,6
+    assert t[1, 0] == 0xAA and t[1, 1] == 0x56   # n = 4 is +1, n = 5..7 pad (code 1)
+    assert (t[2] == 0x55).all()
+    assert (t[:, 2:] == 0x55).all()
+    rng = np.random.default_rng(81)
+    q = rng.integers(-1, 2, size=(37, 11), dtype=np.int8)
+    t = oracle.pack_ste_t(q).astype(int)
+    for n in range(37):
+        for k in range(11):
+            assert ((t[k, n // 4] >> (2 * (n % 4))) & 3) == q[n, k] + 1
+
+
+def test_ste_dx_identity_and_ones():
+    rng = np.random.default_rng(82)
+    dy = _bf16_bits(rng.standard_normal((3, 40)))
+    g = np.float32(0.0173)
+    dyf = wl.bf16_bits_to_f32(dy).astype(np.float64)
+    eye = np.eye(40, dtype=np.int8)
+    assert np.array_equal(oracle.ste_dx(dy, eye, g), (dyf * np.float64(g)).astype(np.float32))
+    ones = np.ones((40, 5), np.int8)
+    ref = np.array([[math.fsum(row) * float(g)] * 5 for row in dyf], np.float64).astype(np.float32)
+    assert np.array_equal(oracle.ste_dx(dy, ones, g), ref)
+    assert np.array_equal(oracle.ste_dx(dy, -ones, g), -ref)
+    assert (oracle.ste_dx(dy, np.zeros((40, 5), np.int8), g) == 0).all()
+
+
+def test_ste_dx_brute_force_fractions():
+    from fractions import Fraction
+    rng = np.random.default_rng(83)
+    dy = _bf16_bits(rng.standard_normal((2, 9)) * 3)
+    q = rng.integers(-1, 2, size=(9, 4), dtype=np.int8)
+    g = np.float32(0.5)          # exact scale: the result is the exact sum, rounded once
+    dx = oracle.ste_dx(dy, q, g)
+    dyf = wl.bf16_bits_to_f32(dy)
+    for m in range(2):
+        for k in range(4):
+            s = sum(Fraction(float(dyf[m, n])) * int(q[n, k]) for n in range(9)) * Fraction(0.5)
+            assert dx[m, k] == np.float32(float(s))
+
+
+def test_ste_dx_is_the_adjoint_of_the_forward():
+    # <dx, x> = gamma * <dy, x . q^T> for any x: pins the transposition.
+    rng = np.random.default_rng(84)
+    M, N, K = 3, 70, 50
+    dy = _bf16_bits(rng.standard_normal((M, N)))
+    q = rng.integers(-1, 2, size=(N, K), dtype=np.int8)
+    x = rng.integers(-127, 128, size=(M, K), dtype=np.int8)
+    g = np.float32(0.02)
+    dx = oracle.ste_dx(dy, q, g).astype(np.float64)
+    lhs = float((dx * x).sum())
+    yq = oracle.int_matmul(x, q).astype(np.float64)          # x . q^T, [M][N]
+    rhs = float(g) * float((wl.bf16_bits_to_f32(dy).astype(np.float64) * yq).sum())
+    # each dx element carries one fp32 rounding
+    assert abs(lhs - rhs) <= 2.0 ** -23 * float(np.abs(dx * x).sum())
+    assert abs(lhs - rhs) <= 1e-3 * abs(rhs)
+
+
+def test_ste_dx_sum_is_exact_before_rounding():
+    # 2^30 + 1 - 2^30: an fp32 running sum loses the 1, the definition keeps it.
+    dy = _bf16_bits(np.array([[2.0 ** 30, 1.0, -(2.0 ** 30)]], np.float32))
+    q = np.ones((3, 1), np.int8)
+    assert oracle.ste_dx(dy, q, np.float32(0.25))[0, 0] == np.float32(0.25)
