@@ -43,6 +43,7 @@ if ROOT not in sys.path:
 METRIC = "BitLinear decode packed-weight GB/s (% HBM peak); prefill int8 TOPS (% MFMA)"
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
 I8_PEAK_TOPS = 5000.0       # MI355X dense int8 MFMA, published
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 DECODE_WORKLOAD = 2         # 2B4T-shaped FFN at decode
 PREFILL_WORKLOAD = 3        # one 4096-token sequence
 LARGE_WORKLOAD = 5          # 70B-class shapes
@@ -360,6 +361,52 @@ def main():
         prefill.update(gemm_leg("gemm_prefill_4096", PREFILL_WORKLOAD, pMs[0], pprojs,
                                 max(5, args.steps)))
 
+    # ------------------------------- straight-through backward (dx) ----
+    ste = None
+    if not args.no_prefill:
+        _, pprojs, pMs = wl.WORKLOADS[PREFILL_WORKLOAD]
+        Mp = pMs[0]
+        legs = []
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(2024)
+        for i, (name, K, N) in enumerate(pprojs):
+            pk, g = prepare(PREFILL_WORKLOAD, i, N, K)[0]
+            qT = bl.pack_ste_t(pk, K)
+            dy = (torch.randn((Mp, N), generator=gen, device=dev) * 0.01).to(torch.bfloat16)
+            dx = torch.empty((Mp, K), dtype=torch.float32, device=dev)
+            legs.append((name, K, N, qT, g, dy, dx))
+            del pk
+        for _ in range(1 + args.warmup):
+            for name, K, N, qT, g, dy, dx in legs:
+                bl.ste_backward_dx(dy, qT, g, N, out=dx)
+        torch.cuda.synchronize()
+        tp = Timer(torch)
+        reps = max(5, args.steps)
+        for _ in range(reps):
+            for name, K, N, qT, g, dy, dx in legs:
+                tp.run(name, lambda: bl.ste_backward_dx(dy, qT, g, N, out=dx))
+        torch.cuda.synchronize()
+        per = {}
+        tot_ms = 0.0
+        flops = 0
+        for name, K, N, *_ in legs:
+            ms = tp.total_ms(name)
+            tot_ms += ms
+            flops += 2 * Mp * N * K * reps
+            per[name] = {"M": Mp, "N_reduced": N, "K_out": K,
+                         "avg_us": round(1e3 * ms / reps, 2),
+                         "TFLOPs": round(2 * Mp * N * K * reps / (ms * 1e-3) / 1e12, 1)}
+        tf = flops / (tot_ms * 1e-3) / 1e12
+        ste = {"workload": "dx of the 4096-token projections (dy bf16 [4096][N] -> dx fp32 "
+                           "[4096][K]), straight-through estimator",
+               "roofline": {"bound": "mfma", "kernel": "k_ste_dx (v_mfma_f32_32x32x16_bf16)",
+                            "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                            "traffic": None, "per_projection": per}}
+        del legs
+        torch.cuda.empty_cache()
+        print(f"ste dx: {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+
     # ------------------------------------------- 70B-class shapes ----
     large = None
     ceilings = None
@@ -570,6 +617,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu_baseline,
         "prefill": prefill,
+        "ste_backward": ste,
         "large_70b": large,
         "ceilings": ceilings,
         "weight_prep": {"matrices": list(base), "ms_total": round(wp_ms, 3),

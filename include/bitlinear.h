@@ -262,6 +262,39 @@ int bl_bitlinear_base3(const int8_t* x_q, const float* x_scale, int64_t M, int64
                        const uint8_t* W3, const float* gamma, int64_t N, float* y,
                        int32_t* acc, void* stream);
 
+/* ---- Straight-through backward (training) -------------------------------
+ * The gradient of the loss with respect to the BitLinear input when the
+ * forward's rounding is treated as the identity (straight-through
+ * estimator). Source: juhe.plus (Habr repost), the section on training that
+ * follows BinaryConnect (the forward rounds, the backward passes the gradient
+ * through as if there were no rounding); comrad404.com «Метод…» (gradients
+ * stay in high precision). The weight gradient dW = dy^T . x~ is a dense
+ * product and is not part of this library. */
+
+/* Bytes of the transposed codes bl_pack_ste_t writes:
+ * K * 16*ceil(ceil(N/4)/16); 0 if the shape is invalid. Host-only. */
+size_t bl_ste_t_bytes(int64_t N, int64_t K);
+
+/* Transposes the 2-bit weights for the backward pass (offline, once per
+ * matrix): row k of qT holds q[n][k] for all n, code c = q + 1 of n = 4j + i
+ * at bits 2i of byte j; n >= N is code 1 (weight 0).
+ *   W_packed  in   2-bit weights [N][K/16] from bl_quantize_weights.
+ *   qT        out  uint8 [K][16*ceil(ceil(N/4)/16)], 16-byte aligned. */
+int bl_pack_ste_t(const uint32_t* W_packed, int64_t N, int64_t K, uint8_t* qT, void* stream);
+
+/* dx[m][k] = gamma * sum_n dy[m][n] * q[n][k].
+ *   dy     in   bf16 [M][N] (raw bits), gradient of the BitLinear output;
+ *               N % 8 == 0, 16-byte aligned.
+ *   qT     in   transposed codes from bl_pack_ste_t; gamma from
+ *               bl_quantize_weights (device).
+ *   dx     out  fp32 [M][K]; must not alias an input.
+ * Products of bf16 by {-1, 0, +1} are exact; they are summed in fp32 (within
+ * N * 2^-24 * gamma * sum_n |dy[m][n] q[n][k]| of the exact value) and then
+ * multiplied by gamma in fp32. Shapes: M >= 1, N >= 8, K >= 64, K % 64 == 0,
+ * M*N, M*K, N*K < 2^31. */
+int bl_ste_backward_dx(const uint16_t* dy, int64_t M, int64_t N, const uint8_t* qT,
+                       const float* gamma, int64_t K, float* dx, void* stream);
+
 /* ---- Calibration kernels ------------------------------------------------
  * Measured ceilings for the roofline of the kernels above; they compute
  * nothing of the method. Same conventions as above. */

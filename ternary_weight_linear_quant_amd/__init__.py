@@ -48,6 +48,9 @@ _SIGNATURES = {
     "bl_pack_base3": ([_P, _I, _I, _P, _P], ctypes.c_int),
     "bl_bitlinear_binary": ([_P, _P, _I, _I, _P, _P, _I, _P, _P, _P], ctypes.c_int),
     "bl_bitlinear_base3": ([_P, _P, _I, _I, _P, _P, _I, _P, _P, _P], ctypes.c_int),
+    "bl_ste_t_bytes": ([_I, _I], _S),
+    "bl_pack_ste_t": ([_P, _I, _I, _P, _P], ctypes.c_int),
+    "bl_ste_backward_dx": ([_P, _I, _I, _P, _P, _I, _P, _P], ctypes.c_int),
     "bl_calib_read": ([_P, _S, _P, _P], ctypes.c_int),
     "bl_calib_copy": ([_P, _P, _S, _P], ctypes.c_int),
     "bl_calib_mfma_i8_ops": ([_I], _I),
@@ -338,6 +341,41 @@ def bitlinear_base3(x_q, x_scale, W3, gamma, return_acc: bool = False, out=None)
     torch = _torch()
     return _other_product(lib().bl_bitlinear_base3, "bl_bitlinear_base3", x_q, x_scale, W3,
                           torch.uint8, gamma, W3.shape[0], return_acc, out)
+
+
+# ------------------------------------------- straight-through backward ----
+
+def pack_ste_t(W_packed, K: int):
+    """2-bit packed [N][K/16] -> transposed codes uint8 [K][row bytes], four n
+    per byte, for the backward pass. Calls bl_pack_ste_t."""
+    torch = _torch()
+    N = W_packed.shape[0]
+    L = lib()
+    nbytes = L.bl_ste_t_bytes(N, K)
+    if nbytes == 0 or W_packed.shape[1] * 16 != K:
+        raise BitLinearError("invalid weight shape")
+    qT = torch.empty((K, nbytes // K), dtype=torch.uint8, device=W_packed.device)
+    _check(L.bl_pack_ste_t(_dev(W_packed, torch.int32, "W_packed"), N, K,
+                           _dev(qT, torch.uint8, "qT"), _stream_ptr(W_packed)), "bl_pack_ste_t")
+    return qT
+
+
+def ste_backward_dx(dy, qT, gamma, N: int, out=None):
+    """dx fp32 [M][K] = gamma * dy . q for bf16 dy [M][N]. Calls bl_ste_backward_dx."""
+    torch = _torch()
+    if dy.dtype == torch.int16:
+        dy = dy.view(torch.bfloat16)
+    M = dy.shape[0]
+    K = qT.shape[0]
+    if dy.shape[1] != N:
+        raise BitLinearError("dy shape does not match N")
+    dx = torch.empty((M, K), dtype=torch.float32, device=dy.device) if out is None else out
+    _check(lib().bl_ste_backward_dx(_dev(dy, torch.bfloat16, "dy"), M, N,
+                                    _dev(qT, torch.uint8, "qT"),
+                                    _dev(gamma, torch.float32, "gamma"), K,
+                                    _dev(dx, torch.float32, "dx"), _stream_ptr(dy)),
+           "bl_ste_backward_dx")
+    return dx
 
 
 # ---------------------------------------------------------- calibration ----

@@ -328,6 +328,36 @@ int bl_bitlinear_base3(const int8_t* x_q, const float* x_scale, int64_t M, int64
                                             acc, as_stream(stream)));
 }
 
+size_t bl_ste_t_bytes(int64_t N, int64_t K) {
+    if (!shape_ok(N, K)) return 0;
+    return (size_t)K * (size_t)bl::ste_t_row_bytes(N);
+}
+
+int bl_pack_ste_t(const uint32_t* W_packed, int64_t N, int64_t K, uint8_t* qT, void* stream) {
+    if (!W_packed || !qT) return BL_ERR_INVALID_ARG;
+    if (!shape_ok(N, K)) return BL_ERR_INVALID_ARG;
+    if (!aligned16(W_packed) || !aligned16(qT)) return BL_ERR_INVALID_ARG;
+    if (overlaps(qT, bl_ste_t_bytes(N, K), W_packed, (size_t)(N * K) / 4))
+        return BL_ERR_INVALID_ARG;
+    if (int s = device_status()) return s;
+    return hip_status(bl::launch_pack_ste_t(W_packed, N, K, qT, as_stream(stream)));
+}
+
+int bl_ste_backward_dx(const uint16_t* dy, int64_t M, int64_t N, const uint8_t* qT,
+                       const float* gamma, int64_t K, float* dx, void* stream) {
+    if (!dy || !qT || !gamma || !dx) return BL_ERR_INVALID_ARG;
+    if (M < 1 || N < 8 || (N % 8) != 0 || !shape_ok(N, K)) return BL_ERR_INVALID_ARG;
+    if (M > (int64_t{1} << 31) / N || M > (int64_t{1} << 31) / K) return BL_ERR_INVALID_ARG;
+    if (!aligned16(dy) || !aligned16(qT)) return BL_ERR_INVALID_ARG;
+    const size_t ndx = (size_t)(M * K) * 4;
+    if (overlaps(dx, ndx, dy, (size_t)(M * N) * 2) || overlaps(dx, ndx, qT, bl_ste_t_bytes(N, K)) ||
+        overlaps(dx, ndx, gamma, 4))
+        return BL_ERR_INVALID_ARG;
+    if (int s = device_status()) return s;
+    return hip_status(bl::launch_ste_dx(dy, (int)M, (int)N, qT, gamma, (int)K, dx,
+                                        as_stream(stream)));
+}
+
 int bl_calib_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
     if (!src || !sink || bytes < 16 || (bytes % 16) != 0 || !aligned16(src))
         return BL_ERR_INVALID_ARG;

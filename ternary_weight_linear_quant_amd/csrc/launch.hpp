@@ -60,6 +60,14 @@ hipError_t launch_gemv_base3(const int8_t* xq, const float* xs, int M, int K, co
                              const float* gamma, int N, float* y, int32_t* acc,
                              hipStream_t stream);
 
+// Straight-through backward with respect to the input: transposed codes and
+// dx = gamma * dy . q (bf16 matrix cores).
+int64_t ste_t_row_bytes(int64_t N);
+hipError_t launch_pack_ste_t(const uint32_t* packed2, int64_t N, int64_t K, uint8_t* qT,
+                             hipStream_t stream);
+hipError_t launch_ste_dx(const uint16_t* dy, int M, int N, const uint8_t* qT, const float* gamma,
+                         int K, float* dx, hipStream_t stream);
+
 // Calibration kernels (measured ceilings; not part of the method).
 constexpr int kCalibMfmaBlocks = 512;        // 256-thread blocks of the MFMA loop
 hipError_t launch_calib_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);

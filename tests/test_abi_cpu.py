@@ -141,6 +141,22 @@ def test_other_formats_host_side(L):
         assert f(None, S, 1, 64, W, G, 16, Y, None, None) == E
 
 
+def test_ste_backward_host_side(L):
+    E = bl.BL_ERR_INVALID_ARG
+    assert L.bl_ste_t_bytes(6912, 2560) == 2560 * 1728
+    assert L.bl_ste_t_bytes(37, 64) == 64 * 16
+    assert L.bl_ste_t_bytes(16, 100) == 0
+    assert L.bl_pack_ste_t(W, 16, 64, P(0x3000010), None) == E                 # overlapping
+    assert L.bl_pack_ste_t(W, 16, 48, P(0x6000000), None) == E
+    assert L.bl_ste_backward_dx(X, 4, 12, W, G, 64, Y, None) == E              # N % 8
+    assert L.bl_ste_backward_dx(X, 4, 0, W, G, 64, Y, None) == E
+    assert L.bl_ste_backward_dx(X, 0, 16, W, G, 64, Y, None) == E
+    assert L.bl_ste_backward_dx(X, 4, 16, W, G, 96, Y, None) == E              # K % 64
+    assert L.bl_ste_backward_dx(P(0x1000008), 4, 16, W, G, 64, Y, None) == E   # misaligned dy
+    assert L.bl_ste_backward_dx(X, 4, 16, W, G, 64, P(0x1000040), None) == E   # dx over dy
+    assert L.bl_ste_backward_dx(None, 4, 16, W, G, 64, Y, None) == E
+
+
 def test_calibration_arguments(L):
     E = bl.BL_ERR_INVALID_ARG
     assert L.bl_calib_read(A, 8, A, None) == E
@@ -172,6 +188,8 @@ def test_no_device_status(L):
     assert L.bl_bitlinear_binary(X, S, 1, 64, W, G, 16, Y, None, None) == D
     assert L.bl_bitlinear_base3(X, S, 1, 64, W, G, 16, Y, None, None) == D
     assert L.bl_pack_base3(W, 16, 64, P(0x6000000), None) == D
+    assert L.bl_ste_backward_dx(X, 4, 16, W, G, 64, Y, None) == D
+    assert L.bl_pack_ste_t(W, 16, 64, P(0x6000000), None) == D
     need = L.bl_ffn_relu2_workspace_bytes(1, 256, 1024)
     assert L.bl_ffn_relu2(A, 1, 256, A, A, A, A, 1024, A, A, A, P(0x200000), need, None) == D
 

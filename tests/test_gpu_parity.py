@@ -636,3 +636,62 @@ def test_other_formats_reject_prefill_sizes():
     xs = torch.ones(17, device=DEV)
     with pytest.raises(bl.BitLinearError):
         bl.bitlinear_base3(xq, xs, w3, dev_f32([1.0]))
+
+
+# ------------------------------------------- straight-through backward ----
+# dx = gamma * dy . q: transposed codes bit-exact; dx within the fp32
+# summation bound of the exact value (the products bf16 x {-1, 0, +1} are
+# exact; N fp32 additions each within 2^-24 of the running sum, then one
+# rounding of the product with gamma).
+
+def _dx_bound(dy_bits, q, g):
+    absdy = np.abs(wl.bf16_bits_to_f32(dy_bits).astype(np.float64))
+    mag = float(g) * (absdy @ np.abs(q.astype(np.float64)))
+    N = q.shape[0]
+    return (N * 2.0 ** -24 + 2.0 ** -23) * mag + 1e-30
+
+
+STE_CASES = [(1, 8, 64), (3, 40, 128), (130, 264, 192), (64, 2560, 640), (17, 6912, 256)]
+
+
+@pytest.mark.parametrize("M,N,K", STE_CASES)
+def test_ste_backward_dx_parity(M, N, K):
+    rng = np.random.default_rng(M + 7 * N + K)
+    q = rand_codes(rng, N, K)
+    q[:, 0] = 1
+    q[:, -1] = 0
+    g = np.float32(0.0173)
+    qT_ref = oracle.pack_ste_t(q)
+    qT = bl.pack_ste_t(dev_packed(oracle.pack(q)), K)
+    assert np.array_equal(qT.cpu().numpy(), qT_ref)
+    dy = wl.f32_to_bf16_bits((rng.standard_normal((M, N)) * 0.01).astype(np.float32))
+    dx = bl.ste_backward_dx(dev_bf16(dy), qT, dev_f32([g]), N).cpu().numpy()
+    ref = oracle.ste_dx(dy, q, g)
+    err = np.abs(dx.astype(np.float64) - ref.astype(np.float64))
+    assert (err <= _dx_bound(dy, q, g)).all(), float(err.max())
+
+
+def test_ste_pack_odd_n():
+    rng = np.random.default_rng(91)
+    q = rand_codes(rng, 37, 64)
+    qT = bl.pack_ste_t(dev_packed(oracle.pack(q)), 64)
+    assert np.array_equal(qT.cpu().numpy(), oracle.pack_ste_t(q))
+
+
+@pytest.mark.parametrize("idx", [0, 1])
+def test_ste_backward_full_size(idx):
+    """The 4096-token workload's projections: dx for a 4096 x N gradient,
+    oracle on sampled token rows (all K), transposed codes compared in full."""
+    q_ref, g_ref, pk, g = workload_weights(3, idx)
+    N, K = q_ref.shape
+    qT = bl.pack_ste_t(pk, K)
+    assert np.array_equal(qT.cpu().numpy(), oracle.pack_ste_t(q_ref))
+    rng = np.random.default_rng(95 + idx)
+    M = 4096
+    dy = wl.f32_to_bf16_bits((rng.standard_normal((M, N)) * 0.01).astype(np.float32))
+    dx = bl.ste_backward_dx(dev_bf16(dy), qT, g, N)
+    rows = np.unique(np.concatenate([[0, 127, 128, M - 1], rng.choice(M, 6, replace=False)]))
+    ref = oracle.ste_dx(dy[rows], q_ref, g_ref)
+    got = dx[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    err = np.abs(got.astype(np.float64) - ref.astype(np.float64))
+    assert (err <= _dx_bound(dy[rows], q_ref, g_ref)).all(), float(err.max())
