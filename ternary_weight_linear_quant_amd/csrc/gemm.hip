@@ -317,7 +317,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_gemm(
                     const int n = n0 + wn0 + 32 * j + (lane % 32);
                     if (n < N) {
                         const int32_t a = -acc[i][j][v];
-                        yrow[n] = (float)a * sc;
+                        // The output is not read again here: keep it out of
+                        // the L2 that holds the operand tiles.
+                        __builtin_nontemporal_store((float)a * sc, yrow + n);
                         if (arow) arow[n] = a;
                     }
                 }

@@ -695,3 +695,48 @@ def test_ste_backward_full_size(idx):
     got = dx[torch.from_numpy(rows).to(DEV)].cpu().numpy()
     err = np.abs(got.astype(np.float64) - ref.astype(np.float64))
     assert (err <= _dx_bound(dy[rows], q_ref, g_ref)).all(), float(err.max())
+
+
+# ------------------------------------------------------------ HIP graphs ----
+# The benchmark replays captured graphs. Every path it captures is replayed
+# several times, with eager work and synchronisations in between, and each
+# replay must give the eager result bit for bit (split K zeroes its output
+# with a kernel, not a memset node).
+
+def test_graph_replays_match_eager():
+    rng = np.random.default_rng(97)
+    cases = []
+    for (M, K, N) in [(1, 2560, 6912), (16, 6912, 2560), (64, 8192, 700), (300, 2560, 1000)]:
+        q = rand_codes(rng, N, K)
+        xq, xs = oracle.act_quant(wl.activations(97, 0, M, K))
+        cases.append((torch.from_numpy(xq).to(DEV), dev_f32(xs), dev_packed(oracle.pack(q)),
+                      dev_f32([0.0159]), torch.empty((M, N), dtype=torch.float32, device=DEV)))
+    W = {n: gpu_weights(wl.weights(2, i, N, K)) for i, (n, K, N) in enumerate(wl.WORKLOADS[2][1])}
+    ffn_io = []
+    for M in (1, 4, 16):
+        x = dev_bf16(wl.activations(2, 9, M, 2560))
+        ffn_io.append((x, bl.ffn_relu2_workspace(M, 2560, 6912, DEV),
+                       torch.empty((M, 2560), dtype=torch.float32, device=DEV)))
+
+    def run():
+        for xq, xs, pk, g, y in cases:
+            bl.bitlinear(xq, xs, pk, g, out=y)
+        for x, ws, y in ffn_io:
+            bl.ffn_relu2(x, *W["gate"], *W["up"], *W["down"], workspace=ws, out=y)
+
+    run()
+    torch.cuda.synchronize()
+    ref = [c[-1].clone() for c in cases] + [io[-1].clone() for io in ffn_io]
+    outs = [c[-1] for c in cases] + [io[-1] for io in ffn_io]
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        run()
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        gr.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, ref):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32)), f"replay {rep}"
+        run()                       # eager work between replays
+        torch.cuda.synchronize()
