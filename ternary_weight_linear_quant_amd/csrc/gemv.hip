@@ -24,9 +24,10 @@
 // group in the output stream, the five weight bytes already shifted into
 // place, so one 8-byte table read and two ORs place five weights.
 //
-// Layout of the work. A workgroup of KS waves owns 16 weight rows (the MFMA
-// A operand: lane l -> row l % 16, k-group l / 16); wave ks takes every
-// KS-th 64-byte chunk of each row.
+// Layout of the work. A workgroup of RG x KS waves owns RG groups of 16
+// weight rows (the MFMA A operand: lane l -> row l % 16, k-group l / 16);
+// wave (rg, ks) takes group rg and every KS-th 64-byte chunk of its rows.
+// Several row groups per workgroup share one staging of the activations.
 // Each lane loads 16 bytes of its row per chunk; the 4 lanes of a row cover
 // 64 contiguous bytes. The whole [M][K] int8 activation block is staged once
 // per workgroup in LDS by direct global-to-LDS loads issued before the weight
@@ -167,16 +168,16 @@ struct GemvArgs {
     GemvMat mat[2];
 };
 
-// KS: waves splitting K; R: ring of chunk loads in flight per lane; WPE:
-// waves per SIMD the register allocation must allow (short rows want many
-// waves, long rows a deep ring).
-template <class F, int KS, int R, int WPE>
-__global__ __launch_bounds__(64 * KS, WPE) void k_gemv(const int8_t* __restrict__ xq,
-                                                     const float* __restrict__ xs, int M, int K,
-                                                     GemvArgs args) {
-    constexpr int NT = 64 * KS;
+// RG: row groups per workgroup; KS: waves splitting K; R: ring of chunk
+// loads in flight per lane; WPE: waves per SIMD the register allocation must
+// allow (short rows want many waves, long rows a deep ring).
+template <class F, int RG, int KS, int R, int WPE>
+__global__ __launch_bounds__(64 * RG * KS, WPE) void k_gemv(const int8_t* __restrict__ xq,
+                                                          const float* __restrict__ xs, int M,
+                                                          int K, GemvArgs args) {
+    constexpr int NT = 64 * RG * KS;
     extern __shared__ __align__(16) uint8_t smem[];
-    __shared__ v4i red[KS][kWave];
+    __shared__ v4i red[RG * KS][kWave];
 
     const bool second = (int)blockIdx.x >= args.mat[0].blocks;
     const GemvMat P = second ? args.mat[1] : args.mat[0];
@@ -186,9 +187,9 @@ __global__ __launch_bounds__(64 * KS, WPE) void k_gemv(const int8_t* __restrict_
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int lane = tid % kWave;
-    const int ks = wave;
+    const int rg = wave % RG, ks = wave / RG;
     const int r = lane % 16, g = lane / 16;
-    const int row0 = lb * 16;
+    const int row0 = (lb * RG + rg) * 16;
     const int row = min(row0 + r, N - 1);
     const int RB = F::row_bytes(K);   // bytes per packed row, a multiple of 16
     const int nfull = RB / 64;        // full 64-byte chunks per row
@@ -288,7 +289,7 @@ __global__ __launch_bounds__(64 * KS, WPE) void k_gemv(const int8_t* __restrict_
         __syncthreads();
         if (ks != 0) return;
 #pragma unroll
-        for (int t = 1; t < KS; ++t) acc += red[t][lane];
+        for (int t = 1; t < KS; ++t) acc += red[rg + t * RG][lane];
     }
 
     // The weights were expanded negated: flip the exact sums back.
@@ -318,39 +319,49 @@ bool gemv_supported(int64_t M, int64_t K) { return gemv_fits<Ternary2>(M, K); }
 bool gemv_binary_supported(int64_t M, int64_t K) { return gemv_fits<Binary1>(M, K); }
 bool gemv_base3_supported(int64_t M, int64_t K) { return gemv_fits<Base3>(M, K); }
 
-template <class F, int KS, int R, int WPE>
+template <class F, int RG, int KS, int R, int WPE>
 static hipError_t launch_gemv_cfg(const int8_t* xq, const float* xs, int M, int K,
                                  const GemvArgs& args, hipStream_t stream) {
     const size_t lds = (size_t)M * F::k_extent(K) + (F::kTable ? kBase3TableBytes : 0);
     static bool attr_set = false;
     if (lds > 64 * 1024 && !attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv<F, KS, R, WPE>),
+        hipError_t e =
+            hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv<F, RG, KS, R, WPE>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)(kGemvMaxXBytes + kBase3TableBytes));
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const int blocks = args.mat[0].blocks + args.mat[1].blocks;
-    hipLaunchKernelGGL((k_gemv<F, KS, R, WPE>), dim3(blocks), dim3(64 * KS), lds, stream, xq, xs,
-                       M, K, args);
+    GemvArgs a = args;
+    for (int i = 0; i < 2; ++i)
+        a.mat[i].blocks = a.mat[i].W ? (a.mat[i].N + 16 * RG - 1) / (16 * RG) : 0;
+    const int blocks = a.mat[0].blocks + a.mat[1].blocks;
+    hipLaunchKernelGGL((k_gemv<F, RG, KS, R, WPE>), dim3(blocks), dim3(64 * RG * KS), lds, stream,
+                       xq, xs, M, K, a);
     return hipGetLastError();
 }
 
 // Four waves per row group, or eight when the grid has fewer than 512 row
 // groups (few output rows, as in a down projection) and rows of at least 16
 // chunks, so that the CUs hold enough waves; rows of more than 8 chunks per
-// wave take the deep ring.
+// wave take the deep ring. With 8 or more tokens and many row groups, two row
+// groups share a workgroup: the activation block, staged once per workgroup,
+// is then read from L2 half as often.
 template <class F>
 static hipError_t launch_gemv_auto(const int8_t* xq, const float* xs, int M, int K,
                                    const GemvArgs& args, hipStream_t stream) {
     const int chunks = F::row_bytes(K) / 64;
     const int groups = args.mat[0].blocks + args.mat[1].blocks;
-    if (groups < 512 && chunks >= 16) {
-        if ((chunks + 7) / 8 > 8) return launch_gemv_cfg<F, 8, 8, 2>(xq, xs, M, K, args, stream);
-        return launch_gemv_cfg<F, 8, 4, 4>(xq, xs, M, K, args, stream);
+    if (M >= 8 && groups >= 384) {
+        if ((chunks + 3) / 4 > 4) return launch_gemv_cfg<F, 2, 4, 8, 2>(xq, xs, M, K, args, stream);
+        return launch_gemv_cfg<F, 2, 4, 4, 2>(xq, xs, M, K, args, stream);
     }
-    if ((chunks + 3) / 4 > 8) return launch_gemv_cfg<F, 4, 8, 1>(xq, xs, M, K, args, stream);
-    return launch_gemv_cfg<F, 4, 4, F::kWaves>(xq, xs, M, K, args, stream);
+    if (groups < 512 && chunks >= 16) {
+        if ((chunks + 7) / 8 > 8) return launch_gemv_cfg<F, 1, 8, 8, 2>(xq, xs, M, K, args, stream);
+        return launch_gemv_cfg<F, 1, 8, 4, 4>(xq, xs, M, K, args, stream);
+    }
+    if ((chunks + 3) / 4 > 8) return launch_gemv_cfg<F, 1, 4, 8, 1>(xq, xs, M, K, args, stream);
+    return launch_gemv_cfg<F, 1, 4, 4, F::kWaves>(xq, xs, M, K, args, stream);
 }
 
 static GemvMat make_mat(const void* Wp, const float* gamma, int N, float* y, int32_t* acc,

@@ -183,7 +183,10 @@ def _product_case(M, K, N, seed):
 
 
 GEMV_CASES = [(1, 64, 1), (1, 320, 200), (2, 3200, 50), (5, 8640, 33), (16, 6912, 257),
-              (16, 2560, 16), (1, 28672, 40), (3, 1024, 4)]
+              (16, 2560, 16), (1, 28672, 40), (3, 1024, 4),
+              # two row groups per workgroup (>= 8 tokens, >= 384 groups), the
+              # last workgroup's second group partly / wholly past N
+              (12, 2560, 6200), (9, 1024, 6150)]
 GEMM_CASES = [(1, 64, 1), (17, 320, 200), (64, 3200, 50), (100, 2560, 300), (300, 8640, 129),
               (513, 640, 260), (256, 256, 256), (70, 28672, 65)]
 
