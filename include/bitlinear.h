@@ -132,8 +132,8 @@ int bl_quantize_acts(const uint16_t* x, int64_t M, int64_t K,
  *                   the fp64-evaluated product).
  *   acc        out  optional int32 [M][N]: acc[m][n] = sum_k q[n][k]*x_q[m][k],
  *                   exact (|acc| <= 127*K). NULL to skip.
- * Small M runs a weight-streaming GEMV, large M an int8 MFMA GEMM; both give
- * identical bits. When the GEMM grid is small (few tokens or few output
+ * Small M runs a weight-streaming GEMV, large M an int8 MFMA GEMM; all give
+ * identical bits. When the grid is small (few tokens or few output
  * features) the K dimension is split across workgroups: the call then
  * enqueues three kernels and y's memory holds int32 partial sums until the
  * last one has rescaled them, so y must not alias any input. */
@@ -143,7 +143,12 @@ int bl_bitlinear(const int8_t* x_q, const float* x_scale, int64_t M, int64_t K,
 
 /* As bl_bitlinear with an explicit kernel choice, for testing and tuning:
  * path 0 = automatic, 1 = GEMV (requires M <= 16 and M*K <= 128 KiB),
- * 2 = GEMM. Any other value, or an unsupported choice, is BL_ERR_INVALID_ARG. */
+ * 2 = GEMM, 3 = wide GEMV for up to 64 tokens (128 weight rows per
+ * workgroup, activations staged in K blocks; requires M <= 64). All give the
+ * same bits. Automatic: GEMV when it applies, else the wide GEMV up to 64
+ * tokens when the weights are large enough that each of its workgroups
+ * streams at least four K blocks of 512, else the GEMM. Any other value, or
+ * an unsupported choice, is BL_ERR_INVALID_ARG. */
 int bl_bitlinear_path(const int8_t* x_q, const float* x_scale, int64_t M,
                       int64_t K, const uint32_t* W_packed, const float* gamma,
                       int64_t N, float* y, int32_t* acc, int path, void* stream);

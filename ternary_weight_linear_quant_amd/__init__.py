@@ -166,7 +166,7 @@ def quantize_acts(x, rms_gain=None, rms_eps: float = 1e-5, out=None):
 def bitlinear(x_q, x_scale, W_packed, gamma, return_acc: bool = False, path: int = 0,
               out=None, acc_out=None):
     """y[m][n] = (x_q . q^T)[m][n] * x_scale[m] * gamma -> fp32 [M][N].
-    path: 0 auto, 1 GEMV, 2 GEMM. acc_out: optional int32 [M][N] buffer for the
+    path: 0 auto, 1 GEMV, 2 GEMM, 3 wide GEMV (M <= 64). acc_out: optional int32 [M][N] buffer for the
     exact sums (returned with y, as with return_acc). Calls bl_bitlinear_path."""
     torch = _torch()
     M, K = x_q.shape

@@ -396,17 +396,28 @@ static hipError_t launch_gemm_tile(const int8_t* xq, const float* xs, int M, int
     const int per = (KT + splits - 1) / splits;
     const int used = (KT + per - 1) / per;
     const size_t total = (size_t)M * N;
-    const int blocks = (int)std::min<size_t>((total / 4 + 255) / 256 + 1, 2048);
-    hipLaunchKernelGGL(k_splitk_zero, dim3(blocks), dim3(256), 0, stream,
-                       reinterpret_cast<int32_t*>(y), total);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_splitk_zero(reinterpret_cast<int32_t*>(y), total, stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(tiles, used), dim3(64 * WGM * WGN), lds, stream, xq, xs, M, K,
                        Wp, gamma, N, y, acc, per);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_splitk_finalize, dim3(blocks), dim3(256), 0, stream, y, xs, gamma, acc,
-                       N, total);
+    return launch_splitk_finalize(y, xs, gamma, acc, N, total, stream);
+}
+
+static int splitk_blocks(size_t total) {
+    return (int)std::min<size_t>((total / 4 + 255) / 256 + 1, 2048);
+}
+
+hipError_t launch_splitk_zero(int32_t* y, size_t total, hipStream_t stream) {
+    hipLaunchKernelGGL(k_splitk_zero, dim3(splitk_blocks(total)), dim3(256), 0, stream, y, total);
+    return hipGetLastError();
+}
+
+hipError_t launch_splitk_finalize(float* y, const float* xs, const float* gamma, int32_t* acc,
+                                  int N, size_t total, hipStream_t stream) {
+    hipLaunchKernelGGL(k_splitk_finalize, dim3(splitk_blocks(total)), dim3(256), 0, stream, y, xs,
+                       gamma, acc, N, total);
     return hipGetLastError();
 }
 

@@ -341,7 +341,8 @@ static hipError_t launch_gemv_cfg(const int8_t* xq, const float* xs, int M, int 
     return hipGetLastError();
 }
 
-// Four waves per row group, or eight when the grid has fewer than 512 row
+// Four waves per row group, sixteen for very long rows, or eight when the
+// grid has fewer than 512 row
 // groups (few output rows, as in a down projection) and rows of at least 16
 // chunks, so that the CUs hold enough waves; rows of more than 8 chunks per
 // wave take the deep ring. With 8 or more tokens and many row groups, two row
@@ -352,6 +353,9 @@ static hipError_t launch_gemv_auto(const int8_t* xq, const float* xs, int M, int
                                    const GemvArgs& args, hipStream_t stream) {
     const int chunks = F::row_bytes(K) / 64;
     const int groups = args.mat[0].blocks + args.mat[1].blocks;
+    // Very long rows (>= 64 chunks, as a 28672-wide down projection): 16
+    // waves split K so that each streams a few chunks.
+    if (chunks >= 64) return launch_gemv_cfg<F, 1, 16, 4, 4>(xq, xs, M, K, args, stream);
     if (M >= 8 && groups >= 384) {
         if ((chunks + 3) / 4 > 4) return launch_gemv_cfg<F, 2, 4, 8, 2>(xq, xs, M, K, args, stream);
         return launch_gemv_cfg<F, 2, 4, 4, 2>(xq, xs, M, K, args, stream);

@@ -18,6 +18,19 @@ bool gemv_supported(int64_t M, int64_t K);
 hipError_t launch_gemv(const int8_t* xq, const float* xs, int M, int K, const uint32_t* Wp,
                        const float* gamma, int N, float* y, int32_t* acc, hipStream_t stream);
 
+// Split K: int32 zeros into y, and y[m][n] = acc * (x_scale[m] * gamma) in
+// place afterwards (acc, if not null, receives the sums).
+hipError_t launch_splitk_zero(int32_t* y, size_t total, hipStream_t stream);
+hipError_t launch_splitk_finalize(float* y, const float* xs, const float* gamma, int32_t* acc,
+                                  int N, size_t total, hipStream_t stream);
+
+// Decode for 17..64 tokens: 128 weight rows per workgroup, the activations
+// staged in 512-wide K blocks.
+bool gemv_wide_supported(int64_t M, int64_t K);
+bool gemv_wide_preferred(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemv_wide(const int8_t* xq, const float* xs, int M, int K, const uint32_t* Wp,
+                            const float* gamma, int N, float* y, int32_t* acc, hipStream_t stream);
+
 // Prefill GEMM (any M).
 hipError_t launch_gemm(const int8_t* xq, const float* xs, int M, int K, const uint32_t* Wp,
                        const float* gamma, int N, float* y, int32_t* acc, hipStream_t stream);

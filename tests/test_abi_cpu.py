@@ -83,7 +83,8 @@ def test_invalid_arguments_rejected_before_launch(L):
     assert L.bl_bitlinear(P(0x100000), P(0x200000), 1, 64, P(0x300000), P(0x400000), 16,
                           P(0x3000F0), None, None) == E
     # path selection
-    assert L.bl_bitlinear_path(X, S, 1, 64, W, G, 16, Y, None, 3, None) == E
+    assert L.bl_bitlinear_path(X, S, 1, 64, W, G, 16, Y, None, 4, None) == E
+    assert L.bl_bitlinear_path(X, S, 65, 64, W, G, 16, Y, None, 3, None) == E
     assert L.bl_bitlinear_path(X, S, 17, 64, W, G, 16, Y, None, 1, None) == E
     assert L.bl_bitlinear_path(X, S, 16, 16384, W, G, 16, Y, None, 1, None) == E
     # weight quantisation

@@ -266,6 +266,42 @@ def test_gemm_split_k(M, K, N):
     assert_y_close(y[idx].cpu().numpy(), y_ref, "split-K gemm")
 
 
+# The wide GEMV (17..64 tokens, 128 rows per workgroup, K in 512 blocks):
+# K tails of half a block and half a chunk, ragged N, and the split-K path.
+WIDE_CASES = [(17, 320, 200), (33, 2560, 300), (64, 8192, 700), (64, 6912, 1000),
+              (48, 8640, 257), (64, 28672, 130), (20, 64, 5), (40, 1024, 4000)]
+
+
+@pytest.mark.parametrize("M,K,N", WIDE_CASES)
+def test_wide_gemv_parity(M, K, N):
+    q, xq, xs, g = _product_case(M, K, N, 60)
+    args = (torch.from_numpy(xq).to(DEV), dev_f32(xs), dev_packed(oracle.pack(q)), dev_f32([g]))
+    y, acc = bl.bitlinear(*args, return_acc=True, path=3)
+    y_ref, acc_ref = oracle.bitlinear(xq, xs, q, g)
+    assert np.array_equal(acc.cpu().numpy(), acc_ref)
+    assert_y_close(y.cpu().numpy(), y_ref, "wide gemv")
+    y2, acc2 = bl.bitlinear(*args, return_acc=True, path=2)
+    assert torch.equal(acc, acc2) and torch.equal(y.view(torch.int32), y2.view(torch.int32))
+
+
+@pytest.mark.parametrize("M,K,N", [(37, 9216, 12777), (64, 28672, 8192)])
+def test_wide_gemv_multi_block_splits_sampled(M, K, N):
+    """Wide GEMV where each split streams several K blocks (the first shape's
+    last split is short), on a sample of output features by the oracle."""
+    q, xq, xs, g = _product_case(M, K, N, 61)
+    args = (torch.from_numpy(xq).to(DEV), dev_f32(xs), dev_packed(oracle.pack(q)), dev_f32([g]))
+    y, acc = bl.bitlinear(*args, return_acc=True, path=3)
+    rng = np.random.default_rng(M + N)
+    ns = np.unique(np.concatenate([rng.choice(N, 256, replace=False), [0, 1, 2, N - 1]]))
+    y_ref, acc_ref = oracle.bitlinear(xq, xs, q[ns], g)
+    nsd = torch.from_numpy(ns).to(DEV)
+    assert np.array_equal(acc[:, nsd].cpu().numpy(), acc_ref)
+    assert_y_close(y[:, nsd].cpu().numpy(), y_ref, "wide gemv multi-block")
+    assert torch.equal(y, acc.to(torch.float32) * (dev_f32(xs) * dev_f32([g])).view(-1, 1))
+    y0 = bl.bitlinear(*args)            # automatic choice: same bits
+    assert torch.equal(y0.view(torch.int32), y.view(torch.int32))
+
+
 def test_gemv_and_gemm_agree_bitwise():
     for M, K, N in [(1, 2560, 6912), (16, 6912, 2560), (4, 3200, 8640)]:
         q, xq, xs, g = _product_case(M, K, N, 55)
