@@ -427,19 +427,18 @@ hipError_t launch_gemm(const int8_t* xq, const float* xs, int M, int K, const ui
         return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
     };
     constexpr int kCUs = 256;
-    // 128 x 512 tiles, one 8-wave workgroup per CU, each wave all 128 rows by
-    // its own 64 columns (no weight column is expanded twice): fastest per
-    // tile, chosen when its grid fills at least 95% of whole rounds of the
-    // 256 CUs.
-    const int64_t t512 = tiles(128, 512);
-    const int64_t rounds512 = (t512 + kCUs - 1) / kCUs;
-    if (t512 >= kCUs && t512 * 20 >= rounds512 * kCUs * 19)
+    // 128 x 512 tiles: one 8-wave workgroup per CU, each wave all 128 rows by
+    // its own 64 columns (no weight column is expanded twice); the fastest
+    // per unit of work. 128 x 256 tiles: two 4-wave workgroups per CU (72 KB
+    // of LDS each), not tied by barriers, so one's barrier waits and output
+    // stores overlap the other's MFMAs. The busiest CU does two 128 x 256
+    // units per round of 128 x 512 tiles and one per round of 128 x 256
+    // tiles (a CU's pair shares its matrix cores); the larger tile wins ties,
+    // as long as it keeps at least half the CUs busy.
+    const int64_t t512 = tiles(128, 512), t256 = tiles(128, 256);
+    if (t512 >= kCUs / 2 && 2 * ((t512 + kCUs - 1) / kCUs) <= (t256 + kCUs - 1) / kCUs)
         return launch_gemm_tile<128, 512, 1, 8, 3, 2>(xq, xs, M, K, Wp, gamma, N, y, acc, stream);
-    // Otherwise 128 x 256 tiles, two 4-wave workgroups per CU (72 KB of LDS
-    // each): the pair is not tied by barriers, so one workgroup's barrier
-    // waits and output stores overlap the other's MFMAs, and a partial last
-    // round leaves fewer CUs idle.
-    if (tiles(128, 256) >= kCUs)
+    if (t256 >= kCUs)
         return launch_gemm_tile<128, 256, 1, 4, 3, 2>(xq, xs, M, K, Wp, gamma, N, y, acc, stream);
     if (tiles(128, 128) >= kCUs)
         return launch_gemm_tile<128, 128, 2, 2, 3, 2>(xq, xs, M, K, Wp, gamma, N, y, acc, stream);

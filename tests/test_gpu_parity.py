@@ -211,9 +211,10 @@ def test_gemm_parity(M, K, N):
     assert_y_close(y.cpu().numpy(), y_ref, "gemm")
 
 
-# Grids of at least 256 tiles select the large prefill tiles (128 x 512 with
-# one workgroup per CU, 128 x 256 with two); these shapes are ragged in M and
-# N, and K = 320 / 192 ends in a half (64-deep) K step.
+# Large grids select the large prefill tiles: 128 x 256 with two workgroups
+# per CU for the first shape, 128 x 512 with one for the others (the last
+# with only 160 tiles); these shapes are ragged in M and N, and K = 320 / 192
+# ends in a half (64-deep) K step.
 LARGE_TILE_CASES = [(2000, 320, 4000), (2000, 192, 8000), (2048, 384, 8192), (1935, 448, 5000)]
 
 
