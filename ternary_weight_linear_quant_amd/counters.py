@@ -59,10 +59,10 @@ PHASES = {
     "gemv_70b_m1_binary": (["gemv.hip", "common.hpp"],
                            "bl_bitlinear_binary at M=1 on the 70B shapes, 5 rotated copies",
                            2 * COPIES_70B, "k_gemv launch (1 bit per +-1 weight)"),
-    "gemm_decode_70b_m64": (["gemm.hip", "common.hpp"],
+    "wide_decode_70b_m64": (["gemv_wide.hip", "gemm.hip", "common.hpp"],
                             "bl_bitlinear at M=64 on the 70B shapes, 5 rotated copies",
                             2 * COPIES_70B,
-                            "bl_bitlinear call (split K: zero, k_gemm, finalize)"),
+                            "bl_bitlinear call (split K: zero, k_gemv_wide, finalize)"),
     "gemm_prefill_4096": (["gemm.hip", "common.hpp"],
                           "bl_bitlinear at M=4096 on 2560->6912 and 6912->2560", 2,
                           "bl_bitlinear call (k_gemm)"),
@@ -192,7 +192,7 @@ def run():
     phase("gemv_70b_m1", rotate70(1))
     phase("gemv_70b_m1_base3", rotate70_fmt(bl.bitlinear_base3, w5b3))
     phase("gemv_70b_m1_binary", rotate70_fmt(bl.bitlinear_binary, w5bin))
-    phase("gemm_decode_70b_m64", rotate70(64))
+    phase("wide_decode_70b_m64", rotate70(64))
     phase("gemm_prefill_4096", prefill4096)
     phase("gemm_prefill_70b", prefill70)
     marker()

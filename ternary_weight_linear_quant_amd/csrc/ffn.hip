@@ -209,14 +209,15 @@ __global__ __launch_bounds__(64 * (GLU ? 2 : 1) * KS) void k_ffn_gemv(
         ga = -ga;
         ua = -ua;
         const float sg = xs * (*g0), su = xs * (*g1);
+        // N is a multiple of 64 (checked on the host), so the lane's four
+        // outputs are all in range or all out, and 8-byte aligned.
+        if (nbase < N) {
+            uint32_t hb[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int n = nbase + i;
-            if (n < N) {
-                const float yg = (float)ga[i] * sg;
-                const float yu = (float)ua[i] * su;
-                h[(size_t)tok * N + n] = (uint16_t)relu2_gate_bits(yg, yu);
-            }
+            for (int i = 0; i < 4; ++i)
+                hb[i] = relu2_gate_bits((float)ga[i] * sg, (float)ua[i] * su);
+            *reinterpret_cast<uint2*>(h + (size_t)tok * N + nbase) =
+                make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
         }
     } else {
         v4i ta = red[0][lane];
@@ -224,11 +225,10 @@ __global__ __launch_bounds__(64 * (GLU ? 2 : 1) * KS) void k_ffn_gemv(
         for (int w = 1; w < KS; ++w) ta += red[w][lane];
         ta = -ta;
         const float sc = xs * (*g0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int n = nbase + i;
-            if (n < N) y[(size_t)tok * N + n] = (float)ta[i] * sc;
-        }
+        if (nbase < N)  // four in range, 16-byte aligned (as above)
+            *reinterpret_cast<float4*>(y + (size_t)tok * N + nbase) =
+                make_float4((float)ta[0] * sc, (float)ta[1] * sc, (float)ta[2] * sc,
+                            (float)ta[3] * sc);
     }
 }
 
@@ -240,6 +240,7 @@ constexpr int kKsA = 2, kKsB = 8, kKsBSmall = 4;
 
 bool ffn_fused_supported(int64_t M, int64_t K, int64_t N_ff) {
     if (M < 1 || M > 4 || (256 % M) != 0) return false;
+    if (K % 64 != 0 || N_ff % 64 != 0) return false;  // whole 4-output stores
     // Activation units must fit the register cache; every K-split wave needs
     // at least one full 256-weight chunk.
     if (M * (K / 16) > kFfnMinThreads * kFfnCache || M * (N_ff / 16) > kFfnMinThreads * kFfnCache)
