@@ -101,6 +101,31 @@ __device__ __forceinline__ void wait_vmcnt_le8(int n) {
     }
 }
 
+// Physical 16-byte chunk of logical chunk c in LDS row r: c ^ swz(r). Both
+// depend only on r % 32, so fragment addresses of different 32-row tiles
+// differ by constants. Any 8 (A: 128-byte rows) or 16 aligned consecutive
+// rows map their reads of one logical chunk to distinct banks, for 32 or 64
+// LDS banks alike.
+__device__ __forceinline__ int swz_a(int r) { return (r ^ ((r >> 3) & 3)) & 7; }
+__device__ __forceinline__ int swz_b(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
+
+// Wait until at most `stages` (wave-uniform, 0..S) pipeline stages of LOADS
+// vector memory instructions each are still outstanding (they complete in
+// issue order).
+template <int LOADS, int S>
+__device__ __forceinline__ void wait_stages(int stages) {
+    static_assert(LOADS * S < 64, "vmcnt range");
+    if constexpr (S == 0) {
+        BL_WAIT_VMCNT(0);
+    } else {
+        if (stages >= S) {
+            BL_WAIT_VMCNT(S * LOADS);
+        } else {
+            wait_stages<LOADS, S - 1>(stages);
+        }
+    }
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));

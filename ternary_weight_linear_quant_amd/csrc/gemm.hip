@@ -37,31 +37,6 @@ constexpr int kBK = 128;            // k per stage
 constexpr int kARow = kBK;          // activation bytes per row per stage
 constexpr int kBRow = kBK / 4;      // packed weight bytes per row per stage
 
-// Physical 16-byte chunk of logical chunk c in LDS row r: c ^ swz(r). Both
-// depend only on r % 32, so fragment addresses of different 32-row tiles
-// differ by constants. Any 8 (A: 128-byte rows) or 16 aligned consecutive
-// rows map their reads of one logical chunk to distinct banks, for 32 or 64
-// LDS banks alike.
-__device__ __forceinline__ int swz_a(int r) { return (r ^ ((r >> 3) & 3)) & 7; }
-__device__ __forceinline__ int swz_b(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
-
-// Wait until at most `stages` (wave-uniform, 0..S) pipeline stages of LOADS
-// vector memory instructions each are still outstanding (they complete in
-// issue order).
-template <int LOADS, int S>
-__device__ __forceinline__ void wait_stages(int stages) {
-    static_assert(LOADS * S < 64, "vmcnt range");
-    if constexpr (S == 0) {
-        BL_WAIT_VMCNT(0);
-    } else {
-        if (stages >= S) {
-            BL_WAIT_VMCNT(S * LOADS);
-        } else {
-            wait_stages<LOADS, S - 1>(stages);
-        }
-    }
-}
-
 // WPE: waves per SIMD the register allocation must allow (2 lets two
 // workgroups share a CU so that one's barrier gaps are filled by the other).
 // SPLIT: the K steps are divided among gridDim.y workgroups per tile (kt_split

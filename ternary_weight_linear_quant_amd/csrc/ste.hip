@@ -12,15 +12,18 @@
 //
 // The ternary weights enter the bf16 matrix cores directly: q is first
 // transposed once (offline, like the forward packing) into rows of k with
-// four consecutive n per byte, so a 2-byte read gives the 8 reduction values
-// of one lane of a v_mfma_f32_32x32x16_bf16 B fragment, decoded through a
-// 256-entry LDS table of four bf16 values {-1, 0, +1}. Products of bf16 by
-// {-1, 0, +1} are exact; the sums accumulate in fp32.
+// four consecutive n per byte. The GEMM mirrors the forward one: A = dy tile
+// (rows = tokens, n-contiguous), B = code tile (rows = input features k),
+// v_mfma_f32_32x32x16_bf16, a STAGES-deep LDS ring filled with
+// global_load_lds_dwordx4, reduction steps of 64 n (128 bytes of dy and 16
+// bytes of codes per row). Products of bf16 by {-1, 0, +1} are exact; the
+// sums accumulate in fp32.
 //
-// Tile: 128 (tokens) x 128 (input features), 4 waves in a 2 x 2 grid of
-// 64 x 64, reduction steps of 32 n double-buffered through registers into
-// LDS. dy rows in LDS are padded to 80 bytes, which keeps the 16-byte
-// fragment reads of 8 consecutive rows on distinct banks.
+// Codes are decoded in registers: the 16 bits of codes that feed one B
+// fragment (8 n of one k) become 4 dwords of bf16 pairs with a byte
+// replicate, a packed 16-bit shift, a mask and a byte permute through the
+// table {0xBF, 0x00, 0x3F} (high bytes) / {0x80, 0x00, 0x80} (low bytes):
+// about 3.5 VALU instructions per MFMA, which the matrix cores overlap.
 //
 // Roofline: MFMA (bf16). Work per call = 2*M*N*K flops.
 #include "common.hpp"
@@ -30,11 +33,11 @@ namespace bl {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kSteBM = 128, kSteBN = 128, kSteBR = 32;
-constexpr int kSteThreads = 256;
-constexpr int kSteARow = kSteBR * 2 + 16;  // bytes per padded dy row in LDS
-constexpr int kSteBRow = kSteBR / 4;       // code bytes per qT row per step
+constexpr int kSteBR = 64;             // n per stage
+constexpr int kSteARow = kSteBR * 2;   // dy bytes per row per stage
+constexpr int kSteBRow = kSteBR / 4;   // code bytes per row per stage
 
 int64_t ste_t_row_bytes(int64_t N) { return 16 * (((N + 3) / 4 + 15) / 16); }
 
@@ -60,127 +63,220 @@ __global__ __launch_bounds__(256) void k_pack_ste_t(const uint32_t* __restrict__
     qT[k * row_bytes + j] = (uint8_t)v;
 }
 
-__device__ __forceinline__ uint32_t bf16_of_code(uint32_t c) {
-    return c == 0 ? 0xBF80u : c == 2 ? 0x3F80u : 0u;  // weight c - 1; code 3 unused -> 0
+// Source of the dy chunks past N (N % 64 != 0): sixteen zero bytes, so the
+// padded products are exact zeros whatever the codes there.
+__device__ __align__(16) const uint32_t kSteZero16[4] = {0u, 0u, 0u, 0u};
+
+// One B fragment: bytes b and b+1 of `w` hold the codes of 8 consecutive n
+// (code c = q + 1 of the i-th at bits 2i). rep_lo / rep_hi replicate byte b
+// / b+1 into all four bytes (selectors 0x01010101 * b, * (b+1)).
+__device__ __forceinline__ bf16x8 decode_codes8(uint32_t w, uint32_t rep_lo, uint32_t rep_hi) {
+    const uint32_t hi_tab = 0x003F00BFu;  // sel 0 -> 0xBF, 1 -> 0x00, 2 -> 0x3F
+    const uint32_t lo_tab = 0x00800080u;  // sel 4 -> 0x80, 5 -> 0x00, 6 -> 0x80
+    const uint32_t d0 = __builtin_amdgcn_perm(0u, w, rep_lo);
+    const uint32_t d1 = __builtin_amdgcn_perm(0u, w, rep_hi);
+    // Per 16-bit half: the two bytes of a bf16 both carry one code, and the
+    // low byte's selector gets +4 (the second table).
+    auto pair = [&](uint32_t d, unsigned sa, unsigned sb) -> uint32_t {
+        const u16x2 sh = __builtin_bit_cast(u16x2, d) >> (u16x2){(unsigned short)sa,
+                                                                  (unsigned short)sb};
+        const uint32_t sel = (__builtin_bit_cast(uint32_t, sh) & 0x03030303u) | 0x00040004u;
+        return __builtin_amdgcn_perm(lo_tab, hi_tab, sel);
+    };
+    return __builtin_bit_cast(bf16x8, make_uint4(pair(d0, 0, 2), pair(d0, 4, 6), pair(d1, 0, 2),
+                                                 pair(d1, 4, 6)));
 }
 
-__global__ __launch_bounds__(kSteThreads, 2) void k_ste_dx(
+template <int BM, int BN, int WGM, int WGN, int STAGES, int WPE>
+__global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_ste_dx(
     const uint16_t* __restrict__ dy, int M, int N, const uint8_t* __restrict__ qT, int RBT,
     const float* __restrict__ gamma_p, int K, float* __restrict__ dx) {
-    __shared__ __align__(16) uint8_t As[2][kSteBM * kSteARow];
-    __shared__ __align__(16) uint8_t Bs[2][kSteBN * kSteBRow];
-    __shared__ uint2 lut[256];
+    constexpr int NW = WGM * WGN;
+    constexpr int WM = BM / WGM, WN = BN / WGN;
+    constexpr int TM = WM / 32, TN = WN / 32;
+    constexpr int A_STAGE = BM * kSteARow;
+    constexpr int B_STAGE = BN * kSteBRow;
+    constexpr int STAGE = A_STAGE + B_STAGE;
+    constexpr int A_ROWS = BM / NW;       // dy rows loaded per wave
+    constexpr int A_INSTR = A_ROWS / 8;   // 8 rows of 128 B per instruction
+    constexpr int B_ROWS = BN / NW;       // code rows loaded per wave
+    constexpr int B_INSTR = B_ROWS / 64;  // 64 rows of 16 B per instruction
+    constexpr int LOADS = A_INSTR + B_INSTR;
+    static_assert(TM >= 1 && TN >= 1 && A_INSTR >= 1 && B_INSTR >= 1, "tile shape");
+    static_assert(A_ROWS % 8 == 0 && B_ROWS % 64 == 0, "tile shape");
+    static_assert(STAGES >= 3 && LOADS * (STAGES - 1) < 64, "pipeline depth");
+
+    extern __shared__ __align__(16) uint8_t smem[];
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
-    const int wave = tid / kWave;
-    const int wm0 = (wave % 2) * 64, wn0 = (wave / 2) * 64;
-    const int tilesN = (K + kSteBN - 1) / kSteBN;
-    const int m0 = ((int)blockIdx.x / tilesN) * kSteBM;
-    const int k0 = ((int)blockIdx.x % tilesN) * kSteBN;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wm0 = (wave % WGM) * WM, wn0 = (wave / WGM) * WN;
 
-    // Table: byte b -> four bf16 weights of its codes, low code first.
-    {
-        const uint32_t b = (uint32_t)tid;
-        const uint32_t lo = bf16_of_code(b & 3u) | (bf16_of_code((b >> 2) & 3u) << 16);
-        const uint32_t hi = bf16_of_code((b >> 4) & 3u) | (bf16_of_code((b >> 6) & 3u) << 16);
-        lut[b] = make_uint2(lo, hi);
+    // Tile order as in the forward GEMM: a contiguous range of tiles per XCD,
+    // walked in groups of 8 row tiles.
+    const int nM = (M + BM - 1) / BM, nN = (K + BN - 1) / BN;
+    const int total = nM * nN;
+    const int b = blockIdx.x;
+    const int xcd = b % 8, idx = b / 8;
+    const int t = xcd * (total / 8) + min(xcd, total % 8) + idx;
+    constexpr int G = 8;
+    const int group = t / (G * nN);
+    const int first_m = group * G;
+    const int gsize = min(nM - first_m, G);
+    const int bm = first_m + (t % (G * nN)) % gsize;
+    const int bn = (t % (G * nN)) / gsize;
+    const int m0 = bm * BM, k0 = bn * BN;
+
+    const int NK = (N + kSteBR - 1) / kSteBR;
+
+    // Stage loads. dy: instruction i of this wave fills rows 8i + lane/8 of
+    // its A_ROWS; the DMA puts lane l's 16 bytes at physical chunk l%8 of the
+    // row, so the lane loads the logical chunk (8 n) that the swizzle maps
+    // there; rows past M are clamped (not stored). Codes: one 16-byte
+    // chunk per row, rows past K clamped; the row padding holds code 1.
+    const uint16_t* a_src[A_INSTR];
+    int a_chunk[A_INSTR];
+#pragma unroll
+    for (int i = 0; i < A_INSTR; ++i) {
+        const int r = wave * A_ROWS + 8 * i + lane / 8;
+        a_chunk[i] = (lane % 8) ^ swz_a(r);
+        a_src[i] = dy + (size_t)min(m0 + r, M - 1) * N + 8 * a_chunk[i];
     }
+    const uint8_t* b_src[B_INSTR];
+#pragma unroll
+    for (int i = 0; i < B_INSTR; ++i)
+        b_src[i] = qT + (size_t)min(k0 + wave * B_ROWS + 64 * i + lane, K - 1) * RBT;
 
-    // Stage loads: dy 128 rows x 64 bytes (two 16-byte chunks per thread),
-    // qT 128 rows x 8 bytes (threads 0..127). Rows past M or K are clamped
-    // (their results are not stored); chunks past N are zero.
-    const int steps = (N + kSteBR - 1) / kSteBR;
-    uint4 ra[2];
-    uint2 rb = make_uint2(0x55555555u, 0x55555555u);
-    auto load = [&](int st) {
-        const int n0 = st * kSteBR;
+    const uint32_t smem_base = (uint32_t)(size_t)(lds_u8_t*)smem;
+    auto issue = [&](int kt) {
+        const uint32_t st = smem_base + (uint32_t)((kt % STAGES) * STAGE);
+        const int n0 = kt * kSteBR;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int c = tid + kSteThreads * i;  // chunk 0..511: row c/4, part c%4
-            const int row = min(m0 + c / 4, M - 1);
-            const int n = n0 + 8 * (c % 4);
-            ra[i] = n < N ? *reinterpret_cast<const uint4*>(dy + (size_t)row * N + n)
-                          : make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < A_INSTR; ++i) {
+            // The lane's 8 n are all below N or all at/after it (N % 8 == 0).
+            const void* src = n0 + 8 * a_chunk[i] < N ? (const void*)(a_src[i] + n0)
+                                                      : (const void*)kSteZero16;
+            lds_dma16(src, st + (wave * A_ROWS + 8 * i) * kSteARow);
         }
-        if (tid < kSteBN) {
-            const int krow = min(k0 + tid, K - 1);
-            rb = *reinterpret_cast<const uint2*>(qT + (size_t)krow * RBT + n0 / 4);
-        }
-    };
-    auto store = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int c = tid + kSteThreads * i;
-            *reinterpret_cast<uint4*>(&As[buf][(c / 4) * kSteARow + 16 * (c % 4)]) = ra[i];
-        }
-        if (tid < kSteBN) *reinterpret_cast<uint2*>(&Bs[buf][tid * kSteBRow]) = rb;
+        for (int i = 0; i < B_INSTR; ++i)
+            lds_dma16(b_src[i] + n0 / 4, st + A_STAGE + (wave * B_ROWS + 64 * i) * kSteBRow);
     };
 
-    f32x16 acc[2][2];
+    f32x16 acc[TM][TN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
     const int fr = lane % 32, fg = lane / 32;
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int st = 0; st < steps; ++st) {
-        const int buf = st & 1;
-        if (st + 1 < steps) load(st + 1);
+    // Byte selectors of this lane group's code bytes within a stage dword.
+    const uint32_t rep_lo = 0x01010101u * (2 * fg), rep_hi = 0x01010101u * (2 * fg + 1);
+
+    auto read_b = [&](uint4* bp, int kt) {
+        const uint8_t* Bs = smem + (kt % STAGES) * STAGE + A_STAGE;
 #pragma unroll
-        for (int s = 0; s < kSteBR / 16; ++s) {
-            // A: dy row, reduction n = 16s + 8*fg .. +8 (16 bytes).
-            bf16x8 a[2], b[2];
+        for (int j = 0; j < TN; ++j)
+            bp[j] = *reinterpret_cast<const uint4*>(Bs + (wn0 + 32 * j + fr) * kSteBRow);
+    };
+    // A fragment of substep s: row r, n = 16s + 8g .. +8 = logical chunk 2s + g.
+    auto read_a = [&](bf16x8* af, int kt, int s) {
+        const uint8_t* As = smem + (kt % STAGES) * STAGE;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int r = wm0 + 32 * i + fr;
-                const uint4 v = *reinterpret_cast<const uint4*>(
-                    &As[buf][r * kSteARow + 32 * s + 16 * fg]);
-                a[i] = __builtin_bit_cast(bf16x8, v);
-            }
-            // B: qT row k, the same 8 n as two code bytes -> 8 bf16.
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int kr = wn0 + 32 * j + fr;
-                const uint32_t two = *reinterpret_cast<const uint16_t*>(
-                    &Bs[buf][kr * kSteBRow + 4 * s + 2 * fg]);
-                const uint2 e0 = lut[two & 0xFFu], e1 = lut[two >> 8];
-                b[j] = __builtin_bit_cast(bf16x8, make_uint4(e0.x, e0.y, e1.x, e1.y));
-            }
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0,
-                                                                        0, 0);
+        for (int i = 0; i < TM; ++i) {
+            const int r = wm0 + 32 * i + fr;
+            af[i] = *reinterpret_cast<const bf16x8*>(As + r * kSteARow +
+                                                     16 * ((2 * s + fg) ^ swz_a(r)));
         }
-        if (st + 1 < steps) {
-            store(buf ^ 1);
+    };
+    auto decode = [&](bf16x8* bf, const uint4* bp, int s) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const uint32_t w = s == 0 ? bp[j].x : s == 1 ? bp[j].y : s == 2 ? bp[j].z : bp[j].w;
+            bf[j] = decode_codes8(w, rep_lo, rep_hi);
         }
-        __syncthreads();
+    };
+
+    // Pipeline as in the forward GEMM: stage kt+STAGES-1 is issued in
+    // substep 1 of step kt, right after the barrier that follows this wave's
+    // wait for stage kt+1 (so stage kt+1 is visible to all) and proves every
+    // wave is done with step kt-1 (whose buffer is refilled).
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st)
+        if (st < NK) issue(st);
+    {
+        wait_stages<LOADS, STAGES - 2>(min(STAGES - 2, NK - 1));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    }
+    uint4 bp[TN], bpn[TN];
+    bf16x8 af[TM], an[TM], bf[TN], bfn[TN];
+    read_b(bp, 0);
+    read_a(af, 0, 0);
+    decode(bf, bp, 0);
+
+    for (int kt = 0; kt < NK; ++kt) {
+        const bool more = kt + 1 < NK;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            if (s < 3) {
+                read_a(an, kt, s + 1);
+                decode(bfn, bp, s + 1);
+            } else if (more) {
+                read_a(an, kt + 1, 0);
+                decode(bfn, bpn, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j],
+                                                                        0, 0, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, TM, 0);
+#pragma unroll
+            for (int q = 0; q < TM * TN; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            }
+            if (s == 1 && more) {
+                wait_stages<LOADS, STAGES - 3>(min(STAGES - 3, NK - 2 - kt));
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+                if (kt + STAGES - 1 < NK) issue(kt + STAGES - 1);
+                read_b(bpn, kt + 1);
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i) af[i] = an[i];
+#pragma unroll
+            for (int j = 0; j < TN; ++j) bf[j] = bfn[j];
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bp[j] = bpn[j];
     }
 
     // C layout of the 32x32 MFMA: lane l, register v holds row
     // 8*(v/4) + 4*(l/32) + v%4 (token) and column l%32 (input feature).
     const float g = *gamma_p;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TM; ++i) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int m = m0 + wm0 + 32 * i + 8 * (v / 4) + 4 * (lane / 32) + (v % 4);
             if (m < M) {
+                float* row = dx + (size_t)m * K;
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
+                for (int j = 0; j < TN; ++j) {
                     const int k = k0 + wn0 + 32 * j + (lane % 32);
-                    if (k < K) dx[(size_t)m * K + k] = acc[i][j][v] * g;
+                    if (k < K) __builtin_nontemporal_store(acc[i][j][v] * g, row + k);
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
+    }
 }
 
 hipError_t launch_pack_ste_t(const uint32_t* packed2, int64_t N, int64_t K, uint8_t* qT,
@@ -192,12 +288,36 @@ hipError_t launch_pack_ste_t(const uint32_t* packed2, int64_t N, int64_t K, uint
     return hipGetLastError();
 }
 
-hipError_t launch_ste_dx(const uint16_t* dy, int M, int N, const uint8_t* qT, const float* gamma,
-                         int K, float* dx, hipStream_t stream) {
-    const int tiles = ((M + kSteBM - 1) / kSteBM) * ((K + kSteBN - 1) / kSteBN);
-    hipLaunchKernelGGL(k_ste_dx, dim3(tiles), dim3(kSteThreads), 0, stream, dy, M, N, qT,
+template <int BM, int BN, int WGM, int WGN, int STAGES, int WPE>
+static hipError_t launch_ste_tile(const uint16_t* dy, int M, int N, const uint8_t* qT,
+                                  const float* gamma, int K, float* dx, hipStream_t stream) {
+    constexpr size_t lds = (size_t)STAGES * (BM * kSteARow + BN * kSteBRow);
+    auto kern = &k_ste_dx<BM, BN, WGM, WGN, STAGES, WPE>;
+    static bool attr_set = false;
+    if (lds > 64 * 1024 && !attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int tiles = ((M + BM - 1) / BM) * ((K + BN - 1) / BN);
+    hipLaunchKernelGGL(kern, dim3(tiles), dim3(64 * WGM * WGN), lds, stream, dy, M, N, qT,
                        (int)ste_t_row_bytes(N), gamma, K, dx);
     return hipGetLastError();
+}
+
+hipError_t launch_ste_dx(const uint16_t* dy, int M, int N, const uint8_t* qT, const float* gamma,
+                         int K, float* dx, hipStream_t stream) {
+    // The forward GEMM's rule between 128 x 512 tiles (one 8-wave workgroup
+    // per CU) and 128 x 256 tiles (two 4-wave workgroups per CU).
+    constexpr int64_t kCUs = 256;
+    auto tiles = [&](int bm, int bn) {
+        return (int64_t)((M + bm - 1) / bm) * ((K + bn - 1) / bn);
+    };
+    const int64_t t512 = tiles(128, 512), t256 = tiles(128, 256);
+    if (t512 >= kCUs / 2 && 2 * ((t512 + kCUs - 1) / kCUs) <= (t256 + kCUs - 1) / kCUs)
+        return launch_ste_tile<128, 512, 1, 8, 3, 2>(dy, M, N, qT, gamma, K, dx, stream);
+    return launch_ste_tile<128, 256, 1, 4, 3, 2>(dy, M, N, qT, gamma, K, dx, stream);
 }
 
 }  // namespace bl

@@ -711,6 +711,25 @@ def test_ste_backward_dx_parity(M, N, K):
     assert (err <= _dx_bound(dy, q, g)).all(), float(err.max())
 
 
+def test_ste_backward_dx_large_tiles_ragged():
+    """128 x 512 output tiles (2000 x 4800 is 160 of them), ragged in tokens,
+    input features and the reduction (N = 200: the last 64-wide step holds 8
+    valid n); oracle on sampled token rows, all K."""
+    M, N, K = 2000, 200, 4800
+    rng = np.random.default_rng(97)
+    q = rand_codes(rng, N, K)
+    g = np.float32(0.0211)
+    qT = bl.pack_ste_t(dev_packed(oracle.pack(q)), K)
+    dy = wl.f32_to_bf16_bits((rng.standard_normal((M, N)) * 0.01).astype(np.float32))
+    dx = bl.ste_backward_dx(dev_bf16(dy), qT, dev_f32([g]), N)
+    edges = [m for t in range(0, M, 128) for m in (t, min(t + 127, M - 1))]
+    rows = np.unique(np.concatenate([edges[:4], edges[-4:], rng.choice(M, 8, replace=False)]))
+    ref = oracle.ste_dx(dy[rows], q, g)
+    got = dx[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    err = np.abs(got.astype(np.float64) - ref.astype(np.float64))
+    assert (err <= _dx_bound(dy[rows], q, g)).all(), float(err.max())
+
+
 def test_ste_pack_odd_n():
     rng = np.random.default_rng(91)
     q = rand_codes(rng, 37, 64)
