@@ -35,9 +35,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kSteBR = 64;             // n per stage
-constexpr int kSteARow = kSteBR * 2;   // dy bytes per row per stage
-constexpr int kSteBRow = kSteBR / 4;   // code bytes per row per stage
 
 int64_t ste_t_row_bytes(int64_t N) { return 16 * (((N + 3) / 4 + 15) / 16); }
 
@@ -87,23 +84,43 @@ __device__ __forceinline__ bf16x8 decode_codes8(uint32_t w, uint32_t rep_lo, uin
                                                  pair(d1, 4, 6)));
 }
 
-template <int BM, int BN, int WGM, int WGN, int STAGES, int WPE>
+// Physical 16-byte chunk of logical chunk c of LDS row r. dy rows of 8
+// chunks use the forward GEMM's swizzle; rows of 16 chunks XOR with r % 16,
+// so any 16 aligned consecutive rows read one logical chunk from 16
+// distinct bank groups. Code rows of 2 chunks swap halves every 8 rows.
+template <int CH>
+__device__ __forceinline__ int ste_swz_a(int r) {
+    if constexpr (CH == 8) return swz_a(r);
+    else return r & 15;
+}
+template <int CH>
+__device__ __forceinline__ int ste_swz_b(int r) {
+    if constexpr (CH == 1) return 0;
+    else return (r >> 3) & 1;
+}
+
+// BR: n per reduction stage (64 or 128): 2*BR bytes of dy and BR/4 bytes of
+// codes per row.
+template <int BM, int BN, int WGM, int WGN, int BR, int STAGES, int WPE>
 __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_ste_dx(
     const uint16_t* __restrict__ dy, int M, int N, const uint8_t* __restrict__ qT, int RBT,
     const float* __restrict__ gamma_p, int K, float* __restrict__ dx) {
     constexpr int NW = WGM * WGN;
     constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int TM = WM / 32, TN = WN / 32;
-    constexpr int A_STAGE = BM * kSteARow;
-    constexpr int B_STAGE = BN * kSteBRow;
+    constexpr int AROW = 2 * BR, BROW = BR / 4;   // bytes per row per stage
+    constexpr int CH_A = AROW / 16, CH_B = BROW / 16;
+    constexpr int SUB = BR / 16;                  // MFMA substeps per stage
+    constexpr int A_STAGE = BM * AROW;
+    constexpr int B_STAGE = BN * BROW;
     constexpr int STAGE = A_STAGE + B_STAGE;
-    constexpr int A_ROWS = BM / NW;       // dy rows loaded per wave
-    constexpr int A_INSTR = A_ROWS / 8;   // 8 rows of 128 B per instruction
-    constexpr int B_ROWS = BN / NW;       // code rows loaded per wave
-    constexpr int B_INSTR = B_ROWS / 64;  // 64 rows of 16 B per instruction
+    constexpr int A_RPI = 64 / CH_A, B_RPI = 64 / CH_B;  // rows per DMA instruction
+    constexpr int A_ROWS = BM / NW, B_ROWS = BN / NW;    // rows loaded per wave
+    constexpr int A_INSTR = A_ROWS / A_RPI, B_INSTR = B_ROWS / B_RPI;
     constexpr int LOADS = A_INSTR + B_INSTR;
+    static_assert(BR == 64 || BR == 128, "stage width");
     static_assert(TM >= 1 && TN >= 1 && A_INSTR >= 1 && B_INSTR >= 1, "tile shape");
-    static_assert(A_ROWS % 8 == 0 && B_ROWS % 64 == 0, "tile shape");
+    static_assert(A_ROWS % A_RPI == 0 && B_ROWS % B_RPI == 0, "tile shape");
     static_assert(STAGES >= 3 && LOADS * (STAGES - 1) < 64, "pipeline depth");
 
     extern __shared__ __align__(16) uint8_t smem[];
@@ -128,40 +145,47 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_ste_dx(
     const int bn = (t % (G * nN)) / gsize;
     const int m0 = bm * BM, k0 = bn * BN;
 
-    const int NK = (N + kSteBR - 1) / kSteBR;
+    const int NK = (N + BR - 1) / BR;
 
-    // Stage loads. dy: instruction i of this wave fills rows 8i + lane/8 of
-    // its A_ROWS; the DMA puts lane l's 16 bytes at physical chunk l%8 of the
-    // row, so the lane loads the logical chunk (8 n) that the swizzle maps
-    // there; rows past M are clamped (not stored). Codes: one 16-byte
-    // chunk per row, rows past K clamped; the row padding holds code 1.
+    // Stage loads. The DMA puts lane l's 16 bytes at physical chunk l % CH of
+    // row l / CH of the instruction's rows, so each lane loads the logical
+    // chunk that the swizzle maps there. dy rows past M and code rows past K
+    // are clamped (their results are not stored). dy chunks at or past N
+    // (8 n each, all or none valid since N % 8 == 0) and code chunks past the
+    // row's padded length come from a zero array: the dy factor is then 0.
     const uint16_t* a_src[A_INSTR];
     int a_chunk[A_INSTR];
 #pragma unroll
     for (int i = 0; i < A_INSTR; ++i) {
-        const int r = wave * A_ROWS + 8 * i + lane / 8;
-        a_chunk[i] = (lane % 8) ^ swz_a(r);
+        const int r = wave * A_ROWS + A_RPI * i + lane / CH_A;
+        a_chunk[i] = (lane % CH_A) ^ ste_swz_a<CH_A>(r);
         a_src[i] = dy + (size_t)min(m0 + r, M - 1) * N + 8 * a_chunk[i];
     }
     const uint8_t* b_src[B_INSTR];
+    int b_chunk[B_INSTR];
 #pragma unroll
-    for (int i = 0; i < B_INSTR; ++i)
-        b_src[i] = qT + (size_t)min(k0 + wave * B_ROWS + 64 * i + lane, K - 1) * RBT;
+    for (int i = 0; i < B_INSTR; ++i) {
+        const int r = wave * B_ROWS + B_RPI * i + lane / CH_B;
+        b_chunk[i] = (lane % CH_B) ^ ste_swz_b<CH_B>(r);
+        b_src[i] = qT + (size_t)min(k0 + r, K - 1) * RBT + 16 * b_chunk[i];
+    }
 
     const uint32_t smem_base = (uint32_t)(size_t)(lds_u8_t*)smem;
     auto issue = [&](int kt) {
         const uint32_t st = smem_base + (uint32_t)((kt % STAGES) * STAGE);
-        const int n0 = kt * kSteBR;
+        const int n0 = kt * BR;
 #pragma unroll
         for (int i = 0; i < A_INSTR; ++i) {
-            // The lane's 8 n are all below N or all at/after it (N % 8 == 0).
             const void* src = n0 + 8 * a_chunk[i] < N ? (const void*)(a_src[i] + n0)
                                                       : (const void*)kSteZero16;
-            lds_dma16(src, st + (wave * A_ROWS + 8 * i) * kSteARow);
+            lds_dma16(src, st + (wave * A_ROWS + A_RPI * i) * AROW);
         }
 #pragma unroll
-        for (int i = 0; i < B_INSTR; ++i)
-            lds_dma16(b_src[i] + n0 / 4, st + A_STAGE + (wave * B_ROWS + 64 * i) * kSteBRow);
+        for (int i = 0; i < B_INSTR; ++i) {
+            const void* src = n0 / 4 + 16 * b_chunk[i] < RBT ? (const void*)(b_src[i] + n0 / 4)
+                                                            : (const void*)kSteZero16;
+            lds_dma16(src, st + A_STAGE + (wave * B_ROWS + B_RPI * i) * BROW);
+        }
     };
 
     f32x16 acc[TM][TN];
@@ -176,11 +200,18 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_ste_dx(
     // Byte selectors of this lane group's code bytes within a stage dword.
     const uint32_t rep_lo = 0x01010101u * (2 * fg), rep_hi = 0x01010101u * (2 * fg + 1);
 
-    auto read_b = [&](uint4* bp, int kt) {
+    // The codes of a B-fragment row for the whole stage: CH_B * 4 dwords,
+    // dword s feeding substep s.
+    auto read_b = [&](uint4 (*bp)[CH_B], int kt) {
         const uint8_t* Bs = smem + (kt % STAGES) * STAGE + A_STAGE;
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-            bp[j] = *reinterpret_cast<const uint4*>(Bs + (wn0 + 32 * j + fr) * kSteBRow);
+        for (int j = 0; j < TN; ++j) {
+            const int r = wn0 + 32 * j + fr;
+#pragma unroll
+            for (int h = 0; h < CH_B; ++h)
+                bp[j][h] = *reinterpret_cast<const uint4*>(Bs + r * BROW +
+                                                           16 * (h ^ ste_swz_b<CH_B>(r)));
+        }
     };
     // A fragment of substep s: row r, n = 16s + 8g .. +8 = logical chunk 2s + g.
     auto read_a = [&](bf16x8* af, int kt, int s) {
@@ -188,14 +219,16 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_ste_dx(
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int r = wm0 + 32 * i + fr;
-            af[i] = *reinterpret_cast<const bf16x8*>(As + r * kSteARow +
-                                                     16 * ((2 * s + fg) ^ swz_a(r)));
+            af[i] = *reinterpret_cast<const bf16x8*>(As + r * AROW +
+                                                     16 * ((2 * s + fg) ^ ste_swz_a<CH_A>(r)));
         }
     };
-    auto decode = [&](bf16x8* bf, const uint4* bp, int s) {
+    auto decode = [&](bf16x8* bf, const uint4 (*bp)[CH_B], int s) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const uint32_t w = s == 0 ? bp[j].x : s == 1 ? bp[j].y : s == 2 ? bp[j].z : bp[j].w;
+            const uint4 q4 = bp[j][s / 4];
+            const int d = s % 4;
+            const uint32_t w = d == 0 ? q4.x : d == 1 ? q4.y : d == 2 ? q4.z : q4.w;
             bf[j] = decode_codes8(w, rep_lo, rep_hi);
         }
     };
@@ -212,7 +245,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_ste_dx(
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
     }
-    uint4 bp[TN], bpn[TN];
+    uint4 bp[TN][CH_B], bpn[TN][CH_B];
     bf16x8 af[TM], an[TM], bf[TN], bfn[TN];
     read_b(bp, 0);
     read_a(af, 0, 0);
@@ -221,8 +254,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_ste_dx(
     for (int kt = 0; kt < NK; ++kt) {
         const bool more = kt + 1 < NK;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            if (s < 3) {
+        for (int s = 0; s < SUB; ++s) {
+            if (s < SUB - 1) {
                 read_a(an, kt, s + 1);
                 decode(bfn, bp, s + 1);
             } else if (more) {
@@ -255,7 +288,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_ste_dx(
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int j = 0; j < TN; ++j) bp[j] = bpn[j];
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int h = 0; h < CH_B; ++h) bp[j][h] = bpn[j][h];
     }
 
     // C layout of the 32x32 MFMA: lane l, register v holds row
@@ -288,11 +323,11 @@ hipError_t launch_pack_ste_t(const uint32_t* packed2, int64_t N, int64_t K, uint
     return hipGetLastError();
 }
 
-template <int BM, int BN, int WGM, int WGN, int STAGES, int WPE>
+template <int BM, int BN, int WGM, int WGN, int BR, int STAGES, int WPE>
 static hipError_t launch_ste_tile(const uint16_t* dy, int M, int N, const uint8_t* qT,
                                   const float* gamma, int K, float* dx, hipStream_t stream) {
-    constexpr size_t lds = (size_t)STAGES * (BM * kSteARow + BN * kSteBRow);
-    auto kern = &k_ste_dx<BM, BN, WGM, WGN, STAGES, WPE>;
+    constexpr size_t lds = (size_t)STAGES * (BM * 2 * BR + BN * BR / 4);
+    auto kern = &k_ste_dx<BM, BN, WGM, WGN, BR, STAGES, WPE>;
     static bool attr_set = false;
     if (lds > 64 * 1024 && !attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -316,8 +351,8 @@ hipError_t launch_ste_dx(const uint16_t* dy, int M, int N, const uint8_t* qT, co
     };
     const int64_t t512 = tiles(128, 512), t256 = tiles(128, 256);
     if (t512 >= kCUs / 2 && 2 * ((t512 + kCUs - 1) / kCUs) <= (t256 + kCUs - 1) / kCUs)
-        return launch_ste_tile<128, 512, 1, 8, 3, 2>(dy, M, N, qT, gamma, K, dx, stream);
-    return launch_ste_tile<128, 256, 1, 4, 3, 2>(dy, M, N, qT, gamma, K, dx, stream);
+        return launch_ste_tile<128, 512, 1, 8, 128, 3, 2>(dy, M, N, qT, gamma, K, dx, stream);
+    return launch_ste_tile<128, 256, 1, 4, 64, 3, 2>(dy, M, N, qT, gamma, K, dx, stream);
 }
 
 }  // namespace bl

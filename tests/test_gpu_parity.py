@@ -712,10 +712,12 @@ def test_ste_backward_dx_parity(M, N, K):
 
 
 def test_ste_backward_dx_large_tiles_ragged():
-    """128 x 512 output tiles (2000 x 4800 is 160 of them), ragged in tokens,
-    input features and the reduction (N = 200: the last 64-wide step holds 8
-    valid n); oracle on sampled token rows, all K."""
-    M, N, K = 2000, 200, 4800
+    """128 x 512 output tiles (2000 x 4800 is 160 of them, 128-wide reduction
+    stages), ragged in tokens, input features and the reduction: N = 264
+    leaves 8 valid n in the third stage, and the second 16 bytes of that
+    stage's codes lie past the 80-byte rows; oracle on sampled token rows,
+    all K."""
+    M, N, K = 2000, 264, 4800
     rng = np.random.default_rng(97)
     q = rand_codes(rng, N, K)
     g = np.float32(0.0211)
