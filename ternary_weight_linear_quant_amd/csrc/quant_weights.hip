@@ -15,40 +15,92 @@
 
 namespace bl {
 
-// R[n] = sum_k |W[n][k]|, fp64, k increasing. One thread per row.
-__global__ __launch_bounds__(64) void k_absmean_rowsum(
+// R[n] = sum_k |W[n][k]|, fp64, k increasing. A workgroup takes 32 rows and
+// walks K in tiles of 256 columns: all 256 threads load a tile with
+// coalesced 16-byte loads (64 lanes per 1 KB row segment) into LDS (rows
+// padded to 260 floats, so the 32 readers of one column offset hit distinct
+// banks), then thread r runs row r's chain over the tile while the next
+// tile's loads are in flight.
+constexpr int kRsRows = 32, kRsTK = 256, kRsThreads = 256;
+constexpr int kRsPitch = kRsTK + 4;
+constexpr int kRsLoads = kRsRows * kRsTK / 4 / kRsThreads;  // float4 per thread per tile
+
+__global__ __launch_bounds__(kRsThreads) void k_absmean_rowsum(
     const float* __restrict__ W, int64_t N, int64_t K, double* __restrict__ R) {
-    const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (n >= N) return;
-    const float4* row = reinterpret_cast<const float4*>(W + n * K);
-    const int64_t K4 = K / 4;
+    __shared__ __align__(16) float tile[kRsRows * kRsPitch];
+    const int tid = threadIdx.x;
+    const int64_t n0 = (int64_t)blockIdx.x * kRsRows;
+    float4 reg[kRsLoads];
+    auto load = [&](int64_t k0) {
+#pragma unroll
+        for (int i = 0; i < kRsLoads; ++i) {
+            const int f = tid + kRsThreads * i;
+            const int r = f / (kRsTK / 4), c4 = f % (kRsTK / 4);
+            const int64_t row = n0 + r, col = k0 + 4 * c4;
+            reg[i] = (row < N && col < K)
+                         ? *reinterpret_cast<const float4*>(W + row * K + col)
+                         : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+    };
     double s = 0.0;
+    load(0);
+    for (int64_t k0 = 0; k0 < K; k0 += kRsTK) {
+#pragma unroll
+        for (int i = 0; i < kRsLoads; ++i) {
+            const int f = tid + kRsThreads * i;
+            const int r = f / (kRsTK / 4), c4 = f % (kRsTK / 4);
+            *reinterpret_cast<float4*>(&tile[r * kRsPitch + 4 * c4]) = reg[i];
+        }
+        __syncthreads();
+        if (k0 + kRsTK < K) load(k0 + kRsTK);
+        if (tid < kRsRows) {
+            // K % 64 == 0: the tile holds a whole number of float4.
+            const int cnt4 = (int)((K - k0 < kRsTK ? K - k0 : kRsTK) / 4);
+            const float* row = &tile[tid * kRsPitch];
 #pragma unroll 8
-    for (int64_t j = 0; j < K4; ++j) {
-        const float4 v = row[j];
-        s += (double)fabsf(v.x);
-        s += (double)fabsf(v.y);
-        s += (double)fabsf(v.z);
-        s += (double)fabsf(v.w);
+            for (int c = 0; c < cnt4; ++c) {
+                const float4 v = *reinterpret_cast<const float4*>(row + 4 * c);
+                s += (double)fabsf(v.x);
+                s += (double)fabsf(v.y);
+                s += (double)fabsf(v.z);
+                s += (double)fabsf(v.w);
+            }
+        }
+        __syncthreads();
     }
-    R[n] = s;
+    if (tid < kRsRows && n0 + tid < N) R[n0 + tid] = s;
 }
 
 // gamma = (float)((sum_n R[n], n increasing) / (N*K)). The row sums are
 // staged through LDS by the whole block in coalesced tiles; thread 0 adds
-// them in order (the chain, not the loads, is then the critical path).
+// them in order, reading each batch of 16 from LDS while it adds the
+// previous one. The last batch of a tile is padded with +0.0, which leaves
+// the (non-negative) running sum unchanged bit for bit.
 __global__ __launch_bounds__(256) void k_gamma_finalize(
     const double* __restrict__ R, int64_t N, int64_t K, float* __restrict__ gamma) {
-    constexpr int kTile = 2048;
+    constexpr int kTile = 4096, kB = 16;
     __shared__ double tile[kTile];
     double s = 0.0;
     for (int64_t base = 0; base < N; base += kTile) {
         const int cnt = (int)((N - base) < kTile ? (N - base) : kTile);
-        for (int i = threadIdx.x; i < cnt; i += blockDim.x) tile[i] = R[base + i];
+        const int padded = (cnt + kB - 1) / kB * kB;
+        for (int i = threadIdx.x; i < padded; i += blockDim.x)
+            tile[i] = i < cnt ? R[base + i] : 0.0;
         __syncthreads();
         if (threadIdx.x == 0) {
-#pragma unroll 8
-            for (int i = 0; i < cnt; ++i) s += tile[i];
+            double cur[kB];
+#pragma unroll
+            for (int j = 0; j < kB; ++j) cur[j] = tile[j];
+            for (int i = 0; i < padded; i += kB) {
+                double nxt[kB];
+                const int nb = i + kB < padded ? i + kB : i;  // last batch: harmless re-read
+#pragma unroll
+                for (int j = 0; j < kB; ++j) nxt[j] = tile[nb + j];
+#pragma unroll
+                for (int j = 0; j < kB; ++j) s += cur[j];
+#pragma unroll
+                for (int j = 0; j < kB; ++j) cur[j] = nxt[j];
+            }
         }
         __syncthreads();
     }
@@ -87,9 +139,8 @@ __global__ __launch_bounds__(256) void k_ternarize_pack(
 hipError_t launch_quantize_weights(const float* W, int64_t N, int64_t K, uint32_t* packed,
                                    float* gamma, double* rowsums, hipStream_t stream) {
     {
-        const int threads = 64;
-        const int64_t blocks = (N + threads - 1) / threads;
-        hipLaunchKernelGGL(k_absmean_rowsum, dim3((unsigned)blocks), dim3(threads), 0, stream,
+        const int64_t blocks = (N + kRsRows - 1) / kRsRows;
+        hipLaunchKernelGGL(k_absmean_rowsum, dim3((unsigned)blocks), dim3(kRsThreads), 0, stream,
                            W, N, K, rowsums);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -167,9 +218,8 @@ hipError_t launch_quantize_weights_binary(const float* W, int64_t N, int64_t K, 
                                           int64_t row_words, float* gamma, double* rowsums,
                                           hipStream_t stream) {
     {
-        const int threads = 64;
-        const int64_t blocks = (N + threads - 1) / threads;
-        hipLaunchKernelGGL(k_absmean_rowsum, dim3((unsigned)blocks), dim3(threads), 0, stream,
+        const int64_t blocks = (N + kRsRows - 1) / kRsRows;
+        hipLaunchKernelGGL(k_absmean_rowsum, dim3((unsigned)blocks), dim3(kRsThreads), 0, stream,
                            W, N, K, rowsums);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
