@@ -185,6 +185,21 @@ int bl_bitlinear_pair(const int8_t* x_q, const float* x_scale, int64_t M, int64_
 int bl_relu2_glu_quant(const float* gate, const float* up, int64_t M, int64_t K, int8_t* h_q,
                        float* h_scale, void* stream);
 
+/* As bl_relu2_glu_quant with the sub-layer RMSNorm (subln) between the
+ * gating and the quantisation: h_q / h_scale are exactly what
+ * bl_quantize_acts(h, gain, rms_eps) computes from h = bf16_rne(relu(gate)^2
+ * * up): the codes of z = h * gain (bit-exact), and h_scale = a / (127 *
+ * rms) with rms = sqrt(sum h^2 / K + rms_eps), sum h^2 in fp64 in an order
+ * of the kernel's choosing (h_scale within 1e-6 relative of any order).
+ * gain: bf16 [K] (raw bits), 16-byte aligned, not null; rms_eps > 0.
+ * Source: inferownia.pl page above, section "Zrób to sam — Microsoft
+ * wypuścił konkretny model": the 2B4T model normalises with subln; the
+ * norm's place (on the FFN's gated hidden state, before its quantisation for
+ * the down projection) is this library's reading. */
+int bl_relu2_glu_subln_quant(const float* gate, const float* up, int64_t M, int64_t K,
+                             const uint16_t* gain, float rms_eps, int8_t* h_q, float* h_scale,
+                             void* stream);
+
 /* Bytes of the workspace bl_ffn_relu2 needs for these shapes (0 if the
  * shapes are invalid). Host-only. */
 size_t bl_ffn_relu2_workspace_bytes(int64_t M, int64_t K, int64_t N_ff);
@@ -213,6 +228,20 @@ int bl_ffn_relu2(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate
                  const float* gamma_gate, const uint32_t* W_up, const float* gamma_up,
                  int64_t N_ff, const uint32_t* W_down, const float* gamma_down, float* y,
                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* bl_ffn_relu2 with the sub-layer RMSNorm (subln) on h before its
+ * quantisation for the down projection:
+ *   y = BitLinear(quantize_acts(h, subln_gain, subln_eps), W_down)
+ * with h_q bit-exact and h_scale within 1e-6 relative of
+ * bl_relu2_glu_subln_quant's (the fp64 sum of squares is taken in another
+ * order when the step runs in two launches). subln_gain: bf16 [N_ff] (raw
+ * bits), 16-byte aligned, not null; subln_eps > 0. Workspace, shapes and
+ * launches as bl_ffn_relu2. Source: as bl_relu2_glu_subln_quant. */
+int bl_ffn_relu2_subln(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate,
+                       const float* gamma_gate, const uint32_t* W_up, const float* gamma_up,
+                       int64_t N_ff, const uint32_t* W_down, const float* gamma_down,
+                       const uint16_t* subln_gain, float subln_eps, float* y, void* workspace,
+                       size_t workspace_bytes, void* stream);
 
 /* ---- Other weight formats (decode) ----------------------------------------
  * Two storage formats besides the 2-bit one, each with its own decode

@@ -40,8 +40,11 @@ _SIGNATURES = {
     "bl_relu2_glu": ([_P, _P, _I, _P, _P], ctypes.c_int),
     "bl_bitlinear_pair": ([_P, _P, _I, _I, _P, _P, _I, _P, _P, _P, _I, _P, _P], ctypes.c_int),
     "bl_relu2_glu_quant": ([_P, _P, _I, _I, _P, _P, _P], ctypes.c_int),
+    "bl_relu2_glu_subln_quant": ([_P, _P, _I, _I, _P, _F, _P, _P, _P], ctypes.c_int),
     "bl_ffn_relu2_workspace_bytes": ([_I, _I, _I], _S),
     "bl_ffn_relu2": ([_P, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _S, _P], ctypes.c_int),
+    "bl_ffn_relu2_subln": ([_P, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _F, _P, _P, _S, _P],
+                           ctypes.c_int),
     "bl_packed_bytes_binary": ([_I, _I], _S),
     "bl_packed_bytes_base3": ([_I, _I], _S),
     "bl_quantize_weights_binary": ([_P, _I, _I, _P, _P, _P, _S, _P], ctypes.c_int),
@@ -221,8 +224,10 @@ def bitlinear_pair(x_q, x_scale, W1, gamma1, W2, gamma2, out=None):
     return y1, y2
 
 
-def relu2_glu_quant(gate, up, out=None):
-    """(h_q int8, h_scale fp32) of h = bf16(relu(gate)^2 * up). Calls bl_relu2_glu_quant."""
+def relu2_glu_quant(gate, up, out=None, subln_gain=None, subln_eps: float = 1e-5):
+    """(h_q int8, h_scale fp32) of h = bf16(relu(gate)^2 * up). Calls
+    bl_relu2_glu_quant, or bl_relu2_glu_subln_quant when subln_gain (bf16
+    [K]) is given: the sub-layer RMSNorm before the quantisation."""
     torch = _torch()
     M, K = gate.shape
     if gate.shape != up.shape:
@@ -232,10 +237,16 @@ def relu2_glu_quant(gate, up, out=None):
         hs = torch.empty(M, dtype=torch.float32, device=gate.device)
     else:
         hq, hs = out
-    _check(lib().bl_relu2_glu_quant(_dev(gate, torch.float32, "gate"), _dev(up, torch.float32, "up"),
-                                    M, K, _dev(hq, torch.int8, "h_q"),
-                                    _dev(hs, torch.float32, "h_scale"), _stream_ptr(gate)),
-           "bl_relu2_glu_quant")
+    args = (_dev(gate, torch.float32, "gate"), _dev(up, torch.float32, "up"), M, K)
+    outs = (_dev(hq, torch.int8, "h_q"), _dev(hs, torch.float32, "h_scale"), _stream_ptr(gate))
+    if subln_gain is None:
+        _check(lib().bl_relu2_glu_quant(*args, *outs), "bl_relu2_glu_quant")
+    else:
+        if subln_gain.dtype == torch.int16:
+            subln_gain = subln_gain.view(torch.bfloat16)
+        _check(lib().bl_relu2_glu_subln_quant(*args, _dev(subln_gain, torch.bfloat16, "gain"),
+                                              float(subln_eps), *outs),
+               "bl_relu2_glu_subln_quant")
     return hq, hs
 
 
@@ -249,8 +260,10 @@ def ffn_relu2_workspace(M: int, K: int, N_ff: int, device=None):
 
 
 def ffn_relu2(x, W_gate, gamma_gate, W_up, gamma_up, W_down, gamma_down, workspace=None,
-              out=None):
-    """y fp32 [M][K] of one 2B4T-style FFN step on bf16 x. Calls bl_ffn_relu2."""
+              out=None, subln_gain=None, subln_eps: float = 1e-5):
+    """y fp32 [M][K] of one 2B4T-style FFN step on bf16 x. Calls bl_ffn_relu2,
+    or bl_ffn_relu2_subln when subln_gain (bf16 [N_ff]) is given: the
+    sub-layer RMSNorm on the gated hidden state before the down projection."""
     torch = _torch()
     if x.dtype == torch.int16:
         x = x.view(torch.bfloat16)
@@ -262,16 +275,19 @@ def ffn_relu2(x, W_gate, gamma_gate, W_up, gamma_up, W_down, gamma_down, workspa
     if workspace is None:
         workspace = ffn_relu2_workspace(M, K, N_ff, x.device)
     y = torch.empty((M, K), dtype=torch.float32, device=x.device) if out is None else out
-    _check(lib().bl_ffn_relu2(_dev(x, torch.bfloat16, "x"), M, K,
-                              _dev(W_gate, torch.int32, "W_gate"),
-                              _dev(gamma_gate, torch.float32, "gamma_gate"),
-                              _dev(W_up, torch.int32, "W_up"),
-                              _dev(gamma_up, torch.float32, "gamma_up"), N_ff,
-                              _dev(W_down, torch.int32, "W_down"),
-                              _dev(gamma_down, torch.float32, "gamma_down"),
-                              _dev(y, torch.float32, "y"),
-                              _dev(workspace, torch.uint8, "workspace"),
-                              workspace.numel(), _stream_ptr(x)), "bl_ffn_relu2")
+    head = (_dev(x, torch.bfloat16, "x"), M, K,
+            _dev(W_gate, torch.int32, "W_gate"), _dev(gamma_gate, torch.float32, "gamma_gate"),
+            _dev(W_up, torch.int32, "W_up"), _dev(gamma_up, torch.float32, "gamma_up"), N_ff,
+            _dev(W_down, torch.int32, "W_down"), _dev(gamma_down, torch.float32, "gamma_down"))
+    tail = (_dev(y, torch.float32, "y"), _dev(workspace, torch.uint8, "workspace"),
+            workspace.numel(), _stream_ptr(x))
+    if subln_gain is None:
+        _check(lib().bl_ffn_relu2(*head, *tail), "bl_ffn_relu2")
+    else:
+        if subln_gain.dtype == torch.int16:
+            subln_gain = subln_gain.view(torch.bfloat16)
+        _check(lib().bl_ffn_relu2_subln(*head, _dev(subln_gain, torch.bfloat16, "subln_gain"),
+                                        float(subln_eps), *tail), "bl_ffn_relu2_subln")
     return y
 
 

@@ -185,10 +185,15 @@ size_t bl_ffn_relu2_workspace_bytes(int64_t M, int64_t K, int64_t N_ff) {
     return ffn_layout(M, K, N_ff).total;
 }
 
-int bl_ffn_relu2(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate,
-                 const float* gamma_gate, const uint32_t* W_up, const float* gamma_up,
-                 int64_t N_ff, const uint32_t* W_down, const float* gamma_down, float* y,
-                 void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// One FFN step; subln_gain (bf16 [N_ff]) null for none.
+int ffn_step(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate,
+             const float* gamma_gate, const uint32_t* W_up, const float* gamma_up, int64_t N_ff,
+             const uint32_t* W_down, const float* gamma_down, const uint16_t* subln_gain,
+             float subln_eps, float* y, void* workspace, size_t workspace_bytes, void* stream) {
     if (!x || !W_gate || !gamma_gate || !W_up || !gamma_up || !W_down || !gamma_down || !y ||
         !workspace)
         return BL_ERR_INVALID_ARG;
@@ -196,6 +201,7 @@ int bl_ffn_relu2(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate
     if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(W_down) ||
         !aligned16(y) || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return BL_ERR_INVALID_ARG;
+    if (subln_gain && (!aligned16(subln_gain) || !(subln_eps > 0.0f))) return BL_ERR_INVALID_ARG;
     const FfnWorkspace L = ffn_layout(M, K, N_ff);
     if (workspace_bytes < L.total) return BL_ERR_INVALID_ARG;
     if (int s = device_status()) return s;
@@ -205,8 +211,8 @@ int bl_ffn_relu2(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate
     if (bl::ffn_fused_supported(M, K, N_ff))
         return hip_status(bl::launch_ffn_fused(x, (int)M, (int)K, W_gate, gamma_gate, W_up,
                                                gamma_up, (int)N_ff, W_down, gamma_down, h, y,
-                                               st));
-    // Unfused sequence: act quant -> gate/up -> gating + act quant -> down.
+                                               subln_gain, subln_eps, st));
+    // Unfused sequence: act quant -> gate/up -> gating (+ norm) + act quant -> down.
     auto* xq = reinterpret_cast<int8_t*>(ws + L.xq);
     auto* xs = reinterpret_cast<float*>(ws + L.xs);
     auto* yg = reinterpret_cast<float*>(ws + L.yg);
@@ -225,7 +231,8 @@ int bl_ffn_relu2(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate
                 e = bl::launch_gemm(xq, xs, m, k, W_up, gamma_up, n, yu, nullptr, st);
         }
     }
-    if (e == hipSuccess) e = bl::launch_relu2_glu_quant(yg, yu, M, N_ff, hq, hs, st);
+    if (e == hipSuccess)
+        e = bl::launch_relu2_glu_quant(yg, yu, M, N_ff, subln_gain, subln_eps, hq, hs, st);
     if (e == hipSuccess) {
         if (bl::gemv_supported(M, N_ff))
             e = bl::launch_gemv(hq, hs, m, n, W_down, gamma_down, k, y, nullptr, st);
@@ -235,13 +242,49 @@ int bl_ffn_relu2(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate
     return hip_status(e);
 }
 
-int bl_relu2_glu_quant(const float* gate, const float* up, int64_t M, int64_t K, int8_t* h_q,
-                       float* h_scale, void* stream) {
+int glu_quant(const float* gate, const float* up, int64_t M, int64_t K, const uint16_t* gain,
+              float rms_eps, int8_t* h_q, float* h_scale, void* stream) {
     if (!gate || !up || !h_q || !h_scale) return BL_ERR_INVALID_ARG;
     if (!shape_ok(M, K)) return BL_ERR_INVALID_ARG;
     if (!aligned16(gate) || !aligned16(up) || !aligned16(h_q)) return BL_ERR_INVALID_ARG;
+    if (gain && (!aligned16(gain) || !(rms_eps > 0.0f))) return BL_ERR_INVALID_ARG;
     if (int s = device_status()) return s;
-    return hip_status(bl::launch_relu2_glu_quant(gate, up, M, K, h_q, h_scale, as_stream(stream)));
+    return hip_status(
+        bl::launch_relu2_glu_quant(gate, up, M, K, gain, rms_eps, h_q, h_scale, as_stream(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int bl_ffn_relu2(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate,
+                 const float* gamma_gate, const uint32_t* W_up, const float* gamma_up,
+                 int64_t N_ff, const uint32_t* W_down, const float* gamma_down, float* y,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+    return ffn_step(x, M, K, W_gate, gamma_gate, W_up, gamma_up, N_ff, W_down, gamma_down,
+                    nullptr, 0.0f, y, workspace, workspace_bytes, stream);
+}
+
+int bl_ffn_relu2_subln(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate,
+                       const float* gamma_gate, const uint32_t* W_up, const float* gamma_up,
+                       int64_t N_ff, const uint32_t* W_down, const float* gamma_down,
+                       const uint16_t* subln_gain, float subln_eps, float* y, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    if (!subln_gain) return BL_ERR_INVALID_ARG;
+    return ffn_step(x, M, K, W_gate, gamma_gate, W_up, gamma_up, N_ff, W_down, gamma_down,
+                    subln_gain, subln_eps, y, workspace, workspace_bytes, stream);
+}
+
+int bl_relu2_glu_quant(const float* gate, const float* up, int64_t M, int64_t K, int8_t* h_q,
+                       float* h_scale, void* stream) {
+    return glu_quant(gate, up, M, K, nullptr, 0.0f, h_q, h_scale, stream);
+}
+
+int bl_relu2_glu_subln_quant(const float* gate, const float* up, int64_t M, int64_t K,
+                             const uint16_t* gain, float rms_eps, int8_t* h_q, float* h_scale,
+                             void* stream) {
+    if (!gain) return BL_ERR_INVALID_ARG;
+    return glu_quant(gate, up, M, K, gain, rms_eps, h_q, h_scale, stream);
 }
 
 int bl_relu2_glu(const float* gate, const float* up, int64_t count, uint16_t* h, void* stream) {

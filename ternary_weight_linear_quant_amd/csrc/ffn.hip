@@ -53,11 +53,16 @@ __device__ __forceinline__ uint32_t relu2_gate_bits(float g, float u) {
     return f32_to_bf16_rne(sq * u);
 }
 
-template <bool GLU, int KS>
+// SUBLN (quantising launch B only): the sub-layer RMSNorm with gain `gain`
+// before the quantisation, as bl_quantize_acts(h, gain) computes it: codes
+// of z = h*g, scale a / (127 * rms(h)), sum h^2 in fp64.
+template <bool GLU, int KS, bool SUBLN>
 __global__ __launch_bounds__(64 * (GLU ? 2 : 1) * KS) void k_ffn_gemv(
     const uint16_t* __restrict__ xin, int M, int K, const uint32_t* __restrict__ W0,
     const float* __restrict__ g0, const uint32_t* __restrict__ W1,
-    const float* __restrict__ g1, int N, float* __restrict__ y, uint16_t* __restrict__ h) {
+    const float* __restrict__ g1, int N, float* __restrict__ y, uint16_t* __restrict__ h,
+    const uint16_t* __restrict__ gain, float rms_eps) {
+    static_assert(!(GLU && SUBLN), "the norm precedes the down projection only");
     constexpr int NW = (GLU ? 2 : 1) * KS;  // waves
     constexpr int NT = 64 * NW;             // threads
     constexpr int CACHE = kFfnCache * kFfnMinThreads / NT;
@@ -65,6 +70,7 @@ __global__ __launch_bounds__(64 * (GLU ? 2 : 1) * KS) void k_ffn_gemv(
     extern __shared__ __align__(16) uint8_t smem[];  // int8 activations, token-minor
     __shared__ v4i red[NW][kWave];
     __shared__ float s_amax[NW][16];
+    __shared__ double s_ss[SUBLN ? NW : 1][16];
     __shared__ float s_scale[16];
 
     const int tid = threadIdx.x;
@@ -86,6 +92,7 @@ __global__ __launch_bounds__(64 * (GLU ? 2 : 1) * KS) void k_ffn_gemv(
     const int U = M * (K / 16);
     const int mt = tid % M;
     uint4 xa[CACHE], xb[CACHE];
+    uint4 ga[SUBLN ? CACHE : 1], gb[SUBLN ? CACHE : 1];
 #pragma unroll
     for (int i = 0; i < CACHE; ++i) {
         const int u = tid + NT * i;
@@ -93,6 +100,11 @@ __global__ __launch_bounds__(64 * (GLU ? 2 : 1) * KS) void k_ffn_gemv(
             const uint4* src = reinterpret_cast<const uint4*>(xin + (size_t)mt * K + 16 * (u / M));
             xa[i] = src[0];
             xb[i] = src[1];
+            if constexpr (SUBLN) {
+                const uint4* gsrc = reinterpret_cast<const uint4*>(gain + 16 * (u / M));
+                ga[i] = gsrc[0];
+                gb[i] = gsrc[1];
+            }
         }
     }
     asm volatile("" ::: "memory");  // keep the activation loads first
@@ -103,32 +115,61 @@ __global__ __launch_bounds__(64 * (GLU ? 2 : 1) * KS) void k_ffn_gemv(
     for (int i = 0; i < kFfnR; ++i)
         wb[i] = *reinterpret_cast<const uint4*>(wrow + 16 * (ks + KS * min(i, nw - 1)));
 
-    // 3. Per-token absmax (exact, order-free) of the cached units.
+    // 3. Per-token absmax (exact, order-free) of the cached units (of h*g
+    //    under SUBLN, with sum h^2 beside it).
+    auto gain_of = [&](int i, int e) -> float {  // gain of value e (0..15) of unit i
+        const int c = SUBLN ? i : 0;
+        const uint32_t g8[8] = {ga[c].x, ga[c].y, ga[c].z, ga[c].w,
+                                gb[c].x, gb[c].y, gb[c].z, gb[c].w};
+        return bf16_to_f32((g8[e / 2] >> (16 * (e % 2))) & 0xFFFFu);
+    };
     float amax = 0.0f;
+    double ss = 0.0;
 #pragma unroll
     for (int i = 0; i < CACHE; ++i) {
         if (tid + NT * i < U) {
             const uint32_t w8[8] = {xa[i].x, xa[i].y, xa[i].z, xa[i].w,
                                     xb[i].x, xb[i].y, xb[i].z, xb[i].w};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                amax = fmaxf(amax, fabsf(bf16_to_f32(w8[e] & 0xFFFFu)));
-                amax = fmaxf(amax, fabsf(bf16_to_f32(w8[e] >> 16)));
+            for (int e = 0; e < 16; ++e) {
+                const float xf = bf16_to_f32((w8[e / 2] >> (16 * (e % 2))) & 0xFFFFu);
+                if constexpr (SUBLN) {
+                    amax = fmaxf(amax, fabsf(xf * gain_of(i, e)));
+                    ss += (double)xf * (double)xf;
+                } else {
+                    amax = fmaxf(amax, fabsf(xf));
+                }
             }
         }
     }
     // Lanes with equal lane % M hold the same token.
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1)
-        if (o >= M) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
-    if (lane < M) s_amax[wave][lane] = amax;
+        if (o >= M) {
+            amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+            if constexpr (SUBLN) ss += __shfl_xor(ss, o, kWave);
+        }
+    if (lane < M) {
+        s_amax[wave][lane] = amax;
+        if constexpr (SUBLN) s_ss[wave][lane] = ss;
+    }
     lds_barrier();
     float a = s_amax[0][mt];
 #pragma unroll
     for (int w = 1; w < NW; ++w) a = fmaxf(a, s_amax[w][mt]);
     a = a > 1e-5f ? a : 1e-5f;
     const float inv = 127.0f / a;
-    if (tid < M) s_scale[tid] = a / 127.0f;
+    if (tid < M) {
+        if constexpr (SUBLN) {
+            double st = s_ss[0][tid];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) st += s_ss[w][tid];
+            const double rms = sqrt(st / (double)K + (double)rms_eps);
+            s_scale[tid] = (float)((double)a / (127.0 * rms));
+        } else {
+            s_scale[tid] = a / 127.0f;
+        }
+    }
 
     // 4. Codes into LDS slot u (chunk u / M of token u % M).
 #pragma unroll
@@ -140,7 +181,8 @@ __global__ __launch_bounds__(64 * (GLU ? 2 : 1) * KS) void k_ffn_gemv(
             uint32_t q[4] = {0, 0, 0, 0};
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const float z = bf16_to_f32((w8[e / 2] >> (16 * (e % 2))) & 0xFFFFu);
+                float z = bf16_to_f32((w8[e / 2] >> (16 * (e % 2))) & 0xFFFFu);
+                if constexpr (SUBLN) z = z * gain_of(i, e);
                 float t = __builtin_rintf(z * inv);
                 t = fminf(fmaxf(t, -127.0f), 127.0f);
                 q[e / 4] |= ((uint32_t)((int)t) & 0xFFu) << (8 * (e % 4));
@@ -248,23 +290,34 @@ bool ffn_fused_supported(int64_t M, int64_t K, int64_t N_ff) {
     return K / 256 >= kKsA && N_ff / 256 >= kKsBSmall;
 }
 
+namespace {
+
+template <int KS, bool SUBLN>
+void launch_ffn_down(const uint16_t* h, int M, int N_ff, const uint32_t* Wd, const float* gd,
+                     int K, float* y, const uint16_t* gain, float rms_eps, hipStream_t stream) {
+    hipLaunchKernelGGL((k_ffn_gemv<false, KS, SUBLN>), dim3((K + 15) / 16), dim3(64 * KS),
+                       (size_t)M * N_ff, stream, h, M, N_ff, Wd, gd, (const uint32_t*)nullptr,
+                       (const float*)nullptr, K, y, (uint16_t*)nullptr, gain, rms_eps);
+}
+
+}  // namespace
+
 hipError_t launch_ffn_fused(const uint16_t* x, int M, int K, const uint32_t* Wg,
                             const float* gg, const uint32_t* Wu, const float* gu, int N_ff,
                             const uint32_t* Wd, const float* gd, uint16_t* h, float* y,
-                            hipStream_t stream) {
-    hipLaunchKernelGGL((k_ffn_gemv<true, kKsA>), dim3((N_ff + 15) / 16), dim3(64 * 2 * kKsA),
-                       (size_t)M * K, stream, x, M, K, Wg, gg, Wu, gu, N_ff, (float*)nullptr, h);
+                            const uint16_t* subln_gain, float subln_eps, hipStream_t stream) {
+    hipLaunchKernelGGL((k_ffn_gemv<true, kKsA, false>), dim3((N_ff + 15) / 16),
+                       dim3(64 * 2 * kKsA), (size_t)M * K, stream, x, M, K, Wg, gg, Wu, gu, N_ff,
+                       (float*)nullptr, h, (const uint16_t*)nullptr, 0.0f);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (N_ff / 256 >= kKsB) {
-        hipLaunchKernelGGL((k_ffn_gemv<false, kKsB>), dim3((K + 15) / 16), dim3(64 * kKsB),
-                           (size_t)M * N_ff, stream, h, M, N_ff, Wd, gd, (const uint32_t*)nullptr,
-                           (const float*)nullptr, K, y, (uint16_t*)nullptr);
+    const bool big = N_ff / 256 >= kKsB;
+    if (subln_gain) {
+        if (big) launch_ffn_down<kKsB, true>(h, M, N_ff, Wd, gd, K, y, subln_gain, subln_eps, stream);
+        else launch_ffn_down<kKsBSmall, true>(h, M, N_ff, Wd, gd, K, y, subln_gain, subln_eps, stream);
     } else {
-        hipLaunchKernelGGL((k_ffn_gemv<false, kKsBSmall>), dim3((K + 15) / 16),
-                           dim3(64 * kKsBSmall), (size_t)M * N_ff, stream, h, M, N_ff, Wd, gd,
-                           (const uint32_t*)nullptr, (const float*)nullptr, K, y,
-                           (uint16_t*)nullptr);
+        if (big) launch_ffn_down<kKsB, false>(h, M, N_ff, Wd, gd, K, y, nullptr, 0.0f, stream);
+        else launch_ffn_down<kKsBSmall, false>(h, M, N_ff, Wd, gd, K, y, nullptr, 0.0f, stream);
     }
     return hipGetLastError();
 }

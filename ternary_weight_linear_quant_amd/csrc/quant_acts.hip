@@ -157,26 +157,47 @@ __device__ __forceinline__ uint2 relu2_gate4(const float4 g, const float4 u) {
 
 // Squared-ReLU gating fused with per-token absmax quantisation of its bf16
 // result: identical to bl_relu2_glu followed by bl_quantize_acts (plain).
+// SUBLN: the sub-layer RMSNorm with gain g between the gating and the
+// quantisation, as bl_quantize_acts(h, g) computes it: codes of z = h*g,
+// scale a / (127 * rms(h)) with sum h^2 in fp64.
 constexpr int kGluCache = 12;  // 4-element vectors cached per thread (K <= 12288)
 
+template <bool SUBLN>
 __global__ __launch_bounds__(kActThreads) void k_relu2_glu_quant(
     const float* __restrict__ gate, const float* __restrict__ up, int64_t K,
-    int8_t* __restrict__ hq, float* __restrict__ scale) {
+    const uint16_t* __restrict__ gain, float rms_eps, int8_t* __restrict__ hq,
+    float* __restrict__ scale) {
     __shared__ float s_max[kActThreads / kWave];
+    __shared__ double s_ss[kActThreads / kWave];
     const int64_t m = blockIdx.x;
     const float4* grow = reinterpret_cast<const float4*>(gate + m * K);
     const float4* urow = reinterpret_cast<const float4*>(up + m * K);
+    const uint2* gnv = reinterpret_cast<const uint2*>(gain);  // 4 bf16 per vector
     const int tid = threadIdx.x;
     const int nvec = (int)(K / 4);
     const bool cached = nvec <= kGluCache * kActThreads;
 
     uint2 ch[kGluCache];
     float amax = 0.0f;
-    auto absmax2 = [&](const uint2 h) {
-        amax = fmaxf(amax, fabsf(bf16_to_f32(h.x & 0xFFFFu)));
-        amax = fmaxf(amax, fabsf(bf16_to_f32(h.x >> 16)));
-        amax = fmaxf(amax, fabsf(bf16_to_f32(h.y & 0xFFFFu)));
-        amax = fmaxf(amax, fabsf(bf16_to_f32(h.y >> 16)));
+    double ss = 0.0;
+    auto scan = [&](int v, const uint2 h) {
+        const uint32_t hw[2] = {h.x, h.y};
+        uint32_t gw[2] = {0u, 0u};
+        if (SUBLN) {
+            const uint2 gv = gnv[v];
+            gw[0] = gv.x;
+            gw[1] = gv.y;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float hf = bf16_to_f32((hw[e / 2] >> (16 * (e % 2))) & 0xFFFFu);
+            float z = hf;
+            if (SUBLN) {
+                z = hf * bf16_to_f32((gw[e / 2] >> (16 * (e % 2))) & 0xFFFFu);
+                ss += (double)hf * (double)hf;
+            }
+            amax = fmaxf(amax, fabsf(z));
+        }
     };
     if (cached) {
         float4 cg[kGluCache], cu[kGluCache];
@@ -190,25 +211,35 @@ __global__ __launch_bounds__(kActThreads) void k_relu2_glu_quant(
         }
 #pragma unroll
         for (int j = 0; j < kGluCache; ++j) {
-            if (tid + kActThreads * j < nvec) {
+            const int v = tid + kActThreads * j;
+            if (v < nvec) {
                 ch[j] = relu2_gate4(cg[j], cu[j]);
-                absmax2(ch[j]);
+                scan(v, ch[j]);
             }
         }
     } else {
-        for (int v = tid; v < nvec; v += kActThreads) absmax2(relu2_gate4(grow[v], urow[v]));
+        for (int v = tid; v < nvec; v += kActThreads) scan(v, relu2_gate4(grow[v], urow[v]));
     }
     amax = block_reduce(amax, s_max, true);
+    double ss_tot = 0.0;
+    if (SUBLN) ss_tot = block_reduce(ss, s_ss, false);
     const float a = amax > 1e-5f ? amax : 1e-5f;
     const float inv = 127.0f / a;
 
     uint32_t* out = reinterpret_cast<uint32_t*>(hq + m * K);
     auto emit = [&](int v, const uint2 h) {
         const uint32_t hw[2] = {h.x, h.y};
+        uint32_t gw[2] = {0u, 0u};
+        if (SUBLN) {
+            const uint2 gv = gnv[v];
+            gw[0] = gv.x;
+            gw[1] = gv.y;
+        }
         uint32_t packed = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float z = bf16_to_f32((hw[e / 2] >> (16 * (e % 2))) & 0xFFFFu);
+            float z = bf16_to_f32((hw[e / 2] >> (16 * (e % 2))) & 0xFFFFu);
+            if (SUBLN) z = z * bf16_to_f32((gw[e / 2] >> (16 * (e % 2))) & 0xFFFFu);
             float t = __builtin_rintf(z * inv);
             t = fminf(fmaxf(t, -127.0f), 127.0f);
             packed |= ((uint32_t)((int)t) & 0xFFu) << (8 * e);
@@ -224,7 +255,14 @@ __global__ __launch_bounds__(kActThreads) void k_relu2_glu_quant(
     } else {
         for (int v = tid; v < nvec; v += kActThreads) emit(v, relu2_gate4(grow[v], urow[v]));
     }
-    if (tid == 0) scale[m] = a / 127.0f;
+    if (tid == 0) {
+        if (SUBLN) {
+            const double rms = sqrt(ss_tot / (double)K + (double)rms_eps);
+            scale[m] = (float)((double)a / (127.0 * rms));
+        } else {
+            scale[m] = a / 127.0f;
+        }
+    }
 }
 
 hipError_t launch_quantize_acts(const uint16_t* x, int64_t M, int64_t K, const uint16_t* gain,
@@ -239,9 +277,14 @@ hipError_t launch_quantize_acts(const uint16_t* x, int64_t M, int64_t K, const u
 }
 
 hipError_t launch_relu2_glu_quant(const float* gate, const float* up, int64_t M, int64_t K,
-                                  int8_t* hq, float* scale, hipStream_t stream) {
-    hipLaunchKernelGGL(k_relu2_glu_quant, dim3((unsigned)M), dim3(kActThreads), 0, stream, gate,
-                       up, K, hq, scale);
+                                  const uint16_t* gain, float rms_eps, int8_t* hq, float* scale,
+                                  hipStream_t stream) {
+    if (gain)
+        hipLaunchKernelGGL(k_relu2_glu_quant<true>, dim3((unsigned)M), dim3(kActThreads), 0,
+                           stream, gate, up, K, gain, rms_eps, hq, scale);
+    else
+        hipLaunchKernelGGL(k_relu2_glu_quant<false>, dim3((unsigned)M), dim3(kActThreads), 0,
+                           stream, gate, up, K, gain, rms_eps, hq, scale);
     return hipGetLastError();
 }
 

@@ -104,6 +104,11 @@ def test_invalid_arguments_rejected_before_launch(L):
     assert L.bl_relu2_glu_quant(A, A, 0, 64, A, A, None) == E
     assert L.bl_relu2_glu_quant(A, MIS, 1, 64, A, A, None) == E
     assert L.bl_relu2_glu_quant(A, A, 1, 64, A, None, None) == E
+    # glue with the sub-layer norm: the gain is required, aligned, eps > 0
+    assert L.bl_relu2_glu_subln_quant(A, A, 1, 64, None, 1e-5, A, A, None) == E
+    assert L.bl_relu2_glu_subln_quant(A, A, 1, 64, MIS, 1e-5, A, A, None) == E
+    assert L.bl_relu2_glu_subln_quant(A, A, 1, 64, A, 0.0, A, A, None) == E
+    assert L.bl_relu2_glu_subln_quant(A, A, 1, 100, A, 1e-5, A, A, None) == E
     # fused FFN step
     WS = P(0x200000)  # 256-byte aligned
     need = L.bl_ffn_relu2_workspace_bytes(4, 2560, 6912)
@@ -114,6 +119,14 @@ def test_invalid_arguments_rejected_before_launch(L):
     assert L.bl_ffn_relu2(A, 4, 2560, A, A, None, A, 6912, A, A, A, WS, need, None) == E
     assert L.bl_ffn_relu2(A, 4, 2560, A, A, A, A, 6900, A, A, A, WS, need, None) == E
     assert L.bl_ffn_relu2(MIS, 4, 2560, A, A, A, A, 6912, A, A, A, WS, need, None) == E
+    assert L.bl_ffn_relu2_subln(A, 4, 2560, A, A, A, A, 6912, A, A, None, 1e-5, A, WS, need,
+                                None) == E
+    assert L.bl_ffn_relu2_subln(A, 4, 2560, A, A, A, A, 6912, A, A, MIS, 1e-5, A, WS, need,
+                                None) == E
+    assert L.bl_ffn_relu2_subln(A, 4, 2560, A, A, A, A, 6912, A, A, A, -1.0, A, WS, need,
+                                None) == E
+    assert L.bl_ffn_relu2_subln(A, 4, 2560, A, A, A, A, 6912, A, A, A, 1e-5, A, WS, need - 1,
+                                None) == E
     # pair
     assert L.bl_bitlinear_pair(A, A, 1, 64, A, A, 16, A, None, A, 16, A, None) == E
     assert L.bl_bitlinear_pair(A, A, 1, 64, A, A, 16, A, A, A, 0, A, None) == E
@@ -193,6 +206,9 @@ def test_no_device_status(L):
     assert L.bl_pack_ste_t(W, 16, 64, P(0x6000000), None) == D
     need = L.bl_ffn_relu2_workspace_bytes(1, 256, 1024)
     assert L.bl_ffn_relu2(A, 1, 256, A, A, A, A, 1024, A, A, A, P(0x200000), need, None) == D
+    assert L.bl_ffn_relu2_subln(A, 1, 256, A, A, A, A, 1024, A, A, A, 1e-5, A, P(0x200000),
+                                need, None) == D
+    assert L.bl_relu2_glu_subln_quant(A, A, 1, 64, A, 1e-5, A, A, None) == D
 
 
 def test_binding_fails_loudly_without_gpu():

@@ -566,6 +566,77 @@ def test_ffn_relu2_oracle_end_to_end_small():
     assert rel < 1e-3, rel
 
 
+# ---------------------------------------------- sub-layer norm (subln) ----
+# h -> RMSNorm(h; g) -> per-token quant before the down projection: the codes
+# are those of z = h*g (bit-exact); the scale a / (127 rms) has an fp64 sum
+# of squares whose order is the kernel's (within 1e-6 relative).
+
+@pytest.mark.parametrize("M,K", [(1, 6912), (4, 8640), (16, 6912), (3, 64), (300, 2560)])
+def test_relu2_glu_subln_quant_matches_oracle(M, K):
+    g, u = wl.ffn_hidden(63, K, M, K)
+    gain = wl.rms_gain(63, K, K)
+    hq, hs = bl.relu2_glu_quant(dev_f32(g), dev_f32(u), subln_gain=dev_bf16(gain))
+    hq_ref, hs_ref = oracle.act_quant(oracle.relu2_glu(g, u), gain)
+    assert np.array_equal(hq.cpu().numpy(), hq_ref)
+    hs = hs.cpu().numpy()
+    assert np.all(np.abs(hs - hs_ref) <= RTOL_SCALE_FUSED * hs_ref)
+    # The plain glue quant is unchanged by the option.
+    hq0, hs0 = bl.relu2_glu_quant(dev_f32(g), dev_f32(u))
+    hq0_ref, hs0_ref = oracle.act_quant(oracle.relu2_glu(g, u))
+    assert np.array_equal(hq0.cpu().numpy(), hq0_ref) and np.array_equal(hs0.cpu().numpy(), hs0_ref)
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 5, 16])
+@pytest.mark.parametrize("K,N_ff", [(2560, 6912), (512, 1024)])
+def test_ffn_relu2_subln_matches_unfused_sequence(M, K, N_ff):
+    """bl_ffn_relu2_subln (two launches for M <= 4, four otherwise) against
+    quantize_acts -> bitlinear(gate, up) -> relu2_glu -> quantize_acts(h,
+    gain) -> bitlinear(down): the int32 sums agree exactly (same codes), y
+    within 1e-6 relative (the scales' fp64 sums differ in order)."""
+    wid = 72
+    Wg, Wu = wl.weights(wid, 0, N_ff, K), wl.weights(wid, 1, N_ff, K)
+    Wd = wl.weights(wid, 2, K, N_ff)
+    (pg, gg), (pu, gu), (pd, gd) = gpu_weights(Wg), gpu_weights(Wu), gpu_weights(Wd)
+    x = dev_bf16(wl.activations(wid, M, M, K))
+    gain = dev_bf16(wl.rms_gain(wid, 0, N_ff))
+    y = bl.ffn_relu2(x, pg, gg, pu, gu, pd, gd, subln_gain=gain).cpu().numpy()
+    xq, xs = bl.quantize_acts(x)
+    h = bl.relu2_glu(bl.bitlinear(xq, xs, pg, gg), bl.bitlinear(xq, xs, pu, gu))
+    hq, hs = bl.quantize_acts(h, gain)
+    ref, acc = bl.bitlinear(hq, hs, pd, gd, return_acc=True)
+    # y / (scale * gamma) recovers the sums: compare them through the scale
+    # the reference used, to within the scale tolerance.
+    assert_close = np.abs(y.astype(np.float64) - ref.cpu().numpy()) <= \
+        2e-6 * np.abs(ref.cpu().numpy().astype(np.float64)) + 1e-30
+    assert assert_close.all(), float(np.abs(y - ref.cpu().numpy()).max())
+    # Without the gain the same call is the plain step (bit-exact as before).
+    y0 = bl.ffn_relu2(x, pg, gg, pu, gu, pd, gd)
+    hq0, hs0 = bl.quantize_acts(h)
+    assert torch.equal(y0.view(torch.int32), bl.bitlinear(hq0, hs0, pd, gd).view(torch.int32))
+
+
+def test_ffn_subln_down_input_against_oracle():
+    """Stage-wise against the oracle: from the GPU's own h, the oracle's
+    RMSNorm-fused quantisation gives the codes of the GPU's subln glue quant,
+    and the down projection of those codes matches the fused step."""
+    wid, M, K, N_ff = 73, 4, 512, 1024
+    Wg, Wu, Wd = wl.weights(wid, 0, N_ff, K), wl.weights(wid, 1, N_ff, K), wl.weights(wid, 2, K, N_ff)
+    (pg, gg), (pu, gu), (pd, gd) = gpu_weights(Wg), gpu_weights(Wu), gpu_weights(Wd)
+    x = dev_bf16(wl.activations(wid, 0, M, K))
+    gain_bits = wl.rms_gain(wid, 0, N_ff)
+    xq, xs = bl.quantize_acts(x)
+    yg, yu = bl.bitlinear(xq, xs, pg, gg), bl.bitlinear(xq, xs, pu, gu)
+    hq, hs = bl.relu2_glu_quant(yg, yu, subln_gain=dev_bf16(gain_bits))
+    h_bits = bl.relu2_glu(yg, yu).cpu().view(torch.int16).numpy().view(np.uint16)
+    hq_ref, hs_ref = oracle.act_quant(h_bits, gain_bits)
+    assert np.array_equal(hq.cpu().numpy(), hq_ref)
+    assert np.all(np.abs(hs.cpu().numpy() - hs_ref) <= RTOL_SCALE_FUSED * hs_ref)
+    _, g_d, q_d = oracle.quantize_weights(Wd)
+    y_ref, _ = oracle.bitlinear(hq_ref, hs_ref, q_d, g_d)
+    y = bl.ffn_relu2(x, pg, gg, pu, gu, pd, gd, subln_gain=dev_bf16(gain_bits)).cpu().numpy()
+    assert np.all(np.abs(y.astype(np.float64) - y_ref) <= 2e-6 * np.abs(y_ref.astype(np.float64)))
+
+
 # --------------------------------------------------------- calibration ----
 
 def test_calibration_kernels():
