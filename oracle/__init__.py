@@ -60,6 +60,7 @@ def _load():
         "oracle_addsub_matmul": ([P, I, I, P, I, P], None),
         "oracle_epilogue": ([P, I, I, P, F, P], None),
         "oracle_relu2_glu": ([P, P, I, P], None),
+        "oracle_swiglu": ([P, P, I, P], None),
         "oracle_binarize": ([P, I, I, P], None),
         "oracle_pack_binary": ([P, I, I, I, P], None),
         "oracle_unpack_binary": ([P, I, I, I, P], None),
@@ -195,6 +196,17 @@ def relu2_glu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
         raise ValueError("shape mismatch")
     h = np.empty(g.shape, np.uint16)
     _load().oracle_relu2_glu(_p(g), _p(u), g.size, _p(h))
+    return h
+
+
+def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """bf16 bits of fp32(silu(g)) * u, silu in fp64 (oracle_swiglu)."""
+    g = _c(g, np.float32)
+    u = _c(u, np.float32)
+    if g.shape != u.shape:
+        raise ValueError("shape mismatch")
+    h = np.empty(g.shape, np.uint16)
+    _load().oracle_swiglu(_p(g), _p(u), g.size, _p(h))
     return h
 
 

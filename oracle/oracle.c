@@ -282,3 +282,14 @@ void oracle_relu2_glu(const float* g, const float* u, int64_t count,
         h[i] = float_to_bf16_bits(sq * u[i]);
     }
 }
+
+/* SwiGLU gating: the SiLU (swish) of the gate, g * sigmoid(g), times up.
+ * The SiLU is evaluated in fp64 from the definition and rounded once to
+ * fp32; the product with up is one fp32 multiply, then bf16 rounding. */
+void oracle_swiglu(const float* g, const float* u, int64_t count, uint16_t* h) {
+    for (int64_t i = 0; i < count; ++i) {
+        double gd = (double)g[i];
+        float s = (float)(gd / (1.0 + exp(-gd)));
+        h[i] = float_to_bf16_bits(s * u[i]);
+    }
+}

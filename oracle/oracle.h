@@ -105,6 +105,11 @@ void oracle_epilogue(const int32_t* acc, int64_t M, int64_t N,
 void oracle_relu2_glu(const float* g, const float* u, int64_t count,
                       uint16_t* h);
 
+/* h = bf16_rne(fp32(silu(g)) * u), silu(g) = g / (1 + exp(-g)) in fp64
+ * (SwiGLU, comrad404.com «Метод: как устроен BitNet b1.58»: the b1.58
+ * variant keeps the LLaMA stack's SwiGLU). */
+void oracle_swiglu(const float* g, const float* u, int64_t count, uint16_t* h);
+
 /* Binary codes q = (W >= 0) ? +1 : -1.  [P3d] */
 void oracle_binarize(const float* W, int64_t N, int64_t K, int8_t* q);
 /* 1-bit packing of codes in {-1, +1}; rows of row_words words.  [P3d] */

@@ -475,6 +475,52 @@ def test_relu2_glu_gate_placement():
     assert (h == 0).all()
 
 
+# ------------------------------------------------------------- SwiGLU ----
+# SiLU(x) = x * sigmoid(x) = x / (1 + e^-x), times the up projection. Pins:
+# values that follow from the definition by hand, not a retyped formula.
+
+def test_swiglu_zero_gate_and_large_gates():
+    # SiLU(0) = 0; for x >= 20, 1 - sigmoid(x) < 2.1e-9 is below half an fp32
+    # ulp of 1, so SiLU(x) rounds to x and h = bf16(fp32(x * u)).
+    g = np.array([0.0, 0.0, 20.0, 24.0, 40.0, 96.0], np.float32)
+    u = np.array([1.5, -3.0, 1.0, -0.75, 0.3, 2.0], np.float32)
+    h = wl.bf16_bits_to_f32(oracle.swiglu(g, u))
+    assert h[0] == 0 and h[1] == 0
+    expect = wl.bf16_bits_to_f32(wl.f32_to_bf16_bits((g[2:] * u[2:]).astype(np.float32)))
+    assert np.array_equal(h[2:], expect)
+
+
+def test_swiglu_very_negative_gate_is_nearly_silent():
+    # SiLU(-30) = -30 e^-30 / (1 + e^-30) ~ -2.8e-12: the unit is almost off
+    # (a swapped sign in the exponent would give about -30).
+    h = wl.bf16_bits_to_f32(oracle.swiglu(np.array([-30.0], np.float32),
+                                          np.array([1.0], np.float32)))
+    assert h[0] < 0 and abs(h[0]) < 1e-11
+
+
+def test_swiglu_hand_value_at_one():
+    # SiLU(1) = 1 / (1 + 1/e) = 0.73105857863...; in [0.5, 1) bf16 steps are
+    # 1/256 and 0.73105857863 * 256 = 187.15, so h = 187/256.
+    h = wl.bf16_bits_to_f32(oracle.swiglu(np.array([1.0, -1.0], np.float32),
+                                          np.array([1.0, 1.0], np.float32)))
+    assert h[0] == np.float32(187 / 256)
+    # SiLU(-1) = SiLU(1) - 1 = -0.26894142137; bf16 steps of 1/512 in
+    # [0.25, 0.5): 0.26894142137 * 512 = 137.70 -> 138/512.
+    assert h[1] == np.float32(-138 / 512)
+
+
+def test_swiglu_minimum_and_monotone_branch():
+    # SiLU has one minimum, -0.27846454276 at x = -1.27846454276 (where
+    # 1 + x (1 - sigmoid(x)) = 0), and increases to its right.
+    x = np.linspace(-6.0, 6.0, 24001, dtype=np.float32)
+    h = wl.bf16_bits_to_f32(oracle.swiglu(x, np.ones_like(x))).astype(np.float64)
+    i = int(np.argmin(h))
+    assert abs(h[i] - (-0.27846454276)) <= 2.0 ** -9
+    assert abs(float(x[i]) - (-1.27846454276)) < 0.2   # flat bottom in bf16
+    right = h[x > -1.27]
+    assert np.all(np.diff(right) >= 0)
+
+
 # ----------------------------------------------- workload-sized sanity ----
 
 def test_workload_weight_statistics():
