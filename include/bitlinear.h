@@ -162,6 +162,22 @@ int bl_bitlinear_path(const int8_t* x_q, const float* x_scale, int64_t M,
 int bl_relu2_glu(const float* gate, const float* up, int64_t count,
                  uint16_t* h, void* stream);
 
+/* Gating kinds of a gated FFN, h = bf16_rne(act(gate) * up) in fp32:
+ *   BL_GLU_RELU2   act(g) = relu(g)^2 (the 2B4T FFN, as bl_relu2_glu);
+ *   BL_GLU_SWIGLU  act(g) = SiLU(g) = g / (1 + exp(-g)), exp from the device
+ *                  math library (within a few fp32 ulp of the exact SiLU, so
+ *                  h may differ from a correctly rounded evaluation by one
+ *                  bf16 step at rounding ties); a gate below about -88 gives
+ *                  -0. Source: comrad404.com page above, section «Метод: как
+ *                  устроен BitNet b1.58»: the b1.58 variant keeps the LLaMA
+ *                  stack's SwiGLU. */
+enum { BL_GLU_RELU2 = 0, BL_GLU_SWIGLU = 1 };
+
+/* h[i] = bf16_rne(act(gate[i]) * up[i]) for glu_kind (above); arguments as
+ * bl_relu2_glu; any other kind is BL_ERR_INVALID_ARG. */
+int bl_glu(const float* gate, const float* up, int64_t count, int glu_kind, uint16_t* h,
+           void* stream);
+
 /* Two BitLinear products that share one quantised input -- the gate and up
  * projections of an FFN -- in a single launch: y1 = BitLinear(x_q, W1) and
  * y2 = BitLinear(x_q, W2), each exactly as bl_bitlinear computes it (same
@@ -199,6 +215,14 @@ int bl_relu2_glu_quant(const float* gate, const float* up, int64_t M, int64_t K,
 int bl_relu2_glu_subln_quant(const float* gate, const float* up, int64_t M, int64_t K,
                              const uint16_t* gain, float rms_eps, int8_t* h_q, float* h_scale,
                              void* stream);
+
+/* The gating of glu_kind fused with the per-token quantisation of its
+ * result: h_q / h_scale exactly as bl_quantize_acts(bl_glu(gate, up, kind),
+ * gain, rms_eps) computes them. gain may be null (no norm: every bit as the
+ * two calls) or bf16 [K] (the sub-layer RMSNorm, rules of
+ * bl_relu2_glu_subln_quant). Other arguments as bl_relu2_glu_quant. */
+int bl_glu_quant(const float* gate, const float* up, int64_t M, int64_t K, int glu_kind,
+                 const uint16_t* gain, float rms_eps, int8_t* h_q, float* h_scale, void* stream);
 
 /* Bytes of the workspace bl_ffn_relu2 needs for these shapes (0 if the
  * shapes are invalid). Host-only. */
@@ -242,6 +266,18 @@ int bl_ffn_relu2_subln(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
                        int64_t N_ff, const uint32_t* W_down, const float* gamma_down,
                        const uint16_t* subln_gain, float subln_eps, float* y, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/* The gated FFN step for either gating kind, with or without the sub-layer
+ * norm: bl_ffn_relu2 (glu_kind BL_GLU_RELU2, subln_gain null),
+ * bl_ffn_relu2_subln (BL_GLU_RELU2, gain), or the same steps with SwiGLU
+ * gating (BL_GLU_SWIGLU). Every step is the single call's (bl_glu of the
+ * kind, bl_quantize_acts of h with or without the gain). Workspace, shapes
+ * and launches as bl_ffn_relu2; subln_gain rules of bl_ffn_relu2_subln. */
+int bl_ffn_step(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate,
+                const float* gamma_gate, const uint32_t* W_up, const float* gamma_up,
+                int64_t N_ff, const uint32_t* W_down, const float* gamma_down, int glu_kind,
+                const uint16_t* subln_gain, float subln_eps, float* y, void* workspace,
+                size_t workspace_bytes, void* stream);
 
 /* ---- Other weight formats (decode) ----------------------------------------
  * Two storage formats besides the 2-bit one, each with its own decode

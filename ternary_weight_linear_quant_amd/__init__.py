@@ -23,6 +23,8 @@ _LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
 _lib = None
 
 BL_OK, BL_ERR_INVALID_ARG, BL_ERR_HIP, BL_ERR_NO_DEVICE = 0, 1, 2, 3
+BL_GLU_RELU2, BL_GLU_SWIGLU = 0, 1
+_GLU_KINDS = {"relu2": BL_GLU_RELU2, "swiglu": BL_GLU_SWIGLU}
 
 # name -> (argtypes, restype); the same names and order as include/bitlinear.h
 _P, _I, _F, _S = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -38,13 +40,17 @@ _SIGNATURES = {
     "bl_bitlinear_path": ([_P, _P, _I, _I, _P, _P, _I, _P, _P, ctypes.c_int, _P],
                           ctypes.c_int),
     "bl_relu2_glu": ([_P, _P, _I, _P, _P], ctypes.c_int),
+    "bl_glu": ([_P, _P, _I, ctypes.c_int, _P, _P], ctypes.c_int),
     "bl_bitlinear_pair": ([_P, _P, _I, _I, _P, _P, _I, _P, _P, _P, _I, _P, _P], ctypes.c_int),
     "bl_relu2_glu_quant": ([_P, _P, _I, _I, _P, _P, _P], ctypes.c_int),
     "bl_relu2_glu_subln_quant": ([_P, _P, _I, _I, _P, _F, _P, _P, _P], ctypes.c_int),
+    "bl_glu_quant": ([_P, _P, _I, _I, ctypes.c_int, _P, _F, _P, _P, _P], ctypes.c_int),
     "bl_ffn_relu2_workspace_bytes": ([_I, _I, _I], _S),
     "bl_ffn_relu2": ([_P, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _S, _P], ctypes.c_int),
     "bl_ffn_relu2_subln": ([_P, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _F, _P, _P, _S, _P],
                            ctypes.c_int),
+    "bl_ffn_step": ([_P, _I, _I, _P, _P, _P, _P, _I, _P, _P, ctypes.c_int, _P, _F, _P, _P, _S,
+                     _P], ctypes.c_int),
     "bl_packed_bytes_binary": ([_I, _I], _S),
     "bl_packed_bytes_base3": ([_I, _I], _S),
     "bl_quantize_weights_binary": ([_P, _I, _I, _P, _P, _P, _S, _P], ctypes.c_int),
@@ -250,6 +256,51 @@ def relu2_glu_quant(gate, up, out=None, subln_gain=None, subln_eps: float = 1e-5
     return hq, hs
 
 
+def _glu_kind(kind) -> int:
+    if kind in _GLU_KINDS:
+        return _GLU_KINDS[kind]
+    if kind in (BL_GLU_RELU2, BL_GLU_SWIGLU):
+        return int(kind)
+    raise BitLinearError(f"unknown gating kind {kind!r}")
+
+
+def glu(gate, up, kind="relu2", out=None):
+    """h = bf16(act(gate) * up), act = relu^2 ("relu2") or SiLU ("swiglu").
+    Calls bl_glu."""
+    torch = _torch()
+    h = torch.empty(gate.shape, dtype=torch.bfloat16, device=gate.device) if out is None else out
+    if gate.shape != up.shape:
+        raise BitLinearError("gate and up shapes differ")
+    _check(lib().bl_glu(_dev(gate, torch.float32, "gate"), _dev(up, torch.float32, "up"),
+                        gate.numel(), _glu_kind(kind), _dev(h, torch.bfloat16, "h"),
+                        _stream_ptr(gate)), "bl_glu")
+    return h
+
+
+def glu_quant(gate, up, kind="relu2", subln_gain=None, subln_eps: float = 1e-5, out=None):
+    """(h_q int8, h_scale fp32) of the gating of `kind`, with the sub-layer
+    RMSNorm when subln_gain (bf16 [K]) is given. Calls bl_glu_quant."""
+    torch = _torch()
+    M, K = gate.shape
+    if gate.shape != up.shape:
+        raise BitLinearError("gate and up shapes differ")
+    if out is None:
+        hq = torch.empty((M, K), dtype=torch.int8, device=gate.device)
+        hs = torch.empty(M, dtype=torch.float32, device=gate.device)
+    else:
+        hq, hs = out
+    gp = None
+    if subln_gain is not None:
+        if subln_gain.dtype == torch.int16:
+            subln_gain = subln_gain.view(torch.bfloat16)
+        gp = _dev(subln_gain, torch.bfloat16, "gain")
+    _check(lib().bl_glu_quant(_dev(gate, torch.float32, "gate"), _dev(up, torch.float32, "up"),
+                              M, K, _glu_kind(kind), gp, float(subln_eps),
+                              _dev(hq, torch.int8, "h_q"), _dev(hs, torch.float32, "h_scale"),
+                              _stream_ptr(gate)), "bl_glu_quant")
+    return hq, hs
+
+
 def ffn_relu2_workspace(M: int, K: int, N_ff: int, device=None):
     """A workspace tensor sized by bl_ffn_relu2_workspace_bytes."""
     torch = _torch()
@@ -288,6 +339,40 @@ def ffn_relu2(x, W_gate, gamma_gate, W_up, gamma_up, W_down, gamma_down, workspa
             subln_gain = subln_gain.view(torch.bfloat16)
         _check(lib().bl_ffn_relu2_subln(*head, _dev(subln_gain, torch.bfloat16, "subln_gain"),
                                         float(subln_eps), *tail), "bl_ffn_relu2_subln")
+    return y
+
+
+def ffn_step(x, W_gate, gamma_gate, W_up, gamma_up, W_down, gamma_down, kind="relu2",
+             subln_gain=None, subln_eps: float = 1e-5, workspace=None, out=None):
+    """y fp32 [M][K] of one gated FFN step with the gating of `kind`
+    ("relu2" or "swiglu") and an optional sub-layer RMSNorm. Calls
+    bl_ffn_step."""
+    torch = _torch()
+    if x.dtype == torch.int16:
+        x = x.view(torch.bfloat16)
+    M, K = x.shape
+    N_ff = W_gate.shape[0]
+    if W_gate.shape[1] * 16 != K or W_up.shape != W_gate.shape or \
+            W_down.shape[0] != K or W_down.shape[1] * 16 != N_ff:
+        raise BitLinearError("FFN weight shapes do not match")
+    if workspace is None:
+        workspace = ffn_relu2_workspace(M, K, N_ff, x.device)
+    y = torch.empty((M, K), dtype=torch.float32, device=x.device) if out is None else out
+    gp = None
+    if subln_gain is not None:
+        if subln_gain.dtype == torch.int16:
+            subln_gain = subln_gain.view(torch.bfloat16)
+        gp = _dev(subln_gain, torch.bfloat16, "subln_gain")
+    _check(lib().bl_ffn_step(_dev(x, torch.bfloat16, "x"), M, K,
+                             _dev(W_gate, torch.int32, "W_gate"),
+                             _dev(gamma_gate, torch.float32, "gamma_gate"),
+                             _dev(W_up, torch.int32, "W_up"),
+                             _dev(gamma_up, torch.float32, "gamma_up"), N_ff,
+                             _dev(W_down, torch.int32, "W_down"),
+                             _dev(gamma_down, torch.float32, "gamma_down"), _glu_kind(kind), gp,
+                             float(subln_eps), _dev(y, torch.float32, "y"),
+                             _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+                             _stream_ptr(x)), "bl_ffn_step")
     return y
 
 

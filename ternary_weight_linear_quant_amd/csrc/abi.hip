@@ -189,11 +189,15 @@ size_t bl_ffn_relu2_workspace_bytes(int64_t M, int64_t K, int64_t N_ff) {
 
 namespace {
 
+bool glu_kind_ok(int kind) { return kind == BL_GLU_RELU2 || kind == BL_GLU_SWIGLU; }
+
 // One FFN step; subln_gain (bf16 [N_ff]) null for none.
 int ffn_step(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate,
              const float* gamma_gate, const uint32_t* W_up, const float* gamma_up, int64_t N_ff,
-             const uint32_t* W_down, const float* gamma_down, const uint16_t* subln_gain,
-             float subln_eps, float* y, void* workspace, size_t workspace_bytes, void* stream) {
+             const uint32_t* W_down, const float* gamma_down, int kind,
+             const uint16_t* subln_gain, float subln_eps, float* y, void* workspace,
+             size_t workspace_bytes, void* stream) {
+    if (!glu_kind_ok(kind)) return BL_ERR_INVALID_ARG;
     if (!x || !W_gate || !gamma_gate || !W_up || !gamma_up || !W_down || !gamma_down || !y ||
         !workspace)
         return BL_ERR_INVALID_ARG;
@@ -211,7 +215,7 @@ int ffn_step(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate,
     if (bl::ffn_fused_supported(M, K, N_ff))
         return hip_status(bl::launch_ffn_fused(x, (int)M, (int)K, W_gate, gamma_gate, W_up,
                                                gamma_up, (int)N_ff, W_down, gamma_down, h, y,
-                                               subln_gain, subln_eps, st));
+                                               kind, subln_gain, subln_eps, st));
     // Unfused sequence: act quant -> gate/up -> gating (+ norm) + act quant -> down.
     auto* xq = reinterpret_cast<int8_t*>(ws + L.xq);
     auto* xs = reinterpret_cast<float*>(ws + L.xs);
@@ -232,7 +236,7 @@ int ffn_step(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate,
         }
     }
     if (e == hipSuccess)
-        e = bl::launch_relu2_glu_quant(yg, yu, M, N_ff, subln_gain, subln_eps, hq, hs, st);
+        e = bl::launch_glu_quant(yg, yu, M, N_ff, kind, subln_gain, subln_eps, hq, hs, st);
     if (e == hipSuccess) {
         if (bl::gemv_supported(M, N_ff))
             e = bl::launch_gemv(hq, hs, m, n, W_down, gamma_down, k, y, nullptr, st);
@@ -242,15 +246,15 @@ int ffn_step(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate,
     return hip_status(e);
 }
 
-int glu_quant(const float* gate, const float* up, int64_t M, int64_t K, const uint16_t* gain,
-              float rms_eps, int8_t* h_q, float* h_scale, void* stream) {
-    if (!gate || !up || !h_q || !h_scale) return BL_ERR_INVALID_ARG;
+int glu_quant(const float* gate, const float* up, int64_t M, int64_t K, int kind,
+              const uint16_t* gain, float rms_eps, int8_t* h_q, float* h_scale, void* stream) {
+    if (!gate || !up || !h_q || !h_scale || !glu_kind_ok(kind)) return BL_ERR_INVALID_ARG;
     if (!shape_ok(M, K)) return BL_ERR_INVALID_ARG;
     if (!aligned16(gate) || !aligned16(up) || !aligned16(h_q)) return BL_ERR_INVALID_ARG;
     if (gain && (!aligned16(gain) || !(rms_eps > 0.0f))) return BL_ERR_INVALID_ARG;
     if (int s = device_status()) return s;
     return hip_status(
-        bl::launch_relu2_glu_quant(gate, up, M, K, gain, rms_eps, h_q, h_scale, as_stream(stream)));
+        bl::launch_glu_quant(gate, up, M, K, kind, gain, rms_eps, h_q, h_scale, as_stream(stream)));
 }
 
 }  // namespace
@@ -262,7 +266,7 @@ int bl_ffn_relu2(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate
                  int64_t N_ff, const uint32_t* W_down, const float* gamma_down, float* y,
                  void* workspace, size_t workspace_bytes, void* stream) {
     return ffn_step(x, M, K, W_gate, gamma_gate, W_up, gamma_up, N_ff, W_down, gamma_down,
-                    nullptr, 0.0f, y, workspace, workspace_bytes, stream);
+                    BL_GLU_RELU2, nullptr, 0.0f, y, workspace, workspace_bytes, stream);
 }
 
 int bl_ffn_relu2_subln(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate,
@@ -272,27 +276,46 @@ int bl_ffn_relu2_subln(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
                        size_t workspace_bytes, void* stream) {
     if (!subln_gain) return BL_ERR_INVALID_ARG;
     return ffn_step(x, M, K, W_gate, gamma_gate, W_up, gamma_up, N_ff, W_down, gamma_down,
-                    subln_gain, subln_eps, y, workspace, workspace_bytes, stream);
+                    BL_GLU_RELU2, subln_gain, subln_eps, y, workspace, workspace_bytes, stream);
+}
+
+int bl_ffn_step(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate,
+                const float* gamma_gate, const uint32_t* W_up, const float* gamma_up,
+                int64_t N_ff, const uint32_t* W_down, const float* gamma_down, int glu_kind,
+                const uint16_t* subln_gain, float subln_eps, float* y, void* workspace,
+                size_t workspace_bytes, void* stream) {
+    return ffn_step(x, M, K, W_gate, gamma_gate, W_up, gamma_up, N_ff, W_down, gamma_down,
+                    glu_kind, subln_gain, subln_eps, y, workspace, workspace_bytes, stream);
 }
 
 int bl_relu2_glu_quant(const float* gate, const float* up, int64_t M, int64_t K, int8_t* h_q,
                        float* h_scale, void* stream) {
-    return glu_quant(gate, up, M, K, nullptr, 0.0f, h_q, h_scale, stream);
+    return glu_quant(gate, up, M, K, BL_GLU_RELU2, nullptr, 0.0f, h_q, h_scale, stream);
 }
 
 int bl_relu2_glu_subln_quant(const float* gate, const float* up, int64_t M, int64_t K,
                              const uint16_t* gain, float rms_eps, int8_t* h_q, float* h_scale,
                              void* stream) {
     if (!gain) return BL_ERR_INVALID_ARG;
-    return glu_quant(gate, up, M, K, gain, rms_eps, h_q, h_scale, stream);
+    return glu_quant(gate, up, M, K, BL_GLU_RELU2, gain, rms_eps, h_q, h_scale, stream);
 }
 
-int bl_relu2_glu(const float* gate, const float* up, int64_t count, uint16_t* h, void* stream) {
-    if (!gate || !up || !h || count < 1) return BL_ERR_INVALID_ARG;
+int bl_glu_quant(const float* gate, const float* up, int64_t M, int64_t K, int glu_kind,
+                 const uint16_t* gain, float rms_eps, int8_t* h_q, float* h_scale, void* stream) {
+    return glu_quant(gate, up, M, K, glu_kind, gain, rms_eps, h_q, h_scale, stream);
+}
+
+int bl_glu(const float* gate, const float* up, int64_t count, int glu_kind, uint16_t* h,
+           void* stream) {
+    if (!gate || !up || !h || count < 1 || !glu_kind_ok(glu_kind)) return BL_ERR_INVALID_ARG;
     if (count > (int64_t{1} << 40)) return BL_ERR_INVALID_ARG;
     if (!aligned16(gate) || !aligned16(up) || !aligned16(h)) return BL_ERR_INVALID_ARG;
     if (int s = device_status()) return s;
-    return hip_status(bl::launch_relu2_glu(gate, up, count, h, as_stream(stream)));
+    return hip_status(bl::launch_glu(gate, up, count, glu_kind, h, as_stream(stream)));
+}
+
+int bl_relu2_glu(const float* gate, const float* up, int64_t count, uint16_t* h, void* stream) {
+    return bl_glu(gate, up, count, BL_GLU_RELU2, h, stream);
 }
 
 size_t bl_packed_bytes_binary(int64_t N, int64_t K) {

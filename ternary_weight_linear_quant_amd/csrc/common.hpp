@@ -22,6 +22,23 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return u >> 16;
 }
 
+// Gating of a gated FFN: h = bf16_rne(act(gate) * up), fp32 arithmetic.
+// kGluRelu2: act(g) = relu(g)^2 (the 2B4T FFN). kGluSwiglu: act(g) = SiLU(g)
+// = g / (1 + exp(-g)) (the LLaMA-style SwiGLU), with the library exp; a gate
+// below about -88 gives exp(-g) = inf and SiLU = -0.
+constexpr int kGluRelu2 = 0, kGluSwiglu = 1;
+
+template <int KIND>
+__device__ __forceinline__ uint32_t glu_bits(float g, float u) {
+    if constexpr (KIND == kGluRelu2) {
+        const float r = g > 0.0f ? g : 0.0f;
+        return f32_to_bf16_rne((r * r) * u);
+    } else {
+        const float s = g / (1.0f + expf(-g));
+        return f32_to_bf16_rne(s * u);
+    }
+}
+
 // One packed word holds 16 two-bit codes c = q + 1; (w >> 2p) & 0x03030303
 // gives the codes of weights 4p..4p+3 of the word in bytes 0..3. A byte
 // permute with the table {0xFF, 0x00, 0x01} turns each code into the signed

@@ -47,16 +47,11 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ uint32_t relu2_gate_bits(float g, float u) {
-    const float r = g > 0.0f ? g : 0.0f;
-    const float sq = r * r;
-    return f32_to_bf16_rne(sq * u);
-}
-
 // SUBLN (quantising launch B only): the sub-layer RMSNorm with gain `gain`
 // before the quantisation, as bl_quantize_acts(h, gain) computes it: codes
 // of z = h*g, scale a / (127 * rms(h)), sum h^2 in fp64.
-template <bool GLU, int KS, bool SUBLN>
+// KIND: the gating of launch A (relu^2 or SiLU).
+template <bool GLU, int KS, bool SUBLN, int KIND>
 __global__ __launch_bounds__(64 * (GLU ? 2 : 1) * KS) void k_ffn_gemv(
     const uint16_t* __restrict__ xin, int M, int K, const uint32_t* __restrict__ W0,
     const float* __restrict__ g0, const uint32_t* __restrict__ W1,
@@ -257,7 +252,7 @@ __global__ __launch_bounds__(64 * (GLU ? 2 : 1) * KS) void k_ffn_gemv(
             uint32_t hb[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                hb[i] = relu2_gate_bits((float)ga[i] * sg, (float)ua[i] * su);
+                hb[i] = glu_bits<KIND>((float)ga[i] * sg, (float)ua[i] * su);
             *reinterpret_cast<uint2*>(h + (size_t)tok * N + nbase) =
                 make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
         }
@@ -295,7 +290,7 @@ namespace {
 template <int KS, bool SUBLN>
 void launch_ffn_down(const uint16_t* h, int M, int N_ff, const uint32_t* Wd, const float* gd,
                      int K, float* y, const uint16_t* gain, float rms_eps, hipStream_t stream) {
-    hipLaunchKernelGGL((k_ffn_gemv<false, KS, SUBLN>), dim3((K + 15) / 16), dim3(64 * KS),
+    hipLaunchKernelGGL((k_ffn_gemv<false, KS, SUBLN, kGluRelu2>), dim3((K + 15) / 16), dim3(64 * KS),
                        (size_t)M * N_ff, stream, h, M, N_ff, Wd, gd, (const uint32_t*)nullptr,
                        (const float*)nullptr, K, y, (uint16_t*)nullptr, gain, rms_eps);
 }
@@ -305,10 +300,16 @@ void launch_ffn_down(const uint16_t* h, int M, int N_ff, const uint32_t* Wd, con
 hipError_t launch_ffn_fused(const uint16_t* x, int M, int K, const uint32_t* Wg,
                             const float* gg, const uint32_t* Wu, const float* gu, int N_ff,
                             const uint32_t* Wd, const float* gd, uint16_t* h, float* y,
-                            const uint16_t* subln_gain, float subln_eps, hipStream_t stream) {
-    hipLaunchKernelGGL((k_ffn_gemv<true, kKsA, false>), dim3((N_ff + 15) / 16),
-                       dim3(64 * 2 * kKsA), (size_t)M * K, stream, x, M, K, Wg, gg, Wu, gu, N_ff,
-                       (float*)nullptr, h, (const uint16_t*)nullptr, 0.0f);
+                            int kind, const uint16_t* subln_gain, float subln_eps,
+                            hipStream_t stream) {
+    if (kind == kGluSwiglu)
+        hipLaunchKernelGGL((k_ffn_gemv<true, kKsA, false, kGluSwiglu>), dim3((N_ff + 15) / 16),
+                           dim3(64 * 2 * kKsA), (size_t)M * K, stream, x, M, K, Wg, gg, Wu, gu,
+                           N_ff, (float*)nullptr, h, (const uint16_t*)nullptr, 0.0f);
+    else
+        hipLaunchKernelGGL((k_ffn_gemv<true, kKsA, false, kGluRelu2>), dim3((N_ff + 15) / 16),
+                           dim3(64 * 2 * kKsA), (size_t)M * K, stream, x, M, K, Wg, gg, Wu, gu,
+                           N_ff, (float*)nullptr, h, (const uint16_t*)nullptr, 0.0f);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const bool big = N_ff / 256 >= kKsB;

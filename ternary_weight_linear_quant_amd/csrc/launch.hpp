@@ -35,15 +35,15 @@ hipError_t launch_gemv_wide(const int8_t* xq, const float* xs, int M, int K, con
 hipError_t launch_gemm(const int8_t* xq, const float* xs, int M, int K, const uint32_t* Wp,
                        const float* gamma, int N, float* y, int32_t* acc, hipStream_t stream);
 
-hipError_t launch_relu2_glu(const float* g, const float* u, int64_t count, uint16_t* h,
-                            hipStream_t stream);
+// Gating of a gated FFN (kind kGluRelu2 or kGluSwiglu): h = bf16(act(g) * u).
+hipError_t launch_glu(const float* g, const float* u, int64_t count, int kind, uint16_t* h,
+                      hipStream_t stream);
 
-// Squared-ReLU gating fused with the per-token quantisation of its output.
-// gain (bf16 [K]) may be null; otherwise the sub-layer RMSNorm precedes the
+// The gating fused with the per-token quantisation of its output. gain (bf16 [K]) may be null; otherwise the sub-layer RMSNorm precedes the
 // quantisation.
-hipError_t launch_relu2_glu_quant(const float* gate, const float* up, int64_t M, int64_t K,
-                                  const uint16_t* gain, float rms_eps, int8_t* hq, float* scale,
-                                  hipStream_t stream);
+hipError_t launch_glu_quant(const float* gate, const float* up, int64_t M, int64_t K, int kind,
+                            const uint16_t* gain, float rms_eps, int8_t* hq, float* scale,
+                            hipStream_t stream);
 
 // Two decode GEMVs sharing one quantised input, in one launch.
 hipError_t launch_gemv_pair(const int8_t* xq, const float* xs, int M, int K, const uint32_t* W1,
@@ -56,7 +56,8 @@ bool ffn_fused_supported(int64_t M, int64_t K, int64_t N_ff);
 hipError_t launch_ffn_fused(const uint16_t* x, int M, int K, const uint32_t* Wg,
                             const float* gg, const uint32_t* Wu, const float* gu, int N_ff,
                             const uint32_t* Wd, const float* gd, uint16_t* h, float* y,
-                            const uint16_t* subln_gain, float subln_eps, hipStream_t stream);
+                            int kind, const uint16_t* subln_gain, float subln_eps,
+                            hipStream_t stream);
 
 // Other weight formats (decode GEMV only): 1 bit per {-1, +1} weight and
 // five ternary weights per byte.

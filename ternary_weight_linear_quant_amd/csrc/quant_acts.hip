@@ -144,26 +144,24 @@ __global__ __launch_bounds__(kActThreads) void k_act_quant(
     }
 }
 
-// h = bf16_rne((relu(g)^2) * u) for one 4-wide fp32 vector, as two dwords of
-// bf16 bits.
-__device__ __forceinline__ uint2 relu2_gate4(const float4 g, const float4 u) {
-    auto one = [](float gv, float uv) -> uint32_t {
-        const float r = gv > 0.0f ? gv : 0.0f;
-        const float sq = r * r;
-        return f32_to_bf16_rne(sq * uv);
-    };
-    return make_uint2(one(g.x, u.x) | (one(g.y, u.y) << 16), one(g.z, u.z) | (one(g.w, u.w) << 16));
+// h = bf16_rne(act(g) * u) for one 4-wide fp32 vector, as two dwords of bf16
+// bits.
+template <int KIND>
+__device__ __forceinline__ uint2 glu4(const float4 g, const float4 u) {
+    return make_uint2(glu_bits<KIND>(g.x, u.x) | (glu_bits<KIND>(g.y, u.y) << 16),
+                      glu_bits<KIND>(g.z, u.z) | (glu_bits<KIND>(g.w, u.w) << 16));
 }
 
-// Squared-ReLU gating fused with per-token absmax quantisation of its bf16
-// result: identical to bl_relu2_glu followed by bl_quantize_acts (plain).
+// Gating (squared ReLU or SwiGLU) fused with per-token absmax quantisation of
+// its bf16 result: identical to the gating call followed by bl_quantize_acts
+// (plain).
 // SUBLN: the sub-layer RMSNorm with gain g between the gating and the
 // quantisation, as bl_quantize_acts(h, g) computes it: codes of z = h*g,
 // scale a / (127 * rms(h)) with sum h^2 in fp64.
 constexpr int kGluCache = 12;  // 4-element vectors cached per thread (K <= 12288)
 
-template <bool SUBLN>
-__global__ __launch_bounds__(kActThreads) void k_relu2_glu_quant(
+template <int KIND, bool SUBLN>
+__global__ __launch_bounds__(kActThreads) void k_glu_quant(
     const float* __restrict__ gate, const float* __restrict__ up, int64_t K,
     const uint16_t* __restrict__ gain, float rms_eps, int8_t* __restrict__ hq,
     float* __restrict__ scale) {
@@ -213,12 +211,12 @@ __global__ __launch_bounds__(kActThreads) void k_relu2_glu_quant(
         for (int j = 0; j < kGluCache; ++j) {
             const int v = tid + kActThreads * j;
             if (v < nvec) {
-                ch[j] = relu2_gate4(cg[j], cu[j]);
+                ch[j] = glu4<KIND>(cg[j], cu[j]);
                 scan(v, ch[j]);
             }
         }
     } else {
-        for (int v = tid; v < nvec; v += kActThreads) scan(v, relu2_gate4(grow[v], urow[v]));
+        for (int v = tid; v < nvec; v += kActThreads) scan(v, glu4<KIND>(grow[v], urow[v]));
     }
     amax = block_reduce(amax, s_max, true);
     double ss_tot = 0.0;
@@ -253,7 +251,7 @@ __global__ __launch_bounds__(kActThreads) void k_relu2_glu_quant(
             if (v < nvec) emit(v, ch[j]);
         }
     } else {
-        for (int v = tid; v < nvec; v += kActThreads) emit(v, relu2_gate4(grow[v], urow[v]));
+        for (int v = tid; v < nvec; v += kActThreads) emit(v, glu4<KIND>(grow[v], urow[v]));
     }
     if (tid == 0) {
         if (SUBLN) {
@@ -276,15 +274,27 @@ hipError_t launch_quantize_acts(const uint16_t* x, int64_t M, int64_t K, const u
     return hipGetLastError();
 }
 
-hipError_t launch_relu2_glu_quant(const float* gate, const float* up, int64_t M, int64_t K,
-                                  const uint16_t* gain, float rms_eps, int8_t* hq, float* scale,
-                                  hipStream_t stream) {
+namespace {
+template <int KIND>
+void launch_glu_quant_kind(const float* gate, const float* up, int64_t M, int64_t K,
+                           const uint16_t* gain, float rms_eps, int8_t* hq, float* scale,
+                           hipStream_t stream) {
     if (gain)
-        hipLaunchKernelGGL(k_relu2_glu_quant<true>, dim3((unsigned)M), dim3(kActThreads), 0,
+        hipLaunchKernelGGL((k_glu_quant<KIND, true>), dim3((unsigned)M), dim3(kActThreads), 0,
                            stream, gate, up, K, gain, rms_eps, hq, scale);
     else
-        hipLaunchKernelGGL(k_relu2_glu_quant<false>, dim3((unsigned)M), dim3(kActThreads), 0,
+        hipLaunchKernelGGL((k_glu_quant<KIND, false>), dim3((unsigned)M), dim3(kActThreads), 0,
                            stream, gate, up, K, gain, rms_eps, hq, scale);
+}
+}  // namespace
+
+hipError_t launch_glu_quant(const float* gate, const float* up, int64_t M, int64_t K, int kind,
+                            const uint16_t* gain, float rms_eps, int8_t* hq, float* scale,
+                            hipStream_t stream) {
+    if (kind == kGluSwiglu)
+        launch_glu_quant_kind<kGluSwiglu>(gate, up, M, K, gain, rms_eps, hq, scale, stream);
+    else
+        launch_glu_quant_kind<kGluRelu2>(gate, up, M, K, gain, rms_eps, hq, scale, stream);
     return hipGetLastError();
 }
 

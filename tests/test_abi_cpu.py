@@ -104,6 +104,13 @@ def test_invalid_arguments_rejected_before_launch(L):
     assert L.bl_relu2_glu_quant(A, A, 0, 64, A, A, None) == E
     assert L.bl_relu2_glu_quant(A, MIS, 1, 64, A, A, None) == E
     assert L.bl_relu2_glu_quant(A, A, 1, 64, A, None, None) == E
+    # gating kinds: only BL_GLU_RELU2 (0) and BL_GLU_SWIGLU (1)
+    assert L.bl_glu(A, A, 4, 2, A, None) == E
+    assert L.bl_glu(A, A, 4, -1, A, None) == E
+    assert L.bl_glu(A, A, 0, 1, A, None) == E
+    assert L.bl_glu_quant(A, A, 1, 64, 2, None, 0.0, A, A, None) == E
+    assert L.bl_glu_quant(A, A, 1, 64, 1, MIS, 1e-5, A, A, None) == E
+    assert L.bl_glu_quant(A, A, 1, 64, 1, A, 0.0, A, A, None) == E
     # glue with the sub-layer norm: the gain is required, aligned, eps > 0
     assert L.bl_relu2_glu_subln_quant(A, A, 1, 64, None, 1e-5, A, A, None) == E
     assert L.bl_relu2_glu_subln_quant(A, A, 1, 64, MIS, 1e-5, A, A, None) == E
@@ -127,6 +134,10 @@ def test_invalid_arguments_rejected_before_launch(L):
                                 None) == E
     assert L.bl_ffn_relu2_subln(A, 4, 2560, A, A, A, A, 6912, A, A, A, 1e-5, A, WS, need - 1,
                                 None) == E
+    assert L.bl_ffn_step(A, 4, 2560, A, A, A, A, 6912, A, A, 3, None, 0.0, A, WS, need,
+                         None) == E
+    assert L.bl_ffn_step(A, 4, 2560, A, A, A, A, 6912, A, A, 1, A, 0.0, A, WS, need,
+                         None) == E
     # pair
     assert L.bl_bitlinear_pair(A, A, 1, 64, A, A, 16, A, None, A, 16, A, None) == E
     assert L.bl_bitlinear_pair(A, A, 1, 64, A, A, 16, A, A, A, 0, A, None) == E
@@ -209,6 +220,10 @@ def test_no_device_status(L):
     assert L.bl_ffn_relu2_subln(A, 1, 256, A, A, A, A, 1024, A, A, A, 1e-5, A, P(0x200000),
                                 need, None) == D
     assert L.bl_relu2_glu_subln_quant(A, A, 1, 64, A, 1e-5, A, A, None) == D
+    assert L.bl_glu(A, A, 4, 1, A, None) == D
+    assert L.bl_glu_quant(A, A, 1, 64, 1, None, 0.0, A, A, None) == D
+    assert L.bl_ffn_step(A, 1, 256, A, A, A, A, 1024, A, A, 1, None, 0.0, A, P(0x200000),
+                         need, None) == D
 
 
 def test_binding_fails_loudly_without_gpu():

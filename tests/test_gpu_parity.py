@@ -637,6 +637,88 @@ def test_ffn_subln_down_input_against_oracle():
     assert np.all(np.abs(y.astype(np.float64) - y_ref) <= 2e-6 * np.abs(y_ref.astype(np.float64)))
 
 
+# -------------------------------------------------------------- SwiGLU ----
+# h = bf16(fp32(SiLU(g)) * u): the device exp is within a few fp32 ulp of the
+# exact SiLU the oracle rounds from fp64, so h may be one bf16 step apart
+# where the fp32 product lies at a rounding tie; everything downstream is
+# checked bit-exactly from the GPU's own h.
+
+def _bf16_step(v):
+    a = np.abs(np.asarray(v, np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, 2.0 ** (e - 7), 0.0)
+
+
+def _h_close(h_bits, h_ref_bits):
+    h = wl.bf16_bits_to_f32(h_bits).astype(np.float64)
+    r = wl.bf16_bits_to_f32(h_ref_bits).astype(np.float64)
+    ok = np.abs(h - r) <= np.maximum(_bf16_step(h), _bf16_step(r)) + 1e-30
+    return ok.all(), int((h_bits != h_ref_bits).sum())
+
+
+def test_swiglu_parity():
+    g, u = wl.ffn_hidden(64, 0, 37, 1024)
+    g[0, :10] = [0.0, 1.0, -1.0, 20.0, -20.0, -30.0, -100.0, 100.0, 3.5, -1.2785]
+    u[0, :10] = 1.0
+    h = bl.glu(dev_f32(g), dev_f32(u), "swiglu").cpu().view(torch.int16).numpy().view(np.uint16)
+    h_ref = oracle.swiglu(g, u)
+    ok, differ = _h_close(h, h_ref)
+    assert ok and differ <= 0.005 * h.size, differ
+    # The two hand values the oracle is pinned to.
+    hv = wl.bf16_bits_to_f32(h[0, 1:3])
+    assert hv[0] == np.float32(187 / 256) and hv[1] == np.float32(-138 / 512)
+
+
+@pytest.mark.parametrize("M,K", [(1, 6912), (4, 8640), (16, 2560), (300, 1024)])
+def test_swiglu_quant_from_gpu_h(M, K):
+    g, u = wl.ffn_hidden(65, K, M, K)
+    gain = wl.rms_gain(65, 1, K)
+    h_dev = bl.glu(dev_f32(g), dev_f32(u), "swiglu")
+    h = h_dev.cpu().view(torch.int16).numpy().view(np.uint16)
+    assert _h_close(h, oracle.swiglu(g, u))[0]
+    hq, hs = bl.glu_quant(dev_f32(g), dev_f32(u), "swiglu")
+    hq_ref, hs_ref = oracle.act_quant(h)
+    assert np.array_equal(hq.cpu().numpy(), hq_ref) and np.array_equal(hs.cpu().numpy(), hs_ref)
+    hq2, hs2 = bl.quantize_acts(h_dev)
+    assert torch.equal(hq, hq2) and torch.equal(hs, hs2)
+    hq, hs = bl.glu_quant(dev_f32(g), dev_f32(u), "swiglu", subln_gain=dev_bf16(gain))
+    hq_ref, hs_ref = oracle.act_quant(h, gain)
+    assert np.array_equal(hq.cpu().numpy(), hq_ref)
+    assert np.all(np.abs(hs.cpu().numpy() - hs_ref) <= RTOL_SCALE_FUSED * hs_ref)
+
+
+@pytest.mark.parametrize("M", [1, 4, 5, 16])
+@pytest.mark.parametrize("K,N_ff", [(3200, 8640), (512, 1024)])
+def test_ffn_step_swiglu_matches_unfused_sequence(M, K, N_ff):
+    """bl_ffn_step with SwiGLU gating (two launches for M <= 4, four
+    otherwise) against the single calls: bit-exact without the norm, y within
+    2e-6 relative with it."""
+    wid = 74
+    Wg, Wu = wl.weights(wid, 0, N_ff, K), wl.weights(wid, 1, N_ff, K)
+    Wd = wl.weights(wid, 2, K, N_ff)
+    (pg, gg), (pu, gu), (pd, gd) = gpu_weights(Wg), gpu_weights(Wu), gpu_weights(Wd)
+    x = dev_bf16(wl.activations(wid, M, M, K))
+    xq, xs = bl.quantize_acts(x)
+    yg, yu = bl.bitlinear(xq, xs, pg, gg), bl.bitlinear(xq, xs, pu, gu)
+    h = bl.glu(yg, yu, "swiglu")
+    hq, hs = bl.quantize_acts(h)
+    ref = bl.bitlinear(hq, hs, pd, gd)
+    y = bl.ffn_step(x, pg, gg, pu, gu, pd, gd, kind="swiglu")
+    assert torch.equal(y.view(torch.int32), ref.view(torch.int32))
+    # Stage-wise against the oracle from the GPU's own gate/up outputs.
+    h_bits = h.cpu().view(torch.int16).numpy().view(np.uint16)
+    assert _h_close(h_bits, oracle.swiglu(yg.cpu().numpy(), yu.cpu().numpy()))[0]
+    gain = wl.rms_gain(wid, 0, N_ff)
+    hq2, hs2 = bl.quantize_acts(h, dev_bf16(gain))
+    ref2 = bl.bitlinear(hq2, hs2, pd, gd).cpu().numpy().astype(np.float64)
+    y2 = bl.ffn_step(x, pg, gg, pu, gu, pd, gd, kind="swiglu",
+                     subln_gain=dev_bf16(gain)).cpu().numpy()
+    assert np.all(np.abs(y2 - ref2) <= 2e-6 * np.abs(ref2) + 1e-30)
+    # The relu2 kind of the general entry is bl_ffn_relu2 bit for bit.
+    y3 = bl.ffn_step(x, pg, gg, pu, gu, pd, gd, kind="relu2")
+    assert torch.equal(y3.view(torch.int32), bl.ffn_relu2(x, pg, gg, pu, gu, pd, gd).view(torch.int32))
+
+
 # --------------------------------------------------------- calibration ----
 
 def test_calibration_kernels():
