@@ -22,6 +22,22 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return u >> 16;
 }
 
+// Four int8 codes rne(t) packed little-endian, for fp32 t with |t| < 2^22.
+// Adding 1.5 * 2^23 rounds t to an integer (ties to even, the default
+// rounding of the add) and leaves it, in two's complement, in the low
+// mantissa byte; the result is that of rintf on each t. Callers pass
+// t = z * (127 / a) with a = max |z| of the token, so |t| <= 127 (1 + 2^-24)^2
+// and the [-127, 127] clamp of the codes can never act; z * inv must be
+// rounded before the add (the library is built with fp contraction off).
+__device__ __forceinline__ uint32_t pack_codes4(float t0, float t1, float t2, float t3) {
+    constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+    const uint32_t a = __float_as_uint(t0 + kMagic), b = __float_as_uint(t1 + kMagic);
+    const uint32_t c = __float_as_uint(t2 + kMagic), d = __float_as_uint(t3 + kMagic);
+    const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);  // a.b0, b.b0, 0, 0
+    const uint32_t hi = __builtin_amdgcn_perm(d, c, 0x04000c0cu);  // 0, 0, c.b0, d.b0
+    return lo | hi;
+}
+
 // Gating of a gated FFN: h = bf16_rne(act(gate) * up), fp32 arithmetic.
 // kGluRelu2: act(g) = relu(g)^2 (the 2B4T FFN). kGluSwiglu: act(g) = SiLU(g)
 // = g / (1 + exp(-g)) (the LLaMA-style SwiGLU), with the library exp; a gate

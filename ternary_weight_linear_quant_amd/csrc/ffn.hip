@@ -33,6 +33,8 @@
 
 namespace bl {
 
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
 constexpr int kFfnMaxThreads = 1024;
 constexpr int kFfnMinThreads = 256;
 constexpr int kFfnCache = 8;  // 16-value activation units cached per thread (at 256 threads)
@@ -120,23 +122,31 @@ __global__ __launch_bounds__(64 * (GLU ? 2 : 1) * KS) void k_ffn_gemv(
     };
     float amax = 0.0f;
     double ss = 0.0;
+    // Without the norm, max |x| over finite bf16 values is the integer max
+    // of their sign-cleared bit patterns, two per packed 16-bit max.
+    u16x2 mbits = {0, 0};
 #pragma unroll
     for (int i = 0; i < CACHE; ++i) {
         if (tid + NT * i < U) {
             const uint32_t w8[8] = {xa[i].x, xa[i].y, xa[i].z, xa[i].w,
                                     xb[i].x, xb[i].y, xb[i].z, xb[i].w};
+            if constexpr (SUBLN) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float xf = bf16_to_f32((w8[e / 2] >> (16 * (e % 2))) & 0xFFFFu);
-                if constexpr (SUBLN) {
+                for (int e = 0; e < 16; ++e) {
+                    const float xf = bf16_to_f32((w8[e / 2] >> (16 * (e % 2))) & 0xFFFFu);
                     amax = fmaxf(amax, fabsf(xf * gain_of(i, e)));
                     ss += (double)xf * (double)xf;
-                } else {
-                    amax = fmaxf(amax, fabsf(xf));
                 }
+            } else {
+#pragma unroll
+                for (int d = 0; d < 8; ++d)
+                    mbits = __builtin_elementwise_max(
+                        mbits, __builtin_bit_cast(u16x2, w8[d] & 0x7FFF7FFFu));
             }
         }
     }
+    if constexpr (!SUBLN)
+        amax = bf16_to_f32(mbits[0] > mbits[1] ? mbits[0] : mbits[1]);
     // Lanes with equal lane % M hold the same token.
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1)
@@ -173,15 +183,17 @@ __global__ __launch_bounds__(64 * (GLU ? 2 : 1) * KS) void k_ffn_gemv(
         if (u < U) {
             const uint32_t w8[8] = {xa[i].x, xa[i].y, xa[i].z, xa[i].w,
                                     xb[i].x, xb[i].y, xb[i].z, xb[i].w};
-            uint32_t q[4] = {0, 0, 0, 0};
+            float t[16];
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 float z = bf16_to_f32((w8[e / 2] >> (16 * (e % 2))) & 0xFFFFu);
                 if constexpr (SUBLN) z = z * gain_of(i, e);
-                float t = __builtin_rintf(z * inv);
-                t = fminf(fmaxf(t, -127.0f), 127.0f);
-                q[e / 4] |= ((uint32_t)((int)t) & 0xFFu) << (8 * (e % 4));
+                t[e] = z * inv;
             }
+            uint32_t q[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+                q[d] = pack_codes4(t[4 * d], t[4 * d + 1], t[4 * d + 2], t[4 * d + 3]);
             *reinterpret_cast<uint4*>(smem + 16 * u) = make_uint4(q[0], q[1], q[2], q[3]);
         }
     }
