@@ -53,14 +53,15 @@ __device__ __forceinline__ void lds_barrier() {
 // before the quantisation, as bl_quantize_acts(h, gain) computes it: codes
 // of z = h*g, scale a / (127 * rms(h)), sum h^2 in fp64.
 // KIND: the gating of launch A (relu^2 or SiLU).
-template <bool GLU, int KS, bool SUBLN, int KIND>
-__global__ __launch_bounds__(64 * (GLU ? 2 : 1) * KS) void k_ffn_gemv(
+// RG: groups of 16 rows per workgroup (all share the staged activations).
+template <bool GLU, int KS, bool SUBLN, int KIND, int RG>
+__global__ __launch_bounds__(64 * (GLU ? 2 : 1) * RG * KS) void k_ffn_gemv(
     const uint16_t* __restrict__ xin, int M, int K, const uint32_t* __restrict__ W0,
     const float* __restrict__ g0, const uint32_t* __restrict__ W1,
     const float* __restrict__ g1, int N, float* __restrict__ y, uint16_t* __restrict__ h,
     const uint16_t* __restrict__ gain, float rms_eps) {
     static_assert(!(GLU && SUBLN), "the norm precedes the down projection only");
-    constexpr int NW = (GLU ? 2 : 1) * KS;  // waves
+    constexpr int NW = (GLU ? 2 : 1) * RG * KS;  // waves: (matrix, row group, K split)
     constexpr int NT = 64 * NW;             // threads
     constexpr int CACHE = kFfnCache * kFfnMinThreads / NT;
     static_assert(NT >= kFfnMinThreads && NT <= kFfnMaxThreads && CACHE >= 1, "block shape");
@@ -73,11 +74,12 @@ __global__ __launch_bounds__(64 * (GLU ? 2 : 1) * KS) void k_ffn_gemv(
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int lane = tid % kWave;
-    const int mat = GLU ? wave / KS : 0;
+    const int mat = GLU ? wave / (KS * RG) : 0;
+    const int rg = (wave / KS) % RG;
     const int ks = wave % KS;
     const uint32_t* W = (GLU && mat) ? W1 : W0;
     const int r = lane % 16, g = lane / 16;
-    const int row0 = blockIdx.x * 16;
+    const int row0 = ((int)blockIdx.x * RG + rg) * 16;
     const int row = min(row0 + r, N - 1);
     const int KW = K / 16;
     const int nfull = KW / 16;  // >= KS (checked on the host)
@@ -245,15 +247,15 @@ __global__ __launch_bounds__(64 * (GLU ? 2 : 1) * KS) void k_ffn_gemv(
     // 6. Reduce the K split and write the epilogue (wave 0).
     red[wave][lane] = acc;
     __syncthreads();
-    if (wave != 0 || !tok_ok) return;
+    if (ks != 0 || mat != 0 || !tok_ok) return;  // one wave per row group
     const float xs = s_scale[tok];
     const int nbase = row0 + 4 * (lane / 16);
     if constexpr (GLU) {
-        v4i ga = red[0][lane], ua = red[KS][lane];
+        v4i ga = red[rg * KS][lane], ua = red[(RG + rg) * KS][lane];
 #pragma unroll
         for (int w = 1; w < KS; ++w) {
-            ga += red[w][lane];
-            ua += red[KS + w][lane];
+            ga += red[rg * KS + w][lane];
+            ua += red[(RG + rg) * KS + w][lane];
         }
         ga = -ga;
         ua = -ua;
@@ -269,9 +271,9 @@ __global__ __launch_bounds__(64 * (GLU ? 2 : 1) * KS) void k_ffn_gemv(
                 make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
         }
     } else {
-        v4i ta = red[0][lane];
+        v4i ta = red[rg * KS][lane];
 #pragma unroll
-        for (int w = 1; w < KS; ++w) ta += red[w][lane];
+        for (int w = 1; w < KS; ++w) ta += red[rg * KS + w][lane];
         ta = -ta;
         const float sc = xs * (*g0);
         if (nbase < N)  // four in range, 16-byte aligned (as above)
@@ -297,14 +299,51 @@ bool ffn_fused_supported(int64_t M, int64_t K, int64_t N_ff) {
     return K / 256 >= kKsA && N_ff / 256 >= kKsBSmall;
 }
 
+// Row groups per workgroup (launch A / launch B) by token count. Above one
+// token, launch A shares its staged activations between two groups (2B4T
+// layer at 4 tokens 13.3 -> 12.1 us); launch B keeps one, since its 2560
+// output rows would give only 80 workgroups (14.8 us with two).
+constexpr int kRgA1 = 1, kRgAn = 2, kRgB1 = 1, kRgBn = 1;
+
 namespace {
 
-template <int KS, bool SUBLN>
+template <int KS, bool SUBLN, int RG>
 void launch_ffn_down(const uint16_t* h, int M, int N_ff, const uint32_t* Wd, const float* gd,
                      int K, float* y, const uint16_t* gain, float rms_eps, hipStream_t stream) {
-    hipLaunchKernelGGL((k_ffn_gemv<false, KS, SUBLN, kGluRelu2>), dim3((K + 15) / 16), dim3(64 * KS),
-                       (size_t)M * N_ff, stream, h, M, N_ff, Wd, gd, (const uint32_t*)nullptr,
+    hipLaunchKernelGGL((k_ffn_gemv<false, KS, SUBLN, kGluRelu2, RG>),
+                       dim3((K + 16 * RG - 1) / (16 * RG)), dim3(64 * KS * RG), (size_t)M * N_ff,
+                       stream, h, M, N_ff, Wd, gd, (const uint32_t*)nullptr,
                        (const float*)nullptr, K, y, (uint16_t*)nullptr, gain, rms_eps);
+}
+
+template <int KS, bool SUBLN>
+void launch_ffn_down_rg(const uint16_t* h, int M, int N_ff, const uint32_t* Wd,
+                        const float* gd, int K, float* y, const uint16_t* gain, float rms_eps,
+                        hipStream_t stream) {
+    if ((M == 1 ? kRgB1 : kRgBn) == 2)
+        launch_ffn_down<KS, SUBLN, 2>(h, M, N_ff, Wd, gd, K, y, gain, rms_eps, stream);
+    else
+        launch_ffn_down<KS, SUBLN, 1>(h, M, N_ff, Wd, gd, K, y, gain, rms_eps, stream);
+}
+
+template <int KIND, int RG>
+void launch_ffn_up(const uint16_t* x, int M, int K, const uint32_t* Wg, const float* gg,
+                   const uint32_t* Wu, const float* gu, int N_ff, uint16_t* h,
+                   hipStream_t stream) {
+    hipLaunchKernelGGL((k_ffn_gemv<true, kKsA, false, KIND, RG>),
+                       dim3((N_ff + 16 * RG - 1) / (16 * RG)), dim3(64 * 2 * kKsA * RG),
+                       (size_t)M * K, stream, x, M, K, Wg, gg, Wu, gu, N_ff, (float*)nullptr, h,
+                       (const uint16_t*)nullptr, 0.0f);
+}
+
+template <int KIND>
+void launch_ffn_up_rg(const uint16_t* x, int M, int K, const uint32_t* Wg, const float* gg,
+                      const uint32_t* Wu, const float* gu, int N_ff, uint16_t* h,
+                      hipStream_t stream) {
+    if ((M == 1 ? kRgA1 : kRgAn) == 2)
+        launch_ffn_up<KIND, 2>(x, M, K, Wg, gg, Wu, gu, N_ff, h, stream);
+    else
+        launch_ffn_up<KIND, 1>(x, M, K, Wg, gg, Wu, gu, N_ff, h, stream);
 }
 
 }  // namespace
@@ -315,22 +354,18 @@ hipError_t launch_ffn_fused(const uint16_t* x, int M, int K, const uint32_t* Wg,
                             int kind, const uint16_t* subln_gain, float subln_eps,
                             hipStream_t stream) {
     if (kind == kGluSwiglu)
-        hipLaunchKernelGGL((k_ffn_gemv<true, kKsA, false, kGluSwiglu>), dim3((N_ff + 15) / 16),
-                           dim3(64 * 2 * kKsA), (size_t)M * K, stream, x, M, K, Wg, gg, Wu, gu,
-                           N_ff, (float*)nullptr, h, (const uint16_t*)nullptr, 0.0f);
+        launch_ffn_up_rg<kGluSwiglu>(x, M, K, Wg, gg, Wu, gu, N_ff, h, stream);
     else
-        hipLaunchKernelGGL((k_ffn_gemv<true, kKsA, false, kGluRelu2>), dim3((N_ff + 15) / 16),
-                           dim3(64 * 2 * kKsA), (size_t)M * K, stream, x, M, K, Wg, gg, Wu, gu,
-                           N_ff, (float*)nullptr, h, (const uint16_t*)nullptr, 0.0f);
+        launch_ffn_up_rg<kGluRelu2>(x, M, K, Wg, gg, Wu, gu, N_ff, h, stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const bool big = N_ff / 256 >= kKsB;
     if (subln_gain) {
-        if (big) launch_ffn_down<kKsB, true>(h, M, N_ff, Wd, gd, K, y, subln_gain, subln_eps, stream);
-        else launch_ffn_down<kKsBSmall, true>(h, M, N_ff, Wd, gd, K, y, subln_gain, subln_eps, stream);
+        if (big) launch_ffn_down_rg<kKsB, true>(h, M, N_ff, Wd, gd, K, y, subln_gain, subln_eps, stream);
+        else launch_ffn_down_rg<kKsBSmall, true>(h, M, N_ff, Wd, gd, K, y, subln_gain, subln_eps, stream);
     } else {
-        if (big) launch_ffn_down<kKsB, false>(h, M, N_ff, Wd, gd, K, y, nullptr, 0.0f, stream);
-        else launch_ffn_down<kKsBSmall, false>(h, M, N_ff, Wd, gd, K, y, nullptr, 0.0f, stream);
+        if (big) launch_ffn_down_rg<kKsB, false>(h, M, N_ff, Wd, gd, K, y, nullptr, 0.0f, stream);
+        else launch_ffn_down_rg<kKsBSmall, false>(h, M, N_ff, Wd, gd, K, y, nullptr, 0.0f, stream);
     }
     return hipGetLastError();
 }
