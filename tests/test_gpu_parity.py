@@ -303,6 +303,37 @@ def test_wide_gemv_multi_block_splits_sampled(M, K, N):
     assert torch.equal(y0.view(torch.int32), y.view(torch.int32))
 
 
+def _random_shapes(n, seed, budget=1.5e8):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        M = int(rng.choice([1, 2, 3, 5, 8, 13, 16, 17, 31, 33, 47, 64, 65, 100, 129, 257]))
+        K = 64 * int(rng.integers(1, 97))
+        N = int(rng.integers(1, 3001))
+        if M * N * K <= budget:
+            out.append((M, K, N))
+    return out
+
+
+@pytest.mark.parametrize("M,K,N", _random_shapes(24, 1234))
+def test_random_shapes_every_path(M, K, N):
+    """Seeded random shapes through every product path that applies
+    (automatic, GEMV, GEMM, wide GEMV): int32 sums equal to the oracle's,
+    outputs within 1e-6."""
+    q, xq, xs, g = _product_case(M, K, N, 70 + M + K + N)
+    y_ref, acc_ref = oracle.bitlinear(xq, xs, q, g)
+    args = (torch.from_numpy(xq).to(DEV), dev_f32(xs), dev_packed(oracle.pack(q)), dev_f32([g]))
+    paths = [0, 2]
+    if M <= 16 and M * K <= 128 * 1024:
+        paths.append(1)
+    if M <= 64:
+        paths.append(3)
+    for path in paths:
+        y, acc = bl.bitlinear(*args, return_acc=True, path=path)
+        assert np.array_equal(acc.cpu().numpy(), acc_ref), f"path {path}"
+        assert_y_close(y.cpu().numpy(), y_ref, f"path {path}")
+
+
 def test_gemv_and_gemm_agree_bitwise():
     for M, K, N in [(1, 2560, 6912), (16, 6912, 2560), (4, 3200, 8640)]:
         q, xq, xs, g = _product_case(M, K, N, 55)
