@@ -278,6 +278,30 @@ def main():
         "timing": "HIP graph of the M=1 pass (k_ffn_gemv launches only), HIP events on "
                   "the replay stream",
     }
+    # The same bytes through a plain 16-byte read stream in the same launch
+    # pattern (one launch over the gate+up bytes, one over the down bytes,
+    # per layer): the ceiling for launches of this size, where launch latency
+    # and not HBM bandwidth dominates.
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    n_a = bytes_a // 16 * 16
+    n_b = bytes_b // 16 * 16
+    rbufs = [(torch.empty(n_a // 4, dtype=torch.int32, device=dev),
+              torch.empty(n_b // 4, dtype=torch.int32, device=dev)) for _ in range(L)]
+
+    def read_pass():
+        for ra, rb in rbufs:
+            bl.calib_read(ra, sink)
+            bl.calib_read(rb, sink)
+
+    read_pass()
+    gr_read = capture(read_pass)
+    st_read = replay_stats(gr_read, 20, 2 * L)
+    del gr_read, rbufs
+    read_gbps = (n_a + n_b) / 2 / (st_read["mean_us"] * 1e-6) / 1e9
+    roofline["same_size_read_ceiling"] = {
+        "kernel": "k_calib_read", "bytes_per_launch": round((n_a + n_b) / 2),
+        "GBps": round(read_gbps, 1), "us_per_launch": st_read["mean_us"],
+        "achieved_over_it": round(achieved / read_gbps, 4)}
     used_graph = graph is not None
     del layers, graph
     torch.cuda.empty_cache()
@@ -335,6 +359,24 @@ def main():
             per[name] = {"M": M, "K": K, "N": N, "avg_us": round(1e3 * ms / n, 2),
                          "TOPS": round(2 * M * N * K * n / (ms * 1e-3) / 1e12, 1)}
         tops = ops * reps / (gemm_ms * 1e-3) / 1e12
+        # Context only: the vendor's plain int8 GEMM on the same shapes
+        # (int8 x int8 -> int32, no ternary expansion, no fp32 epilogue).
+        vendor_us = {}
+        for name, K, N, x, xq, xs, pk, g, y in legs:
+            b8 = torch.randint(-1, 2, (K, N), dtype=torch.int8, device=dev)
+            torch._int_mm(xq, b8)
+            torch.cuda.synchronize()
+            ea = torch.cuda.Event(enable_timing=True)
+            eb = torch.cuda.Event(enable_timing=True)
+            ea.record()
+            for _ in range(reps):
+                torch._int_mm(xq, b8)
+            eb.record()
+            torch.cuda.synchronize()
+            vendor_us[name] = 1e3 * ea.elapsed_time(eb) / reps
+            per[name]["vendor_int8_gemm_us"] = round(vendor_us[name], 2)
+            del b8
+        vendor_tops = ops / (sum(vendor_us.values()) * 1e-6) / 1e12
         alg = sum(N * K // 4 + 4 + M * K + 4 * M + 4 * M * N for _, K, N, *_ in legs) / len(legs)
         out = {
             "ms_per_step": round(p_ms, 4),
@@ -347,6 +389,11 @@ def main():
                          "alg_bytes_per_call": round(alg),
                          "per_projection": per},
             "act_quant_avg_us": round(1e3 * tp.total_ms("act_quant") / tp.count("act_quant"), 2),
+            "vendor_int8_gemm": {
+                "library": "hipBLASLt through torch._int_mm: int8 x int8 -> int32 on the same "
+                           "shapes, without the ternary expansion or the fp32 epilogue "
+                           "(context, not a target)",
+                "TOPS": round(vendor_tops, 1)},
         }
         del legs
         torch.cuda.empty_cache()
