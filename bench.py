@@ -444,12 +444,36 @@ def main():
                          "avg_us": round(1e3 * ms / reps, 2),
                          "TFLOPs": round(2 * Mp * N * K * reps / (ms * 1e-3) / 1e12, 1)}
         tf = flops / (tot_ms * 1e-3) / 1e12
+        # Context only: the vendor's dense bf16 GEMM dy . W on the same shapes
+        # (W as a contiguous bf16 [N][K] matrix of {-1, 0, +1}, bf16 out).
+        v_us = 0.0
+        for name, K, N, qT, g, dy, dx in legs:
+            wb = torch.randint(-1, 2, (N, K), device=dev).to(torch.bfloat16).contiguous()
+            torch.matmul(dy, wb)
+            torch.cuda.synchronize()
+            ea = torch.cuda.Event(enable_timing=True)
+            eb = torch.cuda.Event(enable_timing=True)
+            ea.record()
+            for _ in range(reps):
+                torch.matmul(dy, wb)
+            eb.record()
+            torch.cuda.synchronize()
+            us = 1e3 * ea.elapsed_time(eb) / reps
+            per[name]["vendor_bf16_gemm_us"] = round(us, 2)
+            v_us += us
+            del wb
+        vendor_tf = flops / reps / (v_us * 1e-6) / 1e12
         ste = {"workload": "dx of the 4096-token projections (dy bf16 [4096][N] -> dx fp32 "
                            "[4096][K]), straight-through estimator",
                "roofline": {"bound": "mfma", "kernel": "k_ste_dx (v_mfma_f32_32x32x16_bf16)",
                             "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS,
                             "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
-                            "traffic": None, "per_projection": per}}
+                            "traffic": None, "per_projection": per},
+               "vendor_bf16_gemm": {
+                   "library": "hipBLASLt through torch.matmul: dense bf16 x bf16 -> bf16 on "
+                              "the same shapes, weights stored as bf16 (context, not a "
+                              "target)",
+                   "TFLOPs": round(vendor_tf, 1)}}
         del legs
         torch.cuda.empty_cache()
         print(f"ste dx: {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
