@@ -246,8 +246,9 @@ size_t bl_ffn_relu2_workspace_bytes(int64_t M, int64_t K, int64_t N_ff);
  *   workspace  tmp  >= bl_ffn_relu2_workspace_bytes(M, K, N_ff) bytes,
  *                   256-byte aligned; contents undefined afterwards.
  * Shapes follow the rules above for (M, K), (M, N_ff) and both weight
- * matrices. For M <= 4 (M dividing 256) the step runs in two launches, with
- * each workgroup quantising its activations itself; otherwise in four. */
+ * matrices. For M in {1, 2, 4, 8, 16} with M*K and M*N_ff up to 128 KiB the
+ * step runs in two launches, with each workgroup quantising its activations
+ * itself; otherwise in four. */
 int bl_ffn_relu2(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate,
                  const float* gamma_gate, const uint32_t* W_up, const float* gamma_up,
                  int64_t N_ff, const uint32_t* W_down, const float* gamma_down, float* y,

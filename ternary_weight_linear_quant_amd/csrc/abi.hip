@@ -212,7 +212,7 @@ int ffn_step(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate,
     hipStream_t st = as_stream(stream);
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     auto* h = reinterpret_cast<uint16_t*>(ws + L.h);
-    if (bl::ffn_fused_supported(M, K, N_ff))
+    if (bl::ffn_fused_supported(M, K, N_ff, subln_gain != nullptr))
         return hip_status(bl::launch_ffn_fused(x, (int)M, (int)K, W_gate, gamma_gate, W_up,
                                                gamma_up, (int)N_ff, W_down, gamma_down, h, y,
                                                kind, subln_gain, subln_eps, st));

@@ -18,7 +18,9 @@
 // Each step uses exactly the arithmetic of bl_quantize_acts, bl_bitlinear
 // and bl_relu2_glu, so the output bits equal the unfused sequence. The
 // per-workgroup quantisation re-reads the M tokens from L2 in every
-// workgroup, which is cheap for M <= 4 and removes two launches per layer.
+// workgroup: cheap for a few tokens, and still ahead of the four-launch
+// sequence at 8 and 16 (the bf16 inputs are cached in registers, up to 16
+// units of 16 values per thread, one workgroup per CU at 16 tokens).
 //
 // Ordering inside a workgroup: the activation loads are issued first, the
 // R weight-chunk loads right after (always R, clamped to the wave's range),
@@ -37,7 +39,8 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kFfnMaxThreads = 1024;
 constexpr int kFfnMinThreads = 256;
-constexpr int kFfnCache = 8;  // 16-value activation units cached per thread (at 256 threads)
+constexpr int kFfnMaxCache = 16;  // 16-value activation units cached per thread, at most
+constexpr int kFfnSublnCache = 4;  // with the norm's gain cached beside them
 constexpr int kFfnR = 4;      // weight chunks in flight per lane
 
 // lgkmcnt(0) only: LDS traffic done, vector loads may stay in flight.
@@ -54,7 +57,9 @@ __device__ __forceinline__ void lds_barrier() {
 // of z = h*g, scale a / (127 * rms(h)), sum h^2 in fp64.
 // KIND: the gating of launch A (relu^2 or SiLU).
 // RG: groups of 16 rows per workgroup (all share the staged activations).
-template <bool GLU, int KS, bool SUBLN, int KIND, int RG>
+// CU: activation units (16 values of one token) cached per thread; the M
+// tokens' K values must fit NT * CU units.
+template <bool GLU, int KS, bool SUBLN, int KIND, int RG, int CU>
 __global__ __launch_bounds__(64 * (GLU ? 2 : 1) * RG * KS) void k_ffn_gemv(
     const uint16_t* __restrict__ xin, int M, int K, const uint32_t* __restrict__ W0,
     const float* __restrict__ g0, const uint32_t* __restrict__ W1,
@@ -63,8 +68,9 @@ __global__ __launch_bounds__(64 * (GLU ? 2 : 1) * RG * KS) void k_ffn_gemv(
     static_assert(!(GLU && SUBLN), "the norm precedes the down projection only");
     constexpr int NW = (GLU ? 2 : 1) * RG * KS;  // waves: (matrix, row group, K split)
     constexpr int NT = 64 * NW;             // threads
-    constexpr int CACHE = kFfnCache * kFfnMinThreads / NT;
+    constexpr int CACHE = CU;
     static_assert(NT >= kFfnMinThreads && NT <= kFfnMaxThreads && CACHE >= 1, "block shape");
+    static_assert(!SUBLN || CU <= kFfnSublnCache, "register budget of the norm's gain cache");
     extern __shared__ __align__(16) uint8_t smem[];  // int8 activations, token-minor
     __shared__ v4i red[NW][kWave];
     __shared__ float s_amax[NW][16];
@@ -289,61 +295,113 @@ __global__ __launch_bounds__(64 * (GLU ? 2 : 1) * RG * KS) void k_ffn_gemv(
 // 2048.
 constexpr int kKsA = 2, kKsB = 8, kKsBSmall = 4;
 
-bool ffn_fused_supported(int64_t M, int64_t K, int64_t N_ff) {
-    if (M < 1 || M > 4 || (256 % M) != 0) return false;
-    if (K % 64 != 0 || N_ff % 64 != 0) return false;  // whole 4-output stores
-    // Activation units must fit the register cache; every K-split wave needs
-    // at least one full 256-weight chunk.
-    if (M * (K / 16) > kFfnMinThreads * kFfnCache || M * (N_ff / 16) > kFfnMinThreads * kFfnCache)
-        return false;
-    return K / 256 >= kKsA && N_ff / 256 >= kKsBSmall;
-}
-
 // Row groups per workgroup (launch A / launch B) by token count. Above one
 // token, launch A shares its staged activations between two groups (2B4T
 // layer at 4 tokens 13.3 -> 12.1 us); launch B keeps one, since its 2560
 // output rows would give only 80 workgroups (14.8 us with two).
-constexpr int kRgA1 = 1, kRgAn = 2, kRgB1 = 1, kRgBn = 1;
+constexpr int kRgA1 = 1, kRgAn = 2, kRgB1 = 1;
 
 namespace {
 
-template <int KS, bool SUBLN, int RG>
-void launch_ffn_down(const uint16_t* h, int M, int N_ff, const uint32_t* Wd, const float* gd,
-                     int K, float* y, const uint16_t* gain, float rms_eps, hipStream_t stream) {
-    hipLaunchKernelGGL((k_ffn_gemv<false, KS, SUBLN, kGluRelu2, RG>),
-                       dim3((K + 16 * RG - 1) / (16 * RG)), dim3(64 * KS * RG), (size_t)M * N_ff,
+// Threads of launch A (gate + up) and launch B (down) at M tokens.
+int threads_a(int M) { return 64 * 2 * kKsA * (M == 1 ? kRgA1 : kRgAn); }
+int threads_b(int N_ff) { return 64 * (N_ff / 256 >= kKsB ? kKsB : kKsBSmall) * kRgB1; }
+
+// Smallest instantiated cache (4, 8 or 16 units per thread) holding `units`
+// over `threads`; 0 if none does.
+int cache_for(int64_t units, int threads) {
+    for (int cu : {4, 8, 16})
+        if (units <= (int64_t)cu * threads) return cu;
+    return 0;
+}
+
+}  // namespace
+
+bool ffn_fused_supported(int64_t M, int64_t K, int64_t N_ff, bool subln) {
+    // Token counts dividing a wave (lanes with equal lane % M hold one token).
+    if (M != 1 && M != 2 && M != 4 && M != 8 && M != 16) return false;
+    if (K % 64 != 0 || N_ff % 64 != 0) return false;  // whole 4-output stores
+    if (K > (1 << 20) || N_ff > (1 << 20)) return false;
+    // Every K-split wave needs at least one full 256-weight chunk.
+    if (K / 256 < kKsA || N_ff / 256 < kKsBSmall) return false;
+    const int ca = cache_for(M * (K / 16), threads_a((int)M));
+    const int cb = cache_for(M * (N_ff / 16), threads_b((int)N_ff));
+    if (ca == 0 || cb == 0) return false;
+    if (subln && cb > kFfnSublnCache) return false;
+    // The int8 activations of either launch must fit LDS beside the statics.
+    return M * K <= 128 * 1024 && M * N_ff <= 128 * 1024;
+}
+
+namespace {
+
+template <typename Kern>
+hipError_t allow_lds(Kern kern, size_t lds) {
+    if (lds <= 64 * 1024) return hipSuccess;
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+}
+
+template <int KS, bool SUBLN, int RG, int CU>
+hipError_t launch_ffn_down(const uint16_t* h, int M, int N_ff, const uint32_t* Wd,
+                           const float* gd, int K, float* y, const uint16_t* gain,
+                           float rms_eps, hipStream_t stream) {
+    auto kern = &k_ffn_gemv<false, KS, SUBLN, kGluRelu2, RG, CU>;
+    const size_t lds = (size_t)M * N_ff;
+    hipError_t e = allow_lds(kern, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((K + 16 * RG - 1) / (16 * RG)), dim3(64 * KS * RG), lds,
                        stream, h, M, N_ff, Wd, gd, (const uint32_t*)nullptr,
                        (const float*)nullptr, K, y, (uint16_t*)nullptr, gain, rms_eps);
+    return hipGetLastError();
 }
 
 template <int KS, bool SUBLN>
-void launch_ffn_down_rg(const uint16_t* h, int M, int N_ff, const uint32_t* Wd,
-                        const float* gd, int K, float* y, const uint16_t* gain, float rms_eps,
-                        hipStream_t stream) {
-    if ((M == 1 ? kRgB1 : kRgBn) == 2)
-        launch_ffn_down<KS, SUBLN, 2>(h, M, N_ff, Wd, gd, K, y, gain, rms_eps, stream);
-    else
-        launch_ffn_down<KS, SUBLN, 1>(h, M, N_ff, Wd, gd, K, y, gain, rms_eps, stream);
+hipError_t launch_ffn_down_cu(const uint16_t* h, int M, int N_ff, const uint32_t* Wd,
+                              const float* gd, int K, float* y, const uint16_t* gain,
+                              float rms_eps, hipStream_t stream) {
+    const int cu = cache_for((int64_t)M * (N_ff / 16), 64 * KS * kRgB1);
+    if constexpr (!SUBLN) {
+        if (cu == 16)
+            return launch_ffn_down<KS, false, kRgB1, 16>(h, M, N_ff, Wd, gd, K, y, gain, rms_eps,
+                                                         stream);
+        if (cu == 8)
+            return launch_ffn_down<KS, false, kRgB1, 8>(h, M, N_ff, Wd, gd, K, y, gain, rms_eps,
+                                                        stream);
+    }
+    return launch_ffn_down<KS, SUBLN, kRgB1, 4>(h, M, N_ff, Wd, gd, K, y, gain, rms_eps, stream);
+}
+
+template <int KIND, int RG, int CU>
+hipError_t launch_ffn_up(const uint16_t* x, int M, int K, const uint32_t* Wg, const float* gg,
+                         const uint32_t* Wu, const float* gu, int N_ff, uint16_t* h,
+                         hipStream_t stream) {
+    auto kern = &k_ffn_gemv<true, kKsA, false, KIND, RG, CU>;
+    const size_t lds = (size_t)M * K;
+    hipError_t e = allow_lds(kern, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((N_ff + 16 * RG - 1) / (16 * RG)), dim3(64 * 2 * kKsA * RG),
+                       lds, stream, x, M, K, Wg, gg, Wu, gu, N_ff, (float*)nullptr, h,
+                       (const uint16_t*)nullptr, 0.0f);
+    return hipGetLastError();
 }
 
 template <int KIND, int RG>
-void launch_ffn_up(const uint16_t* x, int M, int K, const uint32_t* Wg, const float* gg,
-                   const uint32_t* Wu, const float* gu, int N_ff, uint16_t* h,
-                   hipStream_t stream) {
-    hipLaunchKernelGGL((k_ffn_gemv<true, kKsA, false, KIND, RG>),
-                       dim3((N_ff + 16 * RG - 1) / (16 * RG)), dim3(64 * 2 * kKsA * RG),
-                       (size_t)M * K, stream, x, M, K, Wg, gg, Wu, gu, N_ff, (float*)nullptr, h,
-                       (const uint16_t*)nullptr, 0.0f);
+hipError_t launch_ffn_up_cu(const uint16_t* x, int M, int K, const uint32_t* Wg,
+                            const float* gg, const uint32_t* Wu, const float* gu, int N_ff,
+                            uint16_t* h, hipStream_t stream) {
+    const int cu = cache_for((int64_t)M * (K / 16), 64 * 2 * kKsA * RG);
+    if (cu == 16) return launch_ffn_up<KIND, RG, 16>(x, M, K, Wg, gg, Wu, gu, N_ff, h, stream);
+    if (cu == 8) return launch_ffn_up<KIND, RG, 8>(x, M, K, Wg, gg, Wu, gu, N_ff, h, stream);
+    return launch_ffn_up<KIND, RG, 4>(x, M, K, Wg, gg, Wu, gu, N_ff, h, stream);
 }
 
 template <int KIND>
-void launch_ffn_up_rg(const uint16_t* x, int M, int K, const uint32_t* Wg, const float* gg,
-                      const uint32_t* Wu, const float* gu, int N_ff, uint16_t* h,
-                      hipStream_t stream) {
+hipError_t launch_ffn_up_rg(const uint16_t* x, int M, int K, const uint32_t* Wg,
+                            const float* gg, const uint32_t* Wu, const float* gu, int N_ff,
+                            uint16_t* h, hipStream_t stream) {
     if ((M == 1 ? kRgA1 : kRgAn) == 2)
-        launch_ffn_up<KIND, 2>(x, M, K, Wg, gg, Wu, gu, N_ff, h, stream);
-    else
-        launch_ffn_up<KIND, 1>(x, M, K, Wg, gg, Wu, gu, N_ff, h, stream);
+        return launch_ffn_up_cu<KIND, 2>(x, M, K, Wg, gg, Wu, gu, N_ff, h, stream);
+    return launch_ffn_up_cu<KIND, 1>(x, M, K, Wg, gg, Wu, gu, N_ff, h, stream);
 }
 
 }  // namespace
@@ -353,21 +411,20 @@ hipError_t launch_ffn_fused(const uint16_t* x, int M, int K, const uint32_t* Wg,
                             const uint32_t* Wd, const float* gd, uint16_t* h, float* y,
                             int kind, const uint16_t* subln_gain, float subln_eps,
                             hipStream_t stream) {
-    if (kind == kGluSwiglu)
-        launch_ffn_up_rg<kGluSwiglu>(x, M, K, Wg, gg, Wu, gu, N_ff, h, stream);
-    else
-        launch_ffn_up_rg<kGluRelu2>(x, M, K, Wg, gg, Wu, gu, N_ff, h, stream);
-    hipError_t e = hipGetLastError();
+    hipError_t e =
+        kind == kGluSwiglu
+            ? launch_ffn_up_rg<kGluSwiglu>(x, M, K, Wg, gg, Wu, gu, N_ff, h, stream)
+            : launch_ffn_up_rg<kGluRelu2>(x, M, K, Wg, gg, Wu, gu, N_ff, h, stream);
     if (e != hipSuccess) return e;
     const bool big = N_ff / 256 >= kKsB;
-    if (subln_gain) {
-        if (big) launch_ffn_down_rg<kKsB, true>(h, M, N_ff, Wd, gd, K, y, subln_gain, subln_eps, stream);
-        else launch_ffn_down_rg<kKsBSmall, true>(h, M, N_ff, Wd, gd, K, y, subln_gain, subln_eps, stream);
-    } else {
-        if (big) launch_ffn_down_rg<kKsB, false>(h, M, N_ff, Wd, gd, K, y, nullptr, 0.0f, stream);
-        else launch_ffn_down_rg<kKsBSmall, false>(h, M, N_ff, Wd, gd, K, y, nullptr, 0.0f, stream);
-    }
-    return hipGetLastError();
+    if (subln_gain)
+        return big ? launch_ffn_down_cu<kKsB, true>(h, M, N_ff, Wd, gd, K, y, subln_gain,
+                                                    subln_eps, stream)
+                   : launch_ffn_down_cu<kKsBSmall, true>(h, M, N_ff, Wd, gd, K, y, subln_gain,
+                                                         subln_eps, stream);
+    return big ? launch_ffn_down_cu<kKsB, false>(h, M, N_ff, Wd, gd, K, y, nullptr, 0.0f, stream)
+               : launch_ffn_down_cu<kKsBSmall, false>(h, M, N_ff, Wd, gd, K, y, nullptr, 0.0f,
+                                                      stream);
 }
 
 }  // namespace bl

@@ -52,7 +52,7 @@ hipError_t launch_gemv_pair(const int8_t* xq, const float* xs, int M, int K, con
 
 // Two-launch decode FFN (act quant + gate/up + squared-ReLU gating, then act
 // quant + down), bit-identical to the unfused sequence.
-bool ffn_fused_supported(int64_t M, int64_t K, int64_t N_ff);
+bool ffn_fused_supported(int64_t M, int64_t K, int64_t N_ff, bool subln);
 hipError_t launch_ffn_fused(const uint16_t* x, int M, int K, const uint32_t* Wg,
                             const float* gg, const uint32_t* Wu, const float* gu, int N_ff,
                             const uint32_t* Wd, const float* gd, uint16_t* h, float* y,

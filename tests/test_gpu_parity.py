@@ -550,10 +550,10 @@ def test_ffn_block_fused_path_equals_unfused():
         assert torch.equal(y.view(torch.int32), ry.view(torch.int32))
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 16, 40])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 16, 40])
 @pytest.mark.parametrize("K,N_ff", [(2560, 6912), (3200, 8640), (512, 1024)])
 def test_ffn_relu2_matches_unfused_sequence(M, K, N_ff):
-    """bl_ffn_relu2 (two launches for M <= 4, four otherwise) gives the bits
+    """bl_ffn_relu2 (two launches for M in 1, 2, 4, 8, 16, four otherwise) gives the bits
     of quantize_acts -> bitlinear(gate, up) -> relu2_glu -> quantize_acts ->
     bitlinear(down); the unfused sequence is checked against the oracle by
     the stage-wise block test."""
@@ -721,7 +721,7 @@ def test_swiglu_quant_from_gpu_h(M, K):
 @pytest.mark.parametrize("M", [1, 4, 5, 16])
 @pytest.mark.parametrize("K,N_ff", [(3200, 8640), (512, 1024)])
 def test_ffn_step_swiglu_matches_unfused_sequence(M, K, N_ff):
-    """bl_ffn_step with SwiGLU gating (two launches for M <= 4, four
+    """bl_ffn_step with SwiGLU gating (two launches for M in 1, 2, 4, 8, 16, four
     otherwise) against the single calls: bit-exact without the norm, y within
     2e-6 relative with it."""
     wid = 74
