@@ -1,6 +1,6 @@
 """bench.py's command-line contract, checked on the CPU: one GPU only (a
-larger --gpus exits with a message before touching a device), and the
-derived figures it reports are computed the way its JSON names say."""
+larger --gpus exits with a message before touching a device), the flags the
+contract names, and a loud failure without a GPU."""
 import os
 import subprocess
 import sys
