@@ -21,6 +21,9 @@ committed rocprofv3 counter summary when the kernel sources are unchanged):
     M = 64 (GEMM), over rotated weight copies;
   - prefill GEMMs: M = 4096 on 2560 <-> 6912 and M = 2048 on the 70B shapes
     (int8 TOPS against the matrix-core peak);
+  - one 2560 -> 2560 projection and a 3B-class block (q, k, v, o 3200 ->
+    3200; gate, up 3200 -> 8640; down 8640 -> 3200) at M = 1 over rotated
+    weight copies, and the 3B block's projections at M = 512;
   - measured ceilings of own-code calibration kernels (a read-only 16-byte
     HBM stream and an int8 matrix-core loop);
   - the CPU oracle timed on a bounded sample of the decode step.
@@ -48,6 +51,8 @@ DECODE_WORKLOAD = 2         # 2B4T-shaped FFN at decode
 PREFILL_WORKLOAD = 3        # one 4096-token sequence
 LARGE_WORKLOAD = 5          # 70B-class shapes
 LARGE_COPIES = 5            # 5 x 2 x 58.7 MB of packed weights > 2 x 256 MB
+SMALL_COPIES = 400          # 400 x 1.64 MB of 2560 x 2560 packed weights
+BLOCK3B_COPIES = 20         # 20 x 31.1 MB of 3B-block packed weights
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
 
 
@@ -63,6 +68,8 @@ def parse_args():
                    help="CPU-oracle sample budget (0 disables the leg)")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-large", action="store_true", help="skip the 70B-class legs")
+    p.add_argument("--no-small", action="store_true",
+                   help="skip the single-2560 and 3B-block legs")
     p.add_argument("--no-graph", action="store_true", help="time eager launches instead")
     return p.parse_args()
 
@@ -401,6 +408,59 @@ def main():
         print(f"{label}: GEMM {tops:.1f} TOPS", file=sys.stderr, flush=True)
         return out
 
+    def rotated_decode(wid, copies):
+        """M = 1 BitLinears over `copies` rotated copies of every projection of
+        a workload, replayed from one HIP graph: per-launch time and rates."""
+        _, wprojs, _ = wl.WORKLOADS[wid]
+        w = {name: prepare(wid, i, N, K, copies) for i, (name, K, N) in enumerate(wprojs)}
+        io = {}
+        for i, (name, K, N) in enumerate(wprojs):
+            xq, xs = bl.quantize_acts(bf16_dev(wl.activations(wid, i, 1, K)))
+            io[name] = (xq, xs, torch.empty((1, N), dtype=torch.float32, device=dev))
+
+        def rotation():
+            for c in range(copies):
+                for name, K, N in wprojs:
+                    xq, xs, y = io[name]
+                    bl.bitlinear(xq, xs, *w[name][c], out=y)
+
+        rotation()
+        torch.cuda.synchronize()
+        gr = capture(rotation)
+        st = replay_stats(gr, 20, copies * len(wprojs))
+        del gr, w, io
+        torch.cuda.empty_cache()
+        t = st["mean_us"] * 1e-6
+        packed = sum(N * K // 4 for _, K, N in wprojs) / len(wprojs)
+        alg = sum(N * K // 4 + 4 + K + 4 + 4 * N for _, K, N in wprojs) / len(wprojs)
+        return {"kernel": "k_gemv", "copies": copies,
+                "packed_GBps": round(packed / t / 1e9, 1),
+                "roofline": {"bound": "hbm", "achieved": round(alg / t / 1e9, 1),
+                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(alg / t / 1e9 / HBM_PEAK_GBS, 4),
+                             "traffic": traffic.get("gemv_2560_m1" if wid == 1
+                                                    else "gemv_3b_m1"),
+                             "traffic_unit": "HBM bytes per bl_bitlinear call",
+                             "alg_bytes_per_call": round(alg)},
+                "per_launch": st,
+                "timing": "HIP graph of the rotation, HIP events on the replay stream"}
+
+    # ----------------------- single 2560 projection and the 3B block ----
+    small = None
+    if not args.no_small:
+        small = {"single_2560_decode_M1": rotated_decode(1, SMALL_COPIES)}
+        small["single_2560_decode_M1"]["workload"] = "one 2560->2560 projection at M=1"
+        small["block_3b_decode_M1"] = rotated_decode(4, BLOCK3B_COPIES)
+        small["block_3b_decode_M1"]["workload"] = (
+            "3B block at M=1: q, k, v, o 3200->3200; gate, up 3200->8640; down 8640->3200")
+        print(f"2560 decode M=1: {small['single_2560_decode_M1']['packed_GBps']} GB/s packed; "
+              f"3B block decode M=1: {small['block_3b_decode_M1']['packed_GBps']} GB/s packed",
+              file=sys.stderr, flush=True)
+        _, p4, _ = wl.WORKLOADS[4]
+        small["block_3b_prefill_M512"] = gemm_leg("gemm_3b_m512", 4, 512, p4,
+                                                  max(10, args.steps))
+        small["block_3b_prefill_M512"]["workload"] = "3B block's seven projections at M=512"
+
     # ------------------------------------------------ prefill GEMM leg ----
     prefill = None
     if not args.no_prefill:
@@ -691,6 +751,7 @@ def main():
         "prefill": prefill,
         "ste_backward": ste,
         "large_70b": large,
+        "small_configs": small,
         "ceilings": ceilings,
         "weight_prep": {"matrices": list(base), "ms_total": round(wp_ms, 3),
                         "fp32_read_GBps": round(wp_bytes / (wp_ms * 1e-3) / 1e9, 1)},

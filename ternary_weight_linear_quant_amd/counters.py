@@ -41,6 +41,8 @@ COPY_CALLS = 3
 MARKER_BYTES = 16 * 256         # one block: a marker dispatch
 LAYERS_2B4T = 40                # weight copies, as in the benchmark
 COPIES_70B = 5                  # 5 x 2 x 58.7 MB > 2 x the 256 MB Infinity Cache
+LAYERS_3B = 20                  # 20 x 31.1 MB of 3B-block weights
+COPIES_2560 = 400               # 400 x 1.64 MB of 2560 x 2560 weights
 
 # phase label -> (sources its kernels are built from, what the phase runs,
 # roofline units in the phase, what one unit is). HBM bytes are reported per
@@ -63,6 +65,16 @@ PHASES = {
                             "bl_bitlinear at M=64 on the 70B shapes, 5 rotated copies",
                             2 * COPIES_70B,
                             "bl_bitlinear call (split K: zero, k_gemv_wide, finalize)"),
+    "gemv_2560_m1": (["gemv.hip", "common.hpp"],
+                     "bl_bitlinear at M=1 on 2560->2560, 400 rotated copies",
+                     COPIES_2560, "k_gemv launch"),
+    "gemv_3b_m1": (["gemv.hip", "common.hpp"],
+                   "bl_bitlinear at M=1 on the 3B block (q, k, v, o 3200->3200; gate, up "
+                   "3200->8640; down 8640->3200), 20 rotated layers",
+                   7 * LAYERS_3B, "bl_bitlinear call (k_gemv)"),
+    "gemm_3b_m512": (["gemm.hip", "gemv_wide.hip", "common.hpp"],
+                     "bl_bitlinear at M=512 on the 3B block's seven projections", 7,
+                     "bl_bitlinear call"),
     "gemm_prefill_4096": (["gemm.hip", "common.hpp"],
                           "bl_bitlinear at M=4096 on 2560->6912 and 6912->2560", 2,
                           "bl_bitlinear call (k_gemm)"),
@@ -134,6 +146,20 @@ def run():
         del W
         w5bin[name] = [(bits.clone(), gb.clone()) for _ in range(COPIES_70B)]
 
+    _, p1, _ = wl.WORKLOADS[1]
+    _, K1, N1 = p1[0]
+    w1 = weights(1, 0, N1, K1, COPIES_2560)
+    xq1, xs1 = bl.quantize_acts(bf16(wl.activations(1, 0, 1, K1)))
+    y1 = torch.empty((1, N1), dtype=torch.float32, device=dev)
+
+    _, p4, _ = wl.WORKLOADS[4]
+    w4 = {name: weights(4, i, N, K, LAYERS_3B) for i, (name, K, N) in enumerate(p4)}
+    q4 = {}
+    for M in (1, 512):
+        for i, (name, K, N) in enumerate(p4):
+            xq, xs = bl.quantize_acts(bf16(wl.activations(4, i, M, K)))
+            q4[(M, name)] = (xq, xs, torch.empty((M, N), dtype=torch.float32, device=dev))
+
     _, p3, M3 = wl.WORKLOADS[3]
     q3 = []
     for i, (name, K, N) in enumerate(p3):
@@ -178,6 +204,18 @@ def run():
                     fn(xq, xs, *wset[name][c], out=y)
         return run_fmt
 
+    def single2560():
+        for c in range(COPIES_2560):
+            bl.bitlinear(xq1, xs1, *w1[c], out=y1)
+
+    def block3b(M):
+        def fn():
+            for c in range(LAYERS_3B if M == 1 else 1):
+                for name, _, _ in p4:
+                    xq, xs, y = q4[(M, name)]
+                    bl.bitlinear(xq, xs, *w4[name][c], out=y)
+        return fn
+
     def prefill4096():
         for xq, xs, pk, g, y in q3:
             bl.bitlinear(xq, xs, pk, g, out=y)
@@ -193,6 +231,9 @@ def run():
     phase("gemv_70b_m1_base3", rotate70_fmt(bl.bitlinear_base3, w5b3))
     phase("gemv_70b_m1_binary", rotate70_fmt(bl.bitlinear_binary, w5bin))
     phase("wide_decode_70b_m64", rotate70(64))
+    phase("gemv_2560_m1", single2560)
+    phase("gemv_3b_m1", block3b(1))
+    phase("gemm_3b_m512", block3b(512))
     phase("gemm_prefill_4096", prefill4096)
     phase("gemm_prefill_70b", prefill70)
     marker()

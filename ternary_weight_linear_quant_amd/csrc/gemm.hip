@@ -87,6 +87,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_gemm(
     const int bn = (t % (G * nN)) / gsize;
     const int m0 = bm * BM, n0 = bn * BN;
 
+    // Thread t < BM fetches the scale of row m0 + t now; the load's latency
+    // is hidden behind the main loop, and the epilogue shares it.
+    static_assert(BM <= 64 * NW, "one row scale per thread");
+    float xs_row = 0.0f;
+    if (!SPLIT && tid < BM && m0 + tid < M) xs_row = xs[m0 + tid];
+
     const int KT = (K + kBK - 1) / kBK;
     const bool k_tail = (K % kBK) != 0;  // last stage holds 64 valid k
     // This workgroup's K steps: global step kt0 + kt for local kt < NK (>= 1).
@@ -277,14 +283,22 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_gemm(
         }
         return;
     }
+    // The tile's row scales reach every lane through LDS (a region past the
+    // ring): a global load issued among the output stores would wait for
+    // those stores as well (vector loads and stores retire through one
+    // counter in issue order), one round trip per row.
+    float* xs_lds = reinterpret_cast<float*>(smem + STAGES * STAGE);
+    if (tid < BM) xs_lds[tid] = xs_row;
+    __syncthreads();
     const float gm = *gamma_p;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const int m = m0 + wm0 + 32 * i + 8 * (v / 4) + 4 * (lane / 32) + (v % 4);
+            const int r = wm0 + 32 * i + 8 * (v / 4) + 4 * (lane / 32) + (v % 4);
+            const int m = m0 + r;
             if (m < M) {
-                const float sc = xs[m] * gm;
+                const float sc = xs_lds[r] * gm;
                 float* yrow = y + (size_t)m * N;
                 int32_t* arow = acc_out ? acc_out + (size_t)m * N : nullptr;
 #pragma unroll
@@ -351,7 +365,8 @@ template <int BM, int BN, int WGM, int WGN, int STAGES, int WPE, bool SPLIT = fa
 static hipError_t launch_gemm_tile(const int8_t* xq, const float* xs, int M, int K,
                                    const uint32_t* Wp, const float* gamma, int N, float* y,
                                    int32_t* acc, hipStream_t stream, int splits = 1) {
-    constexpr size_t lds = (size_t)STAGES * (BM * kARow + BN * kBRow);
+    // The ring, then BM row scales for the epilogue.
+    constexpr size_t lds = (size_t)STAGES * (BM * kARow + BN * kBRow) + (SPLIT ? 0 : BM * 4);
     auto kern = &k_gemm<BM, BN, WGM, WGN, STAGES, WPE, SPLIT>;
     static bool attr_set = false;
     if (lds > 64 * 1024 && !attr_set) {

@@ -157,8 +157,33 @@ __global__ __launch_bounds__(kWideThreads, 2) void k_gemv_wide(
     // C layout: lane l, register v holds token 8*(v/4) + 4*(l/32) + v%4 (+32
     // for the second accumulator) and weight row l % 32 of this wave.
     if (wrow >= N) return;
-    int32_t* yi = reinterpret_cast<int32_t*>(y);
+    // Two straight loops, one per mode, so the compiler's wait placement
+    // sees no joins between the atomics or the stores.
+    if (split) {
+        int32_t* yi = reinterpret_cast<int32_t*>(y);
+#pragma unroll
+        for (int tg = 0; tg < 2; ++tg)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int t = 32 * tg + 8 * (v / 4) + 4 * (lane / 32) + (v % 4);
+                if (t < M)
+                    __hip_atomic_fetch_add(yi + (size_t)t * N + wrow, -acc[tg][v],
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        return;
+    }
+    // Token scales before the first store, then one wait: a load issued among
+    // the stores would wait for them too (one counter, issue order).
     const float gm = *gamma_p;
+    float xsr[2][16];
+#pragma unroll
+    for (int tg = 0; tg < 2; ++tg)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int t = 32 * tg + 8 * (v / 4) + 4 * (lane / 32) + (v % 4);
+            xsr[tg][v] = t < M ? xs[t] : 0.0f;
+        }
+    BL_WAIT_VMCNT(0);
 #pragma unroll
     for (int tg = 0; tg < 2; ++tg)
 #pragma unroll
@@ -167,12 +192,8 @@ __global__ __launch_bounds__(kWideThreads, 2) void k_gemv_wide(
             if (t < M) {
                 const int32_t a = -acc[tg][v];
                 const size_t o = (size_t)t * N + wrow;
-                if (split) {
-                    __hip_atomic_fetch_add(yi + o, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                } else {
-                    y[o] = (float)a * (xs[t] * gm);
-                    if (acc_out) acc_out[o] = a;
-                }
+                y[o] = (float)a * (xsr[tg][v] * gm);
+                if (acc_out) acc_out[o] = a;
             }
         }
 }

@@ -175,17 +175,16 @@ __global__ __launch_bounds__(kActThreads) void k_glu_quant(
     const int nvec = (int)(K / 4);
     const bool cached = nvec <= kGluCache * kActThreads;
 
+    // With a gain, the cached path keeps the gain vectors beside the gated
+    // values: a gain load issued among the code stores would wait for them
+    // (vector loads and stores retire through one counter in issue order).
     uint2 ch[kGluCache];
+    uint2 cgn[SUBLN ? kGluCache : 1];
     float amax = 0.0f;
     double ss = 0.0;
-    auto scan = [&](int v, const uint2 h) {
+    auto scan = [&](const uint2 h, const uint2 gv) {
         const uint32_t hw[2] = {h.x, h.y};
-        uint32_t gw[2] = {0u, 0u};
-        if (SUBLN) {
-            const uint2 gv = gnv[v];
-            gw[0] = gv.x;
-            gw[1] = gv.y;
-        }
+        const uint32_t gw[2] = {gv.x, gv.y};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float hf = bf16_to_f32((hw[e / 2] >> (16 * (e % 2))) & 0xFFFFu);
@@ -205,6 +204,7 @@ __global__ __launch_bounds__(kActThreads) void k_glu_quant(
             if (v < nvec) {
                 cg[j] = grow[v];
                 cu[j] = urow[v];
+                if (SUBLN) cgn[j] = gnv[v];
             }
         }
 #pragma unroll
@@ -212,11 +212,12 @@ __global__ __launch_bounds__(kActThreads) void k_glu_quant(
             const int v = tid + kActThreads * j;
             if (v < nvec) {
                 ch[j] = glu4<KIND>(cg[j], cu[j]);
-                scan(v, ch[j]);
+                scan(ch[j], SUBLN ? cgn[j] : ch[j]);
             }
         }
     } else {
-        for (int v = tid; v < nvec; v += kActThreads) scan(v, glu4<KIND>(grow[v], urow[v]));
+        for (int v = tid; v < nvec; v += kActThreads)
+            scan(glu4<KIND>(grow[v], urow[v]), SUBLN ? gnv[v] : make_uint2(0u, 0u));
     }
     amax = block_reduce(amax, s_max, true);
     double ss_tot = 0.0;
@@ -225,14 +226,9 @@ __global__ __launch_bounds__(kActThreads) void k_glu_quant(
     const float inv = 127.0f / a;
 
     uint32_t* out = reinterpret_cast<uint32_t*>(hq + m * K);
-    auto emit = [&](int v, const uint2 h) {
+    auto emit = [&](int v, const uint2 h, const uint2 gv) {
         const uint32_t hw[2] = {h.x, h.y};
-        uint32_t gw[2] = {0u, 0u};
-        if (SUBLN) {
-            const uint2 gv = gnv[v];
-            gw[0] = gv.x;
-            gw[1] = gv.y;
-        }
+        const uint32_t gw[2] = {gv.x, gv.y};
         uint32_t packed = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -248,10 +244,11 @@ __global__ __launch_bounds__(kActThreads) void k_glu_quant(
 #pragma unroll
         for (int j = 0; j < kGluCache; ++j) {
             const int v = tid + kActThreads * j;
-            if (v < nvec) emit(v, ch[j]);
+            if (v < nvec) emit(v, ch[j], SUBLN ? cgn[j] : ch[j]);
         }
     } else {
-        for (int v = tid; v < nvec; v += kActThreads) emit(v, glu4<KIND>(grow[v], urow[v]));
+        for (int v = tid; v < nvec; v += kActThreads)
+            emit(v, glu4<KIND>(grow[v], urow[v]), SUBLN ? gnv[v] : make_uint2(0u, 0u));
     }
     if (tid == 0) {
         if (SUBLN) {
