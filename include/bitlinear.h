@@ -146,9 +146,11 @@ int bl_bitlinear(const int8_t* x_q, const float* x_scale, int64_t M, int64_t K,
  * 2 = GEMM, 3 = wide GEMV for up to 64 tokens (128 weight rows per
  * workgroup, activations staged in K blocks; requires M <= 64). All give the
  * same bits. Automatic: GEMV when it applies, else the wide GEMV up to 64
- * tokens when the weights are large enough that each of its workgroups
- * streams at least four K blocks of 512, else the GEMM. Any other value, or
- * an unsupported choice, is BL_ERR_INVALID_ARG. */
+ * tokens when each of its workgroups streams at least four K blocks of 512
+ * and the matrix is not one where the GEMM measured faster (from 48 tokens
+ * on matrices of at least 16 Mi weights, from 33 tokens on wide ones, N > K,
+ * of at least 24 Mi), else the GEMM. Any other value, or an unsupported
+ * choice, is BL_ERR_INVALID_ARG. */
 int bl_bitlinear_path(const int8_t* x_q, const float* x_scale, int64_t M,
                       int64_t K, const uint32_t* W_packed, const float* gamma,
                       int64_t N, float* y, int32_t* acc, int path, void* stream);

@@ -42,12 +42,18 @@ constexpr int kBRow = kBK / 4;      // packed weight bytes per row per stage
 // SPLIT: the K steps are divided among gridDim.y workgroups per tile (kt_split
 // steps each); each adds its exact int32 partial sums into y, which holds
 // int32 zeros beforehand, and k_splitk_finalize rescales them afterwards.
-template <int BM, int BN, int WGM, int WGN, int STAGES, int WPE, bool SPLIT>
-__global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_gemm(
+// KS: the workgroup holds KS groups of WGM x WGN waves over the same tile;
+// group g takes K steps g, g+KS, g+2KS, ... into its own part of each ring
+// slot, and the groups' int32 partial sums are added through LDS at the end.
+// A tile with few MFMAs per wave then still has KS waves per SIMD to hide
+// each other's LDS and VALU latencies, without atomics or extra launches.
+template <int BM, int BN, int WGM, int WGN, int STAGES, int WPE, bool SPLIT, int KS>
+__global__ __launch_bounds__(64 * WGM * WGN * KS, WPE) void k_gemm(
     const int8_t* __restrict__ xq, const float* __restrict__ xs, int M, int K,
     const uint32_t* __restrict__ Wp, const float* __restrict__ gamma_p, int N,
     float* __restrict__ y, int32_t* __restrict__ acc_out, int kt_split) {
-    constexpr int NW = WGM * WGN;               // waves per workgroup
+    constexpr int NW = WGM * WGN;               // waves per K group
+    static_assert(KS >= 1, "K groups");
     constexpr int WM = BM / WGM, WN = BN / WGN;  // wave tile
     constexpr int TM = WM / 32, TN = WN / 32;
     constexpr int A_STAGE = BM * kARow;
@@ -68,7 +74,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_gemm(
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
-    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wave_all = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int kg = wave_all / NW;    // K group
+    const int wave = wave_all % NW;  // wave within its group
     const int wm0 = (wave % WGM) * WM, wn0 = (wave / WGM) * WN;
 
     // Tile order: each XCD (workgroups are dealt round-robin to the 8 XCDs)
@@ -95,9 +103,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_gemm(
 
     const int KT = (K + kBK - 1) / kBK;
     const bool k_tail = (K % kBK) != 0;  // last stage holds 64 valid k
-    // This workgroup's K steps: global step kt0 + kt for local kt < NK (>= 1).
+    // This workgroup's K steps are global steps kt0 .. kt0 + nk - 1 (nk >= 1).
+    // Local step kt covers kt*KS .. kt*KS + KS-1 of them, one per K group; a
+    // group whose step lies past the workgroup's range loads its last step
+    // again and expands its weights as zeros.
     const int kt0 = SPLIT ? (int)blockIdx.y * kt_split : 0;
-    const int NK = SPLIT ? min(kt_split, KT - kt0) : KT;
+    const int nk = SPLIT ? min(kt_split, KT - kt0) : KT;
+    const int NK = (nk + KS - 1) / KS;
+    auto lstep = [&](int kt) { return kt * KS + kg; };
+    constexpr int SLOT = KS * STAGE;  // one ring slot: a stage per K group
 
     // Per-lane global sources for the stage loads (k offset added per stage).
     // A instruction i of this wave: rows 8i + lane/8 of the wave's A_ROWS;
@@ -123,9 +137,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_gemm(
     const uint32_t smem_base = (uint32_t)(size_t)(lds_u8_t*)smem;
 
     auto issue = [&](int kt) {
-        const uint32_t st = smem_base + (uint32_t)((kt % STAGES) * STAGE);
-        const int k0 = (kt0 + kt) * kBK;
-        const bool tail = k_tail && kt0 + kt == KT - 1;
+        const uint32_t st = smem_base + (uint32_t)((kt % STAGES) * SLOT + kg * STAGE);
+        const int ks = kt0 + min(lstep(kt), nk - 1);
+        const int k0 = ks * kBK;
+        const bool tail = k_tail && ks == KT - 1;
 #pragma unroll
         for (int i = 0; i < A_INSTR; ++i) {
             int c = a_chunk[i];
@@ -155,7 +170,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_gemm(
 
     // Fragment reads from LDS stage `kt % STAGES`.
     auto read_b = [&](uint4* bp, int kt) {
-        const uint8_t* Bs = smem + (kt % STAGES) * STAGE + A_STAGE;
+        const uint8_t* Bs = smem + (kt % STAGES) * SLOT + kg * STAGE + A_STAGE;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int r = wn0 + 32 * j + fr;
@@ -167,10 +182,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_gemm(
     // (weight 0) when they are expanded. Applied at expansion, not at the
     // LDS read, so the read need not complete right after the barrier.
     auto keep_mask = [&](int kt) -> uint32_t {
-        return (k_tail && kt0 + kt == KT - 1 && fg) ? 0u : 0xFFFFFFFFu;
+        if (KS > 1 && lstep(kt) >= nk) return 0u;
+        return (k_tail && kt0 + lstep(kt) == KT - 1 && fg) ? 0u : 0xFFFFFFFFu;
     };
     auto read_a = [&](v4i* af, int kt, int s) {
-        const uint8_t* As = smem + (kt % STAGES) * STAGE;
+        const uint8_t* As = smem + (kt % STAGES) * SLOT + kg * STAGE;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int r = wm0 + 32 * i + fr;
@@ -262,6 +278,47 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_gemm(
 
     // Epilogue. C layout of the 32x32 MFMA: lane l, register v holds row
     // 8*(v/4) + 4*(l/32) + v%4 (token) and column l%32 (output feature).
+    //
+    // The tile's row scales reach every lane through LDS (a region past the
+    // ring): a global load issued among the output stores would wait for
+    // those stores as well (vector loads and stores retire through one
+    // counter in issue order), one round trip per row. Split K has no scales
+    // here (k_splitk_finalize applies them) and no such region.
+    float* xs_lds = reinterpret_cast<float*>(smem + STAGES * SLOT);
+    if constexpr (KS > 1) {
+        // Groups 1..KS-1 hand their partial sums to group 0 through the ring
+        // (free once every wave has passed this barrier), one int32 per lane
+        // per accumulator register: consecutive lanes, consecutive words.
+        constexpr int PER_WAVE = TM * TN * 16 * kWave;
+        static_assert((KS - 1) * NW * PER_WAVE * 4 <= STAGES * SLOT, "reduction space");
+        int32_t* red = reinterpret_cast<int32_t*>(smem);
+        __syncthreads();
+        if (kg > 0) {
+            int32_t* dst = red + ((kg - 1) * NW + wave) * PER_WAVE + lane;
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) dst[((i * TN + j) * 16 + v) * kWave] = acc[i][j][v];
+        }
+        if (!SPLIT && tid < BM) xs_lds[tid] = xs_row;
+        __syncthreads();
+        if (kg > 0) return;
+#pragma unroll 1
+        for (int g = 1; g < KS; ++g) {
+            const int32_t* src = red + ((g - 1) * NW + wave) * PER_WAVE + lane;
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[i][j][v] += src[((i * TN + j) * 16 + v) * kWave];
+        }
+    } else if constexpr (!SPLIT) {
+        if (tid < BM) xs_lds[tid] = xs_row;
+        __syncthreads();
+    }
     if constexpr (SPLIT) {
         int32_t* yi = reinterpret_cast<int32_t*>(y);
 #pragma unroll
@@ -283,13 +340,6 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_gemm(
         }
         return;
     }
-    // The tile's row scales reach every lane through LDS (a region past the
-    // ring): a global load issued among the output stores would wait for
-    // those stores as well (vector loads and stores retire through one
-    // counter in issue order), one round trip per row.
-    float* xs_lds = reinterpret_cast<float*>(smem + STAGES * STAGE);
-    if (tid < BM) xs_lds[tid] = xs_row;
-    __syncthreads();
     const float gm = *gamma_p;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -361,13 +411,15 @@ __global__ __launch_bounds__(256) void k_splitk_finalize(float* __restrict__ y,
     }
 }
 
-template <int BM, int BN, int WGM, int WGN, int STAGES, int WPE, bool SPLIT = false>
+template <int BM, int BN, int WGM, int WGN, int STAGES, int WPE, bool SPLIT = false, int KS = 1>
 static hipError_t launch_gemm_tile(const int8_t* xq, const float* xs, int M, int K,
                                    const uint32_t* Wp, const float* gamma, int N, float* y,
                                    int32_t* acc, hipStream_t stream, int splits = 1) {
-    // The ring, then BM row scales for the epilogue.
-    constexpr size_t lds = (size_t)STAGES * (BM * kARow + BN * kBRow) + (SPLIT ? 0 : BM * 4);
-    auto kern = &k_gemm<BM, BN, WGM, WGN, STAGES, WPE, SPLIT>;
+    // The ring (a stage per K group in each slot), then BM row scales for
+    // the epilogue.
+    constexpr size_t lds =
+        (size_t)STAGES * KS * (BM * kARow + BN * kBRow) + (SPLIT ? 0 : BM * 4);
+    auto kern = &k_gemm<BM, BN, WGM, WGN, STAGES, WPE, SPLIT, KS>;
     static bool attr_set = false;
     if (lds > 64 * 1024 && !attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -378,8 +430,8 @@ static hipError_t launch_gemm_tile(const int8_t* xq, const float* xs, int M, int
     const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const int KT = (K + kBK - 1) / kBK;
     if (!SPLIT) {
-        hipLaunchKernelGGL(kern, dim3(tiles), dim3(64 * WGM * WGN), lds, stream, xq, xs, M, K,
-                           Wp, gamma, N, y, acc, KT);
+        hipLaunchKernelGGL(kern, dim3(tiles), dim3(64 * WGM * WGN * KS), lds, stream, xq, xs, M,
+                           K, Wp, gamma, N, y, acc, KT);
         return hipGetLastError();
     }
     // Even split of the K steps; every split gets at least one step.
@@ -388,8 +440,8 @@ static hipError_t launch_gemm_tile(const int8_t* xq, const float* xs, int M, int
     const size_t total = (size_t)M * N;
     hipError_t e = launch_splitk_zero(reinterpret_cast<int32_t*>(y), total, stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(tiles, used), dim3(64 * WGM * WGN), lds, stream, xq, xs, M, K,
-                       Wp, gamma, N, y, acc, per);
+    hipLaunchKernelGGL(kern, dim3(tiles, used), dim3(64 * WGM * WGN * KS), lds, stream, xq, xs, M,
+                       K, Wp, gamma, N, y, acc, per);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_splitk_finalize(y, xs, gamma, acc, N, total, stream);
@@ -432,18 +484,38 @@ hipError_t launch_gemm(const int8_t* xq, const float* xs, int M, int K, const ui
         return launch_gemm_tile<128, 256, 1, 4, 3, 2>(xq, xs, M, K, Wp, gamma, N, y, acc, stream);
     if (tiles(128, 128) >= kCUs)
         return launch_gemm_tile<128, 128, 2, 2, 3, 2>(xq, xs, M, K, Wp, gamma, N, y, acc, stream);
-    // Few tiles (few tokens, or few output features): 64 x 128 tiles, two
-    // 4-wave workgroups per CU with six stages in flight each, and the K
-    // steps split across workgroups until the grid covers every CU (each
-    // split keeps at least 8 steps). The partial sums are integers, so their
-    // order of addition does not change a bit of the result.
+    // Few tiles (few tokens, or few output features): 64 x 128 tiles. A
+    // 4-wave workgroup alone on a CU leaves one wave per SIMD, whose LDS and
+    // VALU latencies the matrix cores then wait on; so the workgroup gets two
+    // (or, for long K with at most one tile per CU, four) K groups of 4 waves
+    // that add their partial sums through LDS. With fewer than half as many
+    // tiles as CUs, or few tiles and very long K, the K steps are instead
+    // split across workgroups until the grid covers every CU (each split
+    // keeps at least 8 steps), their exact int32 partial sums added with
+    // atomics into y. Integer addition makes every variant bit-identical.
     const int64_t t64 = tiles(64, 128);
     const int KT = (K + kBK - 1) / kBK;
     const int splits = (int)std::min<int64_t>((kCUs + t64 - 1) / t64, std::max(1, KT / 8));
-    if (splits > 1)
-        return launch_gemm_tile<64, 128, 1, 4, 6, 2, true>(xq, xs, M, K, Wp, gamma, N, y, acc,
-                                                           stream, splits);
-    return launch_gemm_tile<64, 128, 1, 4, 6, 2>(xq, xs, M, K, Wp, gamma, N, y, acc, stream);
+    const bool groups = splits == 1 || (t64 >= kCUs / 2 && (t64 >= 3 * kCUs / 4 || KT <= 128));
+    if (groups) {
+        if (t64 <= kCUs && KT >= 48)
+            return launch_gemm_tile<64, 128, 1, 4, 3, 4, false, 4>(xq, xs, M, K, Wp, gamma, N, y,
+                                                                   acc, stream);
+        return launch_gemm_tile<64, 128, 1, 4, 3, 4, false, 2>(xq, xs, M, K, Wp, gamma, N, y, acc,
+                                                               stream);
+    }
+    // Split K: with many steps per split, K groups inside each workgroup as
+    // well (four from 40 steps, two from 24); fewer steps leave too little
+    // per group to pay for the LDS reduction.
+    const int per = (KT + splits - 1) / splits;
+    if (per >= 40)
+        return launch_gemm_tile<64, 128, 1, 4, 3, 4, true, 4>(xq, xs, M, K, Wp, gamma, N, y, acc,
+                                                              stream, splits);
+    if (per >= 24)
+        return launch_gemm_tile<64, 128, 1, 4, 3, 4, true, 2>(xq, xs, M, K, Wp, gamma, N, y, acc,
+                                                              stream, splits);
+    return launch_gemm_tile<64, 128, 1, 4, 6, 2, true>(xq, xs, M, K, Wp, gamma, N, y, acc, stream,
+                                                       splits);
 }
 
 }  // namespace bl

@@ -225,11 +225,20 @@ WidePlan wide_plan(int N, int K) {
 
 }  // namespace
 
-// Worth it over the GEMM when a workgroup streams at least four K blocks:
-// with fewer, the prologue (first block's loads, nothing to overlap them
-// with) dominates and the GEMM's deeper staging wins.
+// Only worth it when a workgroup streams at least four K blocks: with
+// fewer, the prologue (first block's loads, nothing to overlap them with)
+// dominates and the GEMM's deeper staging wins. Beyond that, against the GEMM (measured with HIP graphs at 17..64 tokens on the 2B4T,
+// 3B and 70B projection shapes): the wide kernel's time grows with the token
+// count, the GEMM's hardly (its 64-row tiles are padded either way). The
+// wide kernel stays ahead up to 24 tokens and on matrices under 16 Mi
+// weights; the GEMM is ahead from 48 tokens on larger matrices, and from 33
+// tokens on wide ones (N > K) of at least 24 Mi weights.
 bool gemv_wide_preferred(int64_t M, int64_t N, int64_t K) {
-    return gemv_wide_supported(M, K) && wide_plan((int)N, (int)K).per >= 4;
+    if (!gemv_wide_supported(M, K) || wide_plan((int)N, (int)K).per < 4) return false;
+    const int64_t w = N * K;
+    if (M >= 48) return w < (16ll << 20);
+    if (M > 24) return !(N > K && w >= (24ll << 20));
+    return true;
 }
 
 hipError_t launch_gemv_wide(const int8_t* xq, const float* xs, int M, int K, const uint32_t* Wp,

@@ -242,9 +242,13 @@ def test_gemm_large_tiles_ragged(M, K, N):
 
 
 # Few tiles split K across workgroups whose int32 partial sums are added into
-# y; y starts with garbage here (NaN bits) to show it is cleared first.
-SPLIT_K_CASES = [(64, 8192, 700), (64, 28672, 260), (33, 6912, 1000), (512, 3200, 3200),
-                 (100, 2560, 300), (300, 8640, 129)]
+# y; y starts with garbage here (NaN bits) to show it is cleared first. With
+# many steps per split the workgroups also hold K groups: four for the 80-
+# and 64-token cases on K near 28672, two for the 100-token one; the last two
+# end K in a half step, and their last split's step count is not a multiple
+# of the group count.
+SPLIT_K_CASES = [(64, 8192, 700), (64, 28672, 260), (33, 6912, 1000), (80, 28672, 8192),
+                 (100, 2560, 300), (300, 8640, 129), (64, 28352, 8100), (100, 24384, 2000)]
 
 
 @pytest.mark.parametrize("M,K,N", SPLIT_K_CASES)
@@ -265,6 +269,38 @@ def test_gemm_split_k(M, K, N):
     idx = torch.from_numpy(ms).to(DEV)
     assert np.array_equal(acc[idx].cpu().numpy(), acc_ref)
     assert_y_close(y[idx].cpu().numpy(), y_ref, "split-K gemm")
+
+
+# Few tiles but many tokens: K groups inside each workgroup (two, or four for
+# long K with at most one tile per CU) add their partial sums through LDS.
+# Step counts are not multiples of the group count, so some group's last step
+# lies past K (its weights expand as zeros); the last three cases end K in a
+# half (64-deep) step; M and N are ragged. y starts as NaN bits.
+K_GROUP_CASES = [(512, 3200, 3200),   # 200 tiles of 64 x 128, 25 steps: two groups
+                 (260, 2624, 6900),   # 270 tiles, 21 steps: two groups
+                 (500, 8512, 3160),   # 200 tiles, 67 steps: four groups
+                 (130, 6976, 8190)]   # 192 tiles, 55 steps: four groups
+
+
+@pytest.mark.parametrize("M,K,N", K_GROUP_CASES)
+def test_gemm_k_groups(M, K, N):
+    q, xq, xs, g = _product_case(M, K, N, 61)
+    args = (torch.from_numpy(xq).to(DEV), dev_f32(xs), dev_packed(oracle.pack(q)), dev_f32([g]))
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    acc = torch.full((M, N), -7, dtype=torch.int32, device=DEV)
+    ref64 = args[0].to(torch.float64) @ torch.from_numpy(q).to(DEV, torch.float64).t().contiguous()
+    for _ in range(2):
+        bl.bitlinear(*args, out=y, acc_out=acc, path=2)
+        assert torch.equal(acc.to(torch.float64), ref64)
+        sc = (args[1] * args[3]).view(-1, 1)
+        assert torch.equal(y, acc.to(torch.float32) * sc)
+    rng = np.random.default_rng(M * N + 1)
+    edges = [m for t in range(0, M, 64) for m in (t, min(t + 63, M - 1))]
+    ms = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 6, replace=False), edges[-4:]]))
+    y_ref, acc_ref = oracle.bitlinear(xq[ms], xs[ms], q, g)
+    idx = torch.from_numpy(ms).to(DEV)
+    assert np.array_equal(acc[idx].cpu().numpy(), acc_ref)
+    assert_y_close(y[idx].cpu().numpy(), y_ref, "k-group gemm")
 
 
 # The wide GEMV (17..64 tokens, 128 rows per workgroup, K in 512 blocks):
