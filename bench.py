@@ -572,13 +572,15 @@ def main():
             ops = sum(2 * M * N * K for _, K, N in lprojs) / len(lprojs)
             t = st["mean_us"] * 1e-6
             leg = {
-                "kernel": "k_gemv" if M <= 16 else "k_gemv_wide",
+                "kernel": "k_gemv" if M <= 16 else
+                          "k_gemm (bl_bitlinear's choice at 64 tokens: four K groups per "
+                          "workgroup; the down projection also splits K)",
                 "packed_GBps": round(packed / t / 1e9, 1),
                 "roofline": {"bound": "hbm", "achieved": round(alg / t / 1e9, 1),
                              "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": round(alg / t / 1e9 / HBM_PEAK_GBS, 4),
                              "traffic": traffic.get("gemv_70b_m1" if M == 1
-                                                    else "wide_decode_70b_m64"),
+                                                    else "decode_70b_m64"),
                              "traffic_unit": "HBM bytes per bl_bitlinear call",
                              "alg_bytes_per_call": round(alg)},
                 "per_launch": st,

@@ -61,10 +61,11 @@ PHASES = {
     "gemv_70b_m1_binary": (["gemv.hip", "common.hpp"],
                            "bl_bitlinear_binary at M=1 on the 70B shapes, 5 rotated copies",
                            2 * COPIES_70B, "k_gemv launch (1 bit per +-1 weight)"),
-    "wide_decode_70b_m64": (["gemv_wide.hip", "gemm.hip", "common.hpp"],
-                            "bl_bitlinear at M=64 on the 70B shapes, 5 rotated copies",
-                            2 * COPIES_70B,
-                            "bl_bitlinear call (split K: zero, k_gemv_wide, finalize)"),
+    "decode_70b_m64": (["gemv_wide.hip", "gemm.hip", "common.hpp"],
+                       "bl_bitlinear at M=64 on the 70B shapes, 5 rotated copies",
+                       2 * COPIES_70B,
+                       "bl_bitlinear call (up: k_gemm with four K groups; down: the same with "
+                       "split K between k_splitk_zero and k_splitk_finalize)"),
     "gemv_2560_m1": (["gemv.hip", "common.hpp"],
                      "bl_bitlinear at M=1 on 2560->2560, 400 rotated copies",
                      COPIES_2560, "k_gemv launch"),
@@ -230,7 +231,7 @@ def run():
     phase("gemv_70b_m1", rotate70(1))
     phase("gemv_70b_m1_base3", rotate70_fmt(bl.bitlinear_base3, w5b3))
     phase("gemv_70b_m1_binary", rotate70_fmt(bl.bitlinear_binary, w5bin))
-    phase("wide_decode_70b_m64", rotate70(64))
+    phase("decode_70b_m64", rotate70(64))
     phase("gemv_2560_m1", single2560)
     phase("gemv_3b_m1", block3b(1))
     phase("gemm_3b_m512", block3b(512))
