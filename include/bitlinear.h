@@ -248,9 +248,10 @@ size_t bl_ffn_relu2_workspace_bytes(int64_t M, int64_t K, int64_t N_ff);
  *   workspace  tmp  >= bl_ffn_relu2_workspace_bytes(M, K, N_ff) bytes,
  *                   256-byte aligned; contents undefined afterwards.
  * Shapes follow the rules above for (M, K), (M, N_ff) and both weight
- * matrices. For M in {1, 2, 4, 8, 16} with M*K and M*N_ff up to 128 KiB the
+ * matrices. For M in {1, 2, 4, 8} with M*K and M*N_ff up to 128 KiB the
  * step runs in two launches, with each workgroup quantising its activations
- * itself; otherwise in four. */
+ * itself; for M = 16 (same limits) in three: the gate/up launch, one act
+ * quant of h, and the GEMV on its codes; otherwise in four. */
 int bl_ffn_relu2(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate,
                  const float* gamma_gate, const uint32_t* W_up, const float* gamma_up,
                  int64_t N_ff, const uint32_t* W_down, const float* gamma_down, float* y,
@@ -261,7 +262,7 @@ int bl_ffn_relu2(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate
  *   y = BitLinear(quantize_acts(h, subln_gain, subln_eps), W_down)
  * with h_q bit-exact and h_scale within 1e-6 relative of
  * bl_relu2_glu_subln_quant's (the fp64 sum of squares is taken in another
- * order when the step runs in two launches). subln_gain: bf16 [N_ff] (raw
+ * order when the step runs in two or three launches). subln_gain: bf16 [N_ff] (raw
  * bits), 16-byte aligned, not null; subln_eps > 0. Workspace, shapes and
  * launches as bl_ffn_relu2. Source: as bl_relu2_glu_subln_quant. */
 int bl_ffn_relu2_subln(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate,

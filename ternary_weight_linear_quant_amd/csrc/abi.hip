@@ -191,6 +191,8 @@ namespace {
 
 bool glu_kind_ok(int kind) { return kind == BL_GLU_RELU2 || kind == BL_GLU_SWIGLU; }
 
+constexpr int64_t kFfnSplitDownM = 16;
+
 // One FFN step; subln_gain (bf16 [N_ff]) null for none.
 int ffn_step(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate,
              const float* gamma_gate, const uint32_t* W_up, const float* gamma_up, int64_t N_ff,
@@ -212,6 +214,22 @@ int ffn_step(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate,
     hipStream_t st = as_stream(stream);
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     auto* h = reinterpret_cast<uint16_t*>(ws + L.h);
+    auto* hq = reinterpret_cast<int8_t*>(ws + L.hq);
+    auto* hs = reinterpret_cast<float*>(ws + L.hs);
+    // From kFfnSplitDownM tokens the down projection's fused launch, whose
+    // every workgroup reads and quantises all of h, costs more than one act
+    // quant launch followed by the plain GEMV on the int8 codes.
+    if (M >= kFfnSplitDownM && bl::ffn_gate_up_supported(M, K, N_ff) &&
+        bl::gemv_supported(M, N_ff)) {
+        hipError_t e = bl::launch_ffn_gate_up(x, (int)M, (int)K, W_gate, gamma_gate, W_up,
+                                              gamma_up, (int)N_ff, h, kind, st);
+        if (e == hipSuccess)
+            e = bl::launch_quantize_acts(h, M, N_ff, subln_gain, subln_eps, hq, hs, st);
+        if (e == hipSuccess)
+            e = bl::launch_gemv(hq, hs, (int)M, (int)N_ff, W_down, gamma_down, (int)K, y,
+                                nullptr, st);
+        return hip_status(e);
+    }
     if (bl::ffn_fused_supported(M, K, N_ff, subln_gain != nullptr))
         return hip_status(bl::launch_ffn_fused(x, (int)M, (int)K, W_gate, gamma_gate, W_up,
                                                gamma_up, (int)N_ff, W_down, gamma_down, h, y,
@@ -221,8 +239,6 @@ int ffn_step(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate,
     auto* xs = reinterpret_cast<float*>(ws + L.xs);
     auto* yg = reinterpret_cast<float*>(ws + L.yg);
     auto* yu = reinterpret_cast<float*>(ws + L.yu);
-    auto* hq = reinterpret_cast<int8_t*>(ws + L.hq);
-    auto* hs = reinterpret_cast<float*>(ws + L.hs);
     const int m = (int)M, k = (int)K, n = (int)N_ff;
     hipError_t e = bl::launch_quantize_acts(x, M, K, nullptr, 0.0f, xq, xs, st);
     if (e == hipSuccess) {

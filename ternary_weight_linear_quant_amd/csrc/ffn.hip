@@ -19,8 +19,10 @@
 // and bl_relu2_glu, so the output bits equal the unfused sequence. The
 // per-workgroup quantisation re-reads the M tokens from L2 in every
 // workgroup: cheap for a few tokens, and still ahead of the four-launch
-// sequence at 8 and 16 (the bf16 inputs are cached in registers, up to 16
-// units of 16 values per thread, one workgroup per CU at 16 tokens).
+// sequence at 8 (the bf16 inputs are cached in registers, up to 16 units of
+// 16 values per thread). At 16 tokens launch B's reads of h (221 KB per
+// workgroup on the 2B4T shapes) cost more than one act quant launch and the
+// plain GEMV on the codes, so the step runs launch A alone, then those two.
 //
 // Ordering inside a workgroup: the activation loads are issued first, the
 // R weight-chunk loads right after (always R, clamped to the wave's range),
@@ -425,6 +427,24 @@ hipError_t launch_ffn_fused(const uint16_t* x, int M, int K, const uint32_t* Wg,
     return big ? launch_ffn_down_cu<kKsB, false>(h, M, N_ff, Wd, gd, K, y, nullptr, 0.0f, stream)
                : launch_ffn_down_cu<kKsBSmall, false>(h, M, N_ff, Wd, gd, K, y, nullptr, 0.0f,
                                                       stream);
+}
+
+// Launch A alone (act quant + gate/up + gating into h), for a step whose
+// down projection runs as a separate act quant and GEMV.
+bool ffn_gate_up_supported(int64_t M, int64_t K, int64_t N_ff) {
+    if (M != 1 && M != 2 && M != 4 && M != 8 && M != 16) return false;
+    if (K % 64 != 0 || N_ff % 64 != 0) return false;
+    if (K > (1 << 20) || N_ff > (1 << 20)) return false;
+    if (K / 256 < kKsA) return false;
+    return cache_for(M * (K / 16), threads_a((int)M)) != 0 && M * K <= 128 * 1024;
+}
+
+hipError_t launch_ffn_gate_up(const uint16_t* x, int M, int K, const uint32_t* Wg,
+                              const float* gg, const uint32_t* Wu, const float* gu, int N_ff,
+                              uint16_t* h, int kind, hipStream_t stream) {
+    return kind == kGluSwiglu
+               ? launch_ffn_up_rg<kGluSwiglu>(x, M, K, Wg, gg, Wu, gu, N_ff, h, stream)
+               : launch_ffn_up_rg<kGluRelu2>(x, M, K, Wg, gg, Wu, gu, N_ff, h, stream);
 }
 
 }  // namespace bl

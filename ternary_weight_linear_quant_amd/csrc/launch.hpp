@@ -59,6 +59,12 @@ hipError_t launch_ffn_fused(const uint16_t* x, int M, int K, const uint32_t* Wg,
                             int kind, const uint16_t* subln_gain, float subln_eps,
                             hipStream_t stream);
 
+// Launch A of the above alone: act quant + gate/up + gating into h (bf16).
+bool ffn_gate_up_supported(int64_t M, int64_t K, int64_t N_ff);
+hipError_t launch_ffn_gate_up(const uint16_t* x, int M, int K, const uint32_t* Wg,
+                              const float* gg, const uint32_t* Wu, const float* gu, int N_ff,
+                              uint16_t* h, int kind, hipStream_t stream);
+
 // Other weight formats (decode GEMV only): 1 bit per {-1, +1} weight and
 // five ternary weights per byte.
 int64_t packed_row_bytes_binary(int64_t K);
