@@ -59,15 +59,20 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, WPE) void k_gemm(
     constexpr int A_STAGE = BM * kARow;
     constexpr int B_STAGE = BN * kBRow;
     constexpr int STAGE = A_STAGE + B_STAGE;
-    constexpr int A_ROWS = BM / NW;              // activation rows loaded per wave
-    constexpr int A_INSTR = A_ROWS / 8;          // 8 rows of 128 B per instruction
+    // Activation rows: BM / 8 load instructions of 8 rows x 128 B. When the
+    // waves divide them evenly, wave w takes a block of A_INSTR consecutive
+    // ones; otherwise they are dealt round-robin (instruction w + NW*i) and
+    // the first A_TOTAL % NW waves take one more.
+    constexpr int A_TOTAL = BM / 8;
+    constexpr int A_INSTR = (A_TOTAL + NW - 1) / NW;  // most per wave
+    constexpr bool A_EVEN = A_TOTAL % NW == 0;
     // Weight rows: 32 rows of 32 B per instruction, spread over the first
     // B_WAVES waves.
     constexpr int B_WAVES = BN / 32 < NW ? BN / 32 : NW;
     constexpr int B_INSTR = BN / 32 / B_WAVES;
     constexpr int B_ROWS = 32 * B_INSTR;         // weight rows loaded per loading wave
-    static_assert(TM >= 1 && TN >= 1 && A_INSTR >= 1 && B_INSTR >= 1, "tile shape");
-    static_assert(A_ROWS % 8 == 0 && B_WAVES * B_ROWS == BN, "tile shape");
+    static_assert(TM >= 1 && TN >= 1 && B_INSTR >= 1, "tile shape");
+    static_assert(BM % 8 == 0 && NW <= A_TOTAL && B_WAVES * B_ROWS == BN, "tile shape");
     static_assert((A_INSTR + B_INSTR) * (STAGES - 1) < 64, "vmcnt range");
 
     extern __shared__ __align__(16) uint8_t smem[];
@@ -114,13 +119,15 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, WPE) void k_gemm(
     constexpr int SLOT = KS * STAGE;  // one ring slot: a stage per K group
 
     // Per-lane global sources for the stage loads (k offset added per stage).
-    // A instruction i of this wave: rows 8i + lane/8 of the wave's A_ROWS;
-    // the lane's LDS slot is physical chunk lane%8 of that row.
+    // A instruction i of this wave covers rows 8q .. 8q+7 (q as above); the
+    // lane takes row 8q + lane/8, whose LDS slot is physical chunk lane%8.
+    const int a_cnt = A_EVEN ? A_INSTR : (A_TOTAL - 1 - wave) / NW + 1;  // wave-uniform
+    auto a_q = [&](int i) { return A_EVEN ? wave * A_INSTR + i : wave + NW * i; };
     const int8_t* a_src[A_INSTR];
     int a_chunk[A_INSTR];
 #pragma unroll
     for (int i = 0; i < A_INSTR; ++i) {
-        const int r = wave * A_ROWS + 8 * i + lane / 8;
+        const int r = 8 * min(a_q(i), A_TOTAL - 1) + lane / 8;
         a_chunk[i] = (lane % 8) ^ swz_a(r);
         a_src[i] = xq + (size_t)min(m0 + r, M - 1) * K;
     }
@@ -143,9 +150,10 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, WPE) void k_gemm(
         const bool tail = k_tail && ks == KT - 1;
 #pragma unroll
         for (int i = 0; i < A_INSTR; ++i) {
+            if (!A_EVEN && i >= a_cnt) break;
             int c = a_chunk[i];
             if (tail && c >= 4) c -= 4;  // beyond K: any valid address (B is zero there)
-            lds_dma16(a_src[i] + k0 + 16 * c, st + (wave * A_ROWS + 8 * i) * kARow);
+            lds_dma16(a_src[i] + k0 + 16 * c, st + 8 * a_q(i) * kARow);
         }
         if (b_loader) {
 #pragma unroll
@@ -208,8 +216,20 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, WPE) void k_gemm(
     // with step kt-1, whose buffer is the one being refilled. Step kt+1's
     // first fragments are then read during the second half of step kt, so
     // the matrix cores never wait on LDS at a step boundary.
-    constexpr int LOADS_B = A_INSTR + B_INSTR;   // per stage, weight-loading waves
-    constexpr int LOADS_A = A_INSTR;             // per stage, other waves
+    // Loads per stage: this wave's activation instructions (A_INSTR, or one
+    // fewer for the later waves of an uneven deal), plus B_INSTR for the
+    // weight-loading waves.
+    auto wait_for = [&](auto s_const, int after) {
+        constexpr int S = decltype(s_const)::value;
+        const bool full = A_EVEN || a_cnt == A_INSTR;
+        if (b_loader) {
+            if (full) wait_stages<A_INSTR + B_INSTR, S>(after);
+            else wait_stages<A_INSTR - 1 + B_INSTR, S>(after);
+        } else {
+            if (full) wait_stages<A_INSTR, S>(after);
+            else wait_stages<(A_INSTR > 1 ? A_INSTR - 1 : 0), S>(after);
+        }
+    };
     static_assert(STAGES >= 3, "pipeline depth");
 #pragma unroll
     for (int st = 0; st < STAGES - 1; ++st)
@@ -217,8 +237,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, WPE) void k_gemm(
     // Stage 0 landed: STAGES-2 later stages may still be in flight.
     {
         const int after = min(STAGES - 2, NK - 1);
-        if (b_loader) wait_stages<LOADS_B, STAGES - 2>(after);
-        else wait_stages<LOADS_A, STAGES - 2>(after);
+        wait_for(std::integral_constant<int, STAGES - 2>(), after);
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
     }
@@ -259,8 +278,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, WPE) void k_gemm(
                 // Stage kt+1 landed once the stages issued after it are the
                 // only loads outstanding.
                 const int after = min(STAGES - 3, NK - 2 - kt);
-                if (b_loader) wait_stages<LOADS_B, STAGES - 3>(after);
-                else wait_stages<LOADS_A, STAGES - 3>(after);
+                wait_for(std::integral_constant<int, STAGES - 3>(), after);
                 __builtin_amdgcn_s_barrier();
                 asm volatile("" ::: "memory");
                 if (kt + STAGES - 1 < NK) issue(kt + STAGES - 1);
@@ -478,6 +496,16 @@ hipError_t launch_gemm(const int8_t* xq, const float* xs, int M, int K, const ui
     // tiles (a CU's pair shares its matrix cores); the larger tile wins ties,
     // as long as it keeps at least half the CUs busy.
     const int64_t t512 = tiles(128, 512), t256 = tiles(128, 256);
+    // N a multiple of 320 where 128 x 512 tiles leave CUs idle: 128 x 320
+    // tiles of 10 waves, 64 x 64 each. A SIMD then runs at most three such
+    // waves against two 128 x 64 waves of the 128 x 512 tile (3/4 of the
+    // work), when one round of them covers at least 3/4 of the CUs.
+    if (N % 320 == 0) {
+        const int64_t t320 = tiles(128, 320);
+        if (t512 < t320 && t320 <= kCUs && 4 * t320 >= 3 * kCUs)
+            return launch_gemm_tile<128, 320, 2, 5, 3, 3>(xq, xs, M, K, Wp, gamma, N, y, acc,
+                                                          stream);
+    }
     if (t512 >= kCUs / 2 && 2 * ((t512 + kCUs - 1) / kCUs) <= (t256 + kCUs - 1) / kCUs)
         return launch_gemm_tile<128, 512, 1, 8, 3, 2>(xq, xs, M, K, Wp, gamma, N, y, acc, stream);
     if (t256 >= kCUs)

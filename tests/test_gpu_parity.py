@@ -212,10 +212,13 @@ def test_gemm_parity(M, K, N):
 
 
 # Large grids select the large prefill tiles: 128 x 256 with two workgroups
-# per CU for the first shape, 128 x 512 with one for the others (the last
-# with only 160 tiles); these shapes are ragged in M and N, and K = 320 / 192
-# ends in a half (64-deep) K step.
-LARGE_TILE_CASES = [(2000, 320, 4000), (2000, 192, 8000), (2048, 384, 8192), (1935, 448, 5000)]
+# per CU for the first shape, 128 x 512 with one for the next three (the
+# fourth with only 160 tiles), and 128 x 320 tiles of 10 waves (activation
+# loads dealt unevenly over the waves) for the last two, whose N is a
+# multiple of 320; the shapes are ragged in M (and N for the first four),
+# and K = 320 / 192 / 2624 / 704 ends in a half (64-deep) K step.
+LARGE_TILE_CASES = [(2000, 320, 4000), (2000, 192, 8000), (2048, 384, 8192), (1935, 448, 5000),
+                    (4000, 2624, 2560), (4050, 704, 1920)]
 
 
 @pytest.mark.parametrize("M,K,N", LARGE_TILE_CASES)
