@@ -590,9 +590,11 @@ def test_ffn_block_fused_path_equals_unfused():
 
 
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 16, 40])
-@pytest.mark.parametrize("K,N_ff", [(2560, 6912), (3200, 8640), (512, 1024)])
+@pytest.mark.parametrize("K,N_ff", [(2560, 6912), (3200, 8640), (512, 1024), (1024, 2624)])
 def test_ffn_relu2_matches_unfused_sequence(M, K, N_ff):
-    """bl_ffn_relu2 (two launches for M in 1, 2, 4, 8, 16, four otherwise) gives the bits
+    """bl_ffn_relu2 (two launches for M in 1, 2, 4, 8; three at 16: gate/up,
+    an act quant of h, the down GEMV; four otherwise; N_ff = 2624 leaves a
+    16-byte tail on the down projection's rows) gives the bits
     of quantize_acts -> bitlinear(gate, up) -> relu2_glu -> quantize_acts ->
     bitlinear(down); the unfused sequence is checked against the oracle by
     the stage-wise block test."""
