@@ -1026,3 +1026,51 @@ def test_graph_replays_match_eager():
             assert torch.equal(a.view(torch.int32), b.view(torch.int32)), f"replay {rep}"
         run()                       # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.gpu
+def test_calls_on_two_streams_do_not_interfere():
+    """The same work issued on two streams at once (default priority, no
+    synchronisation between them, three rounds) gives the bits of the calls
+    run one after another: the library keeps no state that two calls share.
+    Covers the GEMV, the GEMM's K-group, split-K and large-tile variants, and
+    the FFN step at 1 and 16 tokens (each stream with its own workspace)."""
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(77)
+    shapes = [(1, 2560, 6912), (16, 6912, 2560), (512, 3200, 3200), (64, 8192, 700),
+              (2048, 2560, 2560)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    jobs = []  # per stream: (inputs, reference) pairs
+    for _ in streams:
+        mine = []
+        for M, K, N in shapes:
+            pk, g = bl.quantize_weights(torch.randn(N, K, generator=gen, device=DEV) * 0.02)
+            xq, xs = bl.quantize_acts(torch.randn(M, K, generator=gen, device=DEV).to(torch.bfloat16))
+            mine.append(("bitlinear", (xq, xs, pk, g), bl.bitlinear(xq, xs, pk, g)))
+        for M in (1, 16):
+            K, N_ff = 2560, 6912
+            W = [bl.quantize_weights(torch.randn(n, k, generator=gen, device=DEV) * 0.02)
+                 for n, k in ((N_ff, K), (N_ff, K), (K, N_ff))]
+            x = torch.randn(M, K, generator=gen, device=DEV).to(torch.bfloat16)
+            ws = bl.ffn_relu2_workspace(M, K, N_ff, DEV)
+            args = (x, *W[0], *W[1], *W[2])
+            mine.append(("ffn", (args, ws), bl.ffn_relu2(*args, workspace=ws)))
+        jobs.append(mine)
+    torch.cuda.synchronize()
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    outs = [[None] * len(j) for j in jobs]
+    for _ in range(3):
+        for i in range(len(jobs[0])):
+            for si, s in enumerate(streams):
+                kind, a, _ref = jobs[si][i]
+                with torch.cuda.stream(s):
+                    if kind == "bitlinear":
+                        outs[si][i] = bl.bitlinear(*a)
+                    else:
+                        args, ws = a
+                        outs[si][i] = bl.ffn_relu2(*args, workspace=ws)
+    torch.cuda.synchronize()
+    for si in range(len(streams)):
+        for i, (kind, _a, ref) in enumerate(jobs[si]):
+            assert torch.equal(outs[si][i].view(torch.int32), ref.view(torch.int32)), (si, i, kind)
