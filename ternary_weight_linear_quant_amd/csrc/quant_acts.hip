@@ -18,13 +18,15 @@
 // and 1/rms goes into the scale. Tokens longer than the register cache take a
 // second pass that re-reads them (L2-resident). Roofline: HBM, 2 B read +
 // 1 B written per element (8 B read for the gated variant).
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace bl {
 
 constexpr int kActThreads = 256;
-constexpr int kActCache = 14;  // 16-byte vectors cached per thread (K <= 28672)
+constexpr int kActCache = 14;  // 16-byte vectors cached per thread, at most (K <= 28672)
 
 template <typename T>
 __device__ __forceinline__ T block_reduce(T v, T* scratch, bool is_max) {
@@ -62,7 +64,11 @@ __device__ __forceinline__ uint2 quant8(const uint32_t dw[4], const uint32_t gw[
     return make_uint2(packed[0], packed[1]);
 }
 
-template <bool FUSED>
+// CACHE: 16-byte vectors cached per thread, the smallest instantiation that
+// holds the token (a larger cache holds registers the token does not use and
+// lowers the workgroups a CU keeps in flight); tokens longer than
+// kActCache vectors per thread take the uncached two-pass loop.
+template <bool FUSED, int CACHE>
 __global__ __launch_bounds__(kActThreads) void k_act_quant(
     const uint16_t* __restrict__ x, int64_t K, const uint16_t* __restrict__ gain,
     float rms_eps, int8_t* __restrict__ xq, float* __restrict__ scale) {
@@ -73,13 +79,13 @@ __global__ __launch_bounds__(kActThreads) void k_act_quant(
     const uint4* grow = reinterpret_cast<const uint4*>(gain);
     const int tid = threadIdx.x;
     const int nvec = (int)(K / 8);  // 8 bf16 per 16 bytes
-    const bool cached = nvec <= kActCache * kActThreads;
+    const bool cached = nvec <= CACHE * kActThreads;
 
-    uint4 cx[kActCache];
-    uint4 cg[kActCache];
+    uint4 cx[CACHE];
+    uint4 cg[FUSED ? CACHE : 1];
     if (cached) {
 #pragma unroll
-        for (int j = 0; j < kActCache; ++j) {
+        for (int j = 0; j < CACHE; ++j) {
             const int v = tid + kActThreads * j;
             if (v < nvec) {
                 cx[j] = row[v];
@@ -108,7 +114,7 @@ __global__ __launch_bounds__(kActThreads) void k_act_quant(
     };
     if (cached) {
 #pragma unroll
-        for (int j = 0; j < kActCache; ++j)
+        for (int j = 0; j < CACHE; ++j)
             if (tid + kActThreads * j < nvec) scan(cx[j], FUSED ? cg[j] : cx[j]);
     } else {
         for (int v = tid; v < nvec; v += kActThreads) scan(row[v], FUSED ? grow[v] : row[v]);
@@ -127,7 +133,7 @@ __global__ __launch_bounds__(kActThreads) void k_act_quant(
     };
     if (cached) {
 #pragma unroll
-        for (int j = 0; j < kActCache; ++j) {
+        for (int j = 0; j < CACHE; ++j) {
             const int v = tid + kActThreads * j;
             if (v < nvec) emit(v, cx[j], FUSED ? cg[j] : cx[j]);
         }
@@ -158,9 +164,11 @@ __device__ __forceinline__ uint2 glu4(const float4 g, const float4 u) {
 // SUBLN: the sub-layer RMSNorm with gain g between the gating and the
 // quantisation, as bl_quantize_acts(h, g) computes it: codes of z = h*g,
 // scale a / (127 * rms(h)) with sum h^2 in fp64.
-constexpr int kGluCache = 12;  // 4-element vectors cached per thread (K <= 12288)
+constexpr int kGluCache = 12;  // 4-element vectors cached per thread, at most (K <= 12288)
 
-template <int KIND, bool SUBLN>
+// CACHE: as for k_act_quant, the smallest instantiated cache (in 4-element
+// vectors per thread) that holds the row.
+template <int KIND, bool SUBLN, int CACHE>
 __global__ __launch_bounds__(kActThreads) void k_glu_quant(
     const float* __restrict__ gate, const float* __restrict__ up, int64_t K,
     const uint16_t* __restrict__ gain, float rms_eps, int8_t* __restrict__ hq,
@@ -173,13 +181,13 @@ __global__ __launch_bounds__(kActThreads) void k_glu_quant(
     const uint2* gnv = reinterpret_cast<const uint2*>(gain);  // 4 bf16 per vector
     const int tid = threadIdx.x;
     const int nvec = (int)(K / 4);
-    const bool cached = nvec <= kGluCache * kActThreads;
+    const bool cached = nvec <= CACHE * kActThreads;
 
     // With a gain, the cached path keeps the gain vectors beside the gated
     // values: a gain load issued among the code stores would wait for them
     // (vector loads and stores retire through one counter in issue order).
-    uint2 ch[kGluCache];
-    uint2 cgn[SUBLN ? kGluCache : 1];
+    uint2 ch[CACHE];
+    uint2 cgn[SUBLN ? CACHE : 1];
     float amax = 0.0f;
     double ss = 0.0;
     auto scan = [&](const uint2 h, const uint2 gv) {
@@ -197,9 +205,9 @@ __global__ __launch_bounds__(kActThreads) void k_glu_quant(
         }
     };
     if (cached) {
-        float4 cg[kGluCache], cu[kGluCache];
+        float4 cg[CACHE], cu[CACHE];
 #pragma unroll
-        for (int j = 0; j < kGluCache; ++j) {
+        for (int j = 0; j < CACHE; ++j) {
             const int v = tid + kActThreads * j;
             if (v < nvec) {
                 cg[j] = grow[v];
@@ -208,7 +216,7 @@ __global__ __launch_bounds__(kActThreads) void k_glu_quant(
             }
         }
 #pragma unroll
-        for (int j = 0; j < kGluCache; ++j) {
+        for (int j = 0; j < CACHE; ++j) {
             const int v = tid + kActThreads * j;
             if (v < nvec) {
                 ch[j] = glu4<KIND>(cg[j], cu[j]);
@@ -242,7 +250,7 @@ __global__ __launch_bounds__(kActThreads) void k_glu_quant(
     };
     if (cached) {
 #pragma unroll
-        for (int j = 0; j < kGluCache; ++j) {
+        for (int j = 0; j < CACHE; ++j) {
             const int v = tid + kActThreads * j;
             if (v < nvec) emit(v, ch[j], SUBLN ? cgn[j] : ch[j]);
         }
@@ -262,12 +270,25 @@ __global__ __launch_bounds__(kActThreads) void k_glu_quant(
 
 hipError_t launch_quantize_acts(const uint16_t* x, int64_t M, int64_t K, const uint16_t* gain,
                                 float rms_eps, int8_t* xq, float* scale, hipStream_t stream) {
-    if (gain)
-        hipLaunchKernelGGL(k_act_quant<true>, dim3((unsigned)M), dim3(kActThreads), 0, stream, x,
-                           K, gain, rms_eps, xq, scale);
-    else
-        hipLaunchKernelGGL(k_act_quant<false>, dim3((unsigned)M), dim3(kActThreads), 0, stream, x,
-                           K, gain, rms_eps, xq, scale);
+    const int64_t per = (K / 8 + kActThreads - 1) / kActThreads;  // vectors per thread
+    auto go = [&](auto fused, auto cache) {
+        hipLaunchKernelGGL((k_act_quant<decltype(fused)::value, decltype(cache)::value>),
+                           dim3((unsigned)M), dim3(kActThreads), 0, stream, x, K, gain, rms_eps,
+                           xq, scale);
+    };
+    using T = std::true_type;
+    using F = std::false_type;
+    if (gain) {
+        if (per <= 2) go(T(), std::integral_constant<int, 2>());
+        else if (per <= 4) go(T(), std::integral_constant<int, 4>());
+        else if (per <= 8) go(T(), std::integral_constant<int, 8>());
+        else go(T(), std::integral_constant<int, kActCache>());
+    } else {
+        if (per <= 2) go(F(), std::integral_constant<int, 2>());
+        else if (per <= 4) go(F(), std::integral_constant<int, 4>());
+        else if (per <= 8) go(F(), std::integral_constant<int, 8>());
+        else go(F(), std::integral_constant<int, kActCache>());
+    }
     return hipGetLastError();
 }
 
@@ -276,12 +297,20 @@ template <int KIND>
 void launch_glu_quant_kind(const float* gate, const float* up, int64_t M, int64_t K,
                            const uint16_t* gain, float rms_eps, int8_t* hq, float* scale,
                            hipStream_t stream) {
-    if (gain)
-        hipLaunchKernelGGL((k_glu_quant<KIND, true>), dim3((unsigned)M), dim3(kActThreads), 0,
-                           stream, gate, up, K, gain, rms_eps, hq, scale);
-    else
-        hipLaunchKernelGGL((k_glu_quant<KIND, false>), dim3((unsigned)M), dim3(kActThreads), 0,
-                           stream, gate, up, K, gain, rms_eps, hq, scale);
+    const int64_t per = (K / 4 + kActThreads - 1) / kActThreads;  // vectors per thread
+    auto go = [&](auto subln, auto cache) {
+        hipLaunchKernelGGL((k_glu_quant<KIND, decltype(subln)::value, decltype(cache)::value>),
+                           dim3((unsigned)M), dim3(kActThreads), 0, stream, gate, up, K, gain,
+                           rms_eps, hq, scale);
+    };
+    auto pick = [&](auto subln) {
+        if (per <= 2) go(subln, std::integral_constant<int, 2>());
+        else if (per <= 4) go(subln, std::integral_constant<int, 4>());
+        else if (per <= 8) go(subln, std::integral_constant<int, 8>());
+        else go(subln, std::integral_constant<int, kGluCache>());
+    };
+    if (gain) pick(std::true_type());
+    else pick(std::false_type());
 }
 }  // namespace
 
