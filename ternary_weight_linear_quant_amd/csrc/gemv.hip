@@ -31,8 +31,9 @@
 // Each lane loads 16 bytes of its row per chunk; the 4 lanes of a row cover
 // 64 contiguous bytes. The whole [M][K] int8 activation block is staged once
 // per workgroup in LDS by direct global-to-LDS loads issued before the weight
-// loads, token-minor so that a fragment read is 16 consecutive 16-byte slots
-// (slots past K, where a format pads its rows, hold zeros). Then each wave
+// loads, one token row after another (rows padded by 16 bytes against bank
+// conflicts; bytes past K, where a format pads its rows, hold zeros), each
+// load 1 KB of one row. Then each wave
 // issues up to R chunk loads of its weights and waits only for its
 // activation loads before the workgroup barrier, so the weight stream stays
 // in flight; a ring of R slots refills each chunk R ahead. Tokens >= M read
@@ -197,17 +198,22 @@ __global__ __launch_bounds__(64 * RG * KS, WPE) void k_gemv(const int8_t* __rest
     // This wave's chunks: c_i = ks + KS * i, i < nw.
     const int nw = ks < nfull ? (nfull - ks + KS - 1) / KS : 0;
 
-    // 1. Activations straight into LDS, issued first. LDS layout: 16-byte
-    //    chunk j of token t at slot j*M + t, so the 16 tokens of a B fragment
-    //    read 16 consecutive slots. Each DMA instruction fills 64 slots.
-    const int total = M * (K / 16);
+    // 1. Activations straight into LDS, issued first. LDS layout: token t's
+    //    row at t * pitch, pitch = K extent + 16 bytes (16 times an odd
+    //    number, so the 16 tokens of a B fragment read fall on distinct
+    //    16-byte bank groups). Each DMA instruction fills 1 KB of one token's
+    //    row from 1 KB of contiguous memory (lanes past the row's end idle):
+    //    a CU draws about 44 GB/s from contiguous 16-byte loads against
+    //    25-33 GB/s when the lanes of a load spread over the tokens.
+    const int pitch = F::k_extent(K) + 16;
+    const int rowv = K / 16;                 // 16-byte pieces per token
+    const int nblk = (rowv + kWave - 1) / kWave;
     const uint32_t xbase = lds_offset(smem);
-    for (int p0 = wave * kWave; p0 < total; p0 += NT) {
-        const int p = p0 + lane;
-        if (p < total) {
-            const int j = p / M, t = p - j * M;
-            lds_dma16(xq + (size_t)t * K + 16 * j, xbase + 16 * p0);
-        }
+    for (int q = wave; q < M * nblk; q += NT / kWave) {
+        const int t = q / nblk, b = q - t * nblk;
+        const int v = b * kWave + lane;
+        if (v < rowv)
+            lds_dma16(xq + (size_t)t * K + 16 * v, xbase + t * pitch + b * kWave * 16);
     }
     asm volatile("" ::: "memory");
 
@@ -218,12 +224,15 @@ __global__ __launch_bounds__(64 * RG * KS, WPE) void k_gemv(const int8_t* __rest
         if (i < nw) wb[i] = *reinterpret_cast<const uint4*>(wrow + 64 * (ks + KS * i));
     asm volatile("" ::: "memory");
 
-    // Slots of the padded K extent hold zeros; the base-3 table follows the
+    // Each row's padded K extent holds zeros; the base-3 table follows the
     // activations.
-    const int xslots = M * (F::k_extent(K) / 16);
-    for (int p = total + tid; p < xslots; p += NT)
-        *reinterpret_cast<uint4*>(smem + 16 * p) = make_uint4(0, 0, 0, 0);
-    uint2* tab = reinterpret_cast<uint2*>(smem + 16 * xslots);
+    const int padv = (F::k_extent(K) - K) / 16;
+    for (int p = tid; p < M * padv; p += NT) {
+        const int t = p / padv;
+        *reinterpret_cast<uint4*>(smem + t * pitch + K + 16 * (p - t * padv)) =
+            make_uint4(0, 0, 0, 0);
+    }
+    uint2* tab = reinterpret_cast<uint2*>(smem + M * pitch);
     if constexpr (F::kTable) build_base3_table(tab, tid, NT);
 
     // 3. Wait for this wave's activation DMA only (the weight loads, issued
@@ -236,7 +245,7 @@ __global__ __launch_bounds__(64 * RG * KS, WPE) void k_gemv(const int8_t* __rest
 
     const int tok = lane % 16;
     const bool tok_ok = tok < M;
-    const int8_t* xl = reinterpret_cast<const int8_t*>(smem) + 16 * (tok_ok ? tok : 0);
+    const int8_t* xl = reinterpret_cast<const int8_t*>(smem) + (tok_ok ? tok : 0) * pitch;
 
     v4i acc = {0, 0, 0, 0};
     const v4i zero = {0, 0, 0, 0};
@@ -248,7 +257,7 @@ __global__ __launch_bounds__(64 * RG * KS, WPE) void k_gemv(const int8_t* __rest
         for (int s = 0; s < F::kSub; ++s) {
             const v4i a = dec.frag(s);
             const int j = c * (4 * F::kSub) + g * F::kSub + s;
-            const v4i b = tok_ok ? *reinterpret_cast<const v4i*>(xl + 16 * j * M) : zero;
+            const v4i b = tok_ok ? *reinterpret_cast<const v4i*>(xl + 16 * j) : zero;
             acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc, 0, 0, 0);
         }
     };
@@ -279,7 +288,7 @@ __global__ __launch_bounds__(64 * RG * KS, WPE) void k_gemv(const int8_t* __rest
         for (int s = 0; s < F::kSub; ++s) {
             const v4i a = gv ? dec.frag(s) : zero;
             const int j = nfull * (4 * F::kSub) + g * F::kSub + s;
-            const v4i b = (gv && tok_ok) ? *reinterpret_cast<const v4i*>(xl + 16 * j * M) : zero;
+            const v4i b = (gv && tok_ok) ? *reinterpret_cast<const v4i*>(xl + 16 * j) : zero;
             acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc, 0, 0, 0);
         }
     }
@@ -322,13 +331,15 @@ bool gemv_base3_supported(int64_t M, int64_t K) { return gemv_fits<Base3>(M, K);
 template <class F, int RG, int KS, int R, int WPE>
 static hipError_t launch_gemv_cfg(const int8_t* xq, const float* xs, int M, int K,
                                  const GemvArgs& args, hipStream_t stream) {
-    const size_t lds = (size_t)M * F::k_extent(K) + (F::kTable ? kBase3TableBytes : 0);
+    // Token rows of K extent + 16 bytes, then the base-3 table.
+    const size_t lds = (size_t)M * (F::k_extent(K) + 16) + (F::kTable ? kBase3TableBytes : 0);
     static bool attr_set = false;
     if (lds > 64 * 1024 && !attr_set) {
         hipError_t e =
             hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv<F, RG, KS, R, WPE>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)(kGemvMaxXBytes + kBase3TableBytes));
+                                           (int)(kGemvMaxXBytes + 16 * kGemvMaxM +
+                                                 kBase3TableBytes));
         if (e != hipSuccess) return e;
         attr_set = true;
     }
