@@ -531,7 +531,9 @@ def main():
                "roofline": {"bound": "mfma", "kernel": "k_ste_dx (v_mfma_f32_32x32x16_bf16)",
                             "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS,
                             "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
-                            "traffic": None, "per_projection": per},
+                            "traffic": traffic.get("ste_dx_4096"),
+                            "traffic_unit": "HBM bytes per bl_ste_backward_dx call",
+                            "per_projection": per},
                "vendor_bf16_gemm": {
                    "library": "hipBLASLt through torch.matmul: dense bf16 x bf16 -> bf16 on "
                               "the same shapes, weights stored as bf16 (context, not a "

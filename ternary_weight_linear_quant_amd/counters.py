@@ -79,6 +79,10 @@ PHASES = {
     "gemm_prefill_4096": (["gemm.hip", "common.hpp"],
                           "bl_bitlinear at M=4096 on 2560->6912 and 6912->2560", 2,
                           "bl_bitlinear call (k_gemm)"),
+    "ste_dx_4096": (["ste.hip", "common.hpp"],
+                    "bl_ste_backward_dx at M=4096 on 2560->6912 and 6912->2560 "
+                    "(dy bf16 [4096][N] -> dx fp32 [4096][K])", 2,
+                    "bl_ste_backward_dx call (k_ste_dx)"),
     "gemm_prefill_70b": (["gemm.hip", "common.hpp"],
                          "bl_bitlinear at M=2048 on 8192->28672 and 28672->8192", 2,
                          "bl_bitlinear call (k_gemm)"),
@@ -162,6 +166,15 @@ def run():
             q4[(M, name)] = (xq, xs, torch.empty((M, N), dtype=torch.float32, device=dev))
 
     _, p3, M3 = wl.WORKLOADS[3]
+    s3 = []
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2024)
+    for i, (name, K, N) in enumerate(p3):
+        pk, g = weights(3, i, N, K, 1)[0]
+        dy = (torch.randn((M3[0], N), generator=gen, device=dev) * 0.01).to(torch.bfloat16)
+        s3.append((bl.pack_ste_t(pk, K), g, dy,
+                   torch.empty((M3[0], K), dtype=torch.float32, device=dev), N))
+        del pk
     q3 = []
     for i, (name, K, N) in enumerate(p3):
         pk, g = weights(3, i, N, K, 1)[0]
@@ -217,6 +230,10 @@ def run():
                     bl.bitlinear(xq, xs, *w4[name][c], out=y)
         return fn
 
+    def ste4096():
+        for qT, g, dy, dx, N in s3:
+            bl.ste_backward_dx(dy, qT, g, N, out=dx)
+
     def prefill4096():
         for xq, xs, pk, g, y in q3:
             bl.bitlinear(xq, xs, pk, g, out=y)
@@ -236,6 +253,7 @@ def run():
     phase("gemv_3b_m1", block3b(1))
     phase("gemm_3b_m512", block3b(512))
     phase("gemm_prefill_4096", prefill4096)
+    phase("ste_dx_4096", ste4096)
     phase("gemm_prefill_70b", prefill70)
     marker()
     print("done", flush=True)
