@@ -25,7 +25,10 @@
  *   - All array pointers are DEVICE pointers (hipMalloc'd or equivalent) on
  *     the current HIP device; the caller owns all memory. The library never
  *     allocates, on the hot path or elsewhere, and keeps no state beyond a
- *     cached device count.
+ *     cached device count and, per device, which kernels have had their
+ *     LDS limit raised (set on a kernel's first launch on that device).
+ *     Calls may come from several host threads; bl_last_hip_error() is per
+ *     thread.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Every call only enqueues work on `stream` and never synchronises, so it
  *     may be captured into a HIP graph. Calls on different streams may run

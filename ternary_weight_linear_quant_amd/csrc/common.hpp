@@ -4,7 +4,27 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace bl {
+
+// Raises a kernel's dynamic LDS limit to `max_lds` (when above HIP's 64 KiB
+// default) once per device: the attribute belongs to the kernel on the current
+// device. `done` keeps a bit per device (devices 0..63; others set it on every
+// call). Two threads racing on a first call both set the same value, which is
+// harmless. `max_lds` must cover every launch of the kernel that follows.
+inline hipError_t allow_dynamic_lds(const void* kern, size_t max_lds,
+                                    std::atomic<uint64_t>& done) {
+    if (max_lds <= 64 * 1024) return hipSuccess;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t)1 << dev : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_lds);
+    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));

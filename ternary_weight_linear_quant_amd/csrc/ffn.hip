@@ -336,11 +336,17 @@ bool ffn_fused_supported(int64_t M, int64_t K, int64_t N_ff, bool subln) {
 
 namespace {
 
+// Every supported launch stages at most 128 KiB of int8 activations
+// (ffn_fused_supported, ffn_gate_up_supported); the kernels' static LDS,
+// under 10 KiB, fits beside it.
+constexpr size_t kFfnMaxDynLds = 128 * 1024;
+
+// `done` is a flag set of the launcher's own kernel instance.
 template <typename Kern>
-hipError_t allow_lds(Kern kern, size_t lds) {
+hipError_t allow_lds(Kern kern, size_t lds, std::atomic<uint64_t>& done) {
     if (lds <= 64 * 1024) return hipSuccess;
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (lds > kFfnMaxDynLds) return hipErrorInvalidValue;
+    return allow_dynamic_lds(reinterpret_cast<const void*>(kern), kFfnMaxDynLds, done);
 }
 
 template <int KS, bool SUBLN, int RG, int CU>
@@ -349,7 +355,8 @@ hipError_t launch_ffn_down(const uint16_t* h, int M, int N_ff, const uint32_t* W
                            float rms_eps, hipStream_t stream) {
     auto kern = &k_ffn_gemv<false, KS, SUBLN, kGluRelu2, RG, CU>;
     const size_t lds = (size_t)M * N_ff;
-    hipError_t e = allow_lds(kern, lds);
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = allow_lds(kern, lds, lds_set);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((K + 16 * RG - 1) / (16 * RG)), dim3(64 * KS * RG), lds,
                        stream, h, M, N_ff, Wd, gd, (const uint32_t*)nullptr,
@@ -379,7 +386,8 @@ hipError_t launch_ffn_up(const uint16_t* x, int M, int K, const uint32_t* Wg, co
                          hipStream_t stream) {
     auto kern = &k_ffn_gemv<true, kKsA, false, KIND, RG, CU>;
     const size_t lds = (size_t)M * K;
-    hipError_t e = allow_lds(kern, lds);
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = allow_lds(kern, lds, lds_set);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((N_ff + 16 * RG - 1) / (16 * RG)), dim3(64 * 2 * kKsA * RG),
                        lds, stream, x, M, K, Wg, gg, Wu, gu, N_ff, (float*)nullptr, h,

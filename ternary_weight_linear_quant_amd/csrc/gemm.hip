@@ -438,12 +438,10 @@ static hipError_t launch_gemm_tile(const int8_t* xq, const float* xs, int M, int
     constexpr size_t lds =
         (size_t)STAGES * KS * (BM * kARow + BN * kBRow) + (SPLIT ? 0 : BM * 4);
     auto kern = &k_gemm<BM, BN, WGM, WGN, STAGES, WPE, SPLIT, KS>;
-    static bool attr_set = false;
-    if (lds > 64 * 1024 && !attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    static std::atomic<uint64_t> lds_set{0};
+    {
+        hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kern), lds, lds_set);
         if (e != hipSuccess) return e;
-        attr_set = true;
     }
     const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const int KT = (K + kBK - 1) / kBK;

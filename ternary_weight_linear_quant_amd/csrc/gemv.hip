@@ -333,15 +333,13 @@ static hipError_t launch_gemv_cfg(const int8_t* xq, const float* xs, int M, int 
                                  const GemvArgs& args, hipStream_t stream) {
     // Token rows of K extent + 16 bytes, then the base-3 table.
     const size_t lds = (size_t)M * (F::k_extent(K) + 16) + (F::kTable ? kBase3TableBytes : 0);
-    static bool attr_set = false;
-    if (lds > 64 * 1024 && !attr_set) {
-        hipError_t e =
-            hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv<F, RG, KS, R, WPE>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)(kGemvMaxXBytes + 16 * kGemvMaxM +
-                                                 kBase3TableBytes));
+    // The attribute takes the largest block any supported shape stages.
+    static std::atomic<uint64_t> lds_set{0};
+    if (lds > 64 * 1024) {
+        hipError_t e = allow_dynamic_lds(
+            reinterpret_cast<const void*>(&k_gemv<F, RG, KS, R, WPE>),
+            (size_t)(kGemvMaxXBytes + 16 * kGemvMaxM + kBase3TableBytes), lds_set);
         if (e != hipSuccess) return e;
-        attr_set = true;
     }
     GemvArgs a = args;
     for (int i = 0; i < 2; ++i)

@@ -328,12 +328,10 @@ static hipError_t launch_ste_tile(const uint16_t* dy, int M, int N, const uint8_
                                   const float* gamma, int K, float* dx, hipStream_t stream) {
     constexpr size_t lds = (size_t)STAGES * (BM * 2 * BR + BN * BR / 4);
     auto kern = &k_ste_dx<BM, BN, WGM, WGN, BR, STAGES, WPE>;
-    static bool attr_set = false;
-    if (lds > 64 * 1024 && !attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    static std::atomic<uint64_t> lds_set{0};
+    {
+        hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kern), lds, lds_set);
         if (e != hipSuccess) return e;
-        attr_set = true;
     }
     const int tiles = ((M + BM - 1) / BM) * ((K + BN - 1) / BN);
     hipLaunchKernelGGL(kern, dim3(tiles), dim3(64 * WGM * WGN), lds, stream, dy, M, N, qT,
