@@ -37,6 +37,9 @@
  *     violation the call returns BL_ERR_INVALID_ARG and enqueues nothing.
  *     If no HIP device is visible the call returns BL_ERR_NO_DEVICE. A failed
  *     launch returns BL_ERR_HIP (bl_last_hip_error() gives the hipError_t).
+ *     Before enqueuing, a call clears HIP's pending error of the calling
+ *     thread (hipGetLastError), so BL_ERR_HIP always names this call's own
+ *     failed launch; check your own launches before calling in.
  *     Faults inside kernels surface at the caller's next synchronisation.
  *   - Shapes: M tokens, K input features, N output features; 1 <= M, N,
  *     64 <= K, K % 64 == 0, and M*K, N*K below 2^31. Base pointers of x,

@@ -19,13 +19,17 @@ bool shape_ok(int64_t rows, int64_t K) {
     return true;
 }
 
+// Every entry point calls this after validating its arguments and before
+// enqueuing anything. It also clears the thread's pending HIP error, so that
+// the hipGetLastError() after each launch reports that launch, not an error
+// left by an earlier, unrelated call.
 int device_status() {
     int n = g_device_count.load(std::memory_order_relaxed);
     if (n < 0) {
         if (hipGetDeviceCount(&n) != hipSuccess) n = 0;
-        (void)hipGetLastError();
         g_device_count.store(n, std::memory_order_relaxed);
     }
+    (void)hipGetLastError();
     return n > 0 ? BL_OK : BL_ERR_NO_DEVICE;
 }
 
