@@ -1074,3 +1074,23 @@ def test_calls_on_two_streams_do_not_interfere():
     for si in range(len(streams)):
         for i, (kind, _a, ref) in enumerate(jobs[si]):
             assert torch.equal(outs[si][i].view(torch.int32), ref.view(torch.int32)), (si, i, kind)
+
+
+@pytest.mark.gpu
+def test_pending_hip_error_is_not_reported_as_the_calls_own():
+    """A non-sticky HIP error left by an unrelated call (hipSetDevice on a
+    device that does not exist, which changes nothing) does not turn the next
+    library call into BL_ERR_HIP: the call clears it before enqueuing, runs,
+    and leaves no pending error behind."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    x = torch.randn(3, 2560, device=DEV).to(torch.bfloat16)
+    ref_q, ref_s = bl.quantize_acts(x)
+    torch.cuda.synchronize()
+    # No torch kernel may run from here to the library call: torch would
+    # report the pending error itself.
+    assert hip.hipSetDevice(ctypes.c_int(9999)) != 0    # leaves a pending error
+    xq, xs = bl.quantize_acts(x)                         # raises on BL_ERR_HIP
+    assert hip.hipGetLastError() == 0
+    torch.cuda.synchronize()
+    assert torch.equal(xq, ref_q) and torch.equal(xs.view(torch.int32), ref_s.view(torch.int32))
