@@ -39,7 +39,8 @@
  *     launch returns BL_ERR_HIP (bl_last_hip_error() gives the hipError_t).
  *     Before enqueuing, a call clears HIP's pending error of the calling
  *     thread (hipGetLastError), so BL_ERR_HIP always names this call's own
- *     failed launch; check your own launches before calling in.
+ *     failed launch; check your own launches before calling in. A call that
+ *     returns BL_ERR_HIP leaves no pending HIP error behind.
  *     Faults inside kernels surface at the caller's next synchronisation.
  *   - Shapes: M tokens, K input features, N output features; 1 <= M, N,
  *     64 <= K, K % 64 == 0, and M*K, N*K below 2^31. Base pointers of x,

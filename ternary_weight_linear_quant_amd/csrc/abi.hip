@@ -33,9 +33,12 @@ int device_status() {
     return n > 0 ? BL_OK : BL_ERR_NO_DEVICE;
 }
 
+// A failure is recorded for bl_last_hip_error() and taken off HIP's pending
+// error, so it does not resurface in the caller's next, unrelated check.
 int hip_status(hipError_t e) {
     if (e == hipSuccess) return BL_OK;
     g_last_hip_error = (int)e;
+    (void)hipGetLastError();
     return BL_ERR_HIP;
 }
 
