@@ -437,6 +437,7 @@ static hipError_t launch_gemm_tile(const int8_t* xq, const float* xs, int M, int
     // the epilogue.
     constexpr size_t lds =
         (size_t)STAGES * KS * (BM * kARow + BN * kBRow) + (SPLIT ? 0 : BM * 4);
+    static_assert(lds <= 160 * 1024, "a workgroup holds at most 160 KiB of LDS");
     auto kern = &k_gemm<BM, BN, WGM, WGN, STAGES, WPE, SPLIT, KS>;
     static std::atomic<uint64_t> lds_set{0};
     {

@@ -327,6 +327,7 @@ template <int BM, int BN, int WGM, int WGN, int BR, int STAGES, int WPE>
 static hipError_t launch_ste_tile(const uint16_t* dy, int M, int N, const uint8_t* qT,
                                   const float* gamma, int K, float* dx, hipStream_t stream) {
     constexpr size_t lds = (size_t)STAGES * (BM * 2 * BR + BN * BR / 4);
+    static_assert(lds <= 160 * 1024, "a workgroup holds at most 160 KiB of LDS");
     auto kern = &k_ste_dx<BM, BN, WGM, WGN, BR, STAGES, WPE>;
     static std::atomic<uint64_t> lds_set{0};
     {
