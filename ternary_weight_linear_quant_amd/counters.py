@@ -16,6 +16,11 @@ Two parts:
     the call count and average duration, and per launch shape the median,
     p10 and p90.
 
+``python -m ternary_weight_linear_quant_amd.counters busy PASS_DIR``
+    Formats one SQ counter pass over the same workload (matrix-core busy
+    cycles, VALU, MFMA and LDS instruction counts, LDS bank conflicts) per
+    phase and kernel.
+
 ``python -m ternary_weight_linear_quant_amd.counters summarize FETCH_DIR WRITE_DIR``
     Reads the two passes' ``*counter_collection.csv``, scales each counter by
     (known bytes / counter reading) of the calibration copy, and prints a
@@ -365,6 +370,69 @@ def summarize(fetch_dir, write_dir, cmd_fetch, cmd_write):
     return "\n".join(lines)
 
 
+BUSY_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU",
+                 "SQ_ACTIVE_INST_VALU", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT",
+                 "SQ_WAVE_CYCLES", "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE")
+SIMDS, XCDS = 1024, 8
+
+
+def _read_all(d):
+    """Library dispatches of one pass with every counter it collected:
+    (name, grid, {counter: value}) in dispatch order."""
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    rows = {}
+    for f in files:
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                name = r["Kernel_Name"]
+                if name.startswith("void "):
+                    name = name[5:]
+                if not name.startswith("bl::"):
+                    continue
+                key = (int(r["Process_Id"]), int(r["Dispatch_Id"]))
+                ent = rows.setdefault(key, (name, int(r["Grid_Size"]), {}))
+                ent[2][r["Counter_Name"]] = float(r["Counter_Value"])
+    return [rows[k] for k in sorted(rows)]
+
+
+def busy(pass_dir, cmd):
+    """Matrix-core and VALU evidence per phase and kernel from one SQ pass.
+
+    SQ_VALU_MFMA_BUSY_CYCLES sums the matrix-core cycles of every MFMA issued
+    (over all 1024 SIMDs); GRBM_GUI_ACTIVE sums the busy cycles of the 8 XCDs.
+    MFMA busy = (MFMA cycles per SIMD) / (active cycles per XCD), at whatever
+    clock the part ran."""
+    phases = _phases(_read_all(pass_dir))
+    lines = ["# Matrix-core and VALU counters of the BitLinear kernels (rocprofv3 SQ pass)", "",
+             "Command (from the repository root, one pass):", "", "```", cmd,
+             "python -m ternary_weight_linear_quant_amd.counters busy gpurun_out/pmc_busy",
+             "```", "",
+             "Per dispatch means. MFMA busy = (SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs) / "
+             "(GRBM_GUI_ACTIVE / 8 XCDs): the share of the kernel's active cycles in which an "
+             "average SIMD's matrix core works. VALU/MFMA = SQ_INSTS_VALU / SQ_INSTS_MFMA "
+             "(wave instructions; gfx950 co-issues VALU work beside MFMAs of other waves).", "",
+             "| phase | kernel | dispatches | MFMA busy | VALU/MFMA | VALU insts | MFMA insts "
+             "| LDS insts | LDS bank conflicts | active cycles per XCD |",
+             "|---|---|---|---|---|---|---|---|---|---|"]
+    for ph in PHASE_ORDER:
+        by = {}
+        for name, _grid, vals in phases[ph]:
+            by.setdefault(_short(name), []).append(vals)
+        for kern, vs in by.items():
+            mean = {c: sum(v.get(c, 0.0) for v in vs) / len(vs) for c in BUSY_COUNTERS}
+            act = mean["GRBM_GUI_ACTIVE"] / XCDS
+            mb = (mean["SQ_VALU_MFMA_BUSY_CYCLES"] / SIMDS) / act if act else 0.0
+            vpm = (mean["SQ_INSTS_VALU"] / mean["SQ_INSTS_MFMA"]
+                   if mean["SQ_INSTS_MFMA"] else float("nan"))
+            lines.append(f"| {ph} | {kern} | {len(vs)} | {100 * mb:.1f}% | {vpm:.2f} | "
+                         f"{mean['SQ_INSTS_VALU']:.0f} | {mean['SQ_INSTS_MFMA']:.0f} | "
+                         f"{mean['SQ_INSTS_LDS']:.0f} | {mean['SQ_LDS_BANK_CONFLICT']:.0f} | "
+                         f"{act:.0f} |")
+    return "\n".join(lines) + "\n"
+
+
 def trace(prof_dir, cmd, desc):
     def one(pattern):
         f = glob.glob(os.path.join(prof_dir, "**", pattern), recursive=True)
@@ -438,9 +506,16 @@ def main():
                    "-d <FETCH_DIR> -- python3 -m ternary_weight_linear_quant_amd.counters run")
     s.add_argument("--cmd-write", default="rocprofv3 --pmc WRITE_SIZE --output-format csv "
                    "-d <WRITE_DIR> -- python3 -m ternary_weight_linear_quant_amd.counters run")
+    b = sub.add_parser("busy")
+    b.add_argument("pass_dir")
+    b.add_argument("--cmd", dest="busy_cmd", default="rocprofv3 --pmc " + " ".join(BUSY_COUNTERS)
+                   + " --output-format csv -d <PASS_DIR> -- python3 -m "
+                   "ternary_weight_linear_quant_amd.counters run")
     a = ap.parse_args()
     if a.cmd == "run":
         run()
+    elif a.cmd == "busy":
+        print(busy(a.pass_dir, a.busy_cmd), end="")
     elif a.cmd == "trace":
         print(trace(a.prof_dir, a.trace_cmd, a.desc), end="")
     else:
