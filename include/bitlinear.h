@@ -151,8 +151,11 @@ int bl_bitlinear(const int8_t* x_q, const float* x_scale, int64_t M, int64_t K,
 /* As bl_bitlinear with an explicit kernel choice, for testing and tuning:
  * path 0 = automatic, 1 = GEMV (requires M <= 16 and M*K <= 128 KiB),
  * 2 = GEMM, 3 = wide GEMV for up to 64 tokens (128 weight rows per
- * workgroup, activations staged in K blocks; requires M <= 64). All give the
- * same bits. Automatic: GEMV when it applies, else the wide GEMV up to 64
+ * workgroup, activations staged in K blocks; requires M <= 64), 4 = one-token
+ * GEMV (each wave streams whole rows as 1 KB contiguous pieces; requires
+ * M == 1 and K <= 65536). All give the same bits. Automatic: the one-token
+ * GEMV at one token when K <= 8192 or K is a multiple of 4096, else the GEMV
+ * when it applies, else the wide GEMV up to 64
  * tokens when each of its workgroups streams at least four K blocks of 512
  * and the matrix is not one where the GEMM measured faster (from 48 tokens
  * on matrices of at least 16 Mi weights, from 33 tokens on wide ones, N > K,

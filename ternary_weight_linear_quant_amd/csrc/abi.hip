@@ -133,7 +133,7 @@ int bl_bitlinear_path(const int8_t* x_q, const float* x_scale, int64_t M, int64_
     if (!shape_ok(M, K) || !shape_ok(N, K)) return BL_ERR_INVALID_ARG;
     if (M > (int64_t{1} << 31) / N) return BL_ERR_INVALID_ARG;  // M*N < 2^31
     if (!aligned16(x_q) || !aligned16(W_packed)) return BL_ERR_INVALID_ARG;
-    if (path < 0 || path > 3) return BL_ERR_INVALID_ARG;
+    if (path < 0 || path > 4) return BL_ERR_INVALID_ARG;
     // The outputs may not alias an input (y holds partial sums mid-call).
     const size_t ny = (size_t)(M * N) * 4;
     if (overlaps(y, ny, x_q, (size_t)(M * K)) || overlaps(y, ny, x_scale, (size_t)M * 4) ||
@@ -143,13 +143,20 @@ int bl_bitlinear_path(const int8_t* x_q, const float* x_scale, int64_t M, int64_
                 overlaps(acc, ny, x_scale, (size_t)M * 4) ||
                 overlaps(acc, ny, W_packed, (size_t)(N * K) / 4) || overlaps(acc, ny, gamma, 4)))
         return BL_ERR_INVALID_ARG;
+    const bool one_ok = bl::gemv1_supported(M, K);
     const bool gemv_ok = bl::gemv_supported(M, K);
     const bool wide_ok = bl::gemv_wide_supported(M, K);
-    if ((path == 1 && !gemv_ok) || (path == 3 && !wide_ok)) return BL_ERR_INVALID_ARG;
+    if ((path == 1 && !gemv_ok) || (path == 3 && !wide_ok) || (path == 4 && !one_ok))
+        return BL_ERR_INVALID_ARG;
     if (int s = device_status()) return s;
-    const bool use_gemv = path == 1 || (path == 0 && gemv_ok);
-    const bool use_wide = path == 3 || (path == 0 && !gemv_ok && bl::gemv_wide_preferred(M, N, K));
+    const bool use_one = path == 4 || (path == 0 && bl::gemv1_preferred(M, K));
+    const bool use_gemv = path == 1 || (path == 0 && !one_ok && gemv_ok);
+    const bool use_wide = path == 3 || (path == 0 && !one_ok && !gemv_ok &&
+                                        bl::gemv_wide_preferred(M, N, K));
     hipStream_t st = as_stream(stream);
+    if (use_one)
+        return hip_status(bl::launch_gemv1(x_q, x_scale, (int)K, W_packed, gamma, (int)N, y, acc,
+                                           st));
     if (use_gemv)
         return hip_status(bl::launch_gemv(x_q, x_scale, (int)M, (int)K, W_packed, gamma, (int)N,
                                           y, acc, st));

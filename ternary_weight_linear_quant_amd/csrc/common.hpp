@@ -185,6 +185,19 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// Sum of an int32 over the 64 lanes of a wave (all lanes active), returned in
+// every lane: each 16-lane row forms inclusive prefix sums with DPP row shifts
+// (lanes shifted in from outside the row read 0), then the four row totals
+// are read from lanes 15, 31, 47 and 63. VALU only, no LDS round trips.
+__device__ __forceinline__ int wave_sum_i32(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);  // row_shr:8
+    return __builtin_amdgcn_readlane(v, 15) + __builtin_amdgcn_readlane(v, 31) +
+           __builtin_amdgcn_readlane(v, 47) + __builtin_amdgcn_readlane(v, 63);
+}
+
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);

@@ -18,6 +18,13 @@ bool gemv_supported(int64_t M, int64_t K);
 hipError_t launch_gemv(const int8_t* xq, const float* xs, int M, int K, const uint32_t* Wp,
                        const float* gamma, int N, float* y, int32_t* acc, hipStream_t stream);
 
+// Decode for one token: each wave streams whole rows as 1 KB contiguous
+// pieces (K up to 65536). Returns hipErrorInvalidValue otherwise.
+bool gemv1_supported(int64_t M, int64_t K);
+bool gemv1_preferred(int64_t M, int64_t K);
+hipError_t launch_gemv1(const int8_t* xq, const float* xs, int K, const uint32_t* Wp,
+                        const float* gamma, int N, float* y, int32_t* acc, hipStream_t stream);
+
 // Split K: int32 zeros into y, and y[m][n] = acc * (x_scale[m] * gamma) in
 // place afterwards (acc, if not null, receives the sums).
 hipError_t launch_splitk_zero(int32_t* y, size_t total, hipStream_t stream);

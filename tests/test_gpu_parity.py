@@ -201,6 +201,48 @@ def test_gemv_parity(M, K, N):
     assert_y_close(y.cpu().numpy(), y_ref, "gemv")
 
 
+# One-token GEMV (path 4): K <= 4096 and <= 8192 run the register-cached
+# variant (one or two 1 KB pieces per row, four / two rows per wave, one row
+# when N is smaller), longer rows the LDS-streamed one (one row per wave);
+# K = 4160 / 8256 / 2560 / 6912 end in a partial piece, K = 65536 stages
+# more activation slots than a thread holds across the weight issue.
+ONE_TOKEN_CASES = [(64, 1), (320, 200), (4096, 3), (4096, 4), (2560, 6912), (4160, 1),
+                   (4160, 7), (8192, 2049), (6912, 2560), (8256, 33), (12288, 1),
+                   (28672, 40), (65536, 5), (3200, 3203)]
+
+
+@pytest.mark.parametrize("K,N", ONE_TOKEN_CASES)
+def test_one_token_gemv_parity(K, N):
+    """Path 4 against the oracle: int32 sums bit-exact, outputs within 1e-6,
+    and the automatic choice gives the same bits. The token is the extreme
+    +127 row, then one with the full int8 range (-128 included), so the
+    masked-field sums and the activation-sum correction run at their largest."""
+    q, xq, xs, g = _product_case(1, K, N, 57)
+    rng = np.random.default_rng(K + N)
+    tokens = [np.full((1, K), 127, np.int8), rng.integers(-128, 128, (1, K)).astype(np.int8),
+              xq]
+    args_w = (dev_packed(oracle.pack(q)), dev_f32([g]))
+    for t in tokens:
+        y_ref, acc_ref = oracle.bitlinear(t, xs, q, g)
+        xt = torch.from_numpy(t).to(DEV)
+        y, acc = bl.bitlinear(xt, dev_f32(xs), *args_w, return_acc=True, path=4)
+        assert np.array_equal(acc.cpu().numpy(), acc_ref)
+        assert_y_close(y.cpu().numpy(), y_ref, "one-token gemv")
+        y0 = bl.bitlinear(xt, dev_f32(xs), *args_w)
+        assert torch.equal(y0.view(torch.int32), y.view(torch.int32))
+
+
+def test_one_token_gemv_rejects_other_shapes():
+    q, xq, xs, g = _product_case(2, 128, 8, 58)
+    args = (dev_packed(oracle.pack(q)), dev_f32([g]))
+    with pytest.raises(bl.BitLinearError):
+        bl.bitlinear(torch.from_numpy(xq).to(DEV), dev_f32(xs), *args, path=4)
+    q, xq, xs, g = _product_case(1, 65600, 2, 58)
+    with pytest.raises(bl.BitLinearError):
+        bl.bitlinear(torch.from_numpy(xq).to(DEV), dev_f32(xs), dev_packed(oracle.pack(q)),
+                     dev_f32([g]), path=4)
+
+
 @pytest.mark.parametrize("M,K,N", GEMM_CASES)
 def test_gemm_parity(M, K, N):
     q, xq, xs, g = _product_case(M, K, N, 54)
@@ -357,7 +399,7 @@ def _random_shapes(n, seed, budget=1.5e8):
 @pytest.mark.parametrize("M,K,N", _random_shapes(24, 1234))
 def test_random_shapes_every_path(M, K, N):
     """Seeded random shapes through every product path that applies
-    (automatic, GEMV, GEMM, wide GEMV): int32 sums equal to the oracle's,
+    (automatic, GEMV, GEMM, wide GEMV, one-token GEMV): int32 sums equal to the oracle's,
     outputs within 1e-6."""
     q, xq, xs, g = _product_case(M, K, N, 70 + M + K + N)
     y_ref, acc_ref = oracle.bitlinear(xq, xs, q, g)
@@ -365,6 +407,8 @@ def test_random_shapes_every_path(M, K, N):
     paths = [0, 2]
     if M <= 16 and M * K <= 128 * 1024:
         paths.append(1)
+    if M == 1 and K <= 65536:
+        paths.append(4)
     if M <= 64:
         paths.append(3)
     for path in paths:
@@ -393,6 +437,9 @@ def test_determinism_repeated_calls():
     assert all(torch.equal(outs[0], o) for o in outs[1:])
     outs = [bl.bitlinear(args[0][:8].contiguous(), args[1][:8].contiguous(), args[2], args[3],
                          path=1).view(torch.int32).clone() for _ in range(3)]
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+    outs = [bl.bitlinear(args[0][:1].contiguous(), args[1][:1].contiguous(), args[2], args[3],
+                         path=4).view(torch.int32).clone() for _ in range(3)]
     assert all(torch.equal(outs[0], o) for o in outs[1:])
 
 
