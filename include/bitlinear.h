@@ -293,6 +293,25 @@ int bl_ffn_step(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate,
                 const uint16_t* subln_gain, float subln_eps, float* y, void* workspace,
                 size_t workspace_bytes, void* stream);
 
+/* bl_ffn_step for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments without the workspace, the same launches and the same bits.
+ * Its workspace is a fixed 8 MiB array in device memory that the library
+ * holds on every device it runs on until the process ends; the call
+ * allocates nothing. Shapes whose bl_ffn_relu2_workspace_bytes exceed 8 MiB
+ * are BL_ERR_INVALID_ARG (the 8192 -> 28672 -> 8192 FFN fits up to 25
+ * tokens, the 2560 -> 6912 one up to 106). All calls on one device share the
+ * array: calls that overlap in time on the same device (on different
+ * streams, or from different host threads without ordering) race on it and
+ * give undefined results; calls ordered on one stream are safe. The first
+ * call on a device resolves the array's address there (hipGetSymbolAddress);
+ * a failure there is BL_ERR_HIP. */
+int bl_ffn_step_noalloc(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate,
+                        const float* gamma_gate, const uint32_t* W_up, const float* gamma_up,
+                        int64_t N_ff, const uint32_t* W_down, const float* gamma_down,
+                        int glu_kind, const uint16_t* subln_gain, float subln_eps, float* y,
+                        void* stream);
+
 /* ---- Other weight formats (decode) ----------------------------------------
  * Two storage formats besides the 2-bit one, each with its own decode
  * product for M <= 16 tokens (the weight-streaming GEMV; the prefill GEMM

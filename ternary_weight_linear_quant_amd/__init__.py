@@ -51,6 +51,8 @@ _SIGNATURES = {
                            ctypes.c_int),
     "bl_ffn_step": ([_P, _I, _I, _P, _P, _P, _P, _I, _P, _P, ctypes.c_int, _P, _F, _P, _P, _S,
                      _P], ctypes.c_int),
+    "bl_ffn_step_noalloc": ([_P, _I, _I, _P, _P, _P, _P, _I, _P, _P, ctypes.c_int, _P, _F, _P,
+                             _P], ctypes.c_int),
     "bl_packed_bytes_binary": ([_I, _I], _S),
     "bl_packed_bytes_base3": ([_I, _I], _S),
     "bl_quantize_weights_binary": ([_P, _I, _I, _P, _P, _P, _S, _P], ctypes.c_int),
@@ -373,6 +375,37 @@ def ffn_step(x, W_gate, gamma_gate, W_up, gamma_up, W_down, gamma_down, kind="re
                              float(subln_eps), _dev(y, torch.float32, "y"),
                              _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
                              _stream_ptr(x)), "bl_ffn_step")
+    return y
+
+
+def ffn_step_noalloc(x, W_gate, gamma_gate, W_up, gamma_up, W_down, gamma_down, kind="relu2",
+                     subln_gain=None, subln_eps: float = 1e-5, out=None):
+    """ffn_step without a workspace: the library's fixed per-device scratch
+    (up to 8 MiB of FFN workspace). Calls bl_ffn_step_noalloc."""
+    torch = _torch()
+    if x.dtype == torch.int16:
+        x = x.view(torch.bfloat16)
+    M, K = x.shape
+    N_ff = W_gate.shape[0]
+    if W_gate.shape[1] * 16 != K or W_up.shape != W_gate.shape or \
+            W_down.shape[0] != K or W_down.shape[1] * 16 != N_ff:
+        raise BitLinearError("FFN weight shapes do not match")
+    y = torch.empty((M, K), dtype=torch.float32, device=x.device) if out is None else out
+    gp = None
+    if subln_gain is not None:
+        if subln_gain.dtype == torch.int16:
+            subln_gain = subln_gain.view(torch.bfloat16)
+        gp = _dev(subln_gain, torch.bfloat16, "subln_gain")
+    _check(lib().bl_ffn_step_noalloc(_dev(x, torch.bfloat16, "x"), M, K,
+                                     _dev(W_gate, torch.int32, "W_gate"),
+                                     _dev(gamma_gate, torch.float32, "gamma_gate"),
+                                     _dev(W_up, torch.int32, "W_up"),
+                                     _dev(gamma_up, torch.float32, "gamma_up"), N_ff,
+                                     _dev(W_down, torch.int32, "W_down"),
+                                     _dev(gamma_down, torch.float32, "gamma_down"),
+                                     _glu_kind(kind), gp, float(subln_eps),
+                                     _dev(y, torch.float32, "y"), _stream_ptr(x)),
+           "bl_ffn_step_noalloc")
     return y
 
 

@@ -318,6 +318,68 @@ int bl_ffn_step(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate,
                     glu_kind, subln_gain, subln_eps, y, workspace, workspace_bytes, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Fixed scratch of bl_ffn_step_noalloc. Every device that runs the library
+// holds its own copy of this array until the process ends. Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in):
+// it uses the device address that hipGetSymbolAddress returns on each device.
+constexpr size_t kNoAllocScratchBytes = size_t{8} << 20;
+__device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxCachedDevices = 64;
+std::atomic<uintptr_t> g_scratch_addr[kMaxCachedDevices];  // 0 until resolved
+
+// The current device's copy of `scratch`, resolved on the first call on that
+// device (with the device current) and kept; devices past the cache are
+// resolved on every call. Two threads racing on a first call store the same
+// address.
+int current_scratch(uint8_t** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    const bool cached = dev >= 0 && dev < kMaxCachedDevices;
+    uintptr_t addr = cached ? g_scratch_addr[dev].load(std::memory_order_acquire) : 0;
+    if (addr == 0) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e);
+        if (ptr == nullptr) return hip_status(hipErrorInvalidSymbol);
+        addr = reinterpret_cast<uintptr_t>(ptr);
+        if (cached) g_scratch_addr[dev].store(addr, std::memory_order_release);
+    }
+    *out = reinterpret_cast<uint8_t*>(addr);
+    return BL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bl_ffn_step_noalloc(const uint16_t* x, int64_t M, int64_t K, const uint32_t* W_gate,
+                        const float* gamma_gate, const uint32_t* W_up, const float* gamma_up,
+                        int64_t N_ff, const uint32_t* W_down, const float* gamma_down,
+                        int glu_kind, const uint16_t* subln_gain, float subln_eps, float* y,
+                        void* stream) {
+    // Every argument check of ffn_step, before the device is touched.
+    if (!glu_kind_ok(glu_kind)) return BL_ERR_INVALID_ARG;
+    if (!ffn_shapes_ok(M, K, N_ff)) return BL_ERR_INVALID_ARG;
+    if (ffn_layout(M, K, N_ff).total > kNoAllocScratchBytes) return BL_ERR_INVALID_ARG;
+    if (!x || !W_gate || !gamma_gate || !W_up || !gamma_up || !W_down || !gamma_down || !y)
+        return BL_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(W_down) ||
+        !aligned16(y))
+        return BL_ERR_INVALID_ARG;
+    if (subln_gain && (!aligned16(subln_gain) || !(subln_eps > 0.0f))) return BL_ERR_INVALID_ARG;
+    if (int s = device_status()) return s;
+    uint8_t* ws = nullptr;
+    if (int s = current_scratch(&ws)) return s;
+    return ffn_step(x, M, K, W_gate, gamma_gate, W_up, gamma_up, N_ff, W_down, gamma_down,
+                    glu_kind, subln_gain, subln_eps, y, ws, kNoAllocScratchBytes, stream);
+}
+
 int bl_relu2_glu_quant(const float* gate, const float* up, int64_t M, int64_t K, int8_t* h_q,
                        float* h_scale, void* stream) {
     return glu_quant(gate, up, M, K, BL_GLU_RELU2, nullptr, 0.0f, h_q, h_scale, stream);

@@ -141,6 +141,23 @@ def test_invalid_arguments_rejected_before_launch(L):
                          None) == E
     assert L.bl_ffn_step(A, 4, 2560, A, A, A, A, 6912, A, A, 1, A, 0.0, A, WS, need,
                          None) == E
+    # no-allocation FFN step: null pointers, bad shapes, workspace past the 8 MiB scratch
+    assert L.bl_ffn_step_noalloc(None, 4, 2560, A, A, A, A, 6912, A, A, 0, None, 0.0, A,
+                                 None) == E
+    assert L.bl_ffn_step_noalloc(A, 4, 2560, A, A, A, A, 6912, A, A, 0, None, 0.0, None,
+                                 None) == E
+    assert L.bl_ffn_step_noalloc(A, 4, 2560, A, A, A, A, 6900, A, A, 0, None, 0.0, A,
+                                 None) == E
+    assert L.bl_ffn_step_noalloc(A, 4, 2560, A, A, A, A, 6912, A, A, 3, None, 0.0, A,
+                                 None) == E
+    assert L.bl_ffn_step_noalloc(A, 26, 8192, A, A, A, A, 28672, A, A, 0, None, 0.0, A,
+                                 None) == E
+    assert L.bl_ffn_step_noalloc(A, 107, 2560, A, A, A, A, 6912, A, A, 0, None, 0.0, A,
+                                 None) == E
+    assert L.bl_ffn_step_noalloc(MIS, 4, 2560, A, A, A, A, 6912, A, A, 0, None, 0.0, A,
+                                 None) == E
+    assert L.bl_ffn_step_noalloc(A, 4, 2560, A, A, A, A, 6912, A, A, 1, A, -1.0, A,
+                                 None) == E
     # pair
     assert L.bl_bitlinear_pair(A, A, 1, 64, A, A, 16, A, None, A, 16, A, None) == E
     assert L.bl_bitlinear_pair(A, A, 1, 64, A, A, 16, A, A, A, 0, A, None) == E
@@ -227,6 +244,10 @@ def test_no_device_status(L):
     assert L.bl_glu_quant(A, A, 1, 64, 1, None, 0.0, A, A, None) == D
     assert L.bl_ffn_step(A, 1, 256, A, A, A, A, 1024, A, A, 1, None, 0.0, A, P(0x200000),
                          need, None) == D
+    assert L.bl_ffn_step_noalloc(A, 25, 8192, A, A, A, A, 28672, A, A, 0, None, 0.0, A,
+                                 None) == D
+    assert L.bl_ffn_step_noalloc(A, 106, 2560, A, A, A, A, 6912, A, A, 0, None, 0.0, A,
+                                 None) == D
 
 
 def test_binding_fails_loudly_without_gpu():
