@@ -74,6 +74,11 @@ int bl_last_hip_error(void);
 /* Library version string (static). */
 const char* bl_version(void);
 
+/* SHA-256 (hex) of the sources and compile flags this library was built from
+ * (static string; "unknown" when built without it). The Python binding
+ * refuses a library whose digest differs from its source tree's. */
+const char* bl_source_sha256(void);
+
 /* Bytes of the packed weight buffer: N*K/4 (2 bits per weight); 0 if the shape
  * is invalid. Host-only, no device needed. */
 size_t bl_packed_bytes(int64_t N, int64_t K);
@@ -176,11 +181,12 @@ int bl_relu2_glu(const float* gate, const float* up, int64_t count,
 
 /* Gating kinds of a gated FFN, h = bf16_rne(act(gate) * up) in fp32:
  *   BL_GLU_RELU2   act(g) = relu(g)^2 (the 2B4T FFN, as bl_relu2_glu);
- *   BL_GLU_SWIGLU  act(g) = SiLU(g) = g / (1 + exp(-g)), exp from the device
- *                  math library (within a few fp32 ulp of the exact SiLU, so
- *                  h may differ from a correctly rounded evaluation by one
- *                  bf16 step at rounding ties); a gate below about -88 gives
- *                  -0. Source: comrad404.com page above, section «Метод: как
+ *   BL_GLU_SWIGLU  act(g) = SiLU(g) = g / (1 + exp(-g)) evaluated in fp64
+ *                  (exp from the device math library, fp64 division) and
+ *                  rounded once to fp32: the correctly rounded SiLU except
+ *                  where the fp64 value lies within about 1e-16 relative of an
+ *                  fp32 rounding boundary; a gate below about -709 gives -0.
+ *                  Source: comrad404.com page above, section «Метод: как
  *                  устроен BitNet b1.58»: the b1.58 variant keeps the LLaMA
  *                  stack's SwiGLU. */
 enum { BL_GLU_RELU2 = 0, BL_GLU_SWIGLU = 1 };

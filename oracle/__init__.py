@@ -11,6 +11,7 @@ passage of the pages it follows, is documented in ``oracle.h``.
 from __future__ import annotations
 
 import ctypes
+import hashlib
 import os
 import subprocess
 
@@ -19,8 +20,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
-CFLAGS = ["-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math",
+CFLAGS = ["-std=c11", "-O3", "-ffp-contract=off", "-fno-fast-math",
           "-fPIC", "-shared", "-Wall", "-Wextra"]
+_HDR = os.path.join(_HERE, "oracle.h")
 
 WEIGHT_EPS = 1e-5   # s = gamma + eps before rounding the weights
 RMS_EPS = 1e-5      # epsilon inside the RMSNorm square root
@@ -28,24 +30,51 @@ RMS_EPS = 1e-5      # epsilon inside the RMSNorm square root
 _lib = None
 
 
+def source_sha256() -> str:
+    """SHA-256 over oracle.c, oracle.h and the compile flags; embedded in
+    liboracle.so so that a stale build is detected by content, not mtime."""
+    h = hashlib.sha256()
+    for f in (_SRC, _HDR):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+        h.update(b"\0")
+    h.update(" ".join(CFLAGS).encode())
+    return h.hexdigest()
+
+
 def build(force: bool = True) -> str:
-    """Compile oracle.c into liboracle.so with gcc; returns the path."""
-    if force or not os.path.exists(_LIB_PATH) or \
-            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+    """Compile oracle.c into liboracle.so with gcc; returns the path. Without
+    force, only when the library is missing or was built from other sources."""
+    if force or _built_sha256() != source_sha256():
         tmp = _LIB_PATH + ".tmp"
-        subprocess.run(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+        subprocess.run(["gcc", *CFLAGS, f'-DORACLE_SOURCE_SHA256="{source_sha256()}"', _SRC,
+                        "-o", tmp, "-lm"], check=True)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
+
+
+def _built_sha256():
+    """Digest embedded in the library file on disk (None if absent), read by
+    name from the file's bytes, so no stale copy is loaded to ask it."""
+    if not os.path.exists(_LIB_PATH):
+        return None
+    with open(_LIB_PATH, "rb") as fh:
+        data = fh.read()
+    i = data.find(b"oracle-source-sha256:")
+    if i < 0:
+        return None
+    return data[i + 21:i + 21 + 64].decode("ascii", "replace")
 
 
 def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH) or \
-            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-        build(force=True)
+    build(force=False)
     lib = ctypes.CDLL(_LIB_PATH)
+    got = ctypes.c_char_p.in_dll(lib, "oracle_source_sha256").value.decode()
+    if got != "oracle-source-sha256:" + source_sha256():
+        raise RuntimeError(f"{_LIB_PATH} does not match oracle.c (digest {got[21:37]})")
     P = ctypes.c_void_p
     I = ctypes.c_int64
     F = ctypes.c_float

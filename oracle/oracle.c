@@ -2,15 +2,23 @@
  * CPU oracle for the BitNet b1.58 BitLinear forward pass.
  * TEST INFRASTRUCTURE ONLY -- see oracle.h for the sources and the readings.
  *
- * Plain single-threaded C11, built with -O2 -ffp-contract=off and without
+ * Plain single-threaded C11, built with -O3 -ffp-contract=off and without
  * -ffast-math, so every fp32 operation below is one IEEE-754 round-to-nearest
- * operation in the order written. nearbyintf runs under the default
- * FE_TONEAREST mode, i.e. ties go to the even integer.
+ * operation in the order written (no contraction; without -ffast-math the
+ * compiler may not reassociate floating-point sums). nearbyintf runs under
+ * the default FE_TONEAREST mode, i.e. ties go to the even integer.
  */
 #include "oracle.h"
 
 #include <math.h>
 #include <string.h>
+
+#ifndef ORACLE_SOURCE_SHA256
+#define ORACLE_SOURCE_SHA256 "unknown"
+#endif
+/* Digest of the sources and flags this copy was built from, behind a marker
+ * that a loader can find in the file's bytes. */
+const char* oracle_source_sha256 = "oracle-source-sha256:" ORACLE_SOURCE_SHA256;
 
 static float bf16_bits_to_float(uint16_t b) {
     uint32_t u = (uint32_t)b << 16;

@@ -66,6 +66,10 @@
 extern "C" {
 #endif
 
+/* "oracle-source-sha256:" followed by the SHA-256 (hex) of oracle.c, oracle.h
+ * and the compile flags this copy was built from. */
+extern const char* oracle_source_sha256;
+
 /* Per-row sums R[n] = sum_k |W[n][k]| in fp64, k increasing. W fp32 [N][K]. */
 void oracle_absmean_rowsums(const float* W, int64_t N, int64_t K, double* R);
 

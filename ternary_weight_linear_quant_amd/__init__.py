@@ -32,6 +32,7 @@ _SIGNATURES = {
     "bl_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "bl_last_hip_error": ([], ctypes.c_int),
     "bl_version": ([], ctypes.c_char_p),
+    "bl_source_sha256": ([], ctypes.c_char_p),
     "bl_packed_bytes": ([_I, _I], _S),
     "bl_quantize_weights_workspace_bytes": ([_I, _I], _S),
     "bl_quantize_weights": ([_P, _I, _I, _P, _P, _P, _S, _P], ctypes.c_int),
@@ -92,6 +93,13 @@ def lib():
             fn = getattr(handle, name)
             fn.argtypes = args
             fn.restype = res
+        from . import build as _build
+        built, tree = handle.bl_source_sha256().decode(), _build.source_sha256()
+        if built != tree:
+            raise BitLinearError(
+                f"{_LIB_PATH} was built from other sources (digest {built[:16]}, tree "
+                f"{tree[:16]}): rebuild it with `python -c 'import __graft_entry__ as g; "
+                "g.build()'`")
         _lib = handle
     return _lib
 

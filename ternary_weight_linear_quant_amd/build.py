@@ -2,6 +2,7 @@
 from __future__ import annotations
 
 import glob
+import hashlib
 import os
 import subprocess
 import sys
@@ -27,13 +28,31 @@ HIP_FLAGS = [
 ]
 
 
+HEADER = os.path.join(os.path.dirname(PKG), "include", "bitlinear.h")
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+def source_sha256() -> str:
+    """SHA-256 over the library's sources (kernels, internal headers, the C
+    ABI header) and the compile flags; embedded in the library at build time
+    so that a loader can tell a stale build from a current one."""
+    h = hashlib.sha256()
+    files = sources() + sorted(glob.glob(os.path.join(CSRC, "*.hpp"))) + [HEADER]
+    for f in files:
+        h.update(os.path.basename(f).encode() + b"\0")
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+        h.update(b"\0")
+    h.update(" ".join(HIP_FLAGS).encode())
+    return h.hexdigest()
+
+
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *HIP_FLAGS, *sources(), "-o", tmp]
+    cmd = [HIPCC, *HIP_FLAGS, f'-DBL_SOURCE_SHA256="{source_sha256()}"', *sources(), "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

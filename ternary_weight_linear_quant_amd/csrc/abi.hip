@@ -92,6 +92,11 @@ int bl_last_hip_error(void) { return g_last_hip_error; }
 
 const char* bl_version(void) { return "bitlinear-gfx950 0.1.0"; }
 
+#ifndef BL_SOURCE_SHA256
+#define BL_SOURCE_SHA256 "unknown"
+#endif
+const char* bl_source_sha256(void) { return BL_SOURCE_SHA256; }
+
 size_t bl_packed_bytes(int64_t N, int64_t K) {
     if (!shape_ok(N, K)) return 0;
     return (size_t)(N * (K / 4));

@@ -58,10 +58,12 @@ __device__ __forceinline__ uint32_t pack_codes4(float t0, float t1, float t2, fl
     return lo | hi;
 }
 
-// Gating of a gated FFN: h = bf16_rne(act(gate) * up), fp32 arithmetic.
-// kGluRelu2: act(g) = relu(g)^2 (the 2B4T FFN). kGluSwiglu: act(g) = SiLU(g)
-// = g / (1 + exp(-g)) (the LLaMA-style SwiGLU), with the library exp; a gate
-// below about -88 gives exp(-g) = inf and SiLU = -0.
+// Gating of a gated FFN: h = bf16_rne(act(gate) * up), the product in fp32.
+// kGluRelu2: act(g) = relu(g)^2 in fp32 (the 2B4T FFN). kGluSwiglu: act(g) =
+// SiLU(g) = g / (1 + exp(-g)) (the LLaMA-style SwiGLU) evaluated in fp64 and
+// rounded once to fp32, so it is the correctly rounded SiLU unless the fp64
+// value lies within about 1e-16 of an fp32 rounding boundary; a gate below
+// about -709 gives exp(-g) = inf and SiLU = -0.
 constexpr int kGluRelu2 = 0, kGluSwiglu = 1;
 
 template <int KIND>
@@ -70,7 +72,8 @@ __device__ __forceinline__ uint32_t glu_bits(float g, float u) {
         const float r = g > 0.0f ? g : 0.0f;
         return f32_to_bf16_rne((r * r) * u);
     } else {
-        const float s = g / (1.0f + expf(-g));
+        const double gd = (double)g;
+        const float s = (float)(gd / (1.0 + exp(-gd)));
         return f32_to_bf16_rne(s * u);
     }
 }

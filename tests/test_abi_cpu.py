@@ -256,3 +256,24 @@ def test_binding_fails_loudly_without_gpu():
         pytest.skip("a GPU is visible")
     with pytest.raises(bl.BitLinearError):
         bl.quantize_weights(torch.zeros(16, 64))
+
+
+def test_binding_refuses_a_library_built_from_other_sources(monkeypatch):
+    """bl.lib() compares the digest embedded at build time with the source
+    tree's; a mismatch (a stale build) raises instead of loading."""
+    import ternary_weight_linear_quant_amd as blm
+    from ternary_weight_linear_quant_amd import build as blbuild
+    built = blm.lib().bl_source_sha256().decode()
+    assert built == blbuild.source_sha256()
+    monkeypatch.setattr(blm, "_lib", None)
+    monkeypatch.setattr(blbuild, "source_sha256", lambda: "0" * 64)
+    with pytest.raises(blm.BitLinearError, match="built from other sources"):
+        blm.lib()
+
+
+def test_oracle_library_carries_its_source_digest():
+    """The oracle's library on disk carries the digest of oracle.c, oracle.h
+    and its flags (the loader rebuilds on any difference, not by mtime)."""
+    import oracle
+    oracle._load()
+    assert oracle._built_sha256() == oracle.source_sha256()
