@@ -57,9 +57,9 @@ PHASES = {
                     "bl_ffn_relu2 at M=1 on 2560->6912->2560 weights, 40 rotated layers",
                     2 * LAYERS_2B4T,
                     "k_ffn_gemv launch (gate/up+gating, or act-quant+down)"),
-    "gemv_70b_m1": (["gemv.hip", "common.hpp"],
+    "gemv_70b_m1": (["gemv1.hip", "common.hpp"],
                     "bl_bitlinear at M=1 on 8192->28672 and 28672->8192, 5 rotated copies",
-                    2 * COPIES_70B, "k_gemv launch"),
+                    2 * COPIES_70B, "one-token GEMV launch (k_gemv1_cached / k_gemv1_stream)"),
     "gemv_70b_m1_base3": (["gemv.hip", "common.hpp"],
                           "bl_bitlinear_base3 at M=1 on the 70B shapes, 5 rotated copies",
                           2 * COPIES_70B, "k_gemv launch (five ternary weights per byte)"),
@@ -71,13 +71,13 @@ PHASES = {
                        2 * COPIES_70B,
                        "bl_bitlinear call (up: k_gemm with four K groups; down: the same with "
                        "split K between k_splitk_zero and k_splitk_finalize)"),
-    "gemv_2560_m1": (["gemv.hip", "common.hpp"],
+    "gemv_2560_m1": (["gemv1.hip", "common.hpp"],
                      "bl_bitlinear at M=1 on 2560->2560, 400 rotated copies",
-                     COPIES_2560, "k_gemv launch"),
-    "gemv_3b_m1": (["gemv.hip", "common.hpp"],
+                     COPIES_2560, "one-token GEMV launch (k_gemv1_cached)"),
+    "gemv_3b_m1": (["gemv1.hip", "gemv.hip", "common.hpp"],
                    "bl_bitlinear at M=1 on the 3B block (q, k, v, o 3200->3200; gate, up "
                    "3200->8640; down 8640->3200), 20 rotated layers",
-                   7 * LAYERS_3B, "bl_bitlinear call (k_gemv)"),
+                   7 * LAYERS_3B, "bl_bitlinear call (k_gemv1_cached; k_gemv on 8640->3200)"),
     "gemm_3b_m512": (["gemm.hip", "gemv_wide.hip", "common.hpp"],
                      "bl_bitlinear at M=512 on the 3B block's seven projections", 7,
                      "bl_bitlinear call"),
@@ -497,7 +497,7 @@ def main():
     t = sub.add_parser("trace")
     t.add_argument("prof_dir")
     t.add_argument("--cmd", dest="trace_cmd", default="rocprofv3 --kernel-trace --stats -d <PROF_DIR> -o bench "
-                   "--output-format csv -- python3 bench.py --steps 3 --warmup 1 --cpu-seconds 0")
+                   "--output-format csv -- python3 bench.py --cpu-seconds 0")
     t.add_argument("--desc", default="bench.py, all legs")
     s = sub.add_parser("summarize")
     s.add_argument("fetch_dir")
