@@ -97,6 +97,7 @@ def _load():
         "oracle_unpack_base3": ([P, I, I, I, P], None),
         "oracle_pack_ste_t": ([P, I, I, I, P], None),
         "oracle_ste_dx": ([P, I, I, P, I, F, P], None),
+        "oracle_ste_dw": ([P, I, I, P, P, I, P], None),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -326,3 +327,18 @@ def ste_dx(dy_bits: np.ndarray, q: np.ndarray, gamma) -> np.ndarray:
     dx = np.empty((M, K), np.float32)
     _load().oracle_ste_dx(_p(dy_bits), M, N, _p(q), K, float(np.float32(gamma)), _p(dx))
     return dx
+
+
+def ste_dw(dy_bits: np.ndarray, x_q: np.ndarray, x_scale: np.ndarray) -> np.ndarray:
+    """dW fp32 [N][K] = sum_m dy[m][n] * x_q[m][k] * x_scale[m] for bf16 dy
+    [M][N] (raw bits), int8 x_q [M][K] and fp32 x_scale [M]."""
+    dy_bits = _c(dy_bits, np.uint16)
+    x_q = _c(x_q, np.int8)
+    x_scale = _c(x_scale, np.float32)
+    M, N = dy_bits.shape
+    K = x_q.shape[1]
+    if x_q.shape[0] != M or x_scale.shape != (M,):
+        raise ValueError("shape mismatch")
+    dW = np.empty((N, K), np.float32)
+    _load().oracle_ste_dw(_p(dy_bits), M, N, _p(x_q), _p(x_scale), K, _p(dW))
+    return dW

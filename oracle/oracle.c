@@ -202,6 +202,27 @@ void oracle_ste_dx(const uint16_t* dy, int64_t M, int64_t N, const int8_t* q, in
         }
 }
 
+/* Straight-through estimator, gradient with respect to the latent weights
+ * [P5b]: the forward multiplies the dequantised activations x~ = x_q * s_x by
+ * the weights, and the backward treats the weights' rounding as the
+ * identity, so dW[n][k] = sum_m dy[m][n] * x_q[m][k] * s_x[m]. Each product
+ * is exact in fp64 (8 + 24 + 8 significant bits); the sum is taken in fp64
+ * with m increasing and rounded once to fp32. */
+void oracle_ste_dw(const uint16_t* dy, int64_t M, int64_t N, const int8_t* x_q,
+                   const float* x_scale, int64_t K, float* dW) {
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            double s = 0.0;
+            for (int64_t m = 0; m < M; ++m) {
+                int8_t x = x_q[m * K + k];
+                if (x)
+                    s += (double)bf16_bits_to_float(dy[m * N + n]) * (double)x_scale[m] *
+                         (double)x;
+            }
+            dW[n * K + k] = (float)s;
+        }
+}
+
 /* 8-bit activations [P1], per token by absmax into [-127, 127]. */
 void oracle_act_quant(const uint16_t* x, int64_t M, int64_t K,
                       const uint16_t* gain, float rms_eps,

@@ -55,7 +55,9 @@
  *     significant digit first (c = q + 1), rows padded to 16 bytes with 121.
  *   - straight-through backward: dx = gamma * dy . q with dy in bf16, the
  *     sum exact in fp64, rounded once to fp32; the transposed codes are
- *     stored four per byte along n, rows padded to 16 bytes with 0x55.
+ *     stored four per byte along n, rows padded to 16 bytes with 0x55. The
+ *     latent weights' gradient is dW = dy^T . x~ with x~ = x_q * s_x, the
+ *     dequantised activations the forward multiplied (fp64, one rounding).
  */
 #ifndef BITLINEAR_ORACLE_H
 #define BITLINEAR_ORACLE_H
@@ -133,6 +135,12 @@ void oracle_pack_ste_t(const int8_t* q, int64_t N, int64_t K, int64_t row_bytes,
 /* dx = gamma * dy . q, dy bf16 [M][N], q [N][K], fp64 sum, one rounding. [P5b] */
 void oracle_ste_dx(const uint16_t* dy, int64_t M, int64_t N, const int8_t* q, int64_t K,
                    float gamma, float* dx);
+/* dW[n][k] = sum_m dy[m][n] * x_q[m][k] * x_scale[m]: the straight-through
+ * gradient of the latent weights, dy bf16 [M][N], x_q int8 [M][K], x_scale
+ * fp32 [M], dW fp32 [N][K]; exact fp64 products, fp64 sum over m, one
+ * rounding. [P5b] */
+void oracle_ste_dw(const uint16_t* dy, int64_t M, int64_t N, const int8_t* x_q,
+                   const float* x_scale, int64_t K, float* dW);
 
 #ifdef __cplusplus
 }

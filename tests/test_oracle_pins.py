@@ -717,3 +717,87 @@ def test_ste_dx_sum_is_exact_before_rounding():
     dy = _bf16_bits(np.array([[2.0 ** 30, 1.0, -(2.0 ** 30)]], np.float32))
     q = np.ones((3, 1), np.int8)
     assert oracle.ste_dx(dy, q, np.float32(0.25))[0, 0] == np.float32(0.25)
+
+
+# The gradient of the latent weights: with the weights' rounding treated as
+# the identity, y = x~ . W^T gives dW = dy^T . x~, x~ = x_q * s_x the
+# dequantised activations the forward multiplied.
+
+def test_ste_dw_hand_values():
+    # dy = [[1], [2]], x_q = [[1, -2], [3, 4]], s_x = [0.5, 0.25]:
+    # x~ = [[0.5, -1], [0.75, 1]], dW = 1 * [0.5, -1] + 2 * [0.75, 1] = [2, 1].
+    dy = _bf16_bits(np.array([[1.0], [2.0]], np.float32))
+    xq = np.array([[1, -2], [3, 4]], np.int8)
+    sx = np.array([0.5, 0.25], np.float32)
+    assert oracle.ste_dw(dy, xq, sx).tolist() == [[2.0, 1.0]]
+
+
+def test_ste_dw_one_hot_rows_and_columns():
+    rng = np.random.default_rng(85)
+    M, N, K = 6, 5, 9
+    xq = rng.integers(-128, 128, size=(M, K), dtype=np.int8)
+    sx = (rng.random(M) * 0.1 + 0.01).astype(np.float32)
+    for m0, n0 in [(0, 0), (3, 4), (5, 2)]:
+        d = np.zeros((M, N), np.float32)
+        d[m0, n0] = 1.0
+        dW = oracle.ste_dw(_bf16_bits(d), xq, sx)
+        want = (xq[m0].astype(np.float64) * np.float64(sx[m0])).astype(np.float32)
+        assert np.array_equal(dW[n0], want)
+        assert (np.delete(dW, n0, axis=0) == 0).all()
+
+
+def test_ste_dw_is_the_adjoint_of_the_forward():
+    # <dW, gamma q> = <dy, y> with y the oracle's own forward on ternary
+    # weights gamma * q: pins which operand is transposed and where the
+    # per-token scale enters, against the integer product and the epilogue.
+    rng = np.random.default_rng(86)
+    M, N, K = 7, 33, 21
+    dy = _bf16_bits(rng.standard_normal((M, N)))
+    xq = rng.integers(-127, 128, size=(M, K), dtype=np.int8)
+    sx = (rng.random(M) * 0.05 + 0.001).astype(np.float32)
+    q = rng.integers(-1, 2, size=(N, K), dtype=np.int8)
+    g = np.float32(0.0183)
+    dW = oracle.ste_dw(dy, xq, sx).astype(np.float64)
+    lhs = float((dW * (np.float64(g) * q)).sum())
+    y, _ = oracle.bitlinear(xq, sx, q, g)
+    dyf = wl.bf16_bits_to_f32(dy).astype(np.float64)
+    rhs = float((dyf * y.astype(np.float64)).sum())
+    # each dW and each y element carries one fp32 rounding
+    bound = 2.0 ** -23 * (float(np.abs(dW * (np.float64(g) * q)).sum()) +
+                          float(np.abs(dyf * y.astype(np.float64)).sum()))
+    assert abs(lhs - rhs) <= bound
+
+
+def test_ste_dw_brute_force_fractions():
+    from fractions import Fraction
+    rng = np.random.default_rng(87)
+    M, N, K = 11, 3, 4
+    dy = _bf16_bits(rng.standard_normal((M, N)) * 2)
+    xq = rng.integers(-128, 128, size=(M, K), dtype=np.int8)
+    sx = (rng.random(M) * 0.3).astype(np.float32)
+    dW = oracle.ste_dw(dy, xq, sx)
+    dyf = wl.bf16_bits_to_f32(dy)
+    for n in range(N):
+        for k in range(K):
+            s = sum(Fraction(float(dyf[m, n])) * Fraction(float(sx[m])) * int(xq[m, k])
+                    for m in range(M))
+            assert dW[n, k] == np.float32(float(s))
+
+
+def test_ste_dw_linear_in_dy_and_zero_tokens():
+    rng = np.random.default_rng(88)
+    M, N, K = 8, 6, 10
+    xq = rng.integers(-127, 128, size=(M, K), dtype=np.int8)
+    sx = (rng.random(M) * 0.1).astype(np.float32)
+    d = rng.standard_normal((M, N)).astype(np.float32)
+    a = oracle.ste_dw(_bf16_bits(d), xq, sx)
+    b = oracle.ste_dw(_bf16_bits(-d), xq, sx)
+    assert np.array_equal(a, -b)
+    two = oracle.ste_dw(_bf16_bits(2 * d), xq, sx)       # powers of two scale exactly
+    assert np.array_equal(two, 2 * a)
+    xz = xq.copy()
+    xz[3] = 0                                            # a token with all-zero codes
+    d3 = d.copy()
+    d3[3] *= 7
+    assert np.array_equal(oracle.ste_dw(_bf16_bits(d3), xz, sx),
+                          oracle.ste_dw(_bf16_bits(d), xz, sx))
