@@ -230,6 +230,45 @@ def other_workloads(args, bl, wl, np, torch, dev, bf16_dev, capture, time_graph,
         per[name]["vendor_bf16_gemm_us"] = round(us, 2)
         v_us += us
         del wb
+    # dW = dy^T . (x_q * x_scale) on the same shapes: two transposing prep
+    # launches and the bf16 GEMM per call.
+    dw_legs = []
+    for i, (name, K, N) in enumerate(pprojs):
+        dy = legs[i][5]
+        xq, xs = bl.quantize_acts(bf16_dev(wl.activations(PREFILL_WORKLOAD, i, Mp, K)))
+        dw_legs.append((name, K, N, dy, xq, xs, bl.ste_dw_workspace(Mp, N, K, dev),
+                        torch.empty((N, K), dtype=torch.float32, device=dev)))
+    for _ in range(1 + args.warmup):
+        for name, K, N, dy, xq, xs, ws, dW in dw_legs:
+            bl.ste_backward_dw(dy, xq, xs, workspace=ws, out=dW)
+    torch.cuda.synchronize()
+    tw = Timer(torch)
+    for _ in range(reps):
+        for name, K, N, dy, xq, xs, ws, dW in dw_legs:
+            tw.run(name, lambda: bl.ste_backward_dw(dy, xq, xs, workspace=ws, out=dW))
+    torch.cuda.synchronize()
+    per_dw, dw_ms = {}, 0.0
+    for name, K, N, *_ in dw_legs:
+        ms = tw.total_ms(name)
+        dw_ms += ms
+        per_dw[name] = {"M_reduced": Mp, "N": N, "K": K, "avg_us": round(1e3 * ms / reps, 2),
+                        "TFLOPs": round(2 * Mp * N * K * reps / (ms * 1e-3) / 1e12, 1)}
+    tf_dw = flops / (dw_ms * 1e-3) / 1e12
+    del dw_legs
+    out["ste_backward_dw"] = {
+        "workload": "dW of the 4096-token projections (dy bf16 [4096][N], x_q int8 [4096][K] "
+                    "-> dW fp32 [N][K]), straight-through estimator",
+        "roofline": {"bound": "mfma", "kernel": "k_ste_dw (v_mfma_f32_32x32x16_bf16) after "
+                     "k_dw_prep_a / k_dw_prep_b",
+                     "achieved": round(tf_dw, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf_dw / BF16_PEAK_TFLOPS, 4),
+                     "matrix_core_TFLOPs": round(2 * tf_dw, 1),
+                     "note": "achieved counts the 2*M*N*K flops of the product; the matrix "
+                             "cores run twice that (the hi and lo bf16 parts of dy * x_scale)",
+                     "traffic": traffic.get("ste_dw_4096"),
+                     "traffic_unit": "HBM bytes per bl_ste_backward_dw call",
+                     "per_projection": per_dw}}
+    print(f"ste dW: {tf_dw:.1f} TFLOP/s", file=sys.stderr, flush=True)
     out["ste_backward"] = {
         "workload": "dx of the 4096-token projections (dy bf16 [4096][N] -> dx fp32 [4096][K]), "
                     "straight-through estimator",

@@ -377,8 +377,8 @@ int bl_bitlinear_base3(const int8_t* x_q, const float* x_scale, int64_t M, int64
  * estimator). Source: juhe.plus (Habr repost), the section on training that
  * follows BinaryConnect (the forward rounds, the backward passes the gradient
  * through as if there were no rounding); comrad404.com «Метод…» (gradients
- * stay in high precision). The weight gradient dW = dy^T . x~ is a dense
- * product and is not part of this library. */
+ * stay in high precision). Both gradients are here: the input's dx and the
+ * latent weights' dW. */
 
 /* Bytes of the transposed codes bl_pack_ste_t writes:
  * K * 16*ceil(ceil(N/4)/16); 0 if the shape is invalid. Host-only. */
@@ -403,6 +403,33 @@ int bl_pack_ste_t(const uint32_t* W_packed, int64_t N, int64_t K, uint8_t* qT, v
  * M*N, M*K, N*K < 2^31. */
 int bl_ste_backward_dx(const uint16_t* dy, int64_t M, int64_t N, const uint8_t* qT,
                        const float* gamma, int64_t K, float* dx, void* stream);
+
+/* Bytes of the workspace bl_ste_backward_dw needs: 4*N*Mp + 2*K*Mp with Mp
+ * = M rounded up to 64 (bf16 operands with the token index contiguous); 0 if
+ * the shape is invalid (rules of bl_ste_backward_dw). Host-only. */
+size_t bl_ste_dw_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* Gradient of the latent weights under the straight-through estimator: the
+ * forward multiplies the dequantised activations x~ = x_q * x_scale by the
+ * weights, and the backward treats the weights' rounding as the identity, so
+ *     dW[n][k] = sum_m dy[m][n] * x_q[m][k] * x_scale[m].
+ *   dy        in   bf16 [M][N] (raw bits), gradient of the BitLinear output;
+ *                  N % 8 == 0, 16-byte aligned.
+ *   x_q, x_scale in the forward's quantised input, int8 [M][K] and fp32 [M]
+ *                  (bl_quantize_acts); x_q 16-byte aligned.
+ *   dW        out  fp32 [N][K] (the latent weights' layout), 16-byte aligned;
+ *                  must not alias an input or the workspace.
+ *   workspace tmp  >= bl_ste_dw_workspace_bytes(M, N, K) bytes, 256-byte
+ *                  aligned; contents undefined afterwards.
+ * Each dy * x_scale is rounded to fp32 and split into two bf16 parts whose
+ * sum is within 2^-16 of it; products with x_q are exact and accumulate in
+ * fp32, so |dW - exact| <= (2^-16 + 2^-24 + 2*Mp*2^-24) * sum_m |dy x_q
+ * x_scale| elementwise. Shapes: M >= 1, N >= 8, K >= 64, K % 64 == 0,
+ * M*N, M*K, N*K, 2*Mp*N < 2^31. Source: as the section above; juhe.plus
+ * (latent full-precision weights receive the gradient). */
+int bl_ste_backward_dw(const uint16_t* dy, int64_t M, int64_t N, const int8_t* x_q,
+                       const float* x_scale, int64_t K, float* dW, void* workspace,
+                       size_t workspace_bytes, void* stream);
 
 /* ---- Calibration kernels ------------------------------------------------
  * Measured ceilings for the roofline of the kernels above; they compute

@@ -63,6 +63,8 @@ _SIGNATURES = {
     "bl_ste_t_bytes": ([_I, _I], _S),
     "bl_pack_ste_t": ([_P, _I, _I, _P, _P], ctypes.c_int),
     "bl_ste_backward_dx": ([_P, _I, _I, _P, _P, _I, _P, _P], ctypes.c_int),
+    "bl_ste_dw_workspace_bytes": ([_I, _I, _I], _S),
+    "bl_ste_backward_dw": ([_P, _I, _I, _P, _P, _I, _P, _P, _S, _P], ctypes.c_int),
     "bl_calib_read": ([_P, _S, _P, _P], ctypes.c_int),
     "bl_calib_copy": ([_P, _P, _S, _P], ctypes.c_int),
     "bl_calib_mfma_i8_ops": ([_I], _I),
@@ -518,6 +520,37 @@ def ste_backward_dx(dy, qT, gamma, N: int, out=None):
                                     _dev(dx, torch.float32, "dx"), _stream_ptr(dy)),
            "bl_ste_backward_dx")
     return dx
+
+
+def ste_dw_workspace(M: int, N: int, K: int, device=None):
+    """A workspace tensor sized by bl_ste_dw_workspace_bytes."""
+    torch = _torch()
+    n = lib().bl_ste_dw_workspace_bytes(M, N, K)
+    if n == 0:
+        raise BitLinearError("invalid STE shapes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def ste_backward_dw(dy, x_q, x_scale, workspace=None, out=None):
+    """dW fp32 [N][K] = dy^T . (x_q * x_scale) for bf16 dy [M][N], int8 x_q
+    [M][K], fp32 x_scale [M]. Calls bl_ste_backward_dw."""
+    torch = _torch()
+    if dy.dtype == torch.int16:
+        dy = dy.view(torch.bfloat16)
+    M, N = dy.shape
+    K = x_q.shape[1]
+    if x_q.shape[0] != M or x_scale.shape != (M,):
+        raise BitLinearError("dy, x_q and x_scale shapes do not match")
+    if workspace is None:
+        workspace = ste_dw_workspace(M, N, K, dy.device)
+    dW = torch.empty((N, K), dtype=torch.float32, device=dy.device) if out is None else out
+    _check(lib().bl_ste_backward_dw(_dev(dy, torch.bfloat16, "dy"), M, N,
+                                    _dev(x_q, torch.int8, "x_q"),
+                                    _dev(x_scale, torch.float32, "x_scale"), K,
+                                    _dev(dW, torch.float32, "dW"),
+                                    _dev(workspace, torch.uint8, "workspace"),
+                                    workspace.numel(), _stream_ptr(dy)), "bl_ste_backward_dw")
+    return dW
 
 
 # ---------------------------------------------------------- calibration ----

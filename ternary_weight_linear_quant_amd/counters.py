@@ -88,6 +88,10 @@ PHASES = {
                     "bl_ste_backward_dx at M=4096 on 2560->6912 and 6912->2560 "
                     "(dy bf16 [4096][N] -> dx fp32 [4096][K])", 2,
                     "bl_ste_backward_dx call (k_ste_dx)"),
+    "ste_dw_4096": (["ste_dw.hip", "common.hpp"],
+                    "bl_ste_backward_dw at M=4096 on 2560->6912 and 6912->2560 "
+                    "(dy bf16 [4096][N], x_q int8 [4096][K] -> dW fp32 [N][K])", 2,
+                    "bl_ste_backward_dw call (k_dw_prep_a, k_dw_prep_b, k_ste_dw)"),
     "gemm_prefill_70b": (["gemm.hip", "common.hpp"],
                          "bl_bitlinear at M=2048 on 8192->28672 and 28672->8192", 2,
                          "bl_bitlinear call (k_gemm)"),
@@ -180,6 +184,11 @@ def run():
         s3.append((bl.pack_ste_t(pk, K), g, dy,
                    torch.empty((M3[0], K), dtype=torch.float32, device=dev), N))
         del pk
+    d3 = []
+    for i, (name, K, N) in enumerate(p3):
+        xq, xs = bl.quantize_acts(bf16(wl.activations(3, i, M3[0], K)))
+        d3.append((s3[i][2], xq, xs, bl.ste_dw_workspace(M3[0], N, K, dev),
+                   torch.empty((N, K), dtype=torch.float32, device=dev)))
     q3 = []
     for i, (name, K, N) in enumerate(p3):
         pk, g = weights(3, i, N, K, 1)[0]
@@ -239,6 +248,10 @@ def run():
         for qT, g, dy, dx, N in s3:
             bl.ste_backward_dx(dy, qT, g, N, out=dx)
 
+    def ste_dw4096():
+        for dy, xq, xs, ws, dW in d3:
+            bl.ste_backward_dw(dy, xq, xs, workspace=ws, out=dW)
+
     def prefill4096():
         for xq, xs, pk, g, y in q3:
             bl.bitlinear(xq, xs, pk, g, out=y)
@@ -259,6 +272,7 @@ def run():
     phase("gemm_3b_m512", block3b(512))
     phase("gemm_prefill_4096", prefill4096)
     phase("ste_dx_4096", ste4096)
+    phase("ste_dw_4096", ste_dw4096)
     phase("gemm_prefill_70b", prefill70)
     marker()
     print("done", flush=True)

@@ -526,6 +526,36 @@ int bl_ste_backward_dx(const uint16_t* dy, int64_t M, int64_t N, const uint8_t* 
                                         as_stream(stream)));
 }
 
+
+size_t bl_ste_dw_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M < 1 || N < 8 || (N % 8) != 0 || !shape_ok(N, K)) return 0;
+    if (M > (int64_t{1} << 31) / N || M > (int64_t{1} << 31) / K) return 0;
+    const int64_t Mp = bl::ste_dw_padded_tokens(M);
+    if (2 * Mp > (int64_t{1} << 31) / N) return 0;   // operand rows of 2 Mp values
+    return bl::ste_dw_workspace_bytes(M, N, K);
+}
+
+int bl_ste_backward_dw(const uint16_t* dy, int64_t M, int64_t N, const int8_t* x_q,
+                       const float* x_scale, int64_t K, float* dW, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    if (!dy || !x_q || !x_scale || !dW || !workspace) return BL_ERR_INVALID_ARG;
+    const size_t need = bl_ste_dw_workspace_bytes(M, N, K);
+    if (need == 0 || workspace_bytes < need) return BL_ERR_INVALID_ARG;
+    if (!aligned16(dy) || !aligned16(x_q) || !aligned16(dW) ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return BL_ERR_INVALID_ARG;
+    const size_t ndw = (size_t)(N * K) * 4;
+    if (overlaps(dW, ndw, dy, (size_t)(M * N) * 2) || overlaps(dW, ndw, x_q, (size_t)(M * K)) ||
+        overlaps(dW, ndw, x_scale, (size_t)M * 4) || overlaps(dW, ndw, workspace, need) ||
+        overlaps(workspace, need, dy, (size_t)(M * N) * 2) ||
+        overlaps(workspace, need, x_q, (size_t)(M * K)) ||
+        overlaps(workspace, need, x_scale, (size_t)M * 4))
+        return BL_ERR_INVALID_ARG;
+    if (int s = device_status()) return s;
+    return hip_status(bl::launch_ste_dw(dy, (int)M, (int)N, x_q, x_scale, (int)K, dW, workspace,
+                                        as_stream(stream)));
+}
+
 int bl_calib_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
     if (!src || !sink || bytes < 16 || (bytes % 16) != 0 || !aligned16(src))
         return BL_ERR_INVALID_ARG;

@@ -98,6 +98,14 @@ hipError_t launch_pack_ste_t(const uint32_t* packed2, int64_t N, int64_t K, uint
 hipError_t launch_ste_dx(const uint16_t* dy, int M, int N, const uint8_t* qT, const float* gamma,
                          int K, float* dx, hipStream_t stream);
 
+// Straight-through backward with respect to the latent weights: dW = dy^T .
+// (x_q * x_scale), bf16 matrix cores on split operands; workspace for the
+// transposed operands.
+int64_t ste_dw_padded_tokens(int64_t M);
+size_t ste_dw_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_ste_dw(const uint16_t* dy, int M, int N, const int8_t* xq, const float* xs,
+                         int K, float* dW, void* workspace, hipStream_t stream);
+
 // Calibration kernels (measured ceilings; not part of the method).
 constexpr int kCalibMfmaBlocks = 512;        // 256-thread blocks of the MFMA loop
 hipError_t launch_calib_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);

@@ -158,6 +158,18 @@ def test_invalid_arguments_rejected_before_launch(L):
                                  None) == E
     assert L.bl_ffn_step_noalloc(A, 4, 2560, A, A, A, A, 6912, A, A, 1, A, -1.0, A,
                                  None) == E
+    # straight-through weight gradient
+    need_dw = L.bl_ste_dw_workspace_bytes(100, 64, 128)
+    assert need_dw == 4 * 64 * 128 + 2 * 128 * 128
+    assert L.bl_ste_dw_workspace_bytes(100, 60, 128) == 0          # N % 8
+    assert L.bl_ste_dw_workspace_bytes(100, 64, 96) == 0           # K % 64
+    assert L.bl_ste_dw_workspace_bytes(0, 64, 128) == 0
+    assert L.bl_ste_backward_dw(None, 100, 64, A, A, 128, A, WS, need_dw, None) == E
+    assert L.bl_ste_backward_dw(A, 100, 64, A, A, 128, A, None, need_dw, None) == E
+    assert L.bl_ste_backward_dw(A, 100, 64, A, A, 128, A, WS, need_dw - 1, None) == E
+    assert L.bl_ste_backward_dw(A, 100, 60, A, A, 128, A, WS, need_dw, None) == E
+    assert L.bl_ste_backward_dw(MIS, 100, 64, A, A, 128, A, WS, need_dw, None) == E
+    assert L.bl_ste_backward_dw(A, 100, 64, A, A, 128, A, P(0x500010), need_dw, None) == E
     # pair
     assert L.bl_bitlinear_pair(A, A, 1, 64, A, A, 16, A, None, A, 16, A, None) == E
     assert L.bl_bitlinear_pair(A, A, 1, 64, A, A, 16, A, A, A, 0, A, None) == E
@@ -246,6 +258,9 @@ def test_no_device_status(L):
                          need, None) == D
     assert L.bl_ffn_step_noalloc(A, 25, 8192, A, A, A, A, 28672, A, A, 0, None, 0.0, A,
                                  None) == D
+    need_dw = L.bl_ste_dw_workspace_bytes(100, 64, 128)
+    assert L.bl_ste_backward_dw(P(0x100000), 100, 64, P(0x110000), P(0x120000), 128,
+                                P(0x130000), P(0x200000), need_dw, None) == D
     assert L.bl_ffn_step_noalloc(A, 106, 2560, A, A, A, A, 6912, A, A, 0, None, 0.0, A,
                                  None) == D
 

@@ -1185,6 +1185,88 @@ def test_ste_backward_dx_large_tiles_ragged():
     assert (err <= _dx_bound(dy[rows], q, g)).all(), float(err.max())
 
 
+# dW: tokens ragged against the 64-token padding, features ragged against the
+# 128 x 256 tiles and the 64-wide stages.
+STE_DW_CASES = [(1, 8, 64), (3, 40, 128), (70, 136, 320), (200, 264, 576), (64, 128, 256),
+                (130, 520, 704), (257, 1000, 1344)]
+
+
+def _dw_bound(dy_bits, xq, xs):
+    """(2^-16 + 2^-24 + 2 Mp 2^-24) * sum_m |dy x_q x_scale| per element: the
+    split of dy * x_scale into two bf16 parts, its fp32 rounding, and fp32
+    accumulation of 2 Mp exact products."""
+    M = dy_bits.shape[0]
+    Mp = (M + 63) // 64 * 64
+    a = np.abs(wl.bf16_bits_to_f32(dy_bits).astype(np.float64) * xs.astype(np.float64)[:, None])
+    mag = a.T @ np.abs(xq.astype(np.float64))
+    return (2.0 ** -16 + 2.0 ** -24 + 2 * Mp * 2.0 ** -24) * mag + 1e-30
+
+
+def _dw_case(M, N, K, seed):
+    rng = np.random.default_rng(seed)
+    dy = wl.f32_to_bf16_bits((rng.standard_normal((M, N)) * 0.01).astype(np.float32))
+    x = wl.activations(seed % 1000, 1, M, K)
+    xq, xs = oracle.act_quant(x)
+    return dy, xq, xs
+
+
+@pytest.mark.parametrize("M,N,K", STE_DW_CASES)
+def test_ste_backward_dw_parity(M, N, K):
+    """dW against the oracle's exact fp64 sum, within the derived fp32 bound."""
+    dy, xq, xs = _dw_case(M, N, K, 90 + M)
+    ref = oracle.ste_dw(dy, xq, xs).astype(np.float64)
+    dW = bl.ste_backward_dw(dev_bf16(dy), torch.from_numpy(xq).to(DEV), dev_f32(xs))
+    err = np.abs(dW.cpu().numpy().astype(np.float64) - ref)
+    assert (err <= _dw_bound(dy, xq, xs)).all(), float((err / _dw_bound(dy, xq, xs)).max())
+
+
+def test_ste_backward_dw_exact_cases():
+    """Where every value is exact (power-of-two scales, small sums) dW is the
+    oracle's bit for bit; a one-hot dy gives one token's dequantised row
+    within the split's 2^-16 (the two bf16 parts keep 16 of the scale's 24
+    significant bits) and exact zeros elsewhere."""
+    M, N, K = 96, 64, 128
+    rng = np.random.default_rng(93)
+    dy = wl.f32_to_bf16_bits(rng.integers(-4, 5, (M, N)).astype(np.float32))
+    xq = rng.integers(-128, 128, (M, K)).astype(np.int8)
+    xs = (2.0 ** -rng.integers(3, 9, M)).astype(np.float32)
+    dW = bl.ste_backward_dw(dev_bf16(dy), torch.from_numpy(xq).to(DEV), dev_f32(xs))
+    assert np.array_equal(dW.cpu().numpy(), oracle.ste_dw(dy, xq, xs))
+    d1 = np.zeros((M, N), np.float32)
+    d1[37, 11] = 1.0
+    xs2 = (rng.random(M) * 0.05 + 0.001).astype(np.float32)
+    dW1 = bl.ste_backward_dw(dev_bf16(wl.f32_to_bf16_bits(d1)), torch.from_numpy(xq).to(DEV),
+                             dev_f32(xs2)).cpu().numpy()
+    ref1 = oracle.ste_dw(wl.f32_to_bf16_bits(d1), xq, xs2).astype(np.float64)
+    assert (np.abs(dW1[11] - ref1[11]) <= 2.0 ** -16 * np.abs(ref1[11])).all()
+    assert (np.delete(dW1, 11, axis=0) == 0).all()
+
+
+@pytest.mark.parametrize("idx", [0, 1])
+def test_ste_backward_dw_full_size(idx):
+    """The 4096-token shapes: every element against an fp64 product of the
+    same operands (exact products; fp64 sums), within the derived bound; 16
+    rows through the oracle itself; three calls give the same bits."""
+    _, projs, Ms = wl.WORKLOADS[3]
+    name, K, N = projs[idx]
+    M = Ms[0]
+    dy, xq, xs = _dw_case(M, N, K, 95 + idx)
+    args = (dev_bf16(dy), torch.from_numpy(xq).to(DEV), dev_f32(xs))
+    ws = bl.ste_dw_workspace(M, N, K, DEV)
+    dW = bl.ste_backward_dw(*args, workspace=ws)
+    got = dW.cpu().numpy().astype(np.float64)
+    a = wl.bf16_bits_to_f32(dy).astype(np.float64) * xs.astype(np.float64)[:, None]
+    ref = a.T @ xq.astype(np.float64)
+    bound = _dw_bound(dy, xq, xs)
+    assert (np.abs(got - ref) <= bound).all()
+    ns = np.sort(np.random.default_rng(96).choice(N, 16, replace=False))
+    ref_o = oracle.ste_dw(np.ascontiguousarray(dy[:, ns]), xq, xs).astype(np.float64)
+    assert (np.abs(got[ns] - ref_o) <= bound[ns]).all()
+    for _ in range(2):
+        again = bl.ste_backward_dw(*args, workspace=ws)
+        assert torch.equal(again.view(torch.int32), dW.view(torch.int32))
+
+
 def test_ste_pack_odd_n():
     rng = np.random.default_rng(91)
     q = rand_codes(rng, 37, 64)
