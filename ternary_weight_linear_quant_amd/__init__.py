@@ -140,14 +140,18 @@ def packed_bytes(N: int, K: int) -> int:
     return lib().bl_packed_bytes(N, K)
 
 
-def quantize_weights(W, workspace=None):
+def quantize_weights(W, workspace=None, out=None):
     """W: fp32 [N][K] -> (W_packed int32 [N][K/16] holding the uint32 words,
-    gamma fp32 [1]). Calls bl_quantize_weights."""
+    gamma fp32 [1]). out: optional (W_packed, gamma) buffers. Calls
+    bl_quantize_weights."""
     torch = _torch()
     N, K = W.shape
     L = lib()
-    packed = torch.empty((N, K // 16), dtype=torch.int32, device=W.device)
-    gamma = torch.empty(1, dtype=torch.float32, device=W.device)
+    if out is None:
+        packed = torch.empty((N, K // 16), dtype=torch.int32, device=W.device)
+        gamma = torch.empty(1, dtype=torch.float32, device=W.device)
+    else:
+        packed, gamma = out
     ws_bytes = L.bl_quantize_weights_workspace_bytes(N, K)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 8) // 8, dtype=torch.float64, device=W.device)
@@ -423,17 +427,21 @@ def ffn_step_noalloc(x, W_gate, gamma_gate, W_up, gamma_up, W_down, gamma_down, 
 # 1 bit per {-1, +1} weight (the original BitNet's binary weights) and five
 # ternary weights per byte (1.6 bits); decode products for M <= 16.
 
-def quantize_weights_binary(W, workspace=None):
+def quantize_weights_binary(W, workspace=None, out=None):
     """W fp32 [N][K] -> (W_bits int32 [N][4*ceil(K/128)] holding uint32 words,
-    gamma fp32 [1]). Calls bl_quantize_weights_binary."""
+    gamma fp32 [1]). out: optional (W_bits, gamma) buffers. Calls
+    bl_quantize_weights_binary."""
     torch = _torch()
     N, K = W.shape
     L = lib()
     nbytes = L.bl_packed_bytes_binary(N, K)
     if nbytes == 0:
         raise BitLinearError("invalid weight shape")
-    bits = torch.empty((N, nbytes // (4 * N)), dtype=torch.int32, device=W.device)
-    gamma = torch.empty(1, dtype=torch.float32, device=W.device)
+    if out is None:
+        bits = torch.empty((N, nbytes // (4 * N)), dtype=torch.int32, device=W.device)
+        gamma = torch.empty(1, dtype=torch.float32, device=W.device)
+    else:
+        bits, gamma = out
     ws_bytes = L.bl_quantize_weights_workspace_bytes(N, K)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 8) // 8, dtype=torch.float64, device=W.device)
@@ -446,26 +454,30 @@ def quantize_weights_binary(W, workspace=None):
     return bits, gamma
 
 
-def pack_base3(W_packed, K: int):
+def pack_base3(W_packed, K: int, out=None):
     """2-bit packed [N][K/16] -> uint8 [N][16*ceil(ceil(K/5)/16)], five ternary
-    weights per byte. Calls bl_pack_base3."""
+    weights per byte (into `out` when given). Calls bl_pack_base3."""
     torch = _torch()
     N = W_packed.shape[0]
     L = lib()
     nbytes = L.bl_packed_bytes_base3(N, K)
     if nbytes == 0 or W_packed.shape[1] * 16 != K:
         raise BitLinearError("invalid weight shape")
-    out = torch.empty((N, nbytes // N), dtype=torch.uint8, device=W_packed.device)
+    if out is None:
+        out = torch.empty((N, nbytes // N), dtype=torch.uint8, device=W_packed.device)
     _check(L.bl_pack_base3(_dev(W_packed, torch.int32, "W_packed"), N, K,
                            _dev(out, torch.uint8, "W3"), _stream_ptr(W_packed)), "bl_pack_base3")
     return out
 
 
-def _other_product(fn, name, x_q, x_scale, W, wdtype, gamma, N, return_acc, out):
+def _other_product(fn, name, x_q, x_scale, W, wdtype, gamma, N, return_acc, out, acc_out=None):
     torch = _torch()
     M, K = x_q.shape
     y = torch.empty((M, N), dtype=torch.float32, device=x_q.device) if out is None else out
-    acc = torch.empty((M, N), dtype=torch.int32, device=x_q.device) if return_acc else None
+    acc = acc_out
+    if acc is None and return_acc:
+        acc = torch.empty((M, N), dtype=torch.int32, device=x_q.device)
+    return_acc = acc is not None
     _check(fn(_dev(x_q, torch.int8, "x_q"), _dev(x_scale, torch.float32, "x_scale"), M, K,
               _dev(W, wdtype, "W"), _dev(gamma, torch.float32, "gamma"), N,
               _dev(y, torch.float32, "y"),
@@ -473,32 +485,35 @@ def _other_product(fn, name, x_q, x_scale, W, wdtype, gamma, N, return_acc, out)
     return (y, acc) if return_acc else y
 
 
-def bitlinear_binary(x_q, x_scale, W_bits, gamma, return_acc: bool = False, out=None):
+def bitlinear_binary(x_q, x_scale, W_bits, gamma, return_acc: bool = False, out=None,
+                     acc_out=None):
     """BitLinear with 1-bit weights (M <= 16). Calls bl_bitlinear_binary."""
     torch = _torch()
     return _other_product(lib().bl_bitlinear_binary, "bl_bitlinear_binary", x_q, x_scale,
-                          W_bits, torch.int32, gamma, W_bits.shape[0], return_acc, out)
+                          W_bits, torch.int32, gamma, W_bits.shape[0], return_acc, out, acc_out)
 
 
-def bitlinear_base3(x_q, x_scale, W3, gamma, return_acc: bool = False, out=None):
+def bitlinear_base3(x_q, x_scale, W3, gamma, return_acc: bool = False, out=None, acc_out=None):
     """BitLinear with base-3 weights (M <= 16). Calls bl_bitlinear_base3."""
     torch = _torch()
     return _other_product(lib().bl_bitlinear_base3, "bl_bitlinear_base3", x_q, x_scale, W3,
-                          torch.uint8, gamma, W3.shape[0], return_acc, out)
+                          torch.uint8, gamma, W3.shape[0], return_acc, out, acc_out)
 
 
 # ------------------------------------------- straight-through backward ----
 
-def pack_ste_t(W_packed, K: int):
+def pack_ste_t(W_packed, K: int, out=None):
     """2-bit packed [N][K/16] -> transposed codes uint8 [K][row bytes], four n
-    per byte, for the backward pass. Calls bl_pack_ste_t."""
+    per byte, for the backward pass (into `out` when given). Calls
+    bl_pack_ste_t."""
     torch = _torch()
     N = W_packed.shape[0]
     L = lib()
     nbytes = L.bl_ste_t_bytes(N, K)
     if nbytes == 0 or W_packed.shape[1] * 16 != K:
         raise BitLinearError("invalid weight shape")
-    qT = torch.empty((K, nbytes // K), dtype=torch.uint8, device=W_packed.device)
+    qT = torch.empty((K, nbytes // K), dtype=torch.uint8, device=W_packed.device) \
+        if out is None else out
     _check(L.bl_pack_ste_t(_dev(W_packed, torch.int32, "W_packed"), N, K,
                            _dev(qT, torch.uint8, "qT"), _stream_ptr(W_packed)), "bl_pack_ste_t")
     return qT
