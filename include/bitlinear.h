@@ -170,6 +170,30 @@ int bl_bitlinear_path(const int8_t* x_q, const float* x_scale, int64_t M,
                       int64_t K, const uint32_t* W_packed, const float* gamma,
                       int64_t N, float* y, int32_t* acc, int path, void* stream);
 
+/* Activation quantisation (optionally fused with the preceding RMSNorm) and
+ * the BitLinear product in one call: exactly bl_quantize_acts(x, M, K,
+ * rms_gain, rms_eps, x_q, x_scale) followed by bl_bitlinear(x_q, x_scale, M,
+ * K, W_packed, gamma, N, y, NULL). Source: comrad404.com page above, section
+ * «Метод: как устроен BitNet b1.58»: normalise, quantise the activations to
+ * 8 bits, multiply by the ternary weights, rescale.
+ *
+ *   x, rms_gain, rms_eps   in   as bl_quantize_acts.
+ *   W_packed, gamma, N     in   as bl_bitlinear.
+ *   y          out  fp32 [M][N], the same bits as the two calls give.
+ *   x_q        out  int8 [M][K], x_scale out fp32 [M]: the quantised input,
+ *                   the same bits as bl_quantize_acts gives (the caller
+ *                   provides both; they are written whichever way the call
+ *                   runs).
+ * At one token (M == 1) with K <= 4096 a single launch does both: every
+ * workgroup of the one-token GEMV quantises the token itself (its weight
+ * loads already in flight) and workgroup 0 writes x_q and x_scale. Other
+ * shapes enqueue the two calls (for longer rows every workgroup's copy of the
+ * token costs more than the second launch). Pointers 16-byte aligned; y, x_q
+ * and x_scale must not overlap each other or any input. */
+int bl_quant_bitlinear(const uint16_t* x, int64_t M, int64_t K, const uint16_t* rms_gain,
+                       float rms_eps, const uint32_t* W_packed, const float* gamma, int64_t N,
+                       float* y, int8_t* x_q, float* x_scale, void* stream);
+
 /* Squared-ReLU gating between the gate/up and down projections of a 2B4T-style
  * FFN: h[i] = bf16_rne((r*r) * up[i]) with r = gate[i] > 0 ? gate[i] : 0, all
  * fp32. Source: inferownia.pl page above, section "Zrób to sam — Microsoft

@@ -37,6 +37,7 @@ _SIGNATURES = {
     "bl_quantize_weights_workspace_bytes": ([_I, _I], _S),
     "bl_quantize_weights": ([_P, _I, _I, _P, _P, _P, _S, _P], ctypes.c_int),
     "bl_quantize_acts": ([_P, _I, _I, _P, _F, _P, _P, _P], ctypes.c_int),
+    "bl_quant_bitlinear": ([_P, _I, _I, _P, _F, _P, _P, _I, _P, _P, _P, _P], ctypes.c_int),
     "bl_bitlinear": ([_P, _P, _I, _I, _P, _P, _I, _P, _P, _P], ctypes.c_int),
     "bl_bitlinear_path": ([_P, _P, _I, _I, _P, _P, _I, _P, _P, ctypes.c_int, _P],
                           ctypes.c_int),
@@ -186,6 +187,38 @@ def quantize_acts(x, rms_gain=None, rms_eps: float = 1e-5, out=None):
                                   _dev(xs, torch.float32, "x_scale"), _stream_ptr(x)),
            "bl_quantize_acts")
     return xq, xs
+
+
+def quant_bitlinear(x, W_packed, gamma, rms_gain=None, rms_eps: float = 1e-5, out=None):
+    """Activation quantisation (optional fused RMSNorm) and the BitLinear product in
+    one call: x bf16 [M][K] -> (y fp32 [M][N], x_q int8 [M][K], x_scale fp32 [M]),
+    the same bits as quantize_acts followed by bitlinear. out: optional (y, x_q,
+    x_scale) buffers. Calls bl_quant_bitlinear."""
+    torch = _torch()
+    M, K = x.shape
+    N = W_packed.shape[0]
+    if W_packed.shape[1] * 16 != K:
+        raise BitLinearError("W_packed shape does not match K")
+    if x.dtype == torch.int16:
+        x = x.view(torch.bfloat16)
+    if out is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+        xs = torch.empty(M, dtype=torch.float32, device=x.device)
+    else:
+        y, xq, xs = out
+    gp = None
+    if rms_gain is not None:
+        if rms_gain.dtype == torch.int16:
+            rms_gain = rms_gain.view(torch.bfloat16)
+        gp = _dev(rms_gain, torch.bfloat16, "rms_gain")
+    _check(lib().bl_quant_bitlinear(_dev(x, torch.bfloat16, "x"), M, K, gp, float(rms_eps),
+                                    _dev(W_packed, torch.int32, "W_packed"),
+                                    _dev(gamma, torch.float32, "gamma"), N,
+                                    _dev(y, torch.float32, "y"), _dev(xq, torch.int8, "x_q"),
+                                    _dev(xs, torch.float32, "x_scale"), _stream_ptr(x)),
+           "bl_quant_bitlinear")
+    return y, xq, xs
 
 
 def bitlinear(x_q, x_scale, W_packed, gamma, return_acc: bool = False, path: int = 0,

@@ -178,6 +178,38 @@ int bl_bitlinear(const int8_t* x_q, const float* x_scale, int64_t M, int64_t K,
     return bl_bitlinear_path(x_q, x_scale, M, K, W_packed, gamma, N, y, acc, 0, stream);
 }
 
+int bl_quant_bitlinear(const uint16_t* x, int64_t M, int64_t K, const uint16_t* rms_gain,
+                       float rms_eps, const uint32_t* W_packed, const float* gamma, int64_t N,
+                       float* y, int8_t* x_q, float* x_scale, void* stream) {
+    if (!x || !W_packed || !gamma || !y || !x_q || !x_scale) return BL_ERR_INVALID_ARG;
+    if (!shape_ok(M, K) || !shape_ok(N, K)) return BL_ERR_INVALID_ARG;
+    if (M > (int64_t{1} << 31) / N) return BL_ERR_INVALID_ARG;  // M*N < 2^31
+    if (!aligned16(x) || !aligned16(x_q) || !aligned16(x_scale) || !aligned16(W_packed) ||
+        !aligned16(y))
+        return BL_ERR_INVALID_ARG;
+    if (rms_gain && (!aligned16(rms_gain) || !(rms_eps > 0.0f))) return BL_ERR_INVALID_ARG;
+    // No output may overlap another output or an input.
+    const size_t ny = (size_t)(M * N) * 4, nq = (size_t)(M * K), ns = (size_t)M * 4;
+    const void* outs[3] = {y, x_q, x_scale};
+    const size_t out_n[3] = {ny, nq, ns};
+    const void* ins[4] = {x, rms_gain, W_packed, gamma};
+    const size_t in_n[4] = {(size_t)(M * K) * 2, rms_gain ? (size_t)K * 2 : 0,
+                            (size_t)(N * K) / 4, 4};
+    for (int i = 0; i < 3; ++i) {
+        for (int j = i + 1; j < 3; ++j)
+            if (overlaps(outs[i], out_n[i], outs[j], out_n[j])) return BL_ERR_INVALID_ARG;
+        for (int j = 0; j < 4; ++j)
+            if (ins[j] && overlaps(outs[i], out_n[i], ins[j], in_n[j])) return BL_ERR_INVALID_ARG;
+    }
+    if (int s = device_status()) return s;
+    hipStream_t st = as_stream(stream);
+    if (bl::gemv1_quant_supported(M, K))
+        return hip_status(bl::launch_gemv1_quant(x, rms_gain, rms_eps, (int)K, W_packed, gamma,
+                                                 (int)N, y, x_q, x_scale, st));
+    if (int s = bl_quantize_acts(x, M, K, rms_gain, rms_eps, x_q, x_scale, stream)) return s;
+    return bl_bitlinear_path(x_q, x_scale, M, K, W_packed, gamma, N, y, nullptr, 0, stream);
+}
+
 int bl_bitlinear_pair(const int8_t* x_q, const float* x_scale, int64_t M, int64_t K,
                       const uint32_t* W1, const float* gamma1, int64_t N1, float* y1,
                       const uint32_t* W2, const float* gamma2, int64_t N2, float* y2,

@@ -41,8 +41,20 @@
 //                   reads its activations from LDS.
 // Waves are independent after the staging barrier (no barrier at the end).
 //
+// Quantising variant of k_gemv1_cached (QX > 0, rows of one piece): the input
+// is the bf16 token itself (with an optional RMSNorm gain), and every
+// workgroup quantises it on the way into LDS with the stand-alone quantiser's
+// arithmetic and reduction order (the helpers in act_quant.hpp): its 256
+// threads load the token, reduce max|z| (and sum x^2), and write the codes
+// into the staging layout; workgroup 0 also writes them and the scale to
+// global memory. The weight loads are issued before the reductions, so they
+// are in flight across both barriers. One launch then does what the quantiser
+// and the GEMV do in two, at the price of 2K bytes of input per workgroup
+// (from L2) instead of K.
+//
 // Roofline: HBM. Algorithmic bytes per call = N * K/4 (packed weights) + K
 // (activations) + 4 (scale) + 4 (gamma) + 4 * N (y).
+#include "act_quant.hpp"
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -83,29 +95,120 @@ __device__ __forceinline__ void store_row(float* y, int32_t* acc_out, int n, int
 
 }  // namespace
 
+// Kernel arguments. QX == 0: xq / xs are the token's codes and scale. QX > 0:
+// x is the bf16 token (gain: the RMSNorm gain when QX == 2), and xq_out /
+// xs_out receive its codes and scale from workgroup 0.
+struct Gemv1Args {
+    const int8_t* xq;
+    const float* xs;
+    const uint16_t* x;
+    const uint16_t* gain;
+    float rms_eps;
+    int8_t* xq_out;
+    float* xs_out;
+    int K;
+    const uint8_t* W;
+    const float* gamma;
+    int N;
+    float* y;
+    int32_t* acc_out;
+};
+
+// Byte offset in the staging layout of activation k.
+__device__ __forceinline__ int stage_offset(int k) {
+    return (4 * (k / kPieceK) + (k / 16) % 4) * kPiece + 16 * ((k / 64) % 64) + k % 16;
+}
+
+// Quantises the token held by threads 0..255 as 16-byte bf16 vectors v =
+// tid + 256 j (j < VPT, loaded by load_token), the assignment and reduction
+// order of k_act_quant. Writes the codes of every vector below
+// NV8 (vectors past K get zero codes) at their staging offsets and returns
+// the scale. Workgroup 0 also stores the codes and the scale. Contains two
+// barriers: every thread of the workgroup calls it.
+template <bool NORM, int VPT>
+__device__ __forceinline__ float quantise_token(const uint4 (&cx)[VPT], const uint4 (&cg)[VPT],
+                                                int K, int NV8, float rms_eps, uint8_t* smem,
+                                                int8_t* xq_out, float* xs_out) {
+    __shared__ float s_max[kActThreads / kWave];
+    __shared__ double s_ss[kActThreads / kWave];
+    const int tid = threadIdx.x;
+    const int nvec = K / 8;
+    float amax = 0.0f;
+    double ss = 0.0;
+    if (tid < kActThreads) {
+#pragma unroll
+        for (int j = 0; j < VPT; ++j)
+            if (tid + kActThreads * j < nvec) act_scan8<NORM>(cx[j], cg[j], amax, ss);
+    }
+    amax = act_reduce<float, true>(amax, s_max);
+    double ss_tot = 0.0;
+    if (NORM) ss_tot = act_reduce<double, false>(ss, s_ss);
+    const float a = act_clamped_max(amax);
+    const float inv = 127.0f / a;  // correctly rounded
+    const bool first = blockIdx.x == 0;
+    if (tid < kActThreads) {
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            const int v = tid + kActThreads * j;
+            if (v < NV8) {
+                const uint2 c = v < nvec ? act_quant8<NORM>(cx[j], cg[j], inv) : make_uint2(0u, 0u);
+                *reinterpret_cast<uint2*>(smem + stage_offset(8 * v)) = c;
+                if (first && v < nvec) reinterpret_cast<uint2*>(xq_out)[v] = c;
+            }
+        }
+    }
+    const float scale = act_scale<NORM>(a, ss_tot, K, rms_eps);
+    if (first && tid == 0) xs_out[0] = scale;
+    return scale;
+}
+
+// Loads this thread's bf16 vectors of the token (threads 0..255 only).
+template <bool NORM, int VPT>
+__device__ __forceinline__ void load_token(const Gemv1Args& p, uint4 (&cx)[VPT], uint4 (&cg)[VPT]) {
+    const int tid = threadIdx.x;
+    const int nvec = p.K / 8;
+    if (tid >= kActThreads) return;
+    const uint4* xr = reinterpret_cast<const uint4*>(p.x);
+    const uint4* gr = reinterpret_cast<const uint4*>(p.gain);
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        const int v = tid + kActThreads * j;
+        if (v < nvec) {
+            cx[j] = xr[v];
+            cg[j] = NORM ? gr[v] : cx[j];
+        }
+    }
+}
+
 // S pieces per row (K <= 4096 S), RW rows per wave, R loads in flight per lane,
-// WPB waves per workgroup. Requires N >= RW.
-template <int S, int RW, int R, int WPB>
-__global__ __launch_bounds__(64 * WPB) void k_gemv1_cached(
-    const int8_t* __restrict__ xq, const float* __restrict__ xs, int K,
-    const uint8_t* __restrict__ W, const float* __restrict__ gamma_p, int N, float* __restrict__ y,
-    int32_t* __restrict__ acc_out) {
+// WPB waves per workgroup, QX as for Gemv1Args. Requires N >= RW.
+template <int S, int RW, int R, int WPB, int QX>
+__global__ __launch_bounds__(64 * WPB) void k_gemv1_cached(const Gemv1Args p) {
     constexpr int L = S * RW;  // pieces per wave
+    constexpr bool NORM = QX == 2;
+    constexpr int VPT = QX ? S * kPieceK / 8 / kActThreads : 1;  // bf16 vectors per thread
+    static_assert(QX == 0 || 64 * WPB == kActThreads, "the token is quantised by 256 threads");
     __shared__ __align__(16) uint8_t smem[S * kPieceK];
     const int tid = threadIdx.x, lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int K = p.K, N = p.N;
     const int RB = K / 4;
 
-    // 1. Activations straight into LDS: transfer q = 4j + s moves, for each
-    //    lane l, x[4096 j + 64 l + 16 s, +16) to q * 1024 + 16 l; lanes past
-    //    K store zeros instead.
-    const uint32_t xbase = lds_offset(smem);
-    for (int q = wave; q < 4 * S; q += WPB) {
-        const int k0 = kPieceK * (q / 4) + 64 * lane;
-        if (k0 < K)
-            lds_dma16(xq + k0 + 16 * (q % 4), xbase + q * kPiece);
-        else
-            *reinterpret_cast<uint4*>(smem + q * kPiece + 16 * lane) = make_uint4(0, 0, 0, 0);
+    // 1. QX == 0: the codes straight into LDS: transfer q = 4j + s moves, for
+    //    each lane l, x[4096 j + 64 l + 16 s, +16) to q * 1024 + 16 l; lanes
+    //    past K store zeros instead. QX > 0: the bf16 token into registers.
+    uint4 cx[VPT], cg[VPT];
+    if constexpr (QX == 0) {
+        const uint32_t xbase = lds_offset(smem);
+        for (int q = wave; q < 4 * S; q += WPB) {
+            const int k0 = kPieceK * (q / 4) + 64 * lane;
+            if (k0 < K)
+                lds_dma16(p.xq + k0 + 16 * (q % 4), xbase + q * kPiece);
+            else
+                *reinterpret_cast<uint4*>(smem + q * kPiece + 16 * lane) = make_uint4(0, 0, 0, 0);
+        }
+    } else {
+        load_token<NORM, VPT>(p, cx, cg);
     }
     asm volatile("" ::: "memory");
 
@@ -113,7 +216,7 @@ __global__ __launch_bounds__(64 * WPB) void k_gemv1_cached(
     //    to stay inside N and stores only rows from n0 on).
     const int n0 = (blockIdx.x * WPB + wave) * RW;
     const int nb = min(n0, N - RW);
-    const uint8_t* wrow = W + (size_t)nb * RB + 16 * lane;
+    const uint8_t* wrow = p.W + (size_t)nb * RB + 16 * lane;
     auto load = [&](int i) -> uint4 {
         const int r = i / S, j = i % S;
         return kPiece * j + 16 * lane < RB
@@ -126,9 +229,16 @@ __global__ __launch_bounds__(64 * WPB) void k_gemv1_cached(
         if (u < L) wb[u] = load(u);
     asm volatile("" ::: "memory");
 
-    // 3. This wave's transfers landed (the weight loads, issued after them,
-    //    may still be in flight); then every wave's are visible.
-    wait_vmcnt_le8(L < R ? L : R);
+    // 3. QX == 0: this wave's transfers landed (the weight loads, issued after
+    //    them, may still be in flight); then every wave's are visible. QX > 0:
+    //    quantise the token into LDS, then the codes are visible.
+    float scale = 0.0f;
+    if constexpr (QX == 0) {
+        wait_vmcnt_le8(L < R ? L : R);
+    } else {
+        scale = quantise_token<NORM, VPT>(cx, cg, K, S * kPieceK / 8, p.rms_eps, smem, p.xq_out,
+                                          p.xs_out);
+    }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __syncthreads();
 
@@ -152,14 +262,15 @@ __global__ __launch_bounds__(64 * WPB) void k_gemv1_cached(
         if (i + R < L) wb[u] = load(i + R);
     }
 
-    const float sc = xs[0] * (*gamma_p);
+    if constexpr (QX == 0) scale = p.xs[0];
+    const float sc = scale * (*p.gamma);
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
         // Each lane subtracts its own share of sum x, so one reduction gives
         // sum q x.
         const int a = wave_sum_i32(acc[r] - sx);
         const int n = nb + r;
-        if (lane == r && n >= n0) store_row(y, acc_out, n, a, sc);
+        if (lane == r && n >= n0) store_row(p.y, p.acc_out, n, a, sc);
     }
 }
 
@@ -167,17 +278,15 @@ __global__ __launch_bounds__(64 * WPB) void k_gemv1_cached(
 // pieces per row (K = 4096 SP), every bound known at compile time; SP = 0:
 // any K up to kStreamMaxK, the last piece possibly partial.
 template <int SP, int R, int WPB>
-__global__ __launch_bounds__(64 * WPB) void k_gemv1_stream(
-    const int8_t* __restrict__ xq, const float* __restrict__ xs, int K_arg,
-    const uint8_t* __restrict__ W, const float* __restrict__ gamma_p, int N, float* __restrict__ y,
-    int32_t* __restrict__ acc_out) {
+__global__ __launch_bounds__(64 * WPB) void k_gemv1_stream(const Gemv1Args p) {
     constexpr int NT = 64 * WPB;
     constexpr int XPT = SP > 0 ? (SP * (kPieceK / 16) + NT - 1) / NT : 4;  // slots per thread
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ int wsum[WPB];
     const int tid = threadIdx.x, lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int K = SP > 0 ? SP * kPieceK : K_arg;
+    const int K = SP > 0 ? SP * kPieceK : p.K;
+    const int N = p.N;
     const int RB = K / 4;
     const int NP = SP > 0 ? SP : (RB + kPiece - 1) / kPiece;  // pieces per row
     const int XP = NP * (kPieceK / 16);  // 16-byte activation slots, zero past K
@@ -188,14 +297,14 @@ __global__ __launch_bounds__(64 * WPB) void k_gemv1_stream(
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
         const int t = tid + NT * i;
-        xv[i] = 16 * t < K ? *reinterpret_cast<const uint4*>(xq + 16 * t) : make_uint4(0, 0, 0, 0);
+        xv[i] = 16 * t < K ? *reinterpret_cast<const uint4*>(p.xq + 16 * t) : make_uint4(0, 0, 0, 0);
     }
     asm volatile("" ::: "memory");
 
     // 2. The wave's row (the grid's last waves repeat row N-1 and store nothing).
     const int n0 = blockIdx.x * WPB + wave;
     const int n = min(n0, N - 1);
-    const uint8_t* wrow = W + (size_t)n * RB + 16 * lane;
+    const uint8_t* wrow = p.W + (size_t)n * RB + 16 * lane;
     auto load = [&](int j) -> uint4 {
         if (SP > 0) return *reinterpret_cast<const uint4*>(wrow + kPiece * j);
         return kPiece * j + 16 * lane < RB
@@ -222,7 +331,7 @@ __global__ __launch_bounds__(64 * WPB) void k_gemv1_stream(
     }
     for (int t = tid + NT * XPT; SP == 0 && t < XP; t += NT) {  // more slots than XPT per thread
         const uint4 v =
-            16 * t < K ? *reinterpret_cast<const uint4*>(xq + 16 * t) : make_uint4(0, 0, 0, 0);
+            16 * t < K ? *reinterpret_cast<const uint4*>(p.xq + 16 * t) : make_uint4(0, 0, 0, 0);
         *reinterpret_cast<uint4*>(slot(t)) = v;
         s = bytes_sum(v, s);
     }
@@ -251,29 +360,24 @@ __global__ __launch_bounds__(64 * WPB) void k_gemv1_stream(
         }
     }
     const int a = wave_sum_i32(acc) - sx;
-    if (lane == 0 && n == n0) store_row(y, acc_out, n, a, xs[0] * (*gamma_p));
+    if (lane == 0 && n == n0) store_row(p.y, p.acc_out, n, a, p.xs[0] * (*p.gamma));
 }
 
-template <int S, int RW, int R, int WPB>
-static hipError_t launch_cached(const int8_t* xq, const float* xs, int K, const uint32_t* Wp,
-                                const float* gamma, int N, float* y, int32_t* acc,
-                                hipStream_t stream) {
-    const int waves = (N + RW - 1) / RW;
+template <int S, int RW, int R, int WPB, int QX>
+static hipError_t launch_cached(const Gemv1Args& a, hipStream_t stream) {
+    const int waves = (a.N + RW - 1) / RW;
     const int blocks = (waves + WPB - 1) / WPB;
-    hipLaunchKernelGGL((k_gemv1_cached<S, RW, R, WPB>), dim3(blocks), dim3(64 * WPB), 0, stream,
-                       xq, xs, K, reinterpret_cast<const uint8_t*>(Wp), gamma, N, y, acc);
+    hipLaunchKernelGGL((k_gemv1_cached<S, RW, R, WPB, QX>), dim3(blocks), dim3(64 * WPB), 0, stream,
+                       a);
     return hipGetLastError();
 }
 
 template <int SP, int R, int WPB>
-static hipError_t launch_stream(const int8_t* xq, const float* xs, int K, const uint32_t* Wp,
-                                const float* gamma, int N, float* y, int32_t* acc,
-                                hipStream_t stream) {
-    const int NP = (K / 4 + kPiece - 1) / kPiece;
+static hipError_t launch_stream(const Gemv1Args& a, hipStream_t stream) {
+    const int NP = (a.K / 4 + kPiece - 1) / kPiece;
     const size_t lds = (size_t)NP * kPieceK;
-    const int blocks = (N + WPB - 1) / WPB;
-    hipLaunchKernelGGL((k_gemv1_stream<SP, R, WPB>), dim3(blocks), dim3(64 * WPB), lds, stream,
-                       xq, xs, K, reinterpret_cast<const uint8_t*>(Wp), gamma, N, y, acc);
+    const int blocks = (a.N + WPB - 1) / WPB;
+    hipLaunchKernelGGL((k_gemv1_stream<SP, R, WPB>), dim3(blocks), dim3(64 * WPB), lds, stream, a);
     return hipGetLastError();
 }
 
@@ -292,24 +396,64 @@ bool gemv1_preferred(int64_t M, int64_t K) {
 hipError_t launch_gemv1(const int8_t* xq, const float* xs, int K, const uint32_t* Wp,
                         const float* gamma, int N, float* y, int32_t* acc, hipStream_t stream) {
     if (K > kStreamMaxK) return hipErrorInvalidValue;
+    Gemv1Args a{};
+    a.xq = xq;
+    a.xs = xs;
+    a.K = K;
+    a.W = reinterpret_cast<const uint8_t*>(Wp);
+    a.gamma = gamma;
+    a.N = N;
+    a.y = y;
+    a.acc_out = acc;
     if (K <= kPieceK) {
-        if (N >= 4) return launch_cached<1, 4, 4, 4>(xq, xs, K, Wp, gamma, N, y, acc, stream);
-        return launch_cached<1, 1, 1, 4>(xq, xs, K, Wp, gamma, N, y, acc, stream);
+        if (N >= 4) return launch_cached<1, 4, 4, 4, 0>(a, stream);
+        return launch_cached<1, 1, 1, 4, 0>(a, stream);
     }
     if (K <= 2 * kPieceK) {
-        if (N >= 2) return launch_cached<2, 2, 2, 4>(xq, xs, K, Wp, gamma, N, y, acc, stream);
-        return launch_cached<2, 1, 2, 4>(xq, xs, K, Wp, gamma, N, y, acc, stream);
+        if (N >= 2) return launch_cached<2, 2, 2, 4, 0>(a, stream);
+        return launch_cached<2, 1, 2, 4, 0>(a, stream);
     }
     // Whole pieces: the piece count as a template (all of a row's loads in flight).
     switch (K % kPieceK == 0 ? K / kPieceK : 0) {
-        case 3: return launch_stream<3, 3, 8>(xq, xs, K, Wp, gamma, N, y, acc, stream);
-        case 4: return launch_stream<4, 4, 8>(xq, xs, K, Wp, gamma, N, y, acc, stream);
-        case 5: return launch_stream<5, 5, 8>(xq, xs, K, Wp, gamma, N, y, acc, stream);
-        case 6: return launch_stream<6, 6, 8>(xq, xs, K, Wp, gamma, N, y, acc, stream);
-        case 7: return launch_stream<7, 7, 8>(xq, xs, K, Wp, gamma, N, y, acc, stream);
-        case 8: return launch_stream<8, 8, 8>(xq, xs, K, Wp, gamma, N, y, acc, stream);
-        default: return launch_stream<0, 8, 8>(xq, xs, K, Wp, gamma, N, y, acc, stream);
+        case 3: return launch_stream<3, 3, 8>(a, stream);
+        case 4: return launch_stream<4, 4, 8>(a, stream);
+        case 5: return launch_stream<5, 5, 8>(a, stream);
+        case 6: return launch_stream<6, 6, 8>(a, stream);
+        case 7: return launch_stream<7, 7, 8>(a, stream);
+        case 8: return launch_stream<8, 8, 8>(a, stream);
+        default: return launch_stream<0, 8, 8>(a, stream);
     }
+}
+
+// The quantising variant serves rows of one piece (K <= 4096): there the
+// token's 2K bytes per workgroup are small beside the weights, and one launch
+// measured faster than two (2560 -> 2560: 3.9 against 5.2 us per projection,
+// 3200 -> 8640: 6.1 against 7.2). With longer rows every workgroup's copy of
+// the token costs more than the second launch saves (8192 -> 28672: 18.4
+// against 17.8 us; 28672 -> 8192: 24.9 against 17.8).
+bool gemv1_quant_supported(int64_t M, int64_t K) { return M == 1 && K <= kPieceK; }
+
+hipError_t launch_gemv1_quant(const uint16_t* x, const uint16_t* gain, float rms_eps, int K,
+                              const uint32_t* Wp, const float* gamma, int N, float* y,
+                              int8_t* xq_out, float* xs_out, hipStream_t stream) {
+    if (!gemv1_quant_supported(1, K)) return hipErrorInvalidValue;
+    Gemv1Args a{};
+    a.x = x;
+    a.gain = gain;
+    a.rms_eps = rms_eps;
+    a.xq_out = xq_out;
+    a.xs_out = xs_out;
+    a.K = K;
+    a.W = reinterpret_cast<const uint8_t*>(Wp);
+    a.gamma = gamma;
+    a.N = N;
+    a.y = y;
+    if (gain) {
+        if (N >= 4) return launch_cached<1, 4, 4, 4, 2>(a, stream);
+        return launch_cached<1, 1, 1, 4, 2>(a, stream);
+    }
+    if (N >= 4) return launch_cached<1, 4, 4, 4, 1>(a, stream);
+    return launch_cached<1, 1, 1, 4, 1>(a, stream);
 }
 
 }  // namespace bl

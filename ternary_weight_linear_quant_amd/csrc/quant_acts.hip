@@ -20,49 +20,13 @@
 // 1 B written per element (8 B read for the gated variant).
 #include <type_traits>
 
+#include "act_quant.hpp"
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace bl {
 
-constexpr int kActThreads = 256;
 constexpr int kActCache = 14;  // 16-byte vectors cached per thread, at most (K <= 28672)
-
-template <typename T>
-__device__ __forceinline__ T block_reduce(T v, T* scratch, bool is_max) {
-    const int wave = threadIdx.x / kWave;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const T other = __shfl_xor(v, o, kWave);
-        v = is_max ? (v > other ? v : other) : v + other;
-    }
-    if ((threadIdx.x % kWave) == 0) scratch[wave] = v;
-    __syncthreads();
-    T r = scratch[0];
-#pragma unroll
-    for (int w = 1; w < kActThreads / kWave; ++w) r = is_max ? (r > scratch[w] ? r : scratch[w]) : r + scratch[w];
-    return r;
-}
-
-// 8 bf16 (one 16-byte vector) -> 8 int8 codes packed in a uint2.
-__device__ __forceinline__ uint2 quant8(const uint32_t dw[4], const uint32_t gw[4], bool fused,
-                                        float inv) {
-    uint32_t packed[2] = {0, 0};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            float z = bf16_to_f32((dw[i] >> (16 * h)) & 0xFFFFu);
-            if (fused) z = z * bf16_to_f32((gw[i] >> (16 * h)) & 0xFFFFu);
-            float t = __builtin_rintf(z * inv);
-            t = fminf(fmaxf(t, -127.0f), 127.0f);
-            const uint32_t b = (uint32_t)((int)t) & 0xFFu;
-            const int e = 2 * i + h;
-            packed[e / 4] |= b << (8 * (e % 4));
-        }
-    }
-    return make_uint2(packed[0], packed[1]);
-}
 
 // CACHE: 16-byte vectors cached per thread, the smallest instantiation that
 // holds the token (a larger cache holds registers the token does not use and
@@ -95,23 +59,7 @@ __global__ __launch_bounds__(kActThreads) void k_act_quant(
     }
     float amax = 0.0f;
     double ss = 0.0;
-    auto scan = [&](const uint4 d, const uint4 gv) {
-        const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
-        const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const float xf = bf16_to_f32((dw[i] >> (16 * h)) & 0xFFFFu);
-                float z = xf;
-                if (FUSED) {
-                    z = xf * bf16_to_f32((gw[i] >> (16 * h)) & 0xFFFFu);
-                    ss += (double)xf * (double)xf;
-                }
-                amax = fmaxf(amax, fabsf(z));
-            }
-        }
-    };
+    auto scan = [&](const uint4 d, const uint4 gv) { act_scan8<FUSED>(d, gv, amax, ss); };
     if (cached) {
 #pragma unroll
         for (int j = 0; j < CACHE; ++j)
@@ -119,18 +67,14 @@ __global__ __launch_bounds__(kActThreads) void k_act_quant(
     } else {
         for (int v = tid; v < nvec; v += kActThreads) scan(row[v], FUSED ? grow[v] : row[v]);
     }
-    amax = block_reduce(amax, s_max, true);
+    amax = act_reduce<float, true>(amax, s_max);
     double ss_tot = 0.0;
-    if (FUSED) ss_tot = block_reduce(ss, s_ss, false);
-    const float a = amax > 1e-5f ? amax : 1e-5f;
+    if (FUSED) ss_tot = act_reduce<double, false>(ss, s_ss);
+    const float a = act_clamped_max(amax);
     const float inv = 127.0f / a;  // correctly rounded
 
     uint2* out = reinterpret_cast<uint2*>(xq + m * K);
-    auto emit = [&](int v, const uint4 d, const uint4 gv) {
-        const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
-        const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
-        out[v] = quant8(dw, gw, FUSED, inv);
-    };
+    auto emit = [&](int v, const uint4 d, const uint4 gv) { out[v] = act_quant8<FUSED>(d, gv, inv); };
     if (cached) {
 #pragma unroll
         for (int j = 0; j < CACHE; ++j) {
@@ -140,14 +84,7 @@ __global__ __launch_bounds__(kActThreads) void k_act_quant(
     } else {
         for (int v = tid; v < nvec; v += kActThreads) emit(v, row[v], FUSED ? grow[v] : row[v]);
     }
-    if (tid == 0) {
-        if (FUSED) {
-            const double rms = sqrt(ss_tot / (double)K + (double)rms_eps);
-            scale[m] = (float)((double)a / (127.0 * rms));
-        } else {
-            scale[m] = a / 127.0f;
-        }
-    }
+    if (tid == 0) scale[m] = act_scale<FUSED>(a, ss_tot, K, rms_eps);
 }
 
 // h = bf16_rne(act(g) * u) for one 4-wide fp32 vector, as two dwords of bf16
@@ -227,10 +164,10 @@ __global__ __launch_bounds__(kActThreads) void k_glu_quant(
         for (int v = tid; v < nvec; v += kActThreads)
             scan(glu4<KIND>(grow[v], urow[v]), SUBLN ? gnv[v] : make_uint2(0u, 0u));
     }
-    amax = block_reduce(amax, s_max, true);
+    amax = act_reduce<float, true>(amax, s_max);
     double ss_tot = 0.0;
-    if (SUBLN) ss_tot = block_reduce(ss, s_ss, false);
-    const float a = amax > 1e-5f ? amax : 1e-5f;
+    if (SUBLN) ss_tot = act_reduce<double, false>(ss, s_ss);
+    const float a = act_clamped_max(amax);
     const float inv = 127.0f / a;
 
     uint32_t* out = reinterpret_cast<uint32_t*>(hq + m * K);
@@ -258,14 +195,7 @@ __global__ __launch_bounds__(kActThreads) void k_glu_quant(
         for (int v = tid; v < nvec; v += kActThreads)
             emit(v, glu4<KIND>(grow[v], urow[v]), SUBLN ? gnv[v] : make_uint2(0u, 0u));
     }
-    if (tid == 0) {
-        if (SUBLN) {
-            const double rms = sqrt(ss_tot / (double)K + (double)rms_eps);
-            scale[m] = (float)((double)a / (127.0 * rms));
-        } else {
-            scale[m] = a / 127.0f;
-        }
-    }
+    if (tid == 0) scale[m] = act_scale<SUBLN>(a, ss_tot, K, rms_eps);
 }
 
 hipError_t launch_quantize_acts(const uint16_t* x, int64_t M, int64_t K, const uint16_t* gain,

@@ -90,6 +90,24 @@ def test_invalid_arguments_rejected_before_launch(L):
     assert L.bl_bitlinear_path(X, S, 65, 64, W, G, 16, Y, None, 3, None) == E
     assert L.bl_bitlinear_path(X, S, 17, 64, W, G, 16, Y, None, 1, None) == E
     assert L.bl_bitlinear_path(X, S, 16, 16384, W, G, 16, Y, None, 1, None) == E
+    # act quant + product in one call: x, gain, W, gamma in; y, x_q, x_scale out
+    XB, GN, QO, SO = P(0x6000000), P(0x7000000), P(0x8000000), P(0x9000000)
+    assert L.bl_quant_bitlinear(None, 1, 64, None, 0.0, W, G, 16, Y, QO, SO, None) == E
+    assert L.bl_quant_bitlinear(XB, 1, 64, None, 0.0, W, G, 16, Y, None, SO, None) == E
+    assert L.bl_quant_bitlinear(XB, 1, 64, None, 0.0, W, G, 16, Y, QO, None, None) == E
+    assert L.bl_quant_bitlinear(XB, 1, 96, None, 0.0, W, G, 16, Y, QO, SO, None) == E
+    assert L.bl_quant_bitlinear(XB, 0, 64, None, 0.0, W, G, 16, Y, QO, SO, None) == E
+    assert L.bl_quant_bitlinear(XB, 1, 64, None, 0.0, W, G, 0, Y, QO, SO, None) == E
+    assert L.bl_quant_bitlinear(MIS, 1, 64, None, 0.0, W, G, 16, Y, QO, SO, None) == E
+    assert L.bl_quant_bitlinear(XB, 1, 64, None, 0.0, W, G, 16, Y, P(0x8000008), SO, None) == E
+    assert L.bl_quant_bitlinear(XB, 1, 64, GN, 0.0, W, G, 16, Y, QO, SO, None) == E    # eps
+    assert L.bl_quant_bitlinear(XB, 1, 64, MIS, 1e-5, W, G, 16, Y, QO, SO, None) == E
+    # outputs overlapping each other or an input
+    assert L.bl_quant_bitlinear(XB, 1, 64, None, 0.0, W, G, 16, Y, P(0x5000030), SO, None) == E
+    assert L.bl_quant_bitlinear(XB, 1, 64, None, 0.0, W, G, 16, Y, QO, P(0x8000030), None) == E
+    assert L.bl_quant_bitlinear(XB, 1, 64, None, 0.0, W, G, 16, P(0x6000070), QO, SO, None) == E
+    assert L.bl_quant_bitlinear(XB, 1, 64, GN, 1e-5, W, G, 16, Y, P(0x7000070), SO, None) == E
+    assert L.bl_quant_bitlinear(XB, 1, 64, None, 0.0, W, G, 16, Y, QO, P(0x4000000), None) == E
     # weight quantisation
     assert L.bl_quantize_weights(A, 16, 64, A, A, A, 8 * 15, None) == E
     assert L.bl_quantize_weights(A, 16, 64, A, A, P(0x100004), 8 * 16, None) == E
@@ -263,6 +281,9 @@ def test_no_device_status(L):
                                 P(0x130000), P(0x200000), need_dw, None) == D
     assert L.bl_ffn_step_noalloc(A, 106, 2560, A, A, A, A, 6912, A, A, 0, None, 0.0, A,
                                  None) == D
+    XB, GN, QO, SO = P(0x6000000), P(0x7000000), P(0x8000000), P(0x9000000)
+    assert L.bl_quant_bitlinear(XB, 1, 64, None, 0.0, W, G, 16, Y, QO, SO, None) == D
+    assert L.bl_quant_bitlinear(XB, 3, 8192, GN, 1e-5, W, G, 16, Y, QO, SO, None) == D
 
 
 def test_binding_fails_loudly_without_gpu():

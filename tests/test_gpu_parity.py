@@ -167,6 +167,79 @@ def test_act_quant_golden_and_zero_token():
     assert xs[-1] == np.float32(1e-5) / np.float32(127)
 
 
+# ------------------------------- act quant + product in one call ----
+
+# One launch at one token with K <= 4096 (one or several row waves, RW = 1
+# below four rows); the others take the two-call route.
+QUANT_BITLINEAR_CASES = [
+    (1, 64, 7), (1, 64, 1), (1, 320, 200), (1, 2560, 2560), (1, 3200, 8640), (1, 4096, 33),
+    (1, 4096, 3), (1, 4160, 100), (1, 8192, 300), (1, 28672, 64), (3, 2560, 257),
+]
+
+
+@pytest.mark.parametrize("M,K,N", QUANT_BITLINEAR_CASES)
+@pytest.mark.parametrize("norm", [False, True])
+def test_quant_bitlinear(M, K, N, norm):
+    """bl_quant_bitlinear: x_q and x_scale carry the bits of bl_quantize_acts,
+    y the bits of bl_bitlinear on them; against the oracle the codes and the
+    int32 sums are exact and y is within 1e-6."""
+    rng = np.random.default_rng(M * 100003 + K + N)
+    x = wl.activations(67, M, M, K)
+    gain = wl.rms_gain(67, 1, K) if norm else None
+    q = rand_codes(rng, N, K)
+    pk, g = dev_packed(oracle.pack(q)), dev_f32([0.0131])
+    xd = dev_bf16(x)
+    gd = None if gain is None else dev_bf16(gain)
+    y, xq, xs = bl.quant_bitlinear(xd, pk, g, rms_gain=gd)
+    xq2, xs2 = bl.quantize_acts(xd, gd)
+    y2, acc = bl.bitlinear(xq2, xs2, pk, g, return_acc=True)
+    assert torch.equal(xq, xq2)
+    assert torch.equal(xs.view(torch.int32), xs2.view(torch.int32))
+    assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
+    xq_ref, xs_ref = oracle.act_quant(x, gain)
+    assert np.array_equal(xq.cpu().numpy(), xq_ref)
+    xs_h = xs.cpu().numpy()
+    if norm:
+        assert np.all(np.abs(xs_h - xs_ref) <= RTOL_SCALE_FUSED * xs_ref)
+    else:
+        assert np.array_equal(xs_h, xs_ref)
+    acc_ref = oracle.int_matmul(xq_ref, q)
+    assert np.array_equal(acc.cpu().numpy(), acc_ref)
+    assert_y_close(y.cpu().numpy(), oracle.epilogue(acc_ref, xs_ref, np.float32(0.0131)),
+                   f"quant_bitlinear M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("K", [64, 4096])
+def test_quant_bitlinear_golden_ties_and_zero_token(K):
+    """The in-kernel quantiser on the golden tie tokens (each as its own
+    one-token call, mirrored in sign too) and on an all-zero token: the golden
+    codes, and the products of identity rows give codes times the scale."""
+    toks, expect = [], []
+    for vals, codes in _golden_act_cases():
+        toks.append(vals)
+        expect.append(codes)
+        toks.append([vals[0]] + [-v for v in vals[1:]])
+        expect.append([codes[0]] + [-c for c in codes[1:]])
+    toks.append([0.0])
+    expect.append([0])
+    N = 64
+    ident = dev_packed(oracle.pack(_select_codes(N, K, [(n,) for n in range(N)])))
+    one = dev_f32([1.0])
+    for vals, codes in zip(toks, expect):
+        x = np.zeros((1, K), np.float32)
+        x[0, :len(vals)] = vals
+        xb = wl.f32_to_bf16_bits(x)
+        y, xq, xs = bl.quant_bitlinear(dev_bf16(xb), ident, one)
+        xq = xq.cpu().numpy()[0]
+        assert xq[:len(codes)].tolist() == codes
+        assert (xq[len(codes):] == 0).all()
+        ref_q, ref_s = oracle.act_quant(xb)
+        assert np.array_equal(xq, ref_q[0]) and xs.cpu().numpy()[0] == ref_s[0]
+        y = y.cpu().numpy()[0]
+        assert np.array_equal(y, (xq[:N].astype(np.float32) * ref_s[0]).astype(np.float32))
+    assert ref_s[0] == np.float32(1e-5) / np.float32(127)
+
+
 # ------------------------------------------------------------ product ----
 
 def _product_case(M, K, N, seed):

@@ -144,6 +144,19 @@ def test_bitlinear_guards_and_repeats(M, K, N, path):
     assert torch.equal(y0.t.view(torch.int32), y.t.view(torch.int32))
 
 
+@pytest.mark.parametrize("M,K,N", [(1, 64, 7), (1, 320, 200), (1, 4096, 33), (1, 4096, 2),
+                                   (1, 8192, 31), (2, 320, 65)])
+@pytest.mark.parametrize("norm", [False, True])
+def test_quant_bitlinear_guards_and_repeats(M, K, N, norm):
+    rng = np.random.default_rng(M + K + N + 7)
+    x = dev_bf16(wl.activations(68, M, M, K))
+    gain = dev_bf16(wl.rms_gain(68, 0, K)) if norm else None
+    pk, g = dev_packed(oracle.pack(_codes(rng, N, K))), dev_f32([0.021])
+    y, xq, xs = Guarded((M, N), torch.float32), Guarded((M, K), torch.int8), Guarded(M, torch.float32)
+    _three_times(lambda: bl.quant_bitlinear(x, pk, g, rms_gain=gain, out=(y.t, xq.t, xs.t)),
+                 [y, xq, xs])
+
+
 def test_pair_and_other_formats_guards_and_repeats():
     M, K, N1, N2 = 4, 3200, 257, 1000
     rng = np.random.default_rng(63)
