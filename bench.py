@@ -305,7 +305,29 @@ def other_workloads(args, bl, wl, np, torch, dev, bf16_dev, capture, time_graph,
         torch.cuda.synchronize()
         gr = capture(rotation)
         st = replay_stats(gr, 20, copies * len(wprojs))
-        del gr, w, io
+        del gr
+        # The same projections from the bf16 token: bl_quant_bitlinear (one
+        # launch where K <= 4096) against bl_quantize_acts + bl_bitlinear.
+        xb = {name: bf16_dev(wl.activations(wid, i, 1, K)) for i, (name, K, N) in enumerate(wprojs)}
+
+        def rotation_q(one_call):
+            for c in range(copies):
+                for name, K, N in wprojs:
+                    xq, xs, y = io[name]
+                    if one_call:
+                        bl.quant_bitlinear(xb[name], *w[name][c], out=(y, xq, xs))
+                    else:
+                        bl.quantize_acts(xb[name], out=(xq, xs))
+                        bl.bitlinear(xq, xs, *w[name][c], out=y)
+
+        with_q = {}
+        for label, one_call in (("one_call", True), ("two_calls", False)):
+            rotation_q(one_call)
+            torch.cuda.synchronize()
+            gq = capture(lambda: rotation_q(one_call))
+            with_q[label] = replay_stats(gq, 20, copies * len(wprojs))["mean_us"]
+            del gq
+        del w, io, xb
         torch.cuda.empty_cache()
         t = st["mean_us"] * 1e-6
         packed = sum(N * K // 4 for _, K, N in wprojs) / len(wprojs)
@@ -319,6 +341,12 @@ def other_workloads(args, bl, wl, np, torch, dev, bf16_dev, capture, time_graph,
                              "traffic_unit": "HBM bytes per bl_bitlinear call",
                              "alg_bytes_per_call": round(alg)},
                 "per_launch": st,
+                "with_act_quant": {
+                    "us_per_projection": {k: round(v, 3) for k, v in with_q.items()},
+                    "packed_GBps_one_call": round(packed / (with_q["one_call"] * 1e-6) / 1e9, 1),
+                    "note": "from the bf16 token: bl_quant_bitlinear (one_call; a single launch "
+                            "where K <= 4096) against bl_quantize_acts + bl_bitlinear "
+                            "(two_calls)"},
                 "timing": "HIP graph of the rotation, HIP events on the replay stream"}
 
     small = {"single_2560_decode_M1": rotated_decode(1, SMALL_COPIES, "gemv_2560_m1")}

@@ -170,6 +170,11 @@ int bl_bitlinear_path(const int8_t* x_q, const float* x_scale, int64_t M,
                       int64_t K, const uint32_t* W_packed, const float* gamma,
                       int64_t N, float* y, int32_t* acc, int path, void* stream);
 
+/* The kernel bl_bitlinear_path(..., path, ...) runs for an M x K by N x K
+ * product: 1..4 as above (path 0 resolved by the automatic rule), or -1 when
+ * the shape or the choice is invalid. Host only, no device needed. */
+int bl_bitlinear_choice(int64_t M, int64_t K, int64_t N, int path);
+
 /* Activation quantisation (optionally fused with the preceding RMSNorm) and
  * the BitLinear product in one call: exactly bl_quantize_acts(x, M, K,
  * rms_gain, rms_eps, x_q, x_scale) followed by bl_bitlinear(x_q, x_scale, M,

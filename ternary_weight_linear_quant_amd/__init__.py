@@ -37,6 +37,7 @@ _SIGNATURES = {
     "bl_quantize_weights_workspace_bytes": ([_I, _I], _S),
     "bl_quantize_weights": ([_P, _I, _I, _P, _P, _P, _S, _P], ctypes.c_int),
     "bl_quantize_acts": ([_P, _I, _I, _P, _F, _P, _P, _P], ctypes.c_int),
+    "bl_bitlinear_choice": ([_I, _I, _I, ctypes.c_int], ctypes.c_int),
     "bl_quant_bitlinear": ([_P, _I, _I, _P, _F, _P, _P, _I, _P, _P, _P, _P], ctypes.c_int),
     "bl_bitlinear": ([_P, _P, _I, _I, _P, _P, _I, _P, _P, _P], ctypes.c_int),
     "bl_bitlinear_path": ([_P, _P, _I, _I, _P, _P, _I, _P, _P, ctypes.c_int, _P],

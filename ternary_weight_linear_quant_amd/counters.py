@@ -57,7 +57,7 @@ PHASES = {
                     "bl_ffn_relu2 at M=1 on 2560->6912->2560 weights, 40 rotated layers",
                     2 * LAYERS_2B4T,
                     "k_ffn_gemv launch (gate/up+gating, or act-quant+down)"),
-    "gemv_70b_m1": (["gemv1.hip", "common.hpp"],
+    "gemv_70b_m1": (["gemv1.hip", "act_quant.hpp", "common.hpp"],
                     "bl_bitlinear at M=1 on 8192->28672 and 28672->8192, 5 rotated copies",
                     2 * COPIES_70B, "one-token GEMV launch (k_gemv1_cached / k_gemv1_stream)"),
     "gemv_70b_m1_base3": (["gemv.hip", "common.hpp"],
@@ -71,10 +71,10 @@ PHASES = {
                        2 * COPIES_70B,
                        "bl_bitlinear call (up: k_gemm with four K groups; down: the same with "
                        "split K between k_splitk_zero and k_splitk_finalize)"),
-    "gemv_2560_m1": (["gemv1.hip", "common.hpp"],
+    "gemv_2560_m1": (["gemv1.hip", "act_quant.hpp", "common.hpp"],
                      "bl_bitlinear at M=1 on 2560->2560, 400 rotated copies",
                      COPIES_2560, "one-token GEMV launch (k_gemv1_cached)"),
-    "gemv_3b_m1": (["gemv1.hip", "gemv.hip", "common.hpp"],
+    "gemv_3b_m1": (["gemv1.hip", "act_quant.hpp", "gemv.hip", "common.hpp"],
                    "bl_bitlinear at M=1 on the 3B block (q, k, v, o 3200->3200; gate, up "
                    "3200->8640; down 8640->3200), 20 rotated layers",
                    7 * LAYERS_3B, "bl_bitlinear call (k_gemv1_cached; k_gemv on 8640->3200)"),

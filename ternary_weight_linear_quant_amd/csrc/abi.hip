@@ -131,6 +131,25 @@ int bl_quantize_acts(const uint16_t* x, int64_t M, int64_t K, const uint16_t* rm
                                                as_stream(stream)));
 }
 
+int bl_bitlinear_choice(int64_t M, int64_t K, int64_t N, int path) {
+    if (!shape_ok(M, K) || !shape_ok(N, K)) return -1;
+    const bool one_ok = bl::gemv1_supported(M, K);
+    const bool gemv_ok = bl::gemv_supported(M, K);
+    const bool wide_ok = bl::gemv_wide_supported(M, K);
+    switch (path) {
+        case 1: return gemv_ok ? 1 : -1;
+        case 2: return 2;
+        case 3: return wide_ok ? 3 : -1;
+        case 4: return one_ok ? 4 : -1;
+        case 0: break;
+        default: return -1;
+    }
+    if (bl::gemv1_preferred(M, K)) return 4;
+    if (gemv_ok) return 1;
+    if (bl::gemv_wide_preferred(M, N, K)) return 3;
+    return 2;
+}
+
 int bl_bitlinear_path(const int8_t* x_q, const float* x_scale, int64_t M, int64_t K,
                       const uint32_t* W_packed, const float* gamma, int64_t N, float* y,
                       int32_t* acc, int path, void* stream) {
@@ -148,16 +167,10 @@ int bl_bitlinear_path(const int8_t* x_q, const float* x_scale, int64_t M, int64_
                 overlaps(acc, ny, x_scale, (size_t)M * 4) ||
                 overlaps(acc, ny, W_packed, (size_t)(N * K) / 4) || overlaps(acc, ny, gamma, 4)))
         return BL_ERR_INVALID_ARG;
-    const bool one_ok = bl::gemv1_supported(M, K);
-    const bool gemv_ok = bl::gemv_supported(M, K);
-    const bool wide_ok = bl::gemv_wide_supported(M, K);
-    if ((path == 1 && !gemv_ok) || (path == 3 && !wide_ok) || (path == 4 && !one_ok))
-        return BL_ERR_INVALID_ARG;
+    const int chosen = bl_bitlinear_choice(M, K, N, path);
+    if (chosen < 0) return BL_ERR_INVALID_ARG;
     if (int s = device_status()) return s;
-    const bool use_one = path == 4 || (path == 0 && bl::gemv1_preferred(M, K));
-    const bool use_gemv = path == 1 || (path == 0 && !one_ok && gemv_ok);
-    const bool use_wide = path == 3 || (path == 0 && !one_ok && !gemv_ok &&
-                                        bl::gemv_wide_preferred(M, N, K));
+    const bool use_one = chosen == 4, use_gemv = chosen == 1, use_wide = chosen == 3;
     hipStream_t st = as_stream(stream);
     if (use_one)
         return hip_status(bl::launch_gemv1(x_q, x_scale, (int)K, W_packed, gamma, (int)N, y, acc,

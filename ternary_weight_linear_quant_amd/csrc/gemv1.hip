@@ -291,12 +291,16 @@ __global__ __launch_bounds__(64 * WPB) void k_gemv1_stream(const Gemv1Args p) {
     const int NP = SP > 0 ? SP : (RB + kPiece - 1) / kPiece;  // pieces per row
     const int XP = NP * (kPieceK / 16);  // 16-byte activation slots, zero past K
 
-    // 1. This thread's activation slots t = tid + NT i: x[16 t, +16) lands at
-    //    (4j + s) * 1024 + 16 l with t = 256 j + 4 l + s.
+    // 1. This thread's activation slots: x[16 t, +16) lands at (4j + s) * 1024
+    //    + 16 l with t = 256 j + 4 l + s. Within each run of 64 slots, lane
+    //    16 g + i takes slot 4 i + g, so that each quarter-wave writes one
+    //    s-block's 16 consecutive slots (256 bytes, every bank once); the
+    //    wave's loads still cover its 1 KB of x.
+    auto slot_of = [](int u) { return (u & ~63) + 4 * (u % 16) + (u % 64) / 16; };
     uint4 xv[XPT];
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
-        const int t = tid + NT * i;
+        const int t = slot_of(tid + NT * i);
         xv[i] = 16 * t < K ? *reinterpret_cast<const uint4*>(p.xq + 16 * t) : make_uint4(0, 0, 0, 0);
     }
     asm volatile("" ::: "memory");
@@ -323,13 +327,14 @@ __global__ __launch_bounds__(64 * WPB) void k_gemv1_stream(const Gemv1Args p) {
     int s = 0;
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
-        const int t = tid + NT * i;
+        const int t = slot_of(tid + NT * i);
         if (t < XP) {
             *reinterpret_cast<uint4*>(slot(t)) = xv[i];
             s = bytes_sum(xv[i], s);
         }
     }
-    for (int t = tid + NT * XPT; SP == 0 && t < XP; t += NT) {  // more slots than XPT per thread
+    for (int u = tid + NT * XPT; SP == 0 && u < XP; u += NT) {  // more slots than XPT per thread
+        const int t = slot_of(u);
         const uint4 v =
             16 * t < K ? *reinterpret_cast<const uint4*>(p.xq + 16 * t) : make_uint4(0, 0, 0, 0);
         *reinterpret_cast<uint4*>(slot(t)) = v;

@@ -249,6 +249,21 @@ def test_calibration_arguments(L):
     assert L.bl_calib_mfma_i8_ops(10) == 10 * 8 * 2 * 32 ** 3 * 4 * blocks
 
 
+@pytest.mark.parametrize("M,K,N,path,kernel", [
+    (1, 8192, 28672, 0, 4), (1, 28672, 8192, 0, 4), (1, 2560, 2560, 0, 4),
+    (1, 8640, 3200, 0, 1),     # one-token GEMV supported but not preferred: the GEMV
+    (1, 11008, 4096, 0, 1), (4, 2560, 6912, 0, 1), (16, 6912, 2560, 0, 1),
+    (17, 28672, 8192, 0, 3), (24, 8192, 28672, 0, 3), (48, 2560, 6912, 0, 2),
+    (64, 8192, 28672, 0, 2), (2048, 8192, 28672, 0, 2),
+    (1, 8640, 3200, 4, 4), (1, 8640, 3200, 2, 2), (16, 6912, 2560, 3, 3),
+    (1, 100, 16, 0, -1), (2, 64, 16, 4, -1), (17, 64, 16, 1, -1), (1, 64, 16, 5, -1),
+    (65, 64, 16, 3, -1), (1, 65600, 16, 4, -1),
+])
+def test_bitlinear_kernel_choice(L, M, K, N, path, kernel):
+    """The automatic rule documented for bl_bitlinear_path, on the host."""
+    assert L.bl_bitlinear_choice(M, K, N, path) == kernel
+
+
 def test_no_device_status(L):
     import torch
     if torch.cuda.device_count() > 0:
