@@ -90,6 +90,19 @@ int main() {
     EXPECT(bl_bitlinear_path(xq, xs, 1, 2560, W, g, 6912, y, acc, 5, nullptr), E);
     EXPECT(bl_bitlinear_path(xq, xs, 2, 2560, W, g, 6912, y, acc, 4, nullptr), E);
     EXPECT(bl_bitlinear_path(xq, xs, 17, 2560, W, g, 6912, y, acc, 1, nullptr), E);
+    // The kernel choice and the act quant + product in one call.
+    EXPECT(bl_bitlinear_choice(1, 8640, 3200, 0), 1);
+    EXPECT(bl_bitlinear_choice(1, 8192, 28672, 0), 4);
+    EXPECT(bl_bitlinear_choice(BIG, 2560, 6912, 0), -1);
+    EXPECT(bl_bitlinear_choice(1, BIG, 6912, 0), -1);
+    EXPECT(bl_bitlinear_choice(1, 2560, NEG, 0), -1);
+    EXPECT(bl_quant_bitlinear(x, 1, 2560, nullptr, 0.0f, W, g, 6912, y, xq, xs, nullptr), D);
+    EXPECT(bl_quant_bitlinear(x, 3, 8192, h, 1e-5f, W, g, 6912, y, xq, xs, nullptr), D);
+    EXPECT(bl_quant_bitlinear(x, BIG, 2560, nullptr, 0.0f, W, g, 6912, y, xq, xs, nullptr), E);
+    EXPECT(bl_quant_bitlinear(x, 1, 2560, nullptr, 0.0f, W, g, BIG, y, xq, xs, nullptr), E);
+    EXPECT(bl_quant_bitlinear(x, 1, 2560, h, 0.0f, W, g, 6912, y, xq, xs, nullptr), E);
+    EXPECT(bl_quant_bitlinear(x, 1, 2560, nullptr, 0.0f, W, g, 6912, y, xq, P<float>(0x6000100),
+                              nullptr), E);
     EXPECT(bl_bitlinear(xq, xs, BIG, 64, W, g, 16, y, nullptr, nullptr), E);
     EXPECT(bl_bitlinear(xq, xs, 1 << 20, 1 << 12, W, g, 1 << 20, y, nullptr, nullptr), E);
     EXPECT(bl_bitlinear(xq, xs, 1, 64, W, g, BIG, y, nullptr, nullptr), E);
