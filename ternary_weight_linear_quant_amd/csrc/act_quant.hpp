@@ -62,26 +62,45 @@ __device__ __forceinline__ void act_scan8(const uint4 d, const uint4 gv, float& 
     }
 }
 
+// Plain quantisation's max|x| on the raw bits: for finite bf16 values the
+// magnitude order is the integer order of the low 15 bits, so a packed
+// 16-bit integer max over (bits & 0x7FFF) per half finds the largest
+// magnitude exactly (one AND and one max per two values). `m2` accumulates
+// both halves; act_bits_max turns it into the float max|x|.
+typedef unsigned short act_u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void act_scan8_bits(const uint4 d, act_u16x2& m2) {
+    const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(act_u16x2, dw[i] & 0x7FFF7FFFu));
+}
+
+__device__ __forceinline__ float act_bits_max(act_u16x2 m2) {
+    return bf16_to_f32(m2.x > m2.y ? m2.x : m2.y);
+}
+
 // 8 bf16 values (one 16-byte vector) -> 8 int8 codes packed in a uint2.
+// t = z * inv in fp32 (|t| <= 127 (1 + 2^-24)^2 since |z| <= a and inv =
+// fl(127/a), so the [-127, 127] clamp can never act); pack_codes4 rounds each
+// t to nearest even with the 1.5 * 2^23 add, the result of rintf.
 template <bool NORM>
 __device__ __forceinline__ uint2 act_quant8(const uint4 d, const uint4 gv, float inv) {
     const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
     const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
-    uint32_t packed[2] = {0, 0};
+    float t[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            float z = bf16_to_f32((dw[i] >> (16 * h)) & 0xFFFFu);
-            if (NORM) z = z * bf16_to_f32((gw[i] >> (16 * h)) & 0xFFFFu);
-            float t = __builtin_rintf(z * inv);
-            t = fminf(fmaxf(t, -127.0f), 127.0f);
-            const uint32_t b = (uint32_t)((int)t) & 0xFFu;
-            const int e = 2 * i + h;
-            packed[e / 4] |= b << (8 * (e % 4));
+        // bf16 pair -> fp32: the low half shifted up, the high half masked.
+        float z0 = __uint_as_float(dw[i] << 16), z1 = __uint_as_float(dw[i] & 0xFFFF0000u);
+        if (NORM) {
+            z0 = z0 * __uint_as_float(gw[i] << 16);
+            z1 = z1 * __uint_as_float(gw[i] & 0xFFFF0000u);
         }
+        t[2 * i] = z0 * inv;
+        t[2 * i + 1] = z1 * inv;
     }
-    return make_uint2(packed[0], packed[1]);
+    return make_uint2(pack_codes4(t[0], t[1], t[2], t[3]), pack_codes4(t[4], t[5], t[6], t[7]));
 }
 
 // a = max(max|z|, 1e-5); the codes' multiplier 127/a (correctly rounded).

@@ -32,13 +32,14 @@
 // Activations: one token of K int8 values, staged in LDS so that lane l's 64
 // bytes for piece j lie at (4j + s) * 1024 + 16 l, s = 0..3 (conflict-free
 // 16-byte reads; zeros past K). Two variants:
-//   k_gemv1_cached  K <= 4096 * S (S = 1 or 2 pieces per row): the block is
-//                   loaded by direct global-to-LDS transfers and each lane
-//                   keeps its 64 * S bytes in registers; every wave sums its
-//                   own lanes' bytes (no extra barrier);
-//   k_gemv1_stream  longer rows (one row per wave): the block goes through
-//                   registers, summed on the way, one barrier; each piece
-//                   reads its activations from LDS.
+//   k_gemv1_cached  K <= 4096 * S (S = 1 or 2 pieces per row, the second
+//                   partial): the block is loaded by direct global-to-LDS
+//                   transfers and each lane keeps its 64 * S bytes in
+//                   registers; every wave sums its own lanes' bytes (no
+//                   extra barrier);
+//   k_gemv1_stream  whole pieces, or more than two (one row per wave): the
+//                   block goes through registers, summed on the way, one
+//                   barrier; each piece reads its activations from LDS.
 // Waves are independent after the staging barrier (no barrier at the end).
 //
 // Quantising variant of k_gemv1_cached (QX > 0, rows of one piece): the input
@@ -135,11 +136,17 @@ __device__ __forceinline__ float quantise_token(const uint4 (&cx)[VPT], const ui
     const int nvec = K / 8;
     float amax = 0.0f;
     double ss = 0.0;
+    act_u16x2 m2 = {0, 0};  // plain: max|x| on the raw bits
     if (tid < kActThreads) {
 #pragma unroll
-        for (int j = 0; j < VPT; ++j)
-            if (tid + kActThreads * j < nvec) act_scan8<NORM>(cx[j], cg[j], amax, ss);
+        for (int j = 0; j < VPT; ++j) {
+            if (tid + kActThreads * j < nvec) {
+                if constexpr (NORM) act_scan8<true>(cx[j], cg[j], amax, ss);
+                else act_scan8_bits(cx[j], m2);
+            }
+        }
     }
+    if constexpr (!NORM) amax = act_bits_max(m2);
     amax = act_reduce<float, true>(amax, s_max);
     double ss_tot = 0.0;
     if (NORM) ss_tot = act_reduce<double, false>(ss, s_ss);
@@ -395,9 +402,14 @@ bool gemv1_preferred(int64_t M, int64_t K) {
     return gemv1_supported(M, K) && (K <= 2 * kPieceK || K % kPieceK == 0);
 }
 
-// Shapes measured on 8192 -> 28672 (two pieces per row: two rows per wave,
-// two loads in flight, 4-wave workgroups) and 28672 -> 8192 (seven pieces:
-// one row per wave, 8-wave workgroups).
+// Launch shapes, measured on the 70B rows and on 8192-row matrices of 12288,
+// 16384, 11008 and 32768 columns (5 rotated weight copies): whole pieces go to
+// the stream kernel with two pieces in flight per lane, 8-wave workgroups
+// (8192 -> 28672: 11.9 us against 12.9 for the cached kernel; 16384: 6.7
+// against 7.1 with all four pieces in flight), except seven pieces, where
+// 16-wave workgroups take two per CU (28672 -> 8192: 10.7 against 12.0 us),
+// and eight, where all eight in flight stays ahead (13.2 against 14.0). Rows of
+// one piece, and partial second pieces, keep the cached kernel.
 hipError_t launch_gemv1(const int8_t* xq, const float* xs, int K, const uint32_t* Wp,
                         const float* gamma, int N, float* y, int32_t* acc, hipStream_t stream) {
     if (K > kStreamMaxK) return hipErrorInvalidValue;
@@ -414,19 +426,20 @@ hipError_t launch_gemv1(const int8_t* xq, const float* xs, int K, const uint32_t
         if (N >= 4) return launch_cached<1, 4, 4, 4, 0>(a, stream);
         return launch_cached<1, 1, 1, 4, 0>(a, stream);
     }
-    if (K <= 2 * kPieceK) {
+    if (K < 2 * kPieceK) {
         if (N >= 2) return launch_cached<2, 2, 2, 4, 0>(a, stream);
         return launch_cached<2, 1, 2, 4, 0>(a, stream);
     }
-    // Whole pieces: the piece count as a template (all of a row's loads in flight).
+    // Whole pieces: the piece count as a template.
     switch (K % kPieceK == 0 ? K / kPieceK : 0) {
-        case 3: return launch_stream<3, 3, 8>(a, stream);
-        case 4: return launch_stream<4, 4, 8>(a, stream);
-        case 5: return launch_stream<5, 5, 8>(a, stream);
-        case 6: return launch_stream<6, 6, 8>(a, stream);
-        case 7: return launch_stream<7, 7, 8>(a, stream);
+        case 2: return launch_stream<2, 2, 8>(a, stream);
+        case 3: return launch_stream<3, 2, 8>(a, stream);
+        case 4: return launch_stream<4, 2, 8>(a, stream);
+        case 5: return launch_stream<5, 2, 8>(a, stream);
+        case 6: return launch_stream<6, 2, 8>(a, stream);
+        case 7: return launch_stream<7, 2, 16>(a, stream);
         case 8: return launch_stream<8, 8, 8>(a, stream);
-        default: return launch_stream<0, 8, 8>(a, stream);
+        default: return launch_stream<0, 2, 8>(a, stream);
     }
 }
 

@@ -59,7 +59,11 @@ __global__ __launch_bounds__(kActThreads) void k_act_quant(
     }
     float amax = 0.0f;
     double ss = 0.0;
-    auto scan = [&](const uint4 d, const uint4 gv) { act_scan8<FUSED>(d, gv, amax, ss); };
+    act_u16x2 m2 = {0, 0};  // plain: max|x| on the raw bits
+    auto scan = [&](const uint4 d, const uint4 gv) {
+        if constexpr (FUSED) act_scan8<true>(d, gv, amax, ss);
+        else act_scan8_bits(d, m2);
+    };
     if (cached) {
 #pragma unroll
         for (int j = 0; j < CACHE; ++j)
@@ -67,6 +71,7 @@ __global__ __launch_bounds__(kActThreads) void k_act_quant(
     } else {
         for (int v = tid; v < nvec; v += kActThreads) scan(row[v], FUSED ? grow[v] : row[v]);
     }
+    if constexpr (!FUSED) amax = act_bits_max(m2);
     amax = act_reduce<float, true>(amax, s_max);
     double ss_tot = 0.0;
     if (FUSED) ss_tot = act_reduce<double, false>(ss, s_ss);

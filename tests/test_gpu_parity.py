@@ -282,9 +282,13 @@ def test_gemv_parity(M, K, N):
 # when N is smaller), longer rows the LDS-streamed one (one row per wave);
 # K = 4160 / 8256 / 2560 / 6912 end in a partial piece, K = 65536 stages
 # more activation slots than a thread holds across the weight issue.
+# Every launch shape of the one-token GEMV: one piece (four rows or one row
+# per wave), two pieces (partial, whole), three to eight whole pieces, and a
+# partial last piece past two.
 ONE_TOKEN_CASES = [(64, 1), (320, 200), (4096, 3), (4096, 4), (2560, 6912), (4160, 1),
-                   (4160, 7), (8192, 2049), (6912, 2560), (8256, 33), (12288, 1),
-                   (28672, 40), (65536, 5), (3200, 3203)]
+                   (4160, 7), (8192, 2049), (8192, 1), (6912, 2560), (8256, 33), (12288, 1),
+                   (16384, 17), (20480, 9), (24576, 3), (28672, 40), (28672, 8193),
+                   (32768, 15), (65536, 5), (3200, 3203), (11008, 100)]
 
 
 @pytest.mark.parametrize("K,N", ONE_TOKEN_CASES)
