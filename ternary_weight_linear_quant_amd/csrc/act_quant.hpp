@@ -19,13 +19,13 @@ namespace bl {
 
 constexpr int kActThreads = 256;  // threads that hold one token's values
 
-// Reduction over the first kActThreads threads of the workgroup, in a fixed
-// order: a butterfly within each wave, then waves 0, 1, 2, 3 in turn (for the
-// fp64 sum of squares the order decides the rounding). Every thread of the
-// workgroup calls it, since it holds a barrier; threads past kActThreads pass
-// a neutral value and are left out. The result reaches every thread.
-// `scratch` holds kActThreads / 64 entries.
-template <typename T, bool MAX>
+// Reduction over the first NW waves of the workgroup, in a fixed order: a
+// butterfly within each wave, then waves 0, 1, ..., NW-1 in turn (for the fp64
+// sum of squares the order decides the rounding). Every thread of the
+// workgroup calls it, since it holds a barrier; threads of later waves pass a
+// neutral value and are left out. The result reaches every thread. `scratch`
+// holds NW entries.
+template <typename T, bool MAX, int NW = kActThreads / kWave>
 __device__ __forceinline__ T act_reduce(T v, T* scratch) {
     const int wave = threadIdx.x / kWave;
 #pragma unroll
@@ -33,11 +33,11 @@ __device__ __forceinline__ T act_reduce(T v, T* scratch) {
         const T other = __shfl_xor(v, o, kWave);
         v = MAX ? (v > other ? v : other) : v + other;
     }
-    if ((threadIdx.x % kWave) == 0 && wave < kActThreads / kWave) scratch[wave] = v;
+    if ((threadIdx.x % kWave) == 0 && wave < NW) scratch[wave] = v;
     __syncthreads();
     T r = scratch[0];
 #pragma unroll
-    for (int w = 1; w < kActThreads / kWave; ++w) r = MAX ? (r > scratch[w] ? r : scratch[w]) : r + scratch[w];
+    for (int w = 1; w < NW; ++w) r = MAX ? (r > scratch[w] ? r : scratch[w]) : r + scratch[w];
     return r;
 }
 

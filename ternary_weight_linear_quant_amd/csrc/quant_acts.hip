@@ -31,26 +31,30 @@ constexpr int kActCache = 14;  // 16-byte vectors cached per thread, at most (K 
 // CACHE: 16-byte vectors cached per thread, the smallest instantiation that
 // holds the token (a larger cache holds registers the token does not use and
 // lowers the workgroups a CU keeps in flight); tokens longer than
-// kActCache vectors per thread take the uncached two-pass loop.
-template <bool FUSED, int CACHE>
-__global__ __launch_bounds__(kActThreads) void k_act_quant(
+// kActCache vectors per thread take the uncached two-pass loop. NT: threads
+// per token (256, or 1024 for a few long tokens, where one workgroup per
+// token leaves most CUs idle and the per-thread chain of loads, scan and
+// codes is the call's latency).
+template <bool FUSED, int CACHE, int NT>
+__global__ __launch_bounds__(NT) void k_act_quant(
     const uint16_t* __restrict__ x, int64_t K, const uint16_t* __restrict__ gain,
     float rms_eps, int8_t* __restrict__ xq, float* __restrict__ scale) {
-    __shared__ float s_max[kActThreads / kWave];
-    __shared__ double s_ss[kActThreads / kWave];
+    constexpr int NW = NT / kWave;
+    __shared__ float s_max[NW];
+    __shared__ double s_ss[NW];
     const int64_t m = blockIdx.x;
     const uint4* row = reinterpret_cast<const uint4*>(x + m * K);
     const uint4* grow = reinterpret_cast<const uint4*>(gain);
     const int tid = threadIdx.x;
     const int nvec = (int)(K / 8);  // 8 bf16 per 16 bytes
-    const bool cached = nvec <= CACHE * kActThreads;
+    const bool cached = nvec <= CACHE * NT;
 
     uint4 cx[CACHE];
     uint4 cg[FUSED ? CACHE : 1];
     if (cached) {
 #pragma unroll
         for (int j = 0; j < CACHE; ++j) {
-            const int v = tid + kActThreads * j;
+            const int v = tid + NT * j;
             if (v < nvec) {
                 cx[j] = row[v];
                 if (FUSED) cg[j] = grow[v];
@@ -67,14 +71,14 @@ __global__ __launch_bounds__(kActThreads) void k_act_quant(
     if (cached) {
 #pragma unroll
         for (int j = 0; j < CACHE; ++j)
-            if (tid + kActThreads * j < nvec) scan(cx[j], FUSED ? cg[j] : cx[j]);
+            if (tid + NT * j < nvec) scan(cx[j], FUSED ? cg[j] : cx[j]);
     } else {
-        for (int v = tid; v < nvec; v += kActThreads) scan(row[v], FUSED ? grow[v] : row[v]);
+        for (int v = tid; v < nvec; v += NT) scan(row[v], FUSED ? grow[v] : row[v]);
     }
     if constexpr (!FUSED) amax = act_bits_max(m2);
-    amax = act_reduce<float, true>(amax, s_max);
+    amax = act_reduce<float, true, NW>(amax, s_max);
     double ss_tot = 0.0;
-    if (FUSED) ss_tot = act_reduce<double, false>(ss, s_ss);
+    if (FUSED) ss_tot = act_reduce<double, false, NW>(ss, s_ss);
     const float a = act_clamped_max(amax);
     const float inv = 127.0f / a;  // correctly rounded
 
@@ -83,11 +87,11 @@ __global__ __launch_bounds__(kActThreads) void k_act_quant(
     if (cached) {
 #pragma unroll
         for (int j = 0; j < CACHE; ++j) {
-            const int v = tid + kActThreads * j;
+            const int v = tid + NT * j;
             if (v < nvec) emit(v, cx[j], FUSED ? cg[j] : cx[j]);
         }
     } else {
-        for (int v = tid; v < nvec; v += kActThreads) emit(v, row[v], FUSED ? grow[v] : row[v]);
+        for (int v = tid; v < nvec; v += NT) emit(v, row[v], FUSED ? grow[v] : row[v]);
     }
     if (tid == 0) scale[m] = act_scale<FUSED>(a, ss_tot, K, rms_eps);
 }
@@ -205,25 +209,33 @@ __global__ __launch_bounds__(kActThreads) void k_glu_quant(
 
 hipError_t launch_quantize_acts(const uint16_t* x, int64_t M, int64_t K, const uint16_t* gain,
                                 float rms_eps, int8_t* xq, float* scale, hipStream_t stream) {
-    const int64_t per = (K / 8 + kActThreads - 1) / kActThreads;  // vectors per thread
-    auto go = [&](auto fused, auto cache) {
-        hipLaunchKernelGGL((k_act_quant<decltype(fused)::value, decltype(cache)::value>),
-                           dim3((unsigned)M), dim3(kActThreads), 0, stream, x, K, gain, rms_eps,
-                           xq, scale);
+    // 1024 threads per token for fewer than 128 tokens of more than 4096
+    // values; rows of up to 4096 keep 256 (the one-token GEMV's own quantiser
+    // shares that assignment and order, so both give the same scale bits).
+    const bool wide = M < 128 && K > 4096;
+    const int nt = wide ? 1024 : kActThreads;
+    const int64_t per = (K / 8 + nt - 1) / nt;  // vectors per thread
+    auto go = [&](auto fused, auto cache, auto threads) {
+        hipLaunchKernelGGL((k_act_quant<decltype(fused)::value, decltype(cache)::value,
+                                        decltype(threads)::value>),
+                           dim3((unsigned)M), dim3(decltype(threads)::value), 0, stream, x, K,
+                           gain, rms_eps, xq, scale);
     };
-    using T = std::true_type;
-    using F = std::false_type;
-    if (gain) {
-        if (per <= 2) go(T(), std::integral_constant<int, 2>());
-        else if (per <= 4) go(T(), std::integral_constant<int, 4>());
-        else if (per <= 8) go(T(), std::integral_constant<int, 8>());
-        else go(T(), std::integral_constant<int, kActCache>());
-    } else {
-        if (per <= 2) go(F(), std::integral_constant<int, 2>());
-        else if (per <= 4) go(F(), std::integral_constant<int, 4>());
-        else if (per <= 8) go(F(), std::integral_constant<int, 8>());
-        else go(F(), std::integral_constant<int, kActCache>());
-    }
+    // At 1024 threads a cache of 8 vectors is the largest that fits without
+    // spilling (longer tokens take the two-pass loop).
+    auto pick = [&](auto fused, auto threads) {
+        constexpr int kMax = decltype(threads)::value == kActThreads ? kActCache : 8;
+        if (per <= 2) go(fused, std::integral_constant<int, 2>(), threads);
+        else if (per <= 4) go(fused, std::integral_constant<int, 4>(), threads);
+        else if (per <= 8 || kMax == 8) go(fused, std::integral_constant<int, 8>(), threads);
+        else go(fused, std::integral_constant<int, kMax>(), threads);
+    };
+    auto by_threads = [&](auto fused) {
+        if (wide) pick(fused, std::integral_constant<int, 1024>());
+        else pick(fused, std::integral_constant<int, kActThreads>());
+    };
+    if (gain) by_threads(std::true_type());
+    else by_threads(std::false_type());
     return hipGetLastError();
 }
 
