@@ -1168,6 +1168,39 @@ def test_base3_weights_parity(M, K, N):
     assert torch.equal(acc, acc2) and torch.equal(y.view(torch.int32), y2.view(torch.int32))
 
 
+# Base-3 rows at one token: short rows, K not a multiple of 5 or 16 bytes of
+# row, 8192 and 28672 columns, and long rows.
+BASE3_ONE_TOKEN_CASES = [(64, 7), (320, 200), (4160, 33), (8192, 257), (8256, 9), (12800, 3),
+                         (28672, 65), (61440, 17), (61504, 5)]
+
+
+@pytest.mark.parametrize("K,N", BASE3_ONE_TOKEN_CASES)
+def test_base3_one_token_parity(K, N):
+    """bl_bitlinear_base3 at one token against the oracle (int32 sums exact, y
+    within 1e-6) and against the 2-bit path's bits, on random codes with an
+    all-zero, an all-(+1) and an all-(-1) row, for the extreme +127 token, a
+    full-range token (-128 included) and a quantised one."""
+    rng = np.random.default_rng(K * 7 + N)
+    q = rand_codes(rng, N, K)
+    q[0] = 0
+    q[min(1, N - 1)] = 1
+    q[-1] = -1
+    pk = dev_packed(oracle.pack(q))
+    w3 = bl.pack_base3(pk, K)
+    assert np.array_equal(w3.cpu().numpy(), oracle.pack_base3(q))
+    xq_h, xs_h = oracle.act_quant(wl.activations(63, 1, 1, K))
+    tokens = [np.full((1, K), 127, np.int8), rng.integers(-128, 128, (1, K)).astype(np.int8), xq_h]
+    g = dev_f32([0.0137])
+    for t in tokens:
+        xd, xsd = torch.from_numpy(t).to(DEV), dev_f32(xs_h)
+        y, acc = bl.bitlinear_base3(xd, xsd, w3, g, return_acc=True)
+        y_ref, acc_ref = oracle.bitlinear(t, xs_h, q, np.float32(0.0137))
+        assert np.array_equal(acc.cpu().numpy(), acc_ref)
+        assert_y_close(y.cpu().numpy(), y_ref, f"base3 one token K={K}")
+        y2, acc2 = bl.bitlinear(xd, xsd, pk, g, return_acc=True)
+        assert torch.equal(acc, acc2) and torch.equal(y.view(torch.int32), y2.view(torch.int32))
+
+
 @pytest.mark.parametrize("idx", [0, 1])
 def test_other_formats_70b_full_size(idx):
     """70B-class matrices at full size, M = 1: base 3 repacked from the
