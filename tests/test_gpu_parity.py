@@ -1168,6 +1168,35 @@ def test_base3_weights_parity(M, K, N):
     assert torch.equal(acc, acc2) and torch.equal(y.view(torch.int32), y2.view(torch.int32))
 
 
+# 1-bit rows at one token (the streaming kernel): rows of one piece or less,
+# whole pieces, partial last pieces, rows padded to 16 bytes, the longest row.
+BINARY_ONE_TOKEN_CASES = [(64, 7), (128, 1), (320, 200), (4160, 33), (8192, 257), (8256, 9),
+                          (16384, 3), (28672, 65), (65536, 5)]
+
+
+@pytest.mark.parametrize("K,N", BINARY_ONE_TOKEN_CASES)
+def test_binary_one_token_parity(K, N):
+    """bl_bitlinear_binary at one token against the oracle (int32 sums exact, y
+    within 1e-6) on random +-1 codes with an all-(+1) and an all-(-1) row, for
+    the extreme +127 and -128 tokens, a full-range token and a quantised one."""
+    rng = np.random.default_rng(K * 11 + N)
+    q = np.where(rng.random((N, K)) < 0.5, -1, 1).astype(np.int8)
+    q[0] = 1
+    q[-1] = -1
+    packed = oracle.pack_binary(q)
+    bits = torch.from_numpy(packed.view(np.int32)).to(DEV)
+    xq_h, xs_h = oracle.act_quant(wl.activations(64, 1, 1, K))
+    tokens = [np.full((1, K), 127, np.int8), np.full((1, K), -128, np.int8),
+              rng.integers(-128, 128, (1, K)).astype(np.int8), xq_h]
+    g = dev_f32([0.0211])
+    for t in tokens:
+        y, acc = bl.bitlinear_binary(torch.from_numpy(t).to(DEV), dev_f32(xs_h), bits, g,
+                                     return_acc=True)
+        y_ref, acc_ref = oracle.bitlinear(t, xs_h, q, np.float32(0.0211))
+        assert np.array_equal(acc.cpu().numpy(), acc_ref)
+        assert_y_close(y.cpu().numpy(), y_ref, f"binary one token K={K}")
+
+
 # Base-3 rows at one token: short rows, K not a multiple of 5 or 16 bytes of
 # row, 8192 and 28672 columns, and long rows.
 BASE3_ONE_TOKEN_CASES = [(64, 7), (320, 200), (4160, 33), (8192, 257), (8256, 9), (12800, 3),

@@ -178,6 +178,22 @@ def test_pair_and_other_formats_guards_and_repeats():
         _three_times(lambda: fn(xq, xs, w, gg, out=y.t, acc_out=acc.t), [y, acc])
 
 
+@pytest.mark.parametrize("K,N", [(64, 3), (8256, 9), (28672, 17)])
+def test_one_token_formats_guards_and_repeats(K, N):
+    rng = np.random.default_rng(K + N)
+    xq_h, xs_h = oracle.act_quant(wl.activations(69, 0, 1, K))
+    xq, xs = torch.from_numpy(xq_h).to(DEV), dev_f32(xs_h)
+    qb = np.where(rng.random((N, K)) < 0.5, -1, 1).astype(np.int8)
+    bits = torch.from_numpy(oracle.pack_binary(qb).view(np.int32)).to(DEV)
+    q3 = _codes(rng, N, K)
+    w3 = bl.pack_base3(dev_packed(oracle.pack(q3)), K)
+    g = dev_f32([0.03])
+    for fn, w in ((bl.bitlinear_binary, bits), (bl.bitlinear_base3, w3)):
+        y = Guarded((1, N), torch.float32)
+        acc = Guarded((1, N), torch.int32)
+        _three_times(lambda: fn(xq, xs, w, g, out=y.t, acc_out=acc.t), [y, acc])
+
+
 # ---------------------------------------------------------- glue, FFN ----
 
 @pytest.mark.parametrize("kind", ["relu2", "swiglu"])
