@@ -59,7 +59,7 @@ PHASES = {
                     "k_ffn_gemv launch (gate/up+gating, or act-quant+down)"),
     "gemv_70b_m1": (["gemv1.hip", "act_quant.hpp", "common.hpp"],
                     "bl_bitlinear at M=1 on 8192->28672 and 28672->8192, 5 rotated copies",
-                    2 * COPIES_70B, "one-token GEMV launch (k_gemv1_stream)"),
+                    2 * COPIES_70B, "one-token GEMV launch (k_gemv1_rows / k_gemv1_stream)"),
     "gemv_70b_m1_base3": (["gemv.hip", "common.hpp"],
                           "bl_bitlinear_base3 at M=1 on the 70B shapes, 5 rotated copies",
                           2 * COPIES_70B, "k_gemv launch (five ternary weights per byte)"),

@@ -31,13 +31,17 @@
 //
 // Activations: one token of K int8 values, staged in LDS so that lane l's 64
 // bytes for piece j lie at (4j + s) * 1024 + 16 l, s = 0..3 (conflict-free
-// 16-byte reads; zeros past K). Two variants:
+// 16-byte reads; zeros past K). Three variants:
 //   k_gemv1_cached  K <= 4096 * S (S = 1 or 2 pieces per row, the second
 //                   partial): the block is loaded by direct global-to-LDS
 //                   transfers and each lane keeps its 64 * S bytes in
 //                   registers; every wave sums its own lanes' bytes (no
 //                   extra barrier);
-//   k_gemv1_stream  whole pieces, or more than two (one row per wave): the
+//   k_gemv1_rows    two to four whole pieces, several rows per wave: staged
+//                   through registers and summed per workgroup before one
+//                   barrier, then kept in registers while the wave streams
+//                   its rows through one ring;
+//   k_gemv1_stream  other rows longer than one piece (one row per wave): the
 //                   block goes through registers, summed on the way, one
 //                   barrier; each piece reads its activations from LDS.
 // Waves are independent after the staging barrier (no barrier at the end).
@@ -375,12 +379,108 @@ __global__ __launch_bounds__(64 * WPB) void k_gemv1_stream(const Gemv1Args p) {
     if (lane == 0 && n == n0) store_row(p.y, p.acc_out, n, a, p.xs[0] * (*p.gamma));
 }
 
+// Rows of SP whole pieces (K = 4096 SP, SP small), RW rows per wave: the
+// stream kernel's staging (through registers, sum x reduced per workgroup, one
+// barrier), after which each lane keeps its SP x 64 bytes of activations in
+// registers and the wave streams its RW rows through one ring of R pieces, so
+// the staging, the barrier and the sum-x reduction are paid once per RW rows
+// and no LDS is read per piece. Requires N >= RW.
+template <int SP, int RW, int R, int WPB>
+__global__ __launch_bounds__(64 * WPB) void k_gemv1_rows(const Gemv1Args p) {
+    constexpr int NT = 64 * WPB;
+    constexpr int K = SP * kPieceK;
+    constexpr int RB = K / 4;
+    constexpr int XP = SP * (kPieceK / 16);            // 16-byte activation slots
+    constexpr int XPT = (XP + NT - 1) / NT;            // slots per thread
+    constexpr int L = SP * RW;                         // pieces per wave
+    __shared__ __align__(16) uint8_t smem[SP * kPieceK];
+    __shared__ int wsum[WPB];
+    const int tid = threadIdx.x, lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int N = p.N;
+
+    // 1. Activation slots as in k_gemv1_stream (the same quarter-wave order).
+    auto slot_of = [](int u) { return (u & ~63) + 4 * (u % 16) + (u % 64) / 16; };
+    auto slot = [&](int t) { return smem + (4 * (t / 256) + t % 4) * kPiece + 16 * ((t / 4) % 64); };
+    uint4 xv[XPT];
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+        const int t = slot_of(tid + NT * i);
+        xv[i] = t < XP ? *reinterpret_cast<const uint4*>(p.xq + 16 * t) : make_uint4(0, 0, 0, 0);
+    }
+    asm volatile("" ::: "memory");
+
+    // 2. The wave's rows nb .. nb+RW-1 (the last wave of the grid shifts back
+    //    to stay inside N and stores only rows from n0 on); the first R pieces.
+    const int n0 = (blockIdx.x * WPB + wave) * RW;
+    const int nb = min(n0, N - RW);
+    const uint8_t* wrow = p.W + (size_t)nb * RB + 16 * lane;
+    auto load = [&](int i) -> uint4 {
+        return *reinterpret_cast<const uint4*>(wrow + (size_t)(i / SP) * RB + kPiece * (i % SP));
+    };
+    uint4 wb[R];
+#pragma unroll
+    for (int u = 0; u < R; ++u)
+        if (u < L) wb[u] = load(u);
+    asm volatile("" ::: "memory");
+
+    // 3. Stage and sum the activations; one barrier.
+    wait_vmcnt_le8(L < R ? L : R);
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+        const int t = slot_of(tid + NT * i);
+        if (t < XP) {
+            *reinterpret_cast<uint4*>(slot(t)) = xv[i];
+            s = bytes_sum(xv[i], s);
+        }
+    }
+    s = wave_sum_i32(s);
+    if (lane == 0) wsum[wave] = s;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+    int sx = 0;
+#pragma unroll
+    for (int w = 0; w < WPB; ++w) sx += wsum[w];
+    uint4 act[SP][4];
+#pragma unroll
+    for (int j = 0; j < SP; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            act[j][q] = *reinterpret_cast<const uint4*>(smem + (4 * j + q) * kPiece + 16 * lane);
+
+    // 4. The wave's L pieces through a ring of R; each row's sum stored when
+    //    its last piece is in.
+    const float sc = p.xs[0] * (*p.gamma);
+    int acc = 0;
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+        const int u = i % R;
+        acc += piece_dot(wb[u], act[i % SP]);
+        if (i + R < L) wb[u] = load(i + R);
+        if (i % SP == SP - 1) {
+            const int a = wave_sum_i32(acc) - sx;
+            const int n = nb + i / SP;
+            if (lane == 0 && n >= n0) store_row(p.y, p.acc_out, n, a, sc);
+            acc = 0;
+        }
+    }
+}
+
 template <int S, int RW, int R, int WPB, int QX>
 static hipError_t launch_cached(const Gemv1Args& a, hipStream_t stream) {
     const int waves = (a.N + RW - 1) / RW;
     const int blocks = (waves + WPB - 1) / WPB;
     hipLaunchKernelGGL((k_gemv1_cached<S, RW, R, WPB, QX>), dim3(blocks), dim3(64 * WPB), 0, stream,
                        a);
+    return hipGetLastError();
+}
+
+template <int SP, int RW, int R, int WPB>
+static hipError_t launch_rows(const Gemv1Args& a, hipStream_t stream) {
+    const int waves = (a.N + RW - 1) / RW;
+    const int blocks = (waves + WPB - 1) / WPB;
+    hipLaunchKernelGGL((k_gemv1_rows<SP, RW, R, WPB>), dim3(blocks), dim3(64 * WPB), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -402,14 +502,14 @@ bool gemv1_preferred(int64_t M, int64_t K) {
     return gemv1_supported(M, K) && (K <= 2 * kPieceK || K % kPieceK == 0);
 }
 
-// Launch shapes, measured on the 70B rows and on 8192-row matrices of 12288,
-// 16384, 11008 and 32768 columns (5 rotated weight copies): whole pieces go to
-// the stream kernel with two pieces in flight per lane, 8-wave workgroups
-// (8192 -> 28672: 11.9 us against 12.9 for the cached kernel; 16384: 6.7
-// against 7.1 with all four pieces in flight), except seven pieces, where
-// 16-wave workgroups take two per CU (28672 -> 8192: 10.7 against 12.0 us),
-// and eight, where all eight in flight stays ahead (13.2 against 14.0). Rows of
-// one piece, and partial second pieces, keep the cached kernel.
+// Launch shapes, measured (probe copies over ten distinct weight buffers) on
+// the 70B rows and on 8192-row matrices of 12288, 16384, 11008 and 32768
+// columns. Two to four whole pieces: several rows per wave with the token in
+// registers (8192 -> 28672: 11.7 us against 13.2 for one row per wave and 13.5
+// for the cached kernel; 12288: 6.1 against 6.4; 16384: 7.5 against 7.7).
+// Seven pieces: one row per wave, 16-wave workgroups, two pieces in flight
+// (28672 -> 8192: 10.7 against 12.0 us for all seven in flight); eight: all in
+// flight. Rows of one piece, and partial second pieces, keep the cached kernel.
 hipError_t launch_gemv1(const int8_t* xq, const float* xs, int K, const uint32_t* Wp,
                         const float* gamma, int N, float* y, int32_t* acc, hipStream_t stream) {
     if (K > kStreamMaxK) return hipErrorInvalidValue;
@@ -432,9 +532,15 @@ hipError_t launch_gemv1(const int8_t* xq, const float* xs, int K, const uint32_t
     }
     // Whole pieces: the piece count as a template.
     switch (K % kPieceK == 0 ? K / kPieceK : 0) {
-        case 2: return launch_stream<2, 2, 8>(a, stream);
-        case 3: return launch_stream<3, 2, 8>(a, stream);
-        case 4: return launch_stream<4, 2, 8>(a, stream);
+        case 2:
+            if (N >= 4) return launch_rows<2, 4, 4, 4>(a, stream);
+            return launch_stream<2, 2, 8>(a, stream);
+        case 3:
+            if (N >= 4) return launch_rows<3, 4, 4, 4>(a, stream);
+            return launch_stream<3, 2, 8>(a, stream);
+        case 4:
+            if (N >= 2) return launch_rows<4, 2, 4, 8>(a, stream);
+            return launch_stream<4, 2, 8>(a, stream);
         case 5: return launch_stream<5, 2, 8>(a, stream);
         case 6: return launch_stream<6, 2, 8>(a, stream);
         case 7: return launch_stream<7, 2, 16>(a, stream);

@@ -286,9 +286,10 @@ def test_gemv_parity(M, K, N):
 # per wave), two pieces (partial, whole), three to eight whole pieces, and a
 # partial last piece past two.
 ONE_TOKEN_CASES = [(64, 1), (320, 200), (4096, 3), (4096, 4), (2560, 6912), (4160, 1),
-                   (4160, 7), (8192, 2049), (8192, 1), (6912, 2560), (8256, 33), (12288, 1),
-                   (16384, 17), (20480, 9), (24576, 3), (28672, 40), (28672, 8193),
-                   (32768, 15), (65536, 5), (3200, 3203), (11008, 100)]
+                   (4160, 7), (8192, 2049), (8192, 1), (8192, 5), (6912, 2560), (8256, 33),
+                   (12288, 1), (12288, 7), (16384, 17), (16384, 1), (20480, 9), (24576, 3),
+                   (28672, 40), (28672, 8193), (32768, 15), (65536, 5), (3200, 3203),
+                   (11008, 100)]
 
 
 @pytest.mark.parametrize("K,N", ONE_TOKEN_CASES)
