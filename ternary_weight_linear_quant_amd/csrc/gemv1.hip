@@ -5,7 +5,11 @@
 // лучше двух»: with weights in {-1, 0, +1} the product is the sum of the inputs
 // whose weight is +1 minus the sum of those whose weight is -1; zero weights
 // add nothing. At one token the call reads every packed weight once and does
-// little arithmetic per byte, so its bound is HBM bandwidth.
+// little arithmetic per byte: its roofline is HBM bandwidth. What holds it
+// below a plain read of the same bytes is each wave's chain (issue the loads,
+// stage the token, barrier, consume, reduce, retire) and its VALU work at the
+// eight waves per SIMD the hardware keeps, so the variants below amortise the
+// per-wave work over as many weights as they can.
 //
 // Each wave owns RW whole rows (output features) and streams them in order:
 // one load instruction per 1 KB piece of a row (16 bytes per lane, 64 lanes
