@@ -189,12 +189,15 @@ int bl_bitlinear_choice(int64_t M, int64_t K, int64_t N, int path);
  *                   the same bits as bl_quantize_acts gives (the caller
  *                   provides both; they are written whichever way the call
  *                   runs).
- * At one token (M == 1) with K <= 4096 a single launch does both: every
- * workgroup of the one-token GEMV quantises the token itself (its weight
- * loads already in flight) and workgroup 0 writes x_q and x_scale. Other
- * shapes enqueue the two calls (for longer rows every workgroup's copy of the
- * token costs more than the second launch). Pointers 16-byte aligned; y, x_q
- * and x_scale must not overlap each other or any input. */
+ * At one token (M == 1) a single launch does both when K <= 4096, or when K
+ * is 8192, 12288, ..., 32768 (a multiple of 4096 up to eight times it) and
+ * rms_gain is NULL: every workgroup of the one-token GEMV quantises the token
+ * itself (its weight loads already in flight) and workgroup 0 writes x_q and
+ * x_scale. Other shapes enqueue the two calls (rows with a partial second
+ * piece: every workgroup's copy of the token costs more than the second
+ * launch; longer rows with a gain: the fp64 sum of squares would be taken in
+ * another order than bl_quantize_acts takes it). Pointers 16-byte aligned; y,
+ * x_q and x_scale must not overlap each other or any input. */
 int bl_quant_bitlinear(const uint16_t* x, int64_t M, int64_t K, const uint16_t* rms_gain,
                        float rms_eps, const uint32_t* W_packed, const float* gamma, int64_t N,
                        float* y, int8_t* x_q, float* x_scale, void* stream);

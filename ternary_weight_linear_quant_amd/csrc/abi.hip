@@ -216,7 +216,7 @@ int bl_quant_bitlinear(const uint16_t* x, int64_t M, int64_t K, const uint16_t* 
     }
     if (int s = device_status()) return s;
     hipStream_t st = as_stream(stream);
-    if (bl::gemv1_quant_supported(M, K))
+    if (bl::gemv1_quant_supported(M, K, rms_gain != nullptr))
         return hip_status(bl::launch_gemv1_quant(x, rms_gain, rms_eps, (int)K, W_packed, gamma,
                                                  (int)N, y, x_q, x_scale, st));
     if (int s = bl_quantize_acts(x, M, K, rms_gain, rms_eps, x_q, x_scale, stream)) return s;

@@ -50,16 +50,19 @@
 //                   barrier; each piece reads its activations from LDS.
 // Waves are independent after the staging barrier (no barrier at the end).
 //
-// Quantising variant of k_gemv1_cached (QX > 0, rows of one piece): the input
-// is the bf16 token itself (with an optional RMSNorm gain), and every
+// Quantising variants (QX): the input is the bf16 token itself, and every
 // workgroup quantises it on the way into LDS with the stand-alone quantiser's
-// arithmetic and reduction order (the helpers in act_quant.hpp): its 256
-// threads load the token, reduce max|z| (and sum x^2), and write the codes
-// into the staging layout; workgroup 0 also writes them and the scale to
-// global memory. The weight loads are issued before the reductions, so they
-// are in flight across both barriers. One launch then does what the quantiser
-// and the GEMV do in two, at the price of 2K bytes of input per workgroup
-// (from L2) instead of K.
+// arithmetic (the helpers in act_quant.hpp); workgroup 0 also writes the codes
+// and the scale to global memory. The token's loads are issued before the
+// weight loads, which then stay in flight across the reductions and barriers.
+// One launch does what the quantiser and the GEMV do in two, at the price of
+// 2K bytes of input per workgroup (from L2) instead of K.
+//   k_gemv1_cached, QX = 1 or 2 (rows of one piece, optional RMSNorm gain):
+//                   256 threads in k_act_quant's assignment and reduction
+//                   order, so that the fp64 sum of squares matches too;
+//   k_gemv1_rows / k_gemv1_stream, QX (whole pieces, no gain): each thread
+//                   quantises its own activation slots after an exact
+//                   workgroup max|x| (an integer max of the magnitude bits).
 //
 // Roofline: HBM. Algorithmic bytes per call = N * K/4 (packed weights) + K
 // (activations) + 4 (scale) + 4 (gamma) + 4 * N (y).
@@ -195,6 +198,41 @@ __device__ __forceinline__ void load_token(const Gemv1Args& p, uint4 (&cx)[VPT],
     }
 }
 
+// Plain quantisation of the token in the slot layout of k_gemv1_rows and
+// k_gemv1_stream: slot t holds activations 16t .. 16t+15, here as two bf16
+// vectors xb[i][0], xb[i][1] for this thread's slots ts[i] (slots at or past
+// XP hold zeros and get no codes). max|x| is exact (an integer max of the
+// magnitude bits, then over the workgroup's NW waves), and each slot's codes
+// come from the stand-alone quantiser's arithmetic, so codes and scale are the
+// same bits as k_act_quant's. Workgroup 0 also stores them. Contains a
+// barrier: every thread of the workgroup calls it.
+template <int XPT, int NW>
+__device__ __forceinline__ float quantise_slots(const uint4 (&xb)[XPT][2], const int (&ts)[XPT],
+                                                int XP, uint4 (&codes)[XPT], int8_t* xq_out,
+                                                float* xs_out) {
+    __shared__ float s_max[NW];
+    act_u16x2 m2 = {0, 0};
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+        act_scan8_bits(xb[i][0], m2);
+        act_scan8_bits(xb[i][1], m2);
+    }
+    const float amax = act_reduce<float, true, NW>(act_bits_max(m2), s_max);
+    const float a = act_clamped_max(amax);
+    const float inv = 127.0f / a;  // correctly rounded
+    const bool first = blockIdx.x == 0;
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+        const uint2 lo = act_quant8<false>(xb[i][0], xb[i][0], inv);
+        const uint2 hi = act_quant8<false>(xb[i][1], xb[i][1], inv);
+        codes[i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        if (first && ts[i] < XP) reinterpret_cast<uint4*>(xq_out)[ts[i]] = codes[i];
+    }
+    const float scale = act_scale<false>(a, 0.0, 0, 0.0f);
+    if (first && threadIdx.x == 0) xs_out[0] = scale;
+    return scale;
+}
+
 // S pieces per row (K <= 4096 S), RW rows per wave, R loads in flight per lane,
 // WPB waves per workgroup, QX as for Gemv1Args. Requires N >= RW.
 template <int S, int RW, int R, int WPB, int QX>
@@ -292,8 +330,9 @@ __global__ __launch_bounds__(64 * WPB) void k_gemv1_cached(const Gemv1Args p) {
 // One row per wave, R loads in flight per lane. SP > 0: exactly SP whole
 // pieces per row (K = 4096 SP), every bound known at compile time; SP = 0:
 // any K up to kStreamMaxK, the last piece possibly partial.
-template <int SP, int R, int WPB>
+template <int SP, int R, int WPB, bool QX = false>
 __global__ __launch_bounds__(64 * WPB) void k_gemv1_stream(const Gemv1Args p) {
+    static_assert(!QX || SP > 0, "the quantising variant takes whole pieces");
     constexpr int NT = 64 * WPB;
     constexpr int XPT = SP > 0 ? (SP * (kPieceK / 16) + NT - 1) / NT : 4;  // slots per thread
     extern __shared__ __align__(16) uint8_t smem[];
@@ -311,12 +350,23 @@ __global__ __launch_bounds__(64 * WPB) void k_gemv1_stream(const Gemv1Args p) {
     //    16 g + i takes slot 4 i + g, so that each quarter-wave writes one
     //    s-block's 16 consecutive slots (256 bytes, every bank once); the
     //    wave's loads still cover its 1 KB of x.
+    //    QX: the bf16 values of the same slots, quantised in step 3.
     auto slot_of = [](int u) { return (u & ~63) + 4 * (u % 16) + (u % 64) / 16; };
     uint4 xv[XPT];
+    uint4 xb[QX ? XPT : 1][2];
+    int ts[XPT];
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
         const int t = slot_of(tid + NT * i);
-        xv[i] = 16 * t < K ? *reinterpret_cast<const uint4*>(p.xq + 16 * t) : make_uint4(0, 0, 0, 0);
+        ts[i] = t;
+        if constexpr (QX) {
+            const uint4* x16 = reinterpret_cast<const uint4*>(p.x);
+            xb[i][0] = t < XP ? x16[2 * t] : make_uint4(0, 0, 0, 0);
+            xb[i][1] = t < XP ? x16[2 * t + 1] : make_uint4(0, 0, 0, 0);
+        } else {
+            xv[i] = 16 * t < K ? *reinterpret_cast<const uint4*>(p.xq + 16 * t)
+                               : make_uint4(0, 0, 0, 0);
+        }
     }
     asm volatile("" ::: "memory");
 
@@ -336,13 +386,16 @@ __global__ __launch_bounds__(64 * WPB) void k_gemv1_stream(const Gemv1Args p) {
         if (u < NP) wb[u] = load(u);
     asm volatile("" ::: "memory");
 
-    // 3. Only the weight loads may remain in flight; store the slots and sum them.
+    // 3. Only the weight loads may remain in flight; (QX: quantise the token,)
+    //    store the slots and sum them.
     wait_vmcnt_le8(NP < R ? NP : R);
+    float scale = 0.0f;
+    if constexpr (QX) scale = quantise_slots<XPT, WPB>(xb, ts, XP, xv, p.xq_out, p.xs_out);
     auto slot = [&](int t) { return smem + (4 * (t / 256) + t % 4) * kPiece + 16 * ((t / 4) % 64); };
     int s = 0;
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
-        const int t = slot_of(tid + NT * i);
+        const int t = ts[i];
         if (t < XP) {
             *reinterpret_cast<uint4*>(slot(t)) = xv[i];
             s = bytes_sum(xv[i], s);
@@ -379,8 +432,9 @@ __global__ __launch_bounds__(64 * WPB) void k_gemv1_stream(const Gemv1Args p) {
             }
         }
     }
+    if constexpr (!QX) scale = p.xs[0];
     const int a = wave_sum_i32(acc) - sx;
-    if (lane == 0 && n == n0) store_row(p.y, p.acc_out, n, a, p.xs[0] * (*p.gamma));
+    if (lane == 0 && n == n0) store_row(p.y, p.acc_out, n, a, scale * (*p.gamma));
 }
 
 // Rows of SP whole pieces (K = 4096 SP, SP small), RW rows per wave: the
@@ -389,7 +443,7 @@ __global__ __launch_bounds__(64 * WPB) void k_gemv1_stream(const Gemv1Args p) {
 // registers and the wave streams its RW rows through one ring of R pieces, so
 // the staging, the barrier and the sum-x reduction are paid once per RW rows
 // and no LDS is read per piece. Requires N >= RW.
-template <int SP, int RW, int R, int WPB>
+template <int SP, int RW, int R, int WPB, bool QX = false>
 __global__ __launch_bounds__(64 * WPB) void k_gemv1_rows(const Gemv1Args p) {
     constexpr int NT = 64 * WPB;
     constexpr int K = SP * kPieceK;
@@ -403,14 +457,24 @@ __global__ __launch_bounds__(64 * WPB) void k_gemv1_rows(const Gemv1Args p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int N = p.N;
 
-    // 1. Activation slots as in k_gemv1_stream (the same quarter-wave order).
+    // 1. Activation slots as in k_gemv1_stream (the same quarter-wave order;
+    //    QX: their bf16 values).
     auto slot_of = [](int u) { return (u & ~63) + 4 * (u % 16) + (u % 64) / 16; };
     auto slot = [&](int t) { return smem + (4 * (t / 256) + t % 4) * kPiece + 16 * ((t / 4) % 64); };
     uint4 xv[XPT];
+    uint4 xb[QX ? XPT : 1][2];
+    int ts[XPT];
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
         const int t = slot_of(tid + NT * i);
-        xv[i] = t < XP ? *reinterpret_cast<const uint4*>(p.xq + 16 * t) : make_uint4(0, 0, 0, 0);
+        ts[i] = t;
+        if constexpr (QX) {
+            const uint4* x16 = reinterpret_cast<const uint4*>(p.x);
+            xb[i][0] = t < XP ? x16[2 * t] : make_uint4(0, 0, 0, 0);
+            xb[i][1] = t < XP ? x16[2 * t + 1] : make_uint4(0, 0, 0, 0);
+        } else {
+            xv[i] = t < XP ? *reinterpret_cast<const uint4*>(p.xq + 16 * t) : make_uint4(0, 0, 0, 0);
+        }
     }
     asm volatile("" ::: "memory");
 
@@ -428,12 +492,15 @@ __global__ __launch_bounds__(64 * WPB) void k_gemv1_rows(const Gemv1Args p) {
         if (u < L) wb[u] = load(u);
     asm volatile("" ::: "memory");
 
-    // 3. Stage and sum the activations; one barrier.
+    // 3. (QX: quantise the token,) stage and sum the activations; one barrier
+    //    (two with QX).
     wait_vmcnt_le8(L < R ? L : R);
+    float scale = 0.0f;
+    if constexpr (QX) scale = quantise_slots<XPT, WPB>(xb, ts, XP, xv, p.xq_out, p.xs_out);
     int s = 0;
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
-        const int t = slot_of(tid + NT * i);
+        const int t = ts[i];
         if (t < XP) {
             *reinterpret_cast<uint4*>(slot(t)) = xv[i];
             s = bytes_sum(xv[i], s);
@@ -455,7 +522,8 @@ __global__ __launch_bounds__(64 * WPB) void k_gemv1_rows(const Gemv1Args p) {
 
     // 4. The wave's L pieces through a ring of R; each row's sum stored when
     //    its last piece is in.
-    const float sc = p.xs[0] * (*p.gamma);
+    if constexpr (!QX) scale = p.xs[0];
+    const float sc = scale * (*p.gamma);
     int acc = 0;
 #pragma unroll
     for (int i = 0; i < L; ++i) {
@@ -480,20 +548,22 @@ static hipError_t launch_cached(const Gemv1Args& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int SP, int RW, int R, int WPB>
+template <int SP, int RW, int R, int WPB, bool QX = false>
 static hipError_t launch_rows(const Gemv1Args& a, hipStream_t stream) {
     const int waves = (a.N + RW - 1) / RW;
     const int blocks = (waves + WPB - 1) / WPB;
-    hipLaunchKernelGGL((k_gemv1_rows<SP, RW, R, WPB>), dim3(blocks), dim3(64 * WPB), 0, stream, a);
+    hipLaunchKernelGGL((k_gemv1_rows<SP, RW, R, WPB, QX>), dim3(blocks), dim3(64 * WPB), 0, stream,
+                       a);
     return hipGetLastError();
 }
 
-template <int SP, int R, int WPB>
+template <int SP, int R, int WPB, bool QX = false>
 static hipError_t launch_stream(const Gemv1Args& a, hipStream_t stream) {
     const int NP = (a.K / 4 + kPiece - 1) / kPiece;
     const size_t lds = (size_t)NP * kPieceK;
     const int blocks = (a.N + WPB - 1) / WPB;
-    hipLaunchKernelGGL((k_gemv1_stream<SP, R, WPB>), dim3(blocks), dim3(64 * WPB), lds, stream, a);
+    hipLaunchKernelGGL((k_gemv1_stream<SP, R, WPB, QX>), dim3(blocks), dim3(64 * WPB), lds, stream,
+                       a);
     return hipGetLastError();
 }
 
@@ -511,9 +581,11 @@ bool gemv1_preferred(int64_t M, int64_t K) {
 // columns. Two to four whole pieces: several rows per wave with the token in
 // registers (8192 -> 28672: 11.7 us against 13.2 for one row per wave and 13.5
 // for the cached kernel; 12288: 6.1 against 6.4; 16384: 7.5 against 7.7).
-// Seven pieces: one row per wave, 16-wave workgroups, two pieces in flight
-// (28672 -> 8192: 10.7 against 12.0 us for all seven in flight); eight: all in
-// flight. Rows of one piece, and partial second pieces, keep the cached kernel.
+// Five to seven pieces: one row per wave, 16-wave workgroups, two pieces in
+// flight (28672 -> 8192: 10.7 against 12.0 us for all seven in flight in
+// 8-wave workgroups; 20480: 9.4 against 9.8 for two in flight in 8-wave
+// ones); eight: all in flight. Rows of one piece, and partial second pieces,
+// keep the cached kernel.
 hipError_t launch_gemv1(const int8_t* xq, const float* xs, int K, const uint32_t* Wp,
                         const float* gamma, int N, float* y, int32_t* acc, hipStream_t stream) {
     if (K > kStreamMaxK) return hipErrorInvalidValue;
@@ -545,26 +617,40 @@ hipError_t launch_gemv1(const int8_t* xq, const float* xs, int K, const uint32_t
         case 4:
             if (N >= 2) return launch_rows<4, 2, 4, 8>(a, stream);
             return launch_stream<4, 2, 8>(a, stream);
-        case 5: return launch_stream<5, 2, 8>(a, stream);
-        case 6: return launch_stream<6, 2, 8>(a, stream);
+        case 5: return launch_stream<5, 2, 16>(a, stream);
+        case 6: return launch_stream<6, 2, 16>(a, stream);
         case 7: return launch_stream<7, 2, 16>(a, stream);
         case 8: return launch_stream<8, 8, 8>(a, stream);
         default: return launch_stream<0, 2, 8>(a, stream);
     }
 }
 
-// The quantising variant serves rows of one piece (K <= 4096): there the
-// token's 2K bytes per workgroup are small beside the weights, and one launch
-// measured faster than two (2560 -> 2560: 3.9 against 5.2 us per projection,
-// 3200 -> 8640: 6.1 against 7.2). With longer rows every workgroup's copy of
-// the token costs more than the second launch saves (8192 -> 28672: 18.4
-// against 17.8 us; 28672 -> 8192: 24.9 against 17.8).
-bool gemv1_quant_supported(int64_t M, int64_t K) { return M == 1 && K <= kPieceK; }
+// One launch quantises and multiplies: rows of one piece (any gain) through
+// the cached kernel, whose 256 threads take k_act_quant's assignment and
+// reduction order; whole pieces up to eight (no gain) through the rows and
+// stream kernels, whose max|x| is exact whatever the order. Measured (HIP
+// graphs, ten rotated copies per matrix) against act quant + GEMV: 2560 ->
+// 2560 3.9 against 5.2 us per projection, 3200 -> 8640 6.1 against 7.2,
+// 8192 -> 28672 13.7 against 15.6, 28672 -> 8192 14.2 against 16.1; on
+// 8192-row matrices of 12288 / 16384 / 20480 / 24576 / 32768 columns 7.8 /
+// 9.4 / 11.6 / 13.0 / 16.4 against 9.8 / 11.4 / 13.4 / 14.9 / 19.4. From five
+// pieces on, 16-wave workgroups: their threads hold fewer slots of the token
+// (the 8-wave shapes of the GEMV alone measured 13.0, 14.5 and 20.3 us
+// there). With a
+// gain on longer rows the fp64 sum of squares would be taken in another order
+// than the stand-alone quantiser's (the scale could differ in its last bit),
+// and rows with a partial second piece keep the cached kernel, whose per-
+// workgroup token copies cost more than the second launch saves there.
+bool gemv1_quant_supported(int64_t M, int64_t K, bool norm) {
+    if (M != 1) return false;
+    if (K <= kPieceK) return true;
+    return !norm && K % kPieceK == 0 && K <= 8 * kPieceK;
+}
 
 hipError_t launch_gemv1_quant(const uint16_t* x, const uint16_t* gain, float rms_eps, int K,
                               const uint32_t* Wp, const float* gamma, int N, float* y,
                               int8_t* xq_out, float* xs_out, hipStream_t stream) {
-    if (!gemv1_quant_supported(1, K)) return hipErrorInvalidValue;
+    if (!gemv1_quant_supported(1, K, gain != nullptr)) return hipErrorInvalidValue;
     Gemv1Args a{};
     a.x = x;
     a.gain = gain;
@@ -576,12 +662,29 @@ hipError_t launch_gemv1_quant(const uint16_t* x, const uint16_t* gain, float rms
     a.gamma = gamma;
     a.N = N;
     a.y = y;
-    if (gain) {
-        if (N >= 4) return launch_cached<1, 4, 4, 4, 2>(a, stream);
-        return launch_cached<1, 1, 1, 4, 2>(a, stream);
+    if (K <= kPieceK) {
+        if (gain) {
+            if (N >= 4) return launch_cached<1, 4, 4, 4, 2>(a, stream);
+            return launch_cached<1, 1, 1, 4, 2>(a, stream);
+        }
+        if (N >= 4) return launch_cached<1, 4, 4, 4, 1>(a, stream);
+        return launch_cached<1, 1, 1, 4, 1>(a, stream);
     }
-    if (N >= 4) return launch_cached<1, 4, 4, 4, 1>(a, stream);
-    return launch_cached<1, 1, 1, 4, 1>(a, stream);
+    switch (K / kPieceK) {
+        case 2:
+            if (N >= 4) return launch_rows<2, 4, 4, 4, true>(a, stream);
+            return launch_stream<2, 2, 8, true>(a, stream);
+        case 3:
+            if (N >= 4) return launch_rows<3, 4, 4, 4, true>(a, stream);
+            return launch_stream<3, 2, 8, true>(a, stream);
+        case 4:
+            if (N >= 2) return launch_rows<4, 2, 4, 8, true>(a, stream);
+            return launch_stream<4, 2, 8, true>(a, stream);
+        case 5: return launch_stream<5, 2, 16, true>(a, stream);
+        case 6: return launch_stream<6, 2, 16, true>(a, stream);
+        case 7: return launch_stream<7, 2, 16, true>(a, stream);
+        default: return launch_stream<8, 4, 16, true>(a, stream);
+    }
 }
 
 }  // namespace bl

@@ -26,7 +26,7 @@ hipError_t launch_gemv1(const int8_t* xq, const float* xs, int K, const uint32_t
                         const float* gamma, int N, float* y, int32_t* acc, hipStream_t stream);
 // One token quantised in the GEMV's own launch (gain: RMSNorm gain or null):
 // the codes and scale go to xq_out / xs_out as well.
-bool gemv1_quant_supported(int64_t M, int64_t K);
+bool gemv1_quant_supported(int64_t M, int64_t K, bool norm);
 hipError_t launch_gemv1_quant(const uint16_t* x, const uint16_t* gain, float rms_eps, int K,
                               const uint32_t* Wp, const float* gamma, int N, float* y,
                               int8_t* xq_out, float* xs_out, hipStream_t stream);

@@ -171,9 +171,17 @@ def test_act_quant_golden_and_zero_token():
 
 # One launch at one token with K <= 4096 (one or several row waves, RW = 1
 # below four rows); the others take the two-call route.
+# One launch: K <= 4096 (cached kernel), and without a gain whole pieces of
+# 4096 up to 32768 (rows kernel at 2-4 pieces from N >= 4 or 2, else stream;
+# ragged last waves and workgroups included). Two launches: a partial second
+# piece (4160, 6912), nine pieces (36864), several tokens, and every long row
+# with a gain.
 QUANT_BITLINEAR_CASES = [
     (1, 64, 7), (1, 64, 1), (1, 320, 200), (1, 2560, 2560), (1, 3200, 8640), (1, 4096, 33),
-    (1, 4096, 3), (1, 4160, 100), (1, 8192, 300), (1, 28672, 64), (3, 2560, 257),
+    (1, 4096, 3), (1, 4160, 100), (1, 6912, 11), (1, 8192, 300), (1, 8192, 37), (1, 8192, 3),
+    (1, 12288, 100), (1, 12288, 2), (1, 16384, 1), (1, 16384, 9), (1, 16384, 2),
+    (1, 20480, 5), (1, 24576, 17), (1, 28672, 64), (1, 32768, 7), (1, 36864, 3),
+    (3, 2560, 257),
 ]
 
 
@@ -209,7 +217,7 @@ def test_quant_bitlinear(M, K, N, norm):
                    f"quant_bitlinear M={M} K={K} N={N}")
 
 
-@pytest.mark.parametrize("K", [64, 4096])
+@pytest.mark.parametrize("K", [64, 4096, 8192, 16384, 28672, 32768])
 def test_quant_bitlinear_golden_ties_and_zero_token(K):
     """The in-kernel quantiser on the golden tie tokens (each as its own
     one-token call, mirrored in sign too) and on an all-zero token: the golden
@@ -238,6 +246,24 @@ def test_quant_bitlinear_golden_ties_and_zero_token(K):
         y = y.cpu().numpy()[0]
         assert np.array_equal(y, (xq[:N].astype(np.float32) * ref_s[0]).astype(np.float32))
     assert ref_s[0] == np.float32(1e-5) / np.float32(127)
+
+
+@pytest.mark.parametrize("K,N", [(8192, 28672), (28672, 8192)])
+def test_quant_bitlinear_70b_rows(K, N):
+    """bl_quant_bitlinear at the full 70B-class decode shapes (one launch): the
+    codes and the scale are the oracle's bits, and every output is within
+    1e-6 of the oracle's epilogue of its exact int32 product (an int32 sum
+    off by one would move y by 1/|sum|, far more at these sums)."""
+    rng = np.random.default_rng(K + 7 * N)
+    x = wl.activations(71, 0, 1, K)
+    q = rand_codes(rng, N, K)
+    gm = np.float32(0.0173)
+    y, xq, xs = bl.quant_bitlinear(dev_bf16(x), dev_packed(oracle.pack(q)), dev_f32([gm]))
+    xq_ref, xs_ref = oracle.act_quant(x)
+    assert np.array_equal(xq.cpu().numpy(), xq_ref)
+    assert np.array_equal(xs.cpu().numpy(), xs_ref)
+    acc_ref = oracle.int_matmul(xq_ref, q)
+    assert_y_close(y.cpu().numpy(), oracle.epilogue(acc_ref, xs_ref, gm), f"70B rows K={K} N={N}")
 
 
 # ------------------------------------------------------------ product ----

@@ -145,7 +145,8 @@ def test_bitlinear_guards_and_repeats(M, K, N, path):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 64, 7), (1, 320, 200), (1, 4096, 33), (1, 4096, 2),
-                                   (1, 8192, 31), (2, 320, 65)])
+                                   (1, 8192, 31), (1, 8192, 3), (1, 16384, 1), (1, 20480, 17),
+                                   (1, 28672, 9), (1, 32768, 5), (2, 320, 65)])
 @pytest.mark.parametrize("norm", [False, True])
 def test_quant_bitlinear_guards_and_repeats(M, K, N, norm):
     rng = np.random.default_rng(M + K + N + 7)
