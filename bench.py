@@ -6,8 +6,10 @@ Headline (`value`): decode packed-weight GB/s on the 70B-class shapes (hidden
 that fits one GPU, at one token. One step runs, for each of L weight copies
 (identical content at distinct addresses, 5 x 2 x 58.7 MB: more than twice the
 256 MB Infinity Cache, so every call streams its weights from HBM): the
-per-token act quant of the up input, the up BitLinear, the act quant of the
-down input and the down BitLinear -- four launches per copy. Weights are
+per-token act quant of the up input with the up BitLinear, then the act quant
+of the down input with the down BitLinear, each pair one bl_quant_bitlinear
+call -- one launch per projection, which also writes the codes and the scale
+(`two_call_step`: the same with bl_quantize_acts + bl_bitlinear). Weights are
 quantised once before the timed region (offline in the method); that pass is
 timed and reported as weight_prep. The step is captured in a HIP graph and
 replayed.
@@ -15,7 +17,8 @@ replayed.
 Beside it, each with its roofline (achieved against the published peak,
 HIP-event timing on the launching stream, HBM bytes per launch from the
 committed rocprofv3 counter summary while the kernel sources are unchanged):
-  - `roofline`: the one-token GEMV launches of the step alone;
+  - `roofline`: the step's launches (act quant + GEMV in one kernel), and
+    under `gemv_alone` the one-token GEMV on the quantised token;
   - `prefill_M2048`: act quant + GEMM at 2048 tokens on the same matrices
     (int8 TOPS against the matrix-core peak);
   - decode at 64 tokens, and the 1-bit and base-3 weight formats at one token;
@@ -84,6 +87,26 @@ def host_info():
     except OSError:
         pass
     return cpu, os.cpu_count()
+
+
+# Untimed work before each timed region. Between legs the host prepares
+# inputs and the GPU idles; its clocks then need 15-30 ms of continuous work
+# to come back (replays of the 70B step right after an idle ran 15-17.5 us per
+# projection for about 12 ms, then 13.8-14.1), far more than a few warm-up
+# steps of a sub-millisecond step cover.
+SETTLE_MS = 50.0
+
+
+def settle(torch, fn, min_ms=SETTLE_MS):
+    """Runs fn, untimed, until the GPU has been kept busy for min_ms of wall
+    time (checked after every fourth call)."""
+    t0 = time.perf_counter()
+    fn()
+    torch.cuda.synchronize()
+    while (time.perf_counter() - t0) * 1e3 < min_ms:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
 
 
 class Timer:
@@ -196,9 +219,13 @@ def other_workloads(args, bl, wl, np, torch, dev, bf16_dev, capture, time_graph,
         dx = torch.empty((Mp, K), dtype=torch.float32, device=dev)
         legs.append((name, K, N, qT, g, dy, dx))
         del pk
-    for _ in range(1 + args.warmup):
+    def dx_all():
         for name, K, N, qT, g, dy, dx in legs:
             bl.ste_backward_dx(dy, qT, g, N, out=dx)
+
+    settle(torch, dx_all)
+    for _ in range(1 + args.warmup):
+        dx_all()
     torch.cuda.synchronize()
     tp = Timer(torch)
     reps = max(5, args.steps)
@@ -217,8 +244,7 @@ def other_workloads(args, bl, wl, np, torch, dev, bf16_dev, capture, time_graph,
     v_us = 0.0
     for name, K, N, qT, g, dy, dx in legs:
         wb = torch.randint(-1, 2, (N, K), device=dev).to(torch.bfloat16).contiguous()
-        torch.matmul(dy, wb)
-        torch.cuda.synchronize()
+        settle(torch, lambda: torch.matmul(dy, wb))
         ea = torch.cuda.Event(enable_timing=True)
         eb = torch.cuda.Event(enable_timing=True)
         ea.record()
@@ -238,9 +264,13 @@ def other_workloads(args, bl, wl, np, torch, dev, bf16_dev, capture, time_graph,
         xq, xs = bl.quantize_acts(bf16_dev(wl.activations(PREFILL_WORKLOAD, i, Mp, K)))
         dw_legs.append((name, K, N, dy, xq, xs, bl.ste_dw_workspace(Mp, N, K, dev),
                         torch.empty((N, K), dtype=torch.float32, device=dev)))
-    for _ in range(1 + args.warmup):
+    def dw_all():
         for name, K, N, dy, xq, xs, ws, dW in dw_legs:
             bl.ste_backward_dw(dy, xq, xs, workspace=ws, out=dW)
+
+    settle(torch, dw_all)
+    for _ in range(1 + args.warmup):
+        dw_all()
     torch.cuda.synchronize()
     tw = Timer(torch)
     for _ in range(reps):
@@ -306,8 +336,8 @@ def other_workloads(args, bl, wl, np, torch, dev, bf16_dev, capture, time_graph,
         gr = capture(rotation)
         st = replay_stats(gr, 20, copies * len(wprojs))
         del gr
-        # The same projections from the bf16 token: bl_quant_bitlinear (one
-        # launch where K <= 4096) against bl_quantize_acts + bl_bitlinear.
+        # The same projections from the bf16 token: bl_quant_bitlinear against
+        # bl_quantize_acts + bl_bitlinear.
         xb = {name: bf16_dev(wl.activations(wid, i, 1, K)) for i, (name, K, N) in enumerate(wprojs)}
 
         def rotation_q(one_call):
@@ -344,9 +374,9 @@ def other_workloads(args, bl, wl, np, torch, dev, bf16_dev, capture, time_graph,
                 "with_act_quant": {
                     "us_per_projection": {k: round(v, 3) for k, v in with_q.items()},
                     "packed_GBps_one_call": round(packed / (with_q["one_call"] * 1e-6) / 1e9, 1),
-                    "note": "from the bf16 token: bl_quant_bitlinear (one_call; a single launch "
-                            "where K <= 4096) against bl_quantize_acts + bl_bitlinear "
-                            "(two_calls)"},
+                    "note": "from the bf16 token: bl_quant_bitlinear (one_call: a single launch "
+                            "where K <= 4096 or K is whole 4096-weight pieces, else the two "
+                            "calls) against bl_quantize_acts + bl_bitlinear (two_calls)"},
                 "timing": "HIP graph of the rotation, HIP events on the replay stream"}
 
     small = {"single_2560_decode_M1": rotated_decode(1, SMALL_COPIES, "gemv_2560_m1")}
@@ -482,8 +512,7 @@ def main():
         return gr
 
     def time_graph(gr, reps):
-        gr.replay()
-        torch.cuda.synchronize()
+        settle(torch, gr.replay)
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
@@ -551,6 +580,14 @@ def main():
         io[name] = (x, xq, xs, torch.empty((1, N), dtype=torch.float32, device=dev))
 
     def decode_step():
+        # One call per projection: bl_quant_bitlinear quantises the token and
+        # multiplies in one launch on these rows, writing codes and scale too.
+        for c in range(L):
+            for name, _, _ in lprojs:
+                x, xq, xs, y = io[name]
+                bl.quant_bitlinear(x, *wts[name][c], out=(y, xq, xs))
+
+    def two_call_step():
         for c in range(L):
             for name, _, _ in lprojs:
                 x, xq, xs, y = io[name]
@@ -573,6 +610,7 @@ def main():
         else:
             decode_step()
 
+    settle(torch, replay)
     for _ in range(args.warmup):
         replay()
     torch.cuda.synchronize()
@@ -588,41 +626,83 @@ def main():
     packed_per_step = packed_per_copy * L
     value = packed_per_step / (ms_per_step * 1e-3) / 1e9
 
-    # The roofline kernel: the one-token GEMV launches alone, replayed from
-    # their own graph and timed with HIP events on the replaying stream.
+    # The roofline kernel: the step's launches are the fused act quant + GEMV
+    # kernel alone, so the step's own graph times it (HIP events on the
+    # replaying stream), and one graph per projection splits it by matrix.
+    st_step = replay_stats(graph, 20, 2 * L) if graph is not None else None
+    if st_step is None:
+        gs = capture(decode_step)
+        st_step = replay_stats(gs, 20, 2 * L)
+        del gs
+
+    def per_projection(body, kernel_of):
+        out = {}
+        for name, K, N in lprojs:
+            def one(name=name):
+                for c in range(L):
+                    body(name, c)
+            gp = capture(one)
+            stp = replay_stats(gp, 20, L)
+            del gp
+            out[name] = {"K": K, "N": N, "kernel": kernel_of(K), "mean_us": stp["mean_us"],
+                         "median_us": stp["median_us"],
+                         "packed_GBps": round(N * K / 4 / (stp["mean_us"] * 1e-6) / 1e9, 1)}
+        return out
+
+    def fused_one(name, c):
+        x, xq, xs, y = io[name]
+        bl.quant_bitlinear(x, *wts[name][c], out=(y, xq, xs))
+
+    def gemv_one(name, c):
+        _, xq, xs, y = io[name]
+        bl.bitlinear(xq, xs, *wts[name][c], out=y)
+
+    # Algorithmic bytes of the fused launch: packed weights, the bf16 token and
+    # gamma in; y, the codes and the scale out.
+    alg_fused = sum(N * K // 4 + 2 * K + 4 + 4 * N + K + 4 for _, K, N in lprojs) / len(lprojs)
+    achieved = alg_fused / (st_step["mean_us"] * 1e-6) / 1e9
+    roofline = {
+        "bound": "hbm",
+        "kernel": "one-token act quant + GEMV in one launch (quantising k_gemv1_rows on "
+                  "8192->28672, k_gemv1_stream on 28672->8192) with its fused epilogue",
+        "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": traffic.get("quant_gemv_70b_m1"),
+        "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled "
+                        "by a copy kernel)",
+        "alg_bytes_per_launch": round(alg_fused),
+        "launches": 2 * L, "avg_us": st_step["mean_us"], "per_launch": st_step,
+        "per_projection": per_projection(
+            fused_one, lambda K: "k_gemv1_rows (quantising)" if K == 8192
+            else "k_gemv1_stream (quantising)"),
+        "timing": "the step's own HIP graph (its launches are this kernel only), HIP events "
+                  "on the replay stream",
+    }
+    # Context: the GEMV alone on the quantised token (bl_bitlinear), and the
+    # step as two calls per projection (bl_quantize_acts + bl_bitlinear).
     gg = capture(gemv_only)
     st_gemv = replay_stats(gg, 20, 2 * L)
     del gg
-    per_proj = {}
-    for name, K, N in lprojs:
-        def one(name=name):
-            for c in range(L):
-                _, xq, xs, y = io[name]
-                bl.bitlinear(xq, xs, *wts[name][c], out=y)
-        gp = capture(one)
-        stp = replay_stats(gp, 20, L)
-        del gp
-        per_proj[name] = {"K": K, "N": N, "kernel": "k_gemv1_rows" if K == 8192
-                          else "k_gemv1_stream", "mean_us": stp["mean_us"],
-                          "median_us": stp["median_us"],
-                          "packed_GBps": round(N * K / 4 / (stp["mean_us"] * 1e-6) / 1e9, 1)}
-    alg_per_launch = sum(N * K // 4 + 4 + K + 4 + 4 * N for _, K, N in lprojs) / len(lprojs)
-    achieved = alg_per_launch / (st_gemv["mean_us"] * 1e-6) / 1e9
-    act_quant_us = (1e3 * ms_per_step - st_gemv["mean_us"] * 2 * L) / (2 * L)
-    roofline = {
-        "bound": "hbm",
-        "kernel": "one-token GEMV (k_gemv1_rows on 8192->28672, k_gemv1_stream on "
-                  "28672->8192) with its fused epilogue",
-        "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-        "frac": round(achieved / HBM_PEAK_GBS, 4),
-        "traffic": traffic.get("gemv_70b_m1"),
-        "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled "
-                        "by a copy kernel)",
-        "alg_bytes_per_launch": round(alg_per_launch),
-        "launches": 2 * L, "avg_us": st_gemv["mean_us"], "per_launch": st_gemv,
-        "per_projection": per_proj,
-        "timing": "HIP graph of the step's BitLinear launches only (up and down over the "
-                  "weight copies), HIP events on the replay stream",
+    alg_gemv = sum(N * K // 4 + 4 + K + 4 + 4 * N for _, K, N in lprojs) / len(lprojs)
+    gemv_gbps = alg_gemv / (st_gemv["mean_us"] * 1e-6) / 1e9
+    roofline["gemv_alone"] = {
+        "kernel": "one-token GEMV on the quantised token (k_gemv1_rows / k_gemv1_stream), "
+                  "bl_bitlinear",
+        "achieved": round(gemv_gbps, 1), "frac": round(gemv_gbps / HBM_PEAK_GBS, 4),
+        "traffic": traffic.get("gemv_70b_m1"), "alg_bytes_per_launch": round(alg_gemv),
+        "avg_us": st_gemv["mean_us"], "per_launch": st_gemv,
+        "per_projection": per_projection(
+            gemv_one, lambda K: "k_gemv1_rows" if K == 8192 else "k_gemv1_stream"),
+    }
+    g2 = capture(two_call_step)
+    st_two = replay_stats(g2, 20, 1)
+    del g2
+    two_call = {
+        "calls": "bl_quantize_acts + bl_bitlinear per projection",
+        "ms_per_step": round(st_two["mean_us"] * 1e-3, 4),
+        "value": round(packed_per_step / (st_two["mean_us"] * 1e-6) / 1e9, 2),
+        "act_quant_us_per_launch": round(
+            (st_two["mean_us"] - st_gemv["mean_us"] * 2 * L) / (2 * L), 3),
     }
     # The same bytes through the read-only calibration stream, launch for launch.
     rbufs = [wts[name][c][0] for c in range(L) for name, _, _ in lprojs]
@@ -640,9 +720,11 @@ def main():
         "kernel": "k_calib_read", "bytes_per_launch": packed_per_copy // 2,
         "GBps": round(read_gbps, 1), "frac_of_peak": round(read_gbps / HBM_PEAK_GBS, 4),
         "us_per_launch": st_read["mean_us"],
-        "achieved_over_it": round(achieved / read_gbps, 4)}
-    print(f"70b decode step: {value:.1f} GB/s ({ms_per_step * 1e3 / L:.2f} us per copy), GEMV "
-          f"{achieved:.1f} GB/s ({st_gemv['mean_us']} us/launch), read stream "
+        "achieved_over_it": round(achieved / read_gbps, 4),
+        "gemv_alone_over_it": round(gemv_gbps / read_gbps, 4)}
+    print(f"70b decode step: {value:.1f} GB/s ({ms_per_step * 1e3 / L:.2f} us per copy), fused "
+          f"launch {achieved:.1f} GB/s ({st_step['mean_us']} us), GEMV alone {gemv_gbps:.1f} "
+          f"GB/s ({st_gemv['mean_us']} us), two calls {two_call['value']} GB/s, read stream "
           f"{read_gbps:.1f} GB/s", file=sys.stderr, flush=True)
 
     def gemm_leg(label, wid, M, legs_w, reps):
@@ -665,6 +747,7 @@ def main():
                     timer.run("act_quant", lambda: bl.quantize_acts(x, out=(xq, xs)))
                     timer.run(("gemm", name), lambda: bl.bitlinear(xq, xs, pk, g, out=y))
 
+        settle(torch, step)
         for _ in range(1 + args.warmup):
             step()
         torch.cuda.synchronize()
@@ -695,8 +778,7 @@ def main():
         vendor_us = {}
         for name, K, N, x, xq, xs, pk, g, y in legs:
             b8 = torch.randint(-1, 2, (K, N), dtype=torch.int8, device=dev)
-            torch._int_mm(xq, b8)
-            torch.cuda.synchronize()
+            settle(torch, lambda: torch._int_mm(xq, b8))
             ea = torch.cuda.Event(enable_timing=True)
             eb = torch.cuda.Event(enable_timing=True)
             ea.record()
@@ -823,14 +905,15 @@ def main():
             print(f"70b decode M=1 {fmt}: {extra[f'decode_M1_70b_{fmt}']['weights_per_s']} "
                   f"T weights/s", file=sys.stderr, flush=True)
         roofline["weights_per_s"] = round(
+            sum(N * K for _, K, N in lprojs) / 2 / (st_step["mean_us"] * 1e-6) / 1e12, 3)
+        roofline["gemv_alone"]["weights_per_s"] = round(
             sum(N * K for _, K, N in lprojs) / 2 / (st_gemv["mean_us"] * 1e-6) / 1e12, 3)
         del fmt_w, binw
 
         # -------------------------------------- the int8 MFMA ceiling ----
         msink = bl.calib_mfma_sink(dev)
         iters = 4000
-        bl.calib_mfma_i8(iters, msink)
-        torch.cuda.synchronize()
+        settle(torch, lambda: bl.calib_mfma_i8(iters, msink))
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
@@ -874,14 +957,15 @@ def main():
         "config": {
             "workload": "70b_class_decode_M1: per weight copy, act quant + BitLinear up "
                         "(8192->28672) and act quant + BitLinear down (28672->8192) at one "
-                        "token",
+                        "token, one bl_quant_bitlinear call (one launch) per projection",
             "tokens": 1, "weight_copies": L,
             "packed_weight_bytes_per_step": packed_per_step,
             "hip_graph": not args.no_graph,
             "parallelism": "single GPU",
         },
         "frac_hbm_step": round(value / HBM_PEAK_GBS, 4),
-        "act_quant_us_per_launch_in_step": round(act_quant_us, 3),
+        "two_call_step": two_call,
+        "settle_ms_before_timing": SETTLE_MS,
         "roofline": roofline,
         "prefill_M2048": prefill70,
         "cpu_baseline": cpu_baseline,

@@ -60,6 +60,12 @@ PHASES = {
     "gemv_70b_m1": (["gemv1.hip", "act_quant.hpp", "common.hpp"],
                     "bl_bitlinear at M=1 on 8192->28672 and 28672->8192, 5 rotated copies",
                     2 * COPIES_70B, "one-token GEMV launch (k_gemv1_rows / k_gemv1_stream)"),
+    "quant_gemv_70b_m1": (["gemv1.hip", "act_quant.hpp", "common.hpp"],
+                          "bl_quant_bitlinear at M=1 on 8192->28672 and 28672->8192 (the "
+                          "bf16 token in, its codes and scale out), 5 rotated copies",
+                          2 * COPIES_70B,
+                          "one-token act quant + GEMV launch (quantising k_gemv1_rows / "
+                          "k_gemv1_stream)"),
     "gemv_70b_m1_base3": (["gemv.hip", "common.hpp"],
                           "bl_bitlinear_base3 at M=1 on the 70B shapes, 5 rotated copies",
                           2 * COPIES_70B, "k_gemv launch (five ternary weights per byte)"),
@@ -151,6 +157,12 @@ def run():
         for i, (name, K, N) in enumerate(p5):
             xq, xs = bl.quantize_acts(bf16(wl.activations(5, i, M, K)))
             q5[(M, name)] = (xq, xs, torch.empty((M, N), dtype=torch.float32, device=dev))
+    x5 = {}
+    for i, (name, K, N) in enumerate(p5):
+        x5[name] = (bf16(wl.activations(5, i, 1, K)),
+                    torch.empty((1, N), dtype=torch.float32, device=dev),
+                    torch.empty((1, K), dtype=torch.int8, device=dev),
+                    torch.empty(1, dtype=torch.float32, device=dev))
 
     w5b3 = {name: [(bl.pack_base3(pk, K), g) for pk, g in w5[name]] for name, K, N in p5}
     w5bin = {}
@@ -224,6 +236,12 @@ def run():
                     bl.bitlinear(xq, xs, *w5[name][c], out=y)
         return fn
 
+    def rotate70_quant():
+        for c in range(COPIES_70B):
+            for name, _, _ in p5:
+                x, y, xq, xs = x5[name]
+                bl.quant_bitlinear(x, *w5[name][c], out=(y, xq, xs))
+
     def rotate70_fmt(fn, wset):
         def run_fmt():
             for c in range(COPIES_70B):
@@ -264,6 +282,7 @@ def run():
     phase("copy_calibration", copy_cal)
     phase("ffn_2b4t_m1", ffn)
     phase("gemv_70b_m1", rotate70(1))
+    phase("quant_gemv_70b_m1", rotate70_quant)
     phase("gemv_70b_m1_base3", rotate70_fmt(bl.bitlinear_base3, w5b3))
     phase("gemv_70b_m1_binary", rotate70_fmt(bl.bitlinear_binary, w5bin))
     phase("decode_70b_m64", rotate70(64))

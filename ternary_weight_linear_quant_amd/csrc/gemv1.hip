@@ -632,15 +632,17 @@ hipError_t launch_gemv1(const int8_t* xq, const float* xs, int K, const uint32_t
 // graphs, ten rotated copies per matrix) against act quant + GEMV: 2560 ->
 // 2560 3.9 against 5.2 us per projection, 3200 -> 8640 6.1 against 7.2,
 // 8192 -> 28672 13.7 against 15.6, 28672 -> 8192 14.2 against 16.1; on
-// 8192-row matrices of 12288 / 16384 / 20480 / 24576 / 32768 columns 7.8 /
-// 9.4 / 11.6 / 13.0 / 16.4 against 9.8 / 11.4 / 13.4 / 14.9 / 19.4. From five
-// pieces on, 16-wave workgroups: their threads hold fewer slots of the token
-// (the 8-wave shapes of the GEMV alone measured 13.0, 14.5 and 20.3 us
-// there). With a
-// gain on longer rows the fp64 sum of squares would be taken in another order
-// than the stand-alone quantiser's (the scale could differ in its last bit),
-// and rows with a partial second piece keep the cached kernel, whose per-
-// workgroup token copies cost more than the second launch saves there.
+// 8192-row matrices of 12288 / 16384 / 20480 / 24576 / 32768 columns 7.3 /
+// 9.4 / 11.6 / 13.0 / 16.4 against 9.8 / 11.4 / 13.4 / 14.9 / 19.4.
+// Workgroup sizes differ from the GEMV's where that measured faster: three
+// pieces take 8 waves (7.3 against 7.8 us with 4; at two pieces 8 or 16 waves
+// were slower, 14.4-16.0 against 13.6), and from five pieces on 16 waves,
+// whose threads hold fewer slots of the token (8-wave workgroups took 13.0,
+// 14.5 and 20.3 us at five, six and eight pieces). With a gain on longer rows
+// the fp64 sum of squares would be taken in another order than the
+// stand-alone quantiser's (the scale could differ in its last bit), and rows
+// with a partial second piece keep the cached kernel, whose per-workgroup
+// token copies cost more than the second launch saves there.
 bool gemv1_quant_supported(int64_t M, int64_t K, bool norm) {
     if (M != 1) return false;
     if (K <= kPieceK) return true;
@@ -675,7 +677,7 @@ hipError_t launch_gemv1_quant(const uint16_t* x, const uint16_t* gain, float rms
             if (N >= 4) return launch_rows<2, 4, 4, 4, true>(a, stream);
             return launch_stream<2, 2, 8, true>(a, stream);
         case 3:
-            if (N >= 4) return launch_rows<3, 4, 4, 4, true>(a, stream);
+            if (N >= 4) return launch_rows<3, 4, 4, 8, true>(a, stream);
             return launch_stream<3, 2, 8, true>(a, stream);
         case 4:
             if (N >= 2) return launch_rows<4, 2, 4, 8, true>(a, stream);
