@@ -137,6 +137,20 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
         : "memory");
 }
 
+// The same transfer from a wave-uniform 64-bit base (SGPRs) plus a per-lane
+// 32-bit byte offset: a loop that advances the base moves no per-lane address.
+__device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(sbase), "s"(lds_base)
+        : "memory");
+}
+
 // s_waitcnt with vmcnt = n (other counters unconstrained), n < 64.
 #define BL_WAIT_VMCNT(n) \
     __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | ((((n) >> 4) & 3) << 14))

@@ -11,11 +11,14 @@
 // y = x_q . q^T with v_mfma_i32_32x32x32_i8: A = activation tile (rows =
 // tokens), B = weight tile (rows = output features), both k-contiguous.
 // Workgroup: WGM x WGN waves over a BM x BN tile, each wave a (BM/WGM) x
-// (BN/WGN) block of 32 x 32 MFMA tiles; K step 128. A STAGES-deep LDS ring is filled with global_load_lds_dwordx4 (each
-// lane's 16 bytes land directly in LDS, no register staging): per stage the
-// activation tile (BM x 128 B) and the PACKED weight tile (BN x 32 B, 2 bits
-// per weight). Loads for stage kt+STAGES-1 are issued before computing stage
-// kt, and an explicit vmcnt wait keeps STAGES-1 stages in flight.
+// (BN/WGN) block of 32 x 32 MFMA tiles; K step 128. A STAGES-deep LDS ring
+// is filled with global_load_lds_dwordx4 (each lane's 16 bytes land directly
+// in LDS, no register staging; a wave-uniform base in SGPRs plus a fixed
+// per-lane offset, so a stage's addresses cost no vector arithmetic): per
+// stage the activation tile (BM x 128 B) and the PACKED weight tile (BN x 32
+// B, 2 bits per weight). Loads for stage kt+STAGES-1 are issued before
+// computing stage kt, and an explicit vmcnt wait keeps STAGES-1 stages in
+// flight.
 //
 // Fragment reads: lane (r, g) of a B fragment reads 16 B = 4 packed words of
 // its weight row; word s feeds k-substep s after expansion to 16 signed bytes
@@ -118,27 +121,30 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, WPE) void k_gemm(
     auto lstep = [&](int kt) { return kt * KS + kg; };
     constexpr int SLOT = KS * STAGE;  // one ring slot: a stage per K group
 
-    // Per-lane global sources for the stage loads (k offset added per stage).
+    // Stage loads: a wave-uniform base (the tile's first row at this stage's
+    // k, in SGPRs) plus a fixed per-lane byte offset, so advancing a stage
+    // costs no per-lane arithmetic. Offsets stay below 2^31: at most 127
+    // activation rows of K bytes (fewer than M * K) and 511 weight rows of K/4.
     // A instruction i of this wave covers rows 8q .. 8q+7 (q as above); the
     // lane takes row 8q + lane/8, whose LDS slot is physical chunk lane%8.
     const int a_cnt = A_EVEN ? A_INSTR : (A_TOTAL - 1 - wave) / NW + 1;  // wave-uniform
     auto a_q = [&](int i) { return A_EVEN ? wave * A_INSTR + i : wave + NW * i; };
-    const int8_t* a_src[A_INSTR];
-    int a_chunk[A_INSTR];
+    const int8_t* a_base = xq + (size_t)m0 * K;
+    uint32_t a_off[A_INSTR];
 #pragma unroll
     for (int i = 0; i < A_INSTR; ++i) {
         const int r = 8 * min(a_q(i), A_TOTAL - 1) + lane / 8;
-        a_chunk[i] = (lane % 8) ^ swz_a(r);
-        a_src[i] = xq + (size_t)min(m0 + r, M - 1) * K;
+        const int c = (lane % 8) ^ swz_a(r);
+        a_off[i] = (uint32_t)(min(m0 + r, M - 1) - m0) * (uint32_t)K + 16u * c;
     }
     const bool b_loader = wave < B_WAVES;  // wave-uniform
-    const uint8_t* b_src[B_INSTR];
-    int b_chunk[B_INSTR];
+    const uint8_t* b_base = reinterpret_cast<const uint8_t*>(Wp) + (size_t)n0 * (K / 4);
+    uint32_t b_off[B_INSTR];
 #pragma unroll
     for (int i = 0; i < B_INSTR; ++i) {
         const int r = min(wave, B_WAVES - 1) * B_ROWS + 32 * i + lane / 2;
-        b_chunk[i] = (lane % 2) ^ swz_b(r);
-        b_src[i] = reinterpret_cast<const uint8_t*>(Wp) + (size_t)min(n0 + r, N - 1) * (K / 4);
+        const int c = (lane % 2) ^ swz_b(r);
+        b_off[i] = (uint32_t)(min(n0 + r, N - 1) - n0) * (uint32_t)(K / 4) + 16u * c;
     }
 
     const uint32_t smem_base = (uint32_t)(size_t)(lds_u8_t*)smem;
@@ -147,21 +153,40 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, WPE) void k_gemm(
         const uint32_t st = smem_base + (uint32_t)((kt % STAGES) * SLOT + kg * STAGE);
         const int ks = kt0 + min(lstep(kt), nk - 1);
         const int k0 = ks * kBK;
-        const bool tail = k_tail && ks == KT - 1;
+        const int8_t* ab = a_base + k0;
+        const uint8_t* bb = b_base + k0 / 4;
+        if (k_tail && ks == KT - 1) {
+            // Last stage of a ragged K (64 valid k): activation chunks 4..7
+            // and the second weight chunk would lie past K; they read chunk
+            // c - 4 and chunk 0 instead (any valid address: the weights
+            // there are expanded as zeros).
+#pragma unroll
+            for (int i = 0; i < A_INSTR; ++i) {
+                if (!A_EVEN && i >= a_cnt) break;
+                const int r = 8 * min(a_q(i), A_TOTAL - 1) + lane / 8;
+                const bool hi = ((lane % 8) ^ swz_a(r)) >= 4;
+                lds_dma16_s(ab, hi ? a_off[i] - 64u : a_off[i], st + 8 * a_q(i) * kARow);
+            }
+            if (b_loader) {
+#pragma unroll
+                for (int i = 0; i < B_INSTR; ++i) {
+                    const int r = min(wave, B_WAVES - 1) * B_ROWS + 32 * i + lane / 2;
+                    const uint32_t c = (uint32_t)((lane % 2) ^ swz_b(r));
+                    lds_dma16_s(bb, b_off[i] - 16u * c,
+                                st + A_STAGE + (wave * B_ROWS + 32 * i) * kBRow);
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < A_INSTR; ++i) {
             if (!A_EVEN && i >= a_cnt) break;
-            int c = a_chunk[i];
-            if (tail && c >= 4) c -= 4;  // beyond K: any valid address (B is zero there)
-            lds_dma16(a_src[i] + k0 + 16 * c, st + 8 * a_q(i) * kARow);
+            lds_dma16_s(ab, a_off[i], st + 8 * a_q(i) * kARow);
         }
         if (b_loader) {
 #pragma unroll
-            for (int i = 0; i < B_INSTR; ++i) {
-                const int c = tail ? 0 : b_chunk[i];
-                lds_dma16(b_src[i] + k0 / 4 + 16 * c,
-                          st + A_STAGE + (wave * B_ROWS + 32 * i) * kBRow);
-            }
+            for (int i = 0; i < B_INSTR; ++i)
+                lds_dma16_s(bb, b_off[i], st + A_STAGE + (wave * B_ROWS + 32 * i) * kBRow);
         }
     };
 
@@ -241,57 +266,64 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, WPE) void k_gemm(
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
     }
-    uint4 bp[TN], bpn[TN];
-    v4i af[TM], an[TM], bf[TN], bfn[TN];
-    read_b(bp, 0);
-    read_a(af, 0, 0);
-    expand(bf, bp, 0, keep_mask(0));
+    // Operand registers alternate instead of being copied: sub-step s uses
+    // the fragment pair of parity s % 2 while the next sub-step's is read into
+    // the other (four sub-steps, so each K step starts on pair 0), and the
+    // packed weights of step kt and kt + 1 alternate between two buffers as
+    // the K loop runs two steps per trip.
+    uint4 bpA[TN], bpB[TN];
+    v4i a0[TM], a1[TM], b0[TN], b1[TN];
+    read_b(bpA, 0);
+    read_a(a0, 0, 0);
+    expand(b0, bpA, 0, keep_mask(0));
 
-    for (int kt = 0; kt < NK; ++kt) {
-        const bool more = kt + 1 < NK;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            // Next fragments: same step for s < 3, else the first of kt+1.
-            if (s < 3) {
-                read_a(an, kt, s + 1);
-                expand(bfn, bp, s + 1, keep_mask(kt));
-            } else if (more) {
-                read_a(an, kt + 1, 0);
-                expand(bfn, bpn, 0, keep_mask(kt + 1));
-            }
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j],
-                                                                      0, 0, 0);
-            // The next sub-step's LDS fragment reads go first, so they have a
-            // whole sub-step of MFMAs to land; the expansion arithmetic is
-            // interleaved with the MFMAs.
-            __builtin_amdgcn_sched_group_barrier(0x100, TM, 0);
-#pragma unroll
-            for (int q = 0; q < TM * TN; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-            }
-            if (s == 1 && more) {
-                // Stage kt+1 landed once the stages issued after it are the
-                // only loads outstanding.
-                const int after = min(STAGES - 3, NK - 2 - kt);
-                wait_for(std::integral_constant<int, STAGES - 3>(), after);
-                __builtin_amdgcn_s_barrier();
-                asm volatile("" ::: "memory");
-                if (kt + STAGES - 1 < NK) issue(kt + STAGES - 1);
-                read_b(bpn, kt + 1);
-            }
-#pragma unroll
-            for (int i = 0; i < TM; ++i) af[i] = an[i];
-#pragma unroll
-            for (int j = 0; j < TN; ++j) bf[j] = bfn[j];
-            __builtin_amdgcn_sched_barrier(0);
+    auto substep = [&](auto s_const, int kt, bool more, const uint4 (&bp)[TN], uint4 (&bpn)[TN],
+                       const v4i (&ac)[TM], const v4i (&bc)[TN], v4i (&an)[TM], v4i (&bn)[TN]) {
+        constexpr int s = decltype(s_const)::value;
+        // Next fragments: same step for s < 3, else the first of kt+1.
+        if (s < 3) {
+            read_a(an, kt, s + 1);
+            expand(bn, bp, s + 1, keep_mask(kt));
+        } else if (more) {
+            read_a(an, kt + 1, 0);
+            expand(bn, bpn, 0, keep_mask(kt + 1));
         }
 #pragma unroll
-        for (int j = 0; j < TN; ++j) bp[j] = bpn[j];
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ac[i], bc[j], acc[i][j], 0, 0, 0);
+        // The next sub-step's LDS fragment reads go first, so they have a
+        // whole sub-step of MFMAs to land; the expansion arithmetic is
+        // interleaved with the MFMAs.
+        __builtin_amdgcn_sched_group_barrier(0x100, TM, 0);
+#pragma unroll
+        for (int q = 0; q < TM * TN; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+        if (s == 1 && more) {
+            // Stage kt+1 landed once the stages issued after it are the
+            // only loads outstanding.
+            const int after = min(STAGES - 3, NK - 2 - kt);
+            wait_for(std::integral_constant<int, STAGES - 3>(), after);
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            if (kt + STAGES - 1 < NK) issue(kt + STAGES - 1);
+            read_b(bpn, kt + 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto kstep = [&](int kt, const uint4 (&bp)[TN], uint4 (&bpn)[TN]) {
+        const bool more = kt + 1 < NK;
+        substep(std::integral_constant<int, 0>(), kt, more, bp, bpn, a0, b0, a1, b1);
+        substep(std::integral_constant<int, 1>(), kt, more, bp, bpn, a1, b1, a0, b0);
+        substep(std::integral_constant<int, 2>(), kt, more, bp, bpn, a0, b0, a1, b1);
+        substep(std::integral_constant<int, 3>(), kt, more, bp, bpn, a1, b1, a0, b0);
+    };
+    for (int kt = 0; kt < NK; kt += 2) {
+        kstep(kt, bpA, bpB);
+        if (kt + 1 < NK) kstep(kt + 1, bpB, bpA);
     }
 
     // Epilogue. C layout of the 32x32 MFMA: lane l, register v holds row
