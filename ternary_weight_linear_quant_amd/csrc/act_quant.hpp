@@ -13,6 +13,8 @@
 // and sum x^2 in fp64.
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace bl {
@@ -24,14 +26,20 @@ constexpr int kActThreads = 256;  // threads that hold one token's values
 // sum of squares the order decides the rounding). Every thread of the
 // workgroup calls it, since it holds a barrier; threads of later waves pass a
 // neutral value and are left out. The result reaches every thread. `scratch`
-// holds NW entries.
+// holds NW entries. The max (of magnitudes: finite and at least +0, where the
+// float order is the unsigned order of the bits) runs on DPP instead of the
+// butterfly; a max is exact in any order.
 template <typename T, bool MAX, int NW = kActThreads / kWave>
 __device__ __forceinline__ T act_reduce(T v, T* scratch) {
     const int wave = threadIdx.x / kWave;
+    if constexpr (MAX && std::is_same<T, float>::value) {
+        v = __uint_as_float(wave_max_u32(__float_as_uint(v)));
+    } else {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const T other = __shfl_xor(v, o, kWave);
-        v = MAX ? (v > other ? v : other) : v + other;
+        for (int o = 32; o > 0; o >>= 1) {
+            const T other = __shfl_xor(v, o, kWave);
+            v = MAX ? (v > other ? v : other) : v + other;
+        }
     }
     if ((threadIdx.x % kWave) == 0 && wave < NW) scratch[wave] = v;
     __syncthreads();

@@ -215,6 +215,20 @@ __device__ __forceinline__ int wave_sum_i32(int v) {
            __builtin_amdgcn_readlane(v, 47) + __builtin_amdgcn_readlane(v, 63);
 }
 
+// Maximum of a uint32 over the 64 lanes of a wave (all lanes active), in every
+// lane, the same way: DPP row shifts (lanes shifted in read 0, neutral for an
+// unsigned max), then the four row results.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true));
+    return max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 15),
+                   (uint32_t)__builtin_amdgcn_readlane((int)v, 31)),
+               max((uint32_t)__builtin_amdgcn_readlane((int)v, 47),
+                   (uint32_t)__builtin_amdgcn_readlane((int)v, 63)));
+}
+
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
