@@ -157,13 +157,23 @@ __global__ __launch_bounds__(64 * (GLU ? 2 : 1) * RG * KS) void k_ffn_gemv(
     }
     if constexpr (!SUBLN)
         amax = bf16_to_f32(mbits[0] > mbits[1] ? mbits[0] : mbits[1]);
-    // Lanes with equal lane % M hold the same token.
+    // Lanes with equal lane % M hold the same token. One token: the max on DPP
+    // (magnitudes, so the unsigned order of the bits; exact in any order),
+    // the fp64 sum in the butterfly's order as for several tokens.
+    if (M == 1) {
+        amax = __uint_as_float(wave_max_u32(__float_as_uint(amax)));
+        if constexpr (SUBLN) {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        if (o >= M) {
-            amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
-            if constexpr (SUBLN) ss += __shfl_xor(ss, o, kWave);
+            for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, kWave);
         }
+    } else {
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1)
+            if (o >= M) {
+                amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+                if constexpr (SUBLN) ss += __shfl_xor(ss, o, kWave);
+            }
+    }
     if (lane < M) {
         s_amax[wave][lane] = amax;
         if constexpr (SUBLN) s_ss[wave][lane] = ss;
