@@ -1352,9 +1352,11 @@ def test_ste_backward_dx_large_tiles_ragged():
 
 
 # dW: tokens ragged against the 64-token padding, features ragged against the
-# 128 x 256 tiles and the 64-wide stages.
+# 128 x 256 tiles and the 64-wide stages. The last two have more tiles than
+# CUs with a last round at most half full (612 and 273 tiles), so their last
+# row tiles go through the second launch of 64 x 64 tiles (760 and 168 rows).
 STE_DW_CASES = [(1, 8, 64), (3, 40, 128), (70, 136, 320), (200, 264, 576), (64, 128, 256),
-                (130, 520, 704), (257, 1000, 1344)]
+                (130, 520, 704), (257, 1000, 1344), (70, 4344, 4608), (33, 2600, 3328)]
 
 
 def _dw_bound(dy_bits, xq, xs):

@@ -234,7 +234,10 @@ def test_ffn_step_guards_and_repeats(M):
 
 # ------------------------------------------------ straight-through backward ----
 
-@pytest.mark.parametrize("M,N,K", [(3, 40, 128), (130, 264, 192), (257, 1000, 1344)])
+# The last shape's dW takes two launches (273 tiles of 128 x 256: its last
+# two row tiles as 64 x 64 tiles).
+@pytest.mark.parametrize("M,N,K", [(3, 40, 128), (130, 264, 192), (257, 1000, 1344),
+                                   (33, 2600, 3328)])
 def test_ste_guards_and_repeats(M, N, K):
     rng = np.random.default_rng(66 + M)
     q = _codes(rng, N, K)
