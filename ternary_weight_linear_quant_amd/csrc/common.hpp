@@ -196,12 +196,6 @@ __device__ __forceinline__ void wait_stages(int stages) {
     }
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-    return v;
-}
-
 // Sum of an int32 over the 64 lanes of a wave (all lanes active), returned in
 // every lane: each 16-lane row forms inclusive prefix sums with DPP row shifts
 // (lanes shifted in from outside the row read 0), then the four row totals
@@ -227,12 +221,6 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
                    (uint32_t)__builtin_amdgcn_readlane((int)v, 31)),
                max((uint32_t)__builtin_amdgcn_readlane((int)v, 47),
                    (uint32_t)__builtin_amdgcn_readlane((int)v, 63)));
-}
-
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
 }
 
 }  // namespace bl
