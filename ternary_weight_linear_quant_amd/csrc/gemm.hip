@@ -149,13 +149,25 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, WPE) void k_gemm(
 
     const uint32_t smem_base = (uint32_t)(size_t)(lds_u8_t*)smem;
 
-    auto issue = [&](int kt) {
-        const uint32_t st = smem_base + (uint32_t)((kt % STAGES) * SLOT + kg * STAGE);
-        const int ks = kt0 + min(lstep(kt), nk - 1);
+    // CLEAN (chosen once per workgroup, below): K is a whole number of steps
+    // and every K group has the same number of them, so no step is ragged or
+    // past the workgroup's range; the masks are then constants and the
+    // ragged-step branch is not compiled, which takes most of the scalar
+    // control out of the loop (it otherwise rivals the MFMA count when a
+    // wave has only two MFMAs per sub-step). Both forms do the same loads,
+    // expansions and MFMAs in the same order on such shapes.
+    //
+    // Ring slots are byte offsets (slot * SLOT) advanced step by step.
+    auto next_slot = [](int off) { return off + SLOT == STAGES * SLOT ? 0 : off + SLOT; };
+
+    auto issue = [&](auto clean_c, int kt, int slot) {
+        constexpr bool CLEAN = decltype(clean_c)::value;
+        const uint32_t st = smem_base + (uint32_t)(slot + kg * STAGE);
+        const int ks = CLEAN ? kt0 + lstep(kt) : kt0 + min(lstep(kt), nk - 1);
         const int k0 = ks * kBK;
         const int8_t* ab = a_base + k0;
         const uint8_t* bb = b_base + k0 / 4;
-        if (k_tail && ks == KT - 1) {
+        if (!CLEAN && k_tail && ks == KT - 1) {
             // Last stage of a ragged K (64 valid k): activation chunks 4..7
             // and the second weight chunk would lie past K; they read chunk
             // c - 4 and chunk 0 instead (any valid address: the weights
@@ -201,9 +213,9 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, WPE) void k_gemm(
 
     const int fr = lane % 32, fg = lane / 32;
 
-    // Fragment reads from LDS stage `kt % STAGES`.
-    auto read_b = [&](uint4* bp, int kt) {
-        const uint8_t* Bs = smem + (kt % STAGES) * SLOT + kg * STAGE + A_STAGE;
+    // Fragment reads from the LDS ring slot at byte offset `slot`.
+    auto read_b = [&](uint4* bp, int slot) {
+        const uint8_t* Bs = smem + slot + kg * STAGE + A_STAGE;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int r = wn0 + 32 * j + fr;
@@ -214,12 +226,13 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, WPE) void k_gemm(
     // group 1) lie past K, so that group's codes are replaced by code 1
     // (weight 0) when they are expanded. Applied at expansion, not at the
     // LDS read, so the read need not complete right after the barrier.
-    auto keep_mask = [&](int kt) -> uint32_t {
+    auto keep_mask = [&](auto clean_c, int kt) -> uint32_t {
+        if constexpr (decltype(clean_c)::value) return 0xFFFFFFFFu;
         if (KS > 1 && lstep(kt) >= nk) return 0u;
         return (k_tail && kt0 + lstep(kt) == KT - 1 && fg) ? 0u : 0xFFFFFFFFu;
     };
-    auto read_a = [&](v4i* af, int kt, int s) {
-        const uint8_t* As = smem + (kt % STAGES) * SLOT + kg * STAGE;
+    auto read_a = [&](v4i* af, int slot, int s) {
+        const uint8_t* As = smem + slot + kg * STAGE;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int r = wm0 + 32 * i + fr;
@@ -256,75 +269,87 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, WPE) void k_gemm(
         }
     };
     static_assert(STAGES >= 3, "pipeline depth");
+    auto run = [&](auto clean_c) {
 #pragma unroll
-    for (int st = 0; st < STAGES - 1; ++st)
-        if (st < NK) issue(st);
-    // Stage 0 landed: STAGES-2 later stages may still be in flight.
-    {
-        const int after = min(STAGES - 2, NK - 1);
-        wait_for(std::integral_constant<int, STAGES - 2>(), after);
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-    }
-    // Operand registers alternate instead of being copied: sub-step s uses
-    // the fragment pair of parity s % 2 while the next sub-step's is read into
-    // the other (four sub-steps, so each K step starts on pair 0), and the
-    // packed weights of step kt and kt + 1 alternate between two buffers as
-    // the K loop runs two steps per trip.
-    uint4 bpA[TN], bpB[TN];
-    v4i a0[TM], a1[TM], b0[TN], b1[TN];
-    read_b(bpA, 0);
-    read_a(a0, 0, 0);
-    expand(b0, bpA, 0, keep_mask(0));
-
-    auto substep = [&](auto s_const, int kt, bool more, const uint4 (&bp)[TN], uint4 (&bpn)[TN],
-                       const v4i (&ac)[TM], const v4i (&bc)[TN], v4i (&an)[TM], v4i (&bn)[TN]) {
-        constexpr int s = decltype(s_const)::value;
-        // Next fragments: same step for s < 3, else the first of kt+1.
-        if (s < 3) {
-            read_a(an, kt, s + 1);
-            expand(bn, bp, s + 1, keep_mask(kt));
-        } else if (more) {
-            read_a(an, kt + 1, 0);
-            expand(bn, bpn, 0, keep_mask(kt + 1));
-        }
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ac[i], bc[j], acc[i][j], 0, 0, 0);
-        // The next sub-step's LDS fragment reads go first, so they have a
-        // whole sub-step of MFMAs to land; the expansion arithmetic is
-        // interleaved with the MFMAs.
-        __builtin_amdgcn_sched_group_barrier(0x100, TM, 0);
-#pragma unroll
-        for (int q = 0; q < TM * TN; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-        }
-        if (s == 1 && more) {
-            // Stage kt+1 landed once the stages issued after it are the
-            // only loads outstanding.
-            const int after = min(STAGES - 3, NK - 2 - kt);
-            wait_for(std::integral_constant<int, STAGES - 3>(), after);
+        for (int st = 0; st < STAGES - 1; ++st)
+            if (st < NK) issue(clean_c, st, st * SLOT);
+        // Stage 0 landed: STAGES-2 later stages may still be in flight.
+        {
+            const int after = min(STAGES - 2, NK - 1);
+            wait_for(std::integral_constant<int, STAGES - 2>(), after);
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
-            if (kt + STAGES - 1 < NK) issue(kt + STAGES - 1);
-            read_b(bpn, kt + 1);
         }
-        __builtin_amdgcn_sched_barrier(0);
+        // Operand registers alternate instead of being copied: sub-step s uses
+        // the fragment pair of parity s % 2 while the next sub-step's is read into
+        // the other (four sub-steps, so each K step starts on pair 0), and the
+        // packed weights of step kt and kt + 1 alternate between two buffers as
+        // the K loop runs two steps per trip.
+        uint4 bpA[TN], bpB[TN];
+        v4i a0[TM], a1[TM], b0[TN], b1[TN];
+        // Slots of steps kt, kt + 1 and kt + STAGES - 1 (= kt - 1).
+        int slot0 = 0, slot1 = SLOT, slot_w = (STAGES - 1) * SLOT;
+        read_b(bpA, slot0);
+        read_a(a0, slot0, 0);
+        expand(b0, bpA, 0, keep_mask(clean_c, 0));
+
+        auto substep = [&](auto s_const, int kt, bool more, const uint4 (&bp)[TN], uint4 (&bpn)[TN],
+                           const v4i (&ac)[TM], const v4i (&bc)[TN], v4i (&an)[TM], v4i (&bn)[TN]) {
+            constexpr int s = decltype(s_const)::value;
+            // Next fragments: same step for s < 3, else the first of kt+1.
+            if (s < 3) {
+                read_a(an, slot0, s + 1);
+                expand(bn, bp, s + 1, keep_mask(clean_c, kt));
+            } else if (more) {
+                read_a(an, slot1, 0);
+                expand(bn, bpn, 0, keep_mask(clean_c, kt + 1));
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] =
+                        __builtin_amdgcn_mfma_i32_32x32x32_i8(ac[i], bc[j], acc[i][j], 0, 0, 0);
+            // The next sub-step's LDS fragment reads go first, so they have a
+            // whole sub-step of MFMAs to land; the expansion arithmetic is
+            // interleaved with the MFMAs.
+            __builtin_amdgcn_sched_group_barrier(0x100, TM, 0);
+#pragma unroll
+            for (int q = 0; q < TM * TN; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            }
+            if (s == 1 && more) {
+                // Stage kt+1 landed once the stages issued after it are the
+                // only loads outstanding.
+                const int after = min(STAGES - 3, NK - 2 - kt);
+                wait_for(std::integral_constant<int, STAGES - 3>(), after);
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+                if (kt + STAGES - 1 < NK) issue(clean_c, kt + STAGES - 1, slot_w);
+                read_b(bpn, slot1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        auto kstep = [&](int kt, const uint4 (&bp)[TN], uint4 (&bpn)[TN]) {
+            const bool more = kt + 1 < NK;
+            substep(std::integral_constant<int, 0>(), kt, more, bp, bpn, a0, b0, a1, b1);
+            substep(std::integral_constant<int, 1>(), kt, more, bp, bpn, a1, b1, a0, b0);
+            substep(std::integral_constant<int, 2>(), kt, more, bp, bpn, a0, b0, a1, b1);
+            substep(std::integral_constant<int, 3>(), kt, more, bp, bpn, a1, b1, a0, b0);
+            slot_w = slot0;
+            slot0 = slot1;
+            slot1 = next_slot(slot1);
+        };
+        for (int kt = 0; kt < NK; kt += 2) {
+            kstep(kt, bpA, bpB);
+            if (kt + 1 < NK) kstep(kt + 1, bpB, bpA);
+        }
     };
-    auto kstep = [&](int kt, const uint4 (&bp)[TN], uint4 (&bpn)[TN]) {
-        const bool more = kt + 1 < NK;
-        substep(std::integral_constant<int, 0>(), kt, more, bp, bpn, a0, b0, a1, b1);
-        substep(std::integral_constant<int, 1>(), kt, more, bp, bpn, a1, b1, a0, b0);
-        substep(std::integral_constant<int, 2>(), kt, more, bp, bpn, a0, b0, a1, b1);
-        substep(std::integral_constant<int, 3>(), kt, more, bp, bpn, a1, b1, a0, b0);
-    };
-    for (int kt = 0; kt < NK; kt += 2) {
-        kstep(kt, bpA, bpB);
-        if (kt + 1 < NK) kstep(kt + 1, bpB, bpA);
-    }
+    if (!k_tail && nk % KS == 0)
+        run(std::true_type());
+    else
+        run(std::false_type());
 
     // Epilogue. C layout of the 32x32 MFMA: lane l, register v holds row
     // 8*(v/4) + 4*(l/32) + v%4 (token) and column l%32 (output feature).
