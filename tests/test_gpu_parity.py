@@ -436,7 +436,11 @@ K_GROUP_CASES = [(512, 3200, 3200),   # 200 tiles of 64 x 128, 25 steps: two gro
                  # tiles, 48.5 steps, ragged N), or 64 x 64 tiles with four
                  # groups instead of a split (128 tiles of 32 whole steps; 135
                  # tiles of 24.5 steps with ragged N)
-                 (48, 6208, 24600), (50, 4096, 8192), (64, 3136, 8620)]
+                 (48, 6208, 24600), (50, 4096, 8192), (64, 3136, 8620),
+                 # N a multiple of 160 where 128 x 128 tiles would spill
+                 # into a second round: 128 x 160 tiles of two groups (216
+                 # tiles, 24.5 steps; 208 tiles of 24 whole steps)
+                 (500, 3136, 8640), (450, 3072, 8320)]
 
 
 @pytest.mark.parametrize("M,K,N", K_GROUP_CASES)

@@ -125,7 +125,7 @@ PRODUCT_CASES = [
     (3, 2560, 257, 1), (16, 6912, 100, 1), (9, 1024, 6150, 1),
     (37, 3200, 300, 3), (64, 8192, 129, 3),
     (2000, 320, 4000, 2), (1935, 448, 5000, 2), (4050, 704, 1920, 2),
-    (100, 2560, 300, 2), (70, 28672, 65, 2), (33, 8192, 1000, 2),
+    (100, 2560, 300, 2), (70, 28672, 65, 2), (33, 8192, 1000, 2), (500, 3136, 8640, 2),
 ]
 
 
