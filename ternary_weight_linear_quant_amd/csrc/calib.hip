@@ -2,13 +2,15 @@
 // compared against, written with the same load widths and matrix
 // instructions. Not part of the method.
 //
-//   k_calib_read  read-only HBM stream with 16-byte loads, all in flight
-//                 (the practical bandwidth ceiling of the decode GEMV),
+//   k_calib_read  read-only HBM stream with 16-byte non-temporal loads, all
+//                 in flight (the practical bandwidth ceiling of the decode
+//                 GEMV, whose weight loads carry the same hint),
 //   k_calib_copy  plain 16-byte copy of a known byte count (the reference
 //                 for scaling hardware byte counters to bytes),
 //   k_calib_mfma  back-to-back independent v_mfma_i32_32x32x32_i8 on register
 //                 operands (the practical int8 matrix-core ceiling of the
 //                 prefill GEMM).
+#include "common.hpp"
 #include "launch.hpp"
 
 namespace bl {
@@ -44,7 +46,7 @@ __global__ __launch_bounds__(kCalibThreads) void k_calib_read(const uint4* __res
 #pragma unroll
     for (int u = 0; u < kReadPerThread; ++u) {
         const size_t i = base + (size_t)u * kCalibThreads;
-        v[u] = i < n16 ? src[i] : make_uint4(0, 0, 0, 0);
+        v[u] = i < n16 ? load_stream16(src + i) : make_uint4(0, 0, 0, 0);
     }
     uint32_t acc = 0;
 #pragma unroll

@@ -119,6 +119,23 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
     return (uint32_t)(size_t)(const lds_u8_t*)p;
 }
 
+// 16 bytes of a weight stream that the call reads exactly once, in loads
+// whose lines the wave consumes whole at once (the one-token GEMV's 1 KB
+// pieces, the fused FFN kernel's chunks): a non-temporal load, so the stream
+// does not displace the lines that are reused (the staged activations, the
+// token every workgroup reads) from the caches. On the 70B rows at one token
+// this took the GEMV from 12.0 to 11.1 us per launch and a plain read of the
+// same bytes from 10.6 to 9.9; the fused FFN step at 16 tokens 16.7 -> 16.0
+// us per layer. The GEMM's weight tiles (32 bytes of a line per K step) and
+// the multi-token GEMV's chunks keep normal loads: with the hint the rest of
+// a line is gone before it is read (64 x 8192 -> 28672: 25.0 -> 30.7 us;
+// the GEMV at 4 tokens 17.3 -> 18.2, base-3 rows 15.2 -> 16.9).
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+    typedef unsigned v4u_t __attribute__((ext_vector_type(4)));
+    const v4u_t v = __builtin_nontemporal_load(reinterpret_cast<const v4u_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // 16 bytes per lane from global memory straight into LDS at
 // lds_base + 16 * lane (global_load_lds_dwordx4). lds_base must be wave-
 // uniform. Issued through asm so that the compiler adds no conservative

@@ -120,7 +120,7 @@ __global__ __launch_bounds__(64 * (GLU ? 2 : 1) * RG * KS) void k_ffn_gemv(
     uint4 wb[kFfnR];
 #pragma unroll
     for (int i = 0; i < kFfnR; ++i)
-        wb[i] = *reinterpret_cast<const uint4*>(wrow + 16 * (ks + KS * min(i, nw - 1)));
+        wb[i] = load_stream16(wrow + 16 * (ks + KS * min(i, nw - 1)));
 
     // 3. Per-token absmax (exact, order-free) of the cached units (of h*g
     //    under SUBLN, with sum h^2 beside it).
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(64 * (GLU ? 2 : 1) * RG * KS) void k_ffn_gemv(
             if (ci < nw) {
                 process(wb[i], ks + KS * ci);
                 if (ci + kFfnR < nw)
-                    wb[i] = *reinterpret_cast<const uint4*>(wrow + 16 * (ks + KS * (ci + kFfnR)));
+                    wb[i] = load_stream16(wrow + 16 * (ks + KS * (ci + kFfnR)));
             }
         }
     }
@@ -250,7 +250,7 @@ __global__ __launch_bounds__(64 * (GLU ? 2 : 1) * RG * KS) void k_ffn_gemv(
     const int rem = KW - 16 * nfull;
     if (rem != 0 && ks == KS - 1) {
         const bool gv = 4 * g < rem;
-        const uint4 wv = gv ? *reinterpret_cast<const uint4*>(wrow + 16 * nfull)
+        const uint4 wv = gv ? load_stream16(wrow + 16 * nfull)
                             : make_uint4(0, 0, 0, 0);
         const uint32_t w4[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll

@@ -273,7 +273,7 @@ __global__ __launch_bounds__(64 * WPB) void k_gemv1_cached(const Gemv1Args p) {
     auto load = [&](int i) -> uint4 {
         const int r = i / S, j = i % S;
         return kPiece * j + 16 * lane < RB
-                   ? *reinterpret_cast<const uint4*>(wrow + (size_t)r * RB + kPiece * j)
+                   ? load_stream16(wrow + (size_t)r * RB + kPiece * j)
                    : make_uint4(kZeroCodes, kZeroCodes, kZeroCodes, kZeroCodes);
     };
     uint4 wb[R];
@@ -375,9 +375,9 @@ __global__ __launch_bounds__(64 * WPB) void k_gemv1_stream(const Gemv1Args p) {
     const int n = min(n0, N - 1);
     const uint8_t* wrow = p.W + (size_t)n * RB + 16 * lane;
     auto load = [&](int j) -> uint4 {
-        if (SP > 0) return *reinterpret_cast<const uint4*>(wrow + kPiece * j);
+        if (SP > 0) return load_stream16(wrow + kPiece * j);
         return kPiece * j + 16 * lane < RB
-                   ? *reinterpret_cast<const uint4*>(wrow + kPiece * j)
+                   ? load_stream16(wrow + kPiece * j)
                    : make_uint4(kZeroCodes, kZeroCodes, kZeroCodes, kZeroCodes);
     };
     uint4 wb[R];
@@ -484,7 +484,7 @@ __global__ __launch_bounds__(64 * WPB) void k_gemv1_rows(const Gemv1Args p) {
     const int nb = min(n0, N - RW);
     const uint8_t* wrow = p.W + (size_t)nb * RB + 16 * lane;
     auto load = [&](int i) -> uint4 {
-        return *reinterpret_cast<const uint4*>(wrow + (size_t)(i / SP) * RB + kPiece * (i % SP));
+        return load_stream16(wrow + (size_t)(i / SP) * RB + kPiece * (i % SP));
     };
     uint4 wb[R];
 #pragma unroll
