@@ -137,7 +137,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, WPE) void k_gemm(
         const int c = (lane % 8) ^ swz_a(r);
         a_off[i] = (uint32_t)(min(m0 + r, M - 1) - m0) * (uint32_t)K + 16u * c;
     }
-    const bool b_loader = wave < B_WAVES;  // wave-uniform
+    const bool b_loader = B_WAVES == NW || wave < B_WAVES;  // wave-uniform
     const uint8_t* b_base = reinterpret_cast<const uint8_t*>(Wp) + (size_t)n0 * (K / 4);
     uint32_t b_off[B_INSTR];
 #pragma unroll
@@ -293,9 +293,12 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, WPE) void k_gemm(
         read_a(a0, slot0, 0);
         expand(b0, bpA, 0, keep_mask(clean_c, 0));
 
-        auto substep = [&](auto s_const, int kt, bool more, const uint4 (&bp)[TN], uint4 (&bpn)[TN],
-                           const v4i (&ac)[TM], const v4i (&bc)[TN], v4i (&an)[TM], v4i (&bn)[TN]) {
+        auto substep = [&](auto s_const, auto steady_c, int kt, bool more_rt,
+                           const uint4 (&bp)[TN], uint4 (&bpn)[TN], const v4i (&ac)[TM],
+                           const v4i (&bc)[TN], v4i (&an)[TM], v4i (&bn)[TN]) {
             constexpr int s = decltype(s_const)::value;
+            constexpr bool STEADY = decltype(steady_c)::value;
+            const bool more = STEADY || more_rt;
             // Next fragments: same step for s < 3, else the first of kt+1.
             if (s < 3) {
                 read_a(an, slot0, s + 1);
@@ -322,28 +325,43 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, WPE) void k_gemm(
             if (s == 1 && more) {
                 // Stage kt+1 landed once the stages issued after it are the
                 // only loads outstanding.
-                const int after = min(STAGES - 3, NK - 2 - kt);
+                const int after = STEADY ? STAGES - 3 : min(STAGES - 3, NK - 2 - kt);
                 wait_for(std::integral_constant<int, STAGES - 3>(), after);
                 __builtin_amdgcn_s_barrier();
                 asm volatile("" ::: "memory");
-                if (kt + STAGES - 1 < NK) issue(clean_c, kt + STAGES - 1, slot_w);
+                if (STEADY || kt + STAGES - 1 < NK) issue(clean_c, kt + STAGES - 1, slot_w);
                 read_b(bpn, slot1);
             }
             __builtin_amdgcn_sched_barrier(0);
         };
-        auto kstep = [&](int kt, const uint4 (&bp)[TN], uint4 (&bpn)[TN]) {
+        auto kstep = [&](auto steady_c, int kt, const uint4 (&bp)[TN], uint4 (&bpn)[TN]) {
             const bool more = kt + 1 < NK;
-            substep(std::integral_constant<int, 0>(), kt, more, bp, bpn, a0, b0, a1, b1);
-            substep(std::integral_constant<int, 1>(), kt, more, bp, bpn, a1, b1, a0, b0);
-            substep(std::integral_constant<int, 2>(), kt, more, bp, bpn, a0, b0, a1, b1);
-            substep(std::integral_constant<int, 3>(), kt, more, bp, bpn, a1, b1, a0, b0);
+            using S0 = std::integral_constant<int, 0>;
+            using S1 = std::integral_constant<int, 1>;
+            using S2 = std::integral_constant<int, 2>;
+            using S3 = std::integral_constant<int, 3>;
+            substep(S0(), steady_c, kt, more, bp, bpn, a0, b0, a1, b1);
+            substep(S1(), steady_c, kt, more, bp, bpn, a1, b1, a0, b0);
+            substep(S2(), steady_c, kt, more, bp, bpn, a0, b0, a1, b1);
+            substep(S3(), steady_c, kt, more, bp, bpn, a1, b1, a0, b0);
             slot_w = slot0;
             slot0 = slot1;
             slot1 = next_slot(slot1);
         };
-        for (int kt = 0; kt < NK; kt += 2) {
-            kstep(kt, bpA, bpB);
-            if (kt + 1 < NK) kstep(kt + 1, bpB, bpA);
+        // Steady state: while the STAGES - 1 steps after kt exist, every bound
+        // in the loop body is a constant (a next step exists, stage kt +
+        // STAGES - 1 is issued, STAGES - 3 stages stay in flight at the wait),
+        // so the body carries no scalar compare-and-branch chains; the last
+        // steps take the general body. Both do the same loads, waits and
+        // MFMAs in the same order.
+        int kt = 0;
+        for (; kt + 1 < NK - (STAGES - 1); kt += 2) {
+            kstep(std::true_type(), kt, bpA, bpB);
+            kstep(std::true_type(), kt + 1, bpB, bpA);
+        }
+        for (; kt < NK; kt += 2) {
+            kstep(std::false_type(), kt, bpA, bpB);
+            if (kt + 1 < NK) kstep(std::false_type(), kt + 1, bpB, bpA);
         }
     };
     if (!k_tail && nk % KS == 0)
