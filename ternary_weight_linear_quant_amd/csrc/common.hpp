@@ -140,32 +140,21 @@ __device__ __forceinline__ uint4 load_stream16(const void* p) {
 // lds_base + 16 * lane (global_load_lds_dwordx4). lds_base must be wave-
 // uniform. Issued through asm so that the compiler adds no conservative
 // waits before later LDS reads; completion is tracked with explicit vmcnt
-// waits (vector memory operations complete in issue order). M0 is saved and
-// restored around the load.
+// waits (vector memory operations complete in issue order). The LDS address
+// is an input operand bound to M0, so the compiler sets M0 itself (folding
+// the address arithmetic into that move) and knows what M0 holds afterwards:
+// one scalar instruction per transfer instead of a save, a set and a restore.
 __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %2\n\t"
-        "global_load_lds_dwordx4 %1, off\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(gptr), "s"(lds_base)
-        : "memory");
+    asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(gptr), "{m0}"(lds_base) : "memory");
 }
 
 // The same transfer from a wave-uniform 64-bit base (SGPRs) plus a per-lane
 // 32-bit byte offset: a loop that advances the base moves no per-lane address.
 __device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %3\n\t"
-        "global_load_lds_dwordx4 %1, %2\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(voff), "s"(sbase), "s"(lds_base)
-        : "memory");
+    asm volatile("global_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "{m0}"(lds_base)
+                 : "memory");
 }
 
 // s_waitcnt with vmcnt = n (other counters unconstrained), n < 64.
