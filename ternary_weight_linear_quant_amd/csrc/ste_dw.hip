@@ -28,6 +28,8 @@
 //
 // Roofline: MFMA (bf16). Algorithmic work per call = 2*M*N*K flops (the
 // matrix cores run twice that, the hi and the lo halves).
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -242,8 +244,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_ste_dw(
     read_frags(af, 0, 0, 0, wm0, TMc());
     read_frags(bf, 0, 0, A_STAGE, wn0, TNc());
 
-    for (int kt = 0; kt < NK; ++kt) {
-        const bool more = kt + 1 < NK;
+    // One K step; in the steady state (the STAGES - 1 steps after kt exist)
+    // every bound is a constant, so that body carries no compare-and-branch
+    // chains. Both bodies do the same loads, waits and MFMAs in the same order.
+    auto step = [&](auto steady_c, int kt) {
+        constexpr bool STEADY = decltype(steady_c)::value;
+        const bool more = STEADY || kt + 1 < NK;
 #pragma unroll
         for (int s = 0; s < SUB; ++s) {
             // The next substep's fragments (this stage, or the first of the
@@ -252,10 +258,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_ste_dw(
                 // Stage kt+1 landed once only the stages issued after it are
                 // outstanding; the barrier also proves every wave is done
                 // with stage kt-1, whose buffer is refilled now.
-                wait_stages<LOADS, STAGES - 3>(min(STAGES - 3, NK - 2 - kt));
+                wait_stages<LOADS, STAGES - 3>(STEADY ? STAGES - 3 : min(STAGES - 3, NK - 2 - kt));
                 __builtin_amdgcn_s_barrier();
                 asm volatile("" ::: "memory");
-                if (kt + STAGES - 1 < NK) issue(kt + STAGES - 1);
+                if (STEADY || kt + STAGES - 1 < NK) issue(kt + STAGES - 1);
             }
             if (s < SUB - 1) {
                 read_frags(an, kt, s + 1, 0, wm0, TMc());
@@ -276,7 +282,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_ste_dw(
             for (int j = 0; j < TN; ++j) bf[j] = bfn[j];
             __builtin_amdgcn_sched_barrier(0);
         }
-    }
+    };
+    int kt = 0;
+    for (; kt < NK - (STAGES - 1); ++kt) step(std::true_type(), kt);
+    for (; kt < NK; ++kt) step(std::false_type(), kt);
 
     // C layout of the 32x32 MFMA: lane l, register v holds row
     // 8*(v/4) + 4*(l/32) + v%4 (output feature n) and column l%32 (input
