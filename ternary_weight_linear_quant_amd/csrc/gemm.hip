@@ -612,15 +612,16 @@ hipError_t launch_gemm(const int8_t* xq, const float* xs, int M, int K, const ui
     const bool groups = splits == 1 || (t64 >= kCUs / 2 && (t64 >= 3 * kCUs / 4 || KT <= 128));
     // At most 64 tokens (one row of tiles), timed with the weights streamed
     // from HBM (copies rotated past the last-level cache): where four K
-    // groups of 4 waves would take the tile, two groups with a 6-deep ring
-    // instead (64 x 8192 -> 28672: 27.0 against 29.0 us); and where the
+    // groups of 4 waves would take the tile, two groups with a 4-deep ring
+    // instead (64 x 8192 -> 28672: 21.7 against 25.2 us for four groups and
+    // 23.0 for a 6-deep ring, with the steady-state loop); and where the
     // split would leave fewer than 24 steps per workgroup while 64 x 64
     // tiles still cover half the CUs, those tiles with four K groups of two
     // 64 x 32 waves and no split (64 x 3200 -> 8640: 15.2 against 18.2 us).
     if (M <= 64) {
         const int64_t t6464 = tiles(64, 64);
         if (groups && t64 <= kCUs && KT >= 48)
-            return launch_gemm_tile<64, 128, 1, 4, 6, 2, false, 2>(xq, xs, M, K, Wp, gamma, N, y,
+            return launch_gemm_tile<64, 128, 1, 4, 4, 2, false, 2>(xq, xs, M, K, Wp, gamma, N, y,
                                                                    acc, stream);
         if (!groups && (KT + splits - 1) / splits < 24 && 2 * t6464 >= kCUs && t6464 <= kCUs)
             return launch_gemm_tile<64, 64, 1, 2, 3, 2, false, 4>(xq, xs, M, K, Wp, gamma, N, y,

@@ -432,7 +432,7 @@ K_GROUP_CASES = [(512, 3200, 3200),   # 200 tiles of 64 x 128, 25 steps: two gro
                  (260, 2624, 6900),   # 270 tiles, 21 steps: two groups
                  (500, 8512, 3160),   # 200 tiles, 67 steps: four groups
                  (130, 6976, 8190),   # 192 tiles, 55 steps: four groups
-                 # At most 64 tokens: two groups with a 6-deep ring (193
+                 # At most 64 tokens: two groups with a 4-deep ring (193
                  # tiles, 48.5 steps, ragged N), or 64 x 64 tiles with four
                  # groups instead of a split (128 tiles of 32 whole steps; 135
                  # tiles of 24.5 steps with ragged N)
