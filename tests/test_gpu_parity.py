@@ -395,8 +395,9 @@ def test_gemm_large_tiles_ragged(M, K, N):
 
 # Few tiles split K across workgroups whose int32 partial sums are added into
 # y; y starts with garbage here (NaN bits) to show it is cleared first. With
-# many steps per split the workgroups also hold K groups: four for the 80-
-# and 64-token cases on K near 28672, two for the 100-token one; the last two
+# many steps per split the workgroups also hold K groups: four for the
+# 80-token case on K near 28672, two (4-deep ring) for the 64-token one and
+# two for the 100-token one; the last two
 # end K in a half step, and their last split's step count is not a multiple
 # of the group count.
 SPLIT_K_CASES = [(64, 8192, 700), (64, 28672, 260), (33, 6912, 1000), (80, 28672, 8192),
