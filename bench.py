@@ -843,8 +843,8 @@ def main():
         alg = sum(N * K // 4 + 4 + 64 * K + 4 * 64 + 4 * 64 * N for _, K, N in lprojs) / 2
         ops = sum(2 * 64 * N * K for _, K, N in lprojs) / 2
         extra["decode_M64_70b"] = {
-            "kernel": "k_gemm (bl_bitlinear's choice at 64 tokens: four K groups per "
-                      "workgroup; the down projection also splits K)",
+            "kernel": "k_gemm (bl_bitlinear's choice at 64 tokens: two K groups per "
+                      "workgroup with a 4-deep ring; the down projection also splits K)",
             "packed_GBps": round(packed_per_copy / 2 / t / 1e9, 1),
             "roofline": {"bound": "hbm", "achieved": round(alg / t / 1e9, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -75,8 +75,9 @@ PHASES = {
     "decode_70b_m64": (["gemv_wide.hip", "gemm.hip", "common.hpp"],
                        "bl_bitlinear at M=64 on the 70B shapes, 5 rotated copies",
                        2 * COPIES_70B,
-                       "bl_bitlinear call (up: k_gemm with four K groups; down: the same with "
-                       "split K between k_splitk_zero and k_splitk_finalize)"),
+                       "bl_bitlinear call (up: k_gemm with two K groups and a 4-deep ring; "
+                       "down: the same with split K between k_splitk_zero and "
+                       "k_splitk_finalize)"),
     "gemv_2560_m1": (["gemv1.hip", "act_quant.hpp", "common.hpp"],
                      "bl_bitlinear at M=1 on 2560->2560, 400 rotated copies",
                      COPIES_2560, "one-token GEMV launch (k_gemv1_cached)"),

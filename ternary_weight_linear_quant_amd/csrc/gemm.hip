@@ -600,40 +600,38 @@ hipError_t launch_gemm(const int8_t* xq, const float* xs, int M, int K, const ui
     // Few tiles (few tokens, or few output features): 64 x 128 tiles. A
     // 4-wave workgroup alone on a CU leaves one wave per SIMD, whose LDS and
     // VALU latencies the matrix cores then wait on; so the workgroup gets two
-    // (or, for long K with at most one tile per CU, four) K groups of 4 waves
-    // that add their partial sums through LDS. With fewer than half as many
-    // tiles as CUs, or few tiles and very long K, the K steps are instead
-    // split across workgroups until the grid covers every CU (each split
-    // keeps at least 8 steps), their exact int32 partial sums added with
-    // atomics into y. Integer addition makes every variant bit-identical.
+    // K groups of 4 waves that add their partial sums through LDS (a 4-deep
+    // ring where there is at most one tile per CU and K has at least 48
+    // steps). With fewer than half as many tiles as CUs, or few tiles and
+    // very long K, the K steps are instead split across workgroups until the
+    // grid covers every CU (each split keeps at least 8 steps), their exact
+    // int32 partial sums added with atomics into y. Integer addition makes
+    // every variant bit-identical.
     const int64_t t64 = tiles(64, 128);
     const int KT = (K + kBK - 1) / kBK;
     const int splits = (int)std::min<int64_t>((kCUs + t64 - 1) / t64, std::max(1, KT / 8));
     const bool groups = splits == 1 || (t64 >= kCUs / 2 && (t64 >= 3 * kCUs / 4 || KT <= 128));
-    // At most 64 tokens (one row of tiles), timed with the weights streamed
-    // from HBM (copies rotated past the last-level cache): where four K
-    // groups of 4 waves would take the tile, two groups with a 4-deep ring
-    // instead (64 x 8192 -> 28672: 21.7 against 25.2 us for four groups and
-    // 23.0 for a 6-deep ring, with the steady-state loop); and where the
-    // split would leave fewer than 24 steps per workgroup while 64 x 64
-    // tiles still cover half the CUs, those tiles with four K groups of two
-    // 64 x 32 waves and no split (64 x 3200 -> 8640: 15.2 against 18.2 us).
+    // Long K with at most one tile per CU: two groups with a 4-deep ring,
+    // measured with the steady-state loop against four groups with three
+    // stages (the choice before it) and a 6-deep ring: 64 x 8192 -> 28672,
+    // weights streamed from HBM, 21.7 against 25.2 and 23.0 us; 512 x 8640 ->
+    // 3200 25.7 against 29.1 us.
+    if (groups && t64 <= kCUs && KT >= 48)
+        return launch_gemm_tile<64, 128, 1, 4, 4, 2, false, 2>(xq, xs, M, K, Wp, gamma, N, y, acc,
+                                                               stream);
+    // At most 64 tokens (one row of tiles), where the split would leave fewer
+    // than 24 steps per workgroup while 64 x 64 tiles still cover half the
+    // CUs: those tiles with four K groups of two 64 x 32 waves and no split
+    // (64 x 3200 -> 8640: 15.2 against 18.2 us, weights streamed from HBM).
     if (M <= 64) {
         const int64_t t6464 = tiles(64, 64);
-        if (groups && t64 <= kCUs && KT >= 48)
-            return launch_gemm_tile<64, 128, 1, 4, 4, 2, false, 2>(xq, xs, M, K, Wp, gamma, N, y,
-                                                                   acc, stream);
         if (!groups && (KT + splits - 1) / splits < 24 && 2 * t6464 >= kCUs && t6464 <= kCUs)
             return launch_gemm_tile<64, 64, 1, 2, 3, 2, false, 4>(xq, xs, M, K, Wp, gamma, N, y,
                                                                   acc, stream);
     }
-    if (groups) {
-        if (t64 <= kCUs && KT >= 48)
-            return launch_gemm_tile<64, 128, 1, 4, 3, 4, false, 4>(xq, xs, M, K, Wp, gamma, N, y,
-                                                                   acc, stream);
+    if (groups)
         return launch_gemm_tile<64, 128, 1, 4, 3, 4, false, 2>(xq, xs, M, K, Wp, gamma, N, y, acc,
                                                                stream);
-    }
     // Split K: with many steps per split, K groups inside each workgroup as
     // well (four from 40 steps, two from 24); fewer steps leave too little
     // per group to pay for the LDS reduction.

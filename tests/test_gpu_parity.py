@@ -424,15 +424,16 @@ def test_gemm_split_k(M, K, N):
     assert_y_close(y[idx].cpu().numpy(), y_ref, "split-K gemm")
 
 
-# Few tiles but many tokens: K groups inside each workgroup (two, or four for
-# long K with at most one tile per CU) add their partial sums through LDS.
+# Few tiles but many tokens: two K groups inside each workgroup (with a
+# 4-deep ring for long K with at most one tile per CU) add their partial
+# sums through LDS.
 # Step counts are not multiples of the group count, so some group's last step
 # lies past K (its weights expand as zeros); the last three cases end K in a
 # half (64-deep) step; M and N are ragged. y starts as NaN bits.
 K_GROUP_CASES = [(512, 3200, 3200),   # 200 tiles of 64 x 128, 25 steps: two groups
                  (260, 2624, 6900),   # 270 tiles, 21 steps: two groups
-                 (500, 8512, 3160),   # 200 tiles, 67 steps: four groups
-                 (130, 6976, 8190),   # 192 tiles, 55 steps: four groups
+                 (500, 8512, 3160),   # 200 tiles, 66.5 steps: 4-deep ring
+                 (130, 6976, 8190),   # 192 tiles, 54.5 steps: 4-deep ring
                  # At most 64 tokens: two groups with a 4-deep ring (193
                  # tiles, 48.5 steps, ragged N), or 64 x 64 tiles with four
                  # groups instead of a split (128 tiles of 32 whole steps; 135
