@@ -56,6 +56,7 @@ LARGE_COPIES = 5            # 5 x 2 x 58.7 MB of packed weights > 2 x 256 MB
 FFN_LAYERS = 40             # 40 x 13.3 MB of 2B4T FFN weights
 SMALL_COPIES = 400          # 400 x 1.64 MB of 2560 x 2560 packed weights
 BLOCK3B_COPIES = 20         # 20 x 31.1 MB of 3B-block packed weights
+GRAPH_CALLS = 4             # back-to-back calls per graph in the prefill legs
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
 
 
@@ -729,7 +730,7 @@ def main():
 
     def gemm_leg(label, wid, M, legs_w, reps):
         """Prefill GEMMs at M tokens: act quant then BitLinear per projection;
-        GEMM launches timed one by one with HIP events."""
+        the step and each projection's GEMM timed from HIP graphs."""
         legs = []
         for i, (name, K, N) in enumerate(legs_w):
             pk, g = wts[name][0] if wid == HEADLINE_WORKLOAD else prepare(wid, i, N, K)[0]
@@ -738,41 +739,44 @@ def main():
             y = torch.empty((M, N), dtype=torch.float32, device=dev)
             legs.append((name, K, N, x, xq, xs, pk, g, y))
 
-        def step(timer=None):
+        def step():
             for name, K, N, x, xq, xs, pk, g, y in legs:
-                if timer is None:
-                    bl.quantize_acts(x, out=(xq, xs))
-                    bl.bitlinear(xq, xs, pk, g, out=y)
-                else:
-                    timer.run("act_quant", lambda: bl.quantize_acts(x, out=(xq, xs)))
-                    timer.run(("gemm", name), lambda: bl.bitlinear(xq, xs, pk, g, out=y))
+                bl.quantize_acts(x, out=(xq, xs))
+                bl.bitlinear(xq, xs, pk, g, out=y)
 
-        settle(torch, step)
+        # Timed from HIP graphs (HIP events on the replaying stream), so the
+        # host's launch cost never leaves the GPU idle between short calls:
+        # the whole step, then each projection's GEMM and act quant alone,
+        # GRAPH_CALLS back-to-back calls per graph.
         for _ in range(1 + args.warmup):
             step()
         torch.cuda.synchronize()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(reps):
-            step()
-        b.record()
-        torch.cuda.synchronize()
-        p_ms = a.elapsed_time(b) / reps
+        gs = capture(step)
+        p_ms = time_graph(gs, reps)
+        del gs
         ops = sum(2 * M * N * K for _, K, N, *_ in legs)
-        tp = Timer(torch)
-        for _ in range(reps):
-            step(tp)
-        torch.cuda.synchronize()
         per = {}
         gemm_ms = 0.0
-        for name, K, N, *_ in legs:
-            ms = tp.total_ms(("gemm", name))
-            n = tp.count(("gemm", name))
+        aq_ms = 0.0
+        for name, K, N, x, xq, xs, pk, g, y in legs:
+            def gemms(xq=xq, xs=xs, pk=pk, g=g, y=y):
+                for _ in range(GRAPH_CALLS):
+                    bl.bitlinear(xq, xs, pk, g, out=y)
+
+            def quants(x=x, xq=xq, xs=xs):
+                for _ in range(GRAPH_CALLS):
+                    bl.quantize_acts(x, out=(xq, xs))
+
+            gg = capture(gemms)
+            ms = time_graph(gg, reps) / GRAPH_CALLS
+            del gg
+            gq = capture(quants)
+            aq_ms += time_graph(gq, reps) / GRAPH_CALLS
+            del gq
             gemm_ms += ms
-            per[name] = {"M": M, "K": K, "N": N, "avg_us": round(1e3 * ms / n, 2),
-                         "TOPS": round(2 * M * N * K * n / (ms * 1e-3) / 1e12, 1)}
-        tops = ops * reps / (gemm_ms * 1e-3) / 1e12
+            per[name] = {"M": M, "K": K, "N": N, "avg_us": round(1e3 * ms, 2),
+                         "TOPS": round(2 * M * N * K / (ms * 1e-3) / 1e12, 1)}
+        tops = ops / (gemm_ms * 1e-3) / 1e12
         # Context only: the vendor's plain int8 GEMM on the same shapes
         # (int8 x int8 -> int32, no ternary expansion, no fp32 epilogue).
         vendor_us = {}
@@ -802,7 +806,7 @@ def main():
                          "traffic_unit": "HBM bytes per bl_bitlinear call",
                          "alg_bytes_per_call": round(alg),
                          "per_projection": per},
-            "act_quant_avg_us": round(1e3 * tp.total_ms("act_quant") / tp.count("act_quant"), 2),
+            "act_quant_avg_us": round(1e3 * aq_ms / len(legs), 2),
             "vendor_int8_gemm": {
                 "library": "hipBLASLt through torch._int_mm: int8 x int8 -> int32 on the same "
                            "shapes, without the ternary expansion or the fp32 epilogue "
