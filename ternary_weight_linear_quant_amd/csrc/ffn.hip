@@ -71,7 +71,9 @@ __global__ __launch_bounds__(64 * (GLU ? 2 : 1) * RG * KS) void k_ffn_gemv(
     constexpr int NW = (GLU ? 2 : 1) * RG * KS;  // waves: (matrix, row group, K split)
     constexpr int NT = 64 * NW;             // threads
     constexpr int CACHE = CU;
-    static_assert(NT >= kFfnMinThreads && NT <= kFfnMaxThreads && CACHE >= 1, "block shape");
+    static_assert(NT >= kFfnMinThreads && NT <= kFfnMaxThreads && CACHE >= 1 &&
+                      CACHE <= kFfnMaxCache,
+                  "block shape");
     static_assert(!SUBLN || CU <= kFfnSublnCache, "register budget of the norm's gain cache");
     extern __shared__ __align__(16) uint8_t smem[];  // int8 activations, token-minor
     __shared__ v4i red[NW][kWave];

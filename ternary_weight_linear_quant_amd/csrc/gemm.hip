@@ -450,7 +450,8 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, WPE) void k_gemm(
                     if (n < N) {
                         const int32_t a = -acc[i][j][v];
                         // The output is not read again here: keep it out of
-                        // the L2 that holds the operand tiles.
+                        // the L2 that holds the operand tiles (plain stores
+                        // measured 0-9% slower on every prefill shape).
                         __builtin_nontemporal_store((float)a * sc, yrow + n);
                         if (arow) arow[n] = a;
                     }
