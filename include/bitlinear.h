@@ -437,8 +437,12 @@ int bl_ste_backward_dx(const uint16_t* dy, int64_t M, int64_t N, const uint8_t* 
                        const float* gamma, int64_t K, float* dx, void* stream);
 
 /* Bytes of the workspace bl_ste_backward_dw needs: 4*N*Mp + 2*K*Mp with Mp
- * = M rounded up to 64 (bf16 operands with the token index contiguous); 0 if
- * the shape is invalid (rules of bl_ste_backward_dw). Host-only. */
+ * = M rounded up to 64 (bf16 operands with the token index contiguous),
+ * plus S*R*K*4 where the call splits the contraction of its last output
+ * rows over S workgroups (R = those rows rounded up to 128, at most half a
+ * round of 128 x 256 tiles; S >= 2 from 512 tokens on, fp32 partial
+ * results); 0 if the shape is invalid (rules of bl_ste_backward_dw).
+ * Host-only. */
 size_t bl_ste_dw_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* Gradient of the latent weights under the straight-through estimator: the

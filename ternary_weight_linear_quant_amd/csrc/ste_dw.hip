@@ -139,10 +139,12 @@ __device__ __forceinline__ int dw_swz(int r) {
 
 // C[n][k] = sum_{j < 2 Mp} A[n][j] * B[k][j mod Mp]: BM x BN tiles of WGM x
 // WGN waves, BR contraction values per stage (2 * BR bytes per operand row).
-template <int BM, int BN, int WGM, int WGN, int BR, int STAGES, int WPE>
+// PART: workgroup (t, s) sums only stages [s * kt_per, (s + 1) * kt_per) of
+// tile t and stores that partial tile to part + s * N * K (layout of dW).
+template <int BM, int BN, int WGM, int WGN, int BR, int STAGES, int WPE, bool PART = false>
 __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_ste_dw(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, int N, int K, int Mp,
-    float* __restrict__ dW) {
+    float* __restrict__ dW, int kt_per, float* __restrict__ part) {
     constexpr int NW = WGM * WGN;
     constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int TM = WM / 32, TN = WN / 32;
@@ -178,7 +180,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_ste_dw(
     const int bn = (t % (G * nN)) / gsize;
     const int n0 = bm * BM, k0 = bn * BN;
 
-    const int NK = 2 * Mp / BR;  // stages; Mp % BR == 0, so none straddles the halves
+    // Stages; Mp % BR == 0, so none straddles the halves.
+    const int kt0 = PART ? (int)blockIdx.y * kt_per : 0;
+    const int NK = PART ? min(kt_per, 2 * Mp / BR - kt0) : 2 * Mp / BR;
 
     // Lane l of a DMA instruction fills physical chunk l % CH of row l / CH,
     // so it loads the logical chunk the swizzle maps there. Rows past N or
@@ -200,7 +204,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_ste_dw(
     const uint32_t smem_base = (uint32_t)(size_t)(lds_u8_t*)smem;
     auto issue = [&](int kt) {
         const uint32_t st = smem_base + (uint32_t)((kt % STAGES) * STAGE);
-        const int ja = kt * BR, jb = ja < Mp ? ja : ja - Mp;
+        const int ja = (kt0 + kt) * BR, jb = ja < Mp ? ja : ja - Mp;
 #pragma unroll
         for (int i = 0; i < A_INSTR; ++i)
             lds_dma16(a_src[i] + ja, st + (wave * (BM / NW) + RPI * i) * ROW);
@@ -296,11 +300,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_ste_dw(
         for (int v = 0; v < 16; ++v) {
             const int n = n0 + wm0 + 32 * i + 8 * (v / 4) + 4 * (lane / 32) + (v % 4);
             if (n < N) {
-                float* row = dW + (size_t)n * K;
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
                     const int k = k0 + wn0 + 32 * j + (lane % 32);
-                    if (k < K) __builtin_nontemporal_store(acc[i][j][v], row + k);
+                    if (k >= K) continue;
+                    // Partial tiles are read back at once by k_dw_reduce.
+                    if constexpr (PART)
+                        part[(size_t)blockIdx.y * N * K + (size_t)n * K + k] = acc[i][j][v];
+                    else
+                        __builtin_nontemporal_store(acc[i][j][v], dW + (size_t)n * K + k);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -308,24 +316,80 @@ __global__ __launch_bounds__(64 * WGM * WGN, WPE) void k_ste_dw(
     }
 }
 
-size_t ste_dw_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-    const int64_t Mp = ste_dw_padded_tokens(M);
-    return (size_t)(2 * N * 2 * Mp + 2 * K * Mp);  // bf16 A [N][2 Mp] and B [K][Mp]
+// dW[rows][K] = sum over s < S of part[s][rows][K], added in order of s.
+__global__ __launch_bounds__(256) void k_dw_reduce(const float* __restrict__ part, int S,
+                                                   size_t count, float* __restrict__ dW) {
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    const size_t stride = (size_t)gridDim.x * 256;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < count / 4; i += stride) {
+        f4 a = reinterpret_cast<const f4*>(part)[i];
+        for (int s = 1; s < S; ++s) {
+            const f4 b = reinterpret_cast<const f4*>(part + (size_t)s * count)[i];
+            a.x += b.x;
+            a.y += b.y;
+            a.z += b.z;
+            a.w += b.w;
+        }
+        __builtin_nontemporal_store(a, reinterpret_cast<f4*>(dW) + i);
+    }
 }
 
-template <int BM, int BN, int WGM, int WGN, int BR, int STAGES, int WPE>
+namespace {
+
+constexpr int kDwCUs = 256, kDwBM = 128, kDwBN = 256, kDwBR = 64;
+
+// The last round of 128 x 256 tiles, when at most half full, is not run as
+// such. Its row tiles (rows) either split their 2 Mp / 64 stages over
+// `splits` workgroups each (at least 8 stages per split, the grid at most one
+// round), their partial tiles kept in the workspace and added in a third
+// launch; or, where fewer than two splits would result, run as 64 x 64 tiles.
+struct DwPlan {
+    int rows = 0;    // rows of the tail (0: one launch covers dW)
+    int splits = 1;  // > 1: split tail, else 64 x 64 tail
+    int per = 0;     // stages per split
+};
+
+DwPlan dw_plan(int64_t N, int64_t K, int64_t Mp) {
+    DwPlan p;
+    const int64_t nM = (N + kDwBM - 1) / kDwBM, nN = (K + kDwBN - 1) / kDwBN;
+    const int64_t tiles = nM * nN, tail = tiles % kDwCUs;
+    const int64_t rem = (tail + nN - 1) / nN;
+    if (!(tiles > kDwCUs && tail > 0 && 2 * tail <= kDwCUs && rem < nM)) return p;
+    p.rows = (int)(rem * kDwBM);
+    const int64_t NK = 2 * Mp / kDwBR;
+    const int64_t s = std::min<int64_t>(kDwCUs / (rem * nN), NK / 8);
+    if (s >= 2) {
+        p.per = (int)((NK + s - 1) / s);
+        p.splits = (int)((NK + p.per - 1) / p.per);
+    }
+    return p;
+}
+
+}  // namespace
+
+size_t ste_dw_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    const int64_t Mp = ste_dw_padded_tokens(M);
+    const DwPlan p = dw_plan(N, K, Mp);
+    const int64_t part = p.splits > 1 ? (int64_t)p.splits * p.rows * K * 4 : 0;
+    // bf16 A [N][2 Mp] and B [K][Mp], then the split tail's fp32 partial tiles.
+    return (size_t)(2 * N * 2 * Mp + 2 * K * Mp + part);
+}
+
+template <int BM, int BN, int WGM, int WGN, int BR, int STAGES, int WPE, bool PART = false>
 static hipError_t launch_dw_tile(const uint16_t* A, const uint16_t* B, int N, int K, int Mp,
-                                 float* dW, hipStream_t stream) {
+                                 float* dW, hipStream_t stream, int splits = 1, int per = 0,
+                                 float* part = nullptr) {
     constexpr size_t lds = (size_t)STAGES * (BM + BN) * 2 * BR;
     static_assert(lds <= 160 * 1024, "a workgroup holds at most 160 KiB of LDS");
-    auto kern = &k_ste_dw<BM, BN, WGM, WGN, BR, STAGES, WPE>;
+    auto kern = &k_ste_dw<BM, BN, WGM, WGN, BR, STAGES, WPE, PART>;
     static std::atomic<uint64_t> lds_set{0};
     {
         hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kern), lds, lds_set);
         if (e != hipSuccess) return e;
     }
     const int tiles = ((N + BM - 1) / BM) * ((K + BN - 1) / BN);
-    hipLaunchKernelGGL(kern, dim3(tiles), dim3(64 * WGM * WGN), lds, stream, A, B, N, K, Mp, dW);
+    hipLaunchKernelGGL(kern, dim3(tiles, PART ? splits : 1), dim3(64 * WGM * WGN), lds, stream, A,
+                       B, N, K, Mp, dW, per, part);
     return hipGetLastError();
 }
 
@@ -348,26 +412,41 @@ hipError_t launch_ste_dw(const uint16_t* dy, int M, int N, const int8_t* xq, con
     // twice the barriers) or 16 waves of 64 x 64.
     //
     // One such tile per CU (144 KB of LDS): when the last round of tiles is
-    // at most half full, the last row tiles go to a second launch of 64 x 64
-    // tiles (48 KB, several per CU) instead, so that no round runs on a few
-    // CUs. Both launches write disjoint rows, and every output sums its
-    // products in the same order (the same MFMA, the same stages), so the
-    // split changes no bit. The 4096-token projections have 540 tiles (two
-    // rounds and 28): 383 -> 328 us on 6912 x 2560 and 366 -> 312 us on
-    // 2560 x 6912 (a remainder of 64 x 128 tiles: 339 / 321; of 128 x 128:
-    // 345 / 335).
-    constexpr int kCUs = 256, BM = 128, BN = 256;
-    const int nM = (N + BM - 1) / BM, nN = (K + BN - 1) / BN;
-    const int tiles = nM * nN, tail = tiles % kCUs;
-    const int rem = (tail + nN - 1) / nN;  // row tiles that make up the tail
-    if (tiles > kCUs && tail > 0 && 2 * tail <= kCUs && rem < nM) {
-        const int n1 = (nM - rem) * BM;
-        e = launch_dw_tile<BM, BN, 2, 4, 64, 3, 2>(A, B, n1, K, Mp, dW, stream);
+    // at most half full, the last row tiles (dw_plan) leave the first launch
+    // so that no round runs on a few CUs. With enough stages they stay
+    // 128 x 256 tiles whose stages are split over several workgroups each
+    // (the grid at most one round); each split stores its fp32 partial tile
+    // in the workspace and k_dw_reduce adds the partials in split order, so
+    // the result is the same from call to call, and each output is the sum
+    // of the same products, grouped by split. The 4096-token projections
+    // have 540 tiles (two rounds and 28): their last 3 and 2 row tiles take
+    // 8 and 4 splits of 16 and 32 stages. Otherwise the tail runs as 64 x 64
+    // tiles (48 KB, several per CU), in the same stage order as the first
+    // launch (same bits): 383 -> 328 us on 6912 x 2560 and 366 -> 312 us on
+    // 2560 x 6912 against one launch (a remainder of 64 x 128 tiles: 339 /
+    // 321; of 128 x 128: 345 / 335).
+    static_assert(kDwBM == 128 && kDwBN == 256 && kDwBR == 64, "tile of the plan");
+    const DwPlan plan = dw_plan(N, K, Mp);
+    if (plan.rows > 0) {
+        const int n1 = ((N + kDwBM - 1) / kDwBM - plan.rows / kDwBM) * kDwBM;  // first tail row
+        const int nt = N - n1;
+        e = launch_dw_tile<128, 256, 2, 4, 64, 3, 2>(A, B, n1, K, Mp, dW, stream);
         if (e != hipSuccess) return e;
-        return launch_dw_tile<64, 64, 2, 2, 64, 3, 4>(A + (size_t)n1 * 2 * Mp, B, N - n1, K, Mp,
-                                                      dW + (size_t)n1 * K, stream);
+        const uint16_t* At = A + (size_t)n1 * 2 * Mp;
+        float* dWt = dW + (size_t)n1 * K;
+        if (plan.splits < 2)
+            return launch_dw_tile<64, 64, 2, 2, 64, 3, 4>(At, B, nt, K, Mp, dWt, stream);
+        float* part = reinterpret_cast<float*>(B + (size_t)K * Mp);
+        e = launch_dw_tile<128, 256, 2, 4, 64, 3, 2, true>(At, B, nt, K, Mp, dWt, stream,
+                                                           plan.splits, plan.per, part);
+        if (e != hipSuccess) return e;
+        const size_t count = (size_t)nt * K;
+        const int blocks = (int)std::min<size_t>((count / 4 + 255) / 256, 2048);
+        hipLaunchKernelGGL(k_dw_reduce, dim3(blocks), dim3(256), 0, stream, part, plan.splits,
+                           count, dWt);
+        return hipGetLastError();
     }
-    return launch_dw_tile<BM, BN, 2, 4, 64, 3, 2>(A, B, N, K, Mp, dW, stream);
+    return launch_dw_tile<128, 256, 2, 4, 64, 3, 2>(A, B, N, K, Mp, dW, stream);
 }
 
 }  // namespace bl

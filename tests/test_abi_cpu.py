@@ -179,6 +179,15 @@ def test_invalid_arguments_rejected_before_launch(L):
     # straight-through weight gradient
     need_dw = L.bl_ste_dw_workspace_bytes(100, 64, 128)
     assert need_dw == 4 * 64 * 128 + 2 * 128 * 128
+    # Shapes whose last round of 128 x 256 tiles splits its stages add the
+    # fp32 partial tiles: splits x tail row tiles x 128 rows x K x 4 bytes.
+    assert L.bl_ste_dw_workspace_bytes(512, 2600, 3328) == \
+        4 * 2600 * 512 + 2 * 3328 * 512 + 2 * 256 * 3328 * 4
+    assert L.bl_ste_dw_workspace_bytes(4096, 6912, 2560) == \
+        4 * 6912 * 4096 + 2 * 2560 * 4096 + 8 * 384 * 2560 * 4
+    assert L.bl_ste_dw_workspace_bytes(4096, 2560, 6912) == \
+        4 * 2560 * 4096 + 2 * 6912 * 4096 + 4 * 256 * 6912 * 4
+    assert L.bl_ste_dw_workspace_bytes(33, 2600, 3328) == 4 * 2600 * 64 + 2 * 3328 * 64
     assert L.bl_ste_dw_workspace_bytes(100, 60, 128) == 0          # N % 8
     assert L.bl_ste_dw_workspace_bytes(100, 64, 96) == 0           # K % 64
     assert L.bl_ste_dw_workspace_bytes(0, 64, 128) == 0

@@ -1448,6 +1448,32 @@ def test_ste_backward_dw_full_size(idx):
         assert torch.equal(again.view(torch.int32), dW.view(torch.int32))
 
 
+
+def test_ste_backward_dw_split_tail():
+    """512 tokens, 2600 x 3328: 273 tiles of 128 x 256, so the last two row
+    tiles (rows 2432..2599) split their stages over two workgroups and a
+    third launch adds the partial tiles. Every element against an fp64
+    product of the same operands within the derived bound; rows on both
+    sides of the tail boundary through the oracle itself; three calls give
+    the same bits."""
+    M, N, K = 512, 2600, 3328
+    dy, xq, xs = _dw_case(M, N, K, 97)
+    args = (dev_bf16(dy), torch.from_numpy(xq).to(DEV), dev_f32(xs))
+    ws = bl.ste_dw_workspace(M, N, K, DEV)
+    assert ws.numel() == 4 * N * M + 2 * K * M + 2 * 256 * K * 4   # A, B, two partial tiles
+    dW = bl.ste_backward_dw(*args, workspace=ws)
+    got = dW.cpu().numpy().astype(np.float64)
+    a = wl.bf16_bits_to_f32(dy).astype(np.float64) * xs.astype(np.float64)[:, None]
+    ref = a.T @ xq.astype(np.float64)
+    bound = _dw_bound(dy, xq, xs)
+    assert (np.abs(got - ref) <= bound).all(), float((np.abs(got - ref) / bound).max())
+    ns = np.array([0, 1000, 2430, 2431, 2432, 2433, 2500, 2598, 2599])
+    ref_o = oracle.ste_dw(np.ascontiguousarray(dy[:, ns]), xq, xs).astype(np.float64)
+    assert (np.abs(got[ns] - ref_o) <= bound[ns]).all()
+    for _ in range(2):
+        again = bl.ste_backward_dw(*args, workspace=ws)
+        assert torch.equal(again.view(torch.int32), dW.view(torch.int32))
+
 def test_ste_pack_odd_n():
     rng = np.random.default_rng(91)
     q = rand_codes(rng, 37, 64)

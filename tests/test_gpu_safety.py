@@ -234,10 +234,12 @@ def test_ffn_step_guards_and_repeats(M):
 
 # ------------------------------------------------ straight-through backward ----
 
-# The last shape's dW takes two launches (273 tiles of 128 x 256: its last
-# two row tiles as 64 x 64 tiles).
+# The last two shapes' dW take more than one launch (273 tiles of 128 x 256):
+# at 33 tokens the last two row tiles run as 64 x 64 tiles, at 512 tokens
+# they split their 16 stages over two workgroups each, whose partial tiles
+# sit in the workspace until a third launch adds them.
 @pytest.mark.parametrize("M,N,K", [(3, 40, 128), (130, 264, 192), (257, 1000, 1344),
-                                   (33, 2600, 3328)])
+                                   (33, 2600, 3328), (512, 2600, 3328)])
 def test_ste_guards_and_repeats(M, N, K):
     rng = np.random.default_rng(66 + M)
     q = _codes(rng, N, K)
