@@ -98,7 +98,7 @@ PHASES = {
     "ste_dw_4096": (["ste_dw.hip", "common.hpp"],
                     "bl_ste_backward_dw at M=4096 on 2560->6912 and 6912->2560 "
                     "(dy bf16 [4096][N], x_q int8 [4096][K] -> dW fp32 [N][K])", 2,
-                    "bl_ste_backward_dw call (k_dw_prep_a, k_dw_prep_b, k_ste_dw)"),
+                    "bl_ste_backward_dw call (k_dw_prep_a, k_dw_prep_b, k_ste_dw, k_dw_reduce)"),
     "gemm_prefill_70b": (["gemm.hip", "common.hpp"],
                          "bl_bitlinear at M=2048 on 8192->28672 and 28672->8192", 2,
                          "bl_bitlinear call (k_gemm)"),
